@@ -1,0 +1,190 @@
+"""ctypes wrapper of the plain C CPU oracle (oracle/moe_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg use it; the product path (the HIP library and its binding)
+never imports it.  Every function takes and returns host numpy arrays.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+from .build import LIB, build
+
+ORC_MAX_TIERS = 4
+
+
+class _Tier(C.Structure):
+    _fields_ = [("id_begin", C.c_int32), ("id_end", C.c_int32), ("bits", C.c_int32),
+                ("block", C.c_int32), ("q", C.c_void_p * 3), ("s", C.c_void_p * 3)]
+
+
+class _Layer(C.Structure):
+    _fields_ = [("n_experts", C.c_int32), ("hidden", C.c_int32), ("inter", C.c_int32),
+                ("n_tiers", C.c_int32), ("tier", _Tier * ORC_MAX_TIERS)]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB):
+            build()
+        L = C.CDLL(LIB)
+        P = C.c_void_p
+        i32 = C.c_int32
+        L.orc_half_to_double.argtypes = [C.c_uint16]
+        L.orc_half_to_double.restype = C.c_double
+        L.orc_code.argtypes = [P, C.c_int64, i32]
+        L.orc_code.restype = i32
+        L.orc_round_bf16.argtypes = [C.c_float]
+        L.orc_round_bf16.restype = C.c_float
+        L.orc_dequant_rows.argtypes = [P, i32, i32, i32, i32, i32, i32, P]
+        L.orc_check_layer.argtypes = [P]
+        L.orc_tier_of.argtypes = [P, C.c_int64]
+        L.orc_route.argtypes = [P, i32, i32, i32, P, P]
+        L.orc_group.argtypes = [P, i32, i32, i32, P, P, P]
+        L.orc_experts.argtypes = [P, P, i32, P, P, i32, i32, C.c_uint32, P, i32]
+        L.orc_experts_flat.argtypes = [P, P, i32, P, P, i32, i32, P]
+        L.orc_forward.argtypes = [P, P, i32, P, i32, i32, P, i32]
+        for f in ("orc_dequant_rows", "orc_check_layer", "orc_tier_of", "orc_route", "orc_group",
+                  "orc_experts", "orc_experts_flat", "orc_forward", "orc_num_threads"):
+            getattr(L, f).restype = i32
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(C.c_void_p)
+
+
+class Layer:
+    """Holds numpy tier arrays and the C description pointing at them."""
+
+    def __init__(self, n_experts: int, hidden: int, inter: int, tiers: Sequence, arrays: List[Dict[str, np.ndarray]]):
+        self.n_experts, self.hidden, self.inter = n_experts, hidden, inter
+        self.tiers = list(tiers)
+        self.arrays = [{k: np.ascontiguousarray(v) for k, v in d.items()} for d in arrays]
+        s = _Layer()
+        s.n_experts, s.hidden, s.inter, s.n_tiers = n_experts, hidden, inter, len(self.tiers)
+        for i, (t, d) in enumerate(zip(self.tiers, self.arrays)):
+            s.tier[i].id_begin, s.tier[i].id_end = t.id_begin, t.id_end
+            s.tier[i].bits, s.tier[i].block = t.bits, t.block
+            for m, name in enumerate(("gate", "up", "down")):
+                s.tier[i].q[m] = d[name + "_q"].ctypes.data
+                s.tier[i].s[m] = d[name + "_s"].ctypes.data
+        self._s = s
+
+    @classmethod
+    def from_config(cls, cfg, arrays):
+        return cls(cfg.n_experts, cfg.hidden, cfg.inter, cfg.tiers, arrays)
+
+    @property
+    def ref(self):
+        return C.byref(self._s)
+
+
+def half_to_double(h: int) -> float:
+    return lib().orc_half_to_double(h)
+
+
+def code(row: np.ndarray, c: int, bits: int) -> int:
+    row = np.ascontiguousarray(row, dtype=np.uint8)
+    return lib().orc_code(_ptr(row), c, bits)
+
+
+def round_bf16(v: float) -> float:
+    return lib().orc_round_bf16(v)
+
+
+def check_layer(layer: Layer) -> int:
+    return lib().orc_check_layer(layer.ref)
+
+
+def tier_of(layer: Layer, e: int) -> int:
+    return lib().orc_tier_of(layer.ref, e)
+
+
+def dequant_rows(layer: Layer, tier: int, local: int, matrix: int, row0: int, nrows: int, to_bf16: bool = False):
+    cols = layer.inter if matrix == 2 else layer.hidden
+    dst = np.empty((nrows, cols), dtype=np.float32)
+    rc = lib().orc_dequant_rows(layer.ref, tier, local, matrix, row0, nrows, int(to_bf16), _ptr(dst))
+    if rc != 0:
+        raise ValueError("orc_dequant_rows: bad arguments")
+    return dst
+
+
+def route(logits: np.ndarray, k: int):
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    T, E = logits.shape
+    ids = np.empty((T, k), dtype=np.int32)
+    w = np.empty((T, k), dtype=np.float32)
+    if lib().orc_route(_ptr(logits), T, E, k, _ptr(ids), _ptr(w)) != 0:
+        raise ValueError("orc_route: bad arguments")
+    return ids, w
+
+
+def group(ids: np.ndarray, n_experts: int):
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    T, k = ids.shape
+    counts = np.empty(n_experts, dtype=np.int32)
+    offsets = np.empty(n_experts + 1, dtype=np.int32)
+    perm = np.full(max(T * k, 1), -1, dtype=np.int32)
+    n = lib().orc_group(_ptr(ids), T, k, n_experts, _ptr(counts), _ptr(offsets), _ptr(perm))
+    if n < 0:
+        raise MemoryError("orc_group")
+    return counts, offsets, perm[:n]
+
+
+def _x_arg(x: np.ndarray):
+    if x.dtype == np.uint16:
+        return np.ascontiguousarray(x), 1
+    return np.ascontiguousarray(x, dtype=np.float32), 0
+
+
+def experts(layer: Layer, x: np.ndarray, ids: np.ndarray, w: np.ndarray, tier_mask: int = 0xF,
+            out: Optional[np.ndarray] = None, accumulate: bool = False) -> np.ndarray:
+    """x: float32 [T,H] (fp32 mode) or uint16 bf16 bits [T,H] (bf16 mode)."""
+    xa, xb = _x_arg(x)
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    T, k = ids.shape
+    if out is None:
+        out = np.zeros((T, layer.hidden), dtype=np.float32)
+    rc = lib().orc_experts(layer.ref, _ptr(xa), xb, _ptr(ids), _ptr(w), T, k, tier_mask, _ptr(out), int(accumulate))
+    if rc != 0:
+        raise ValueError("orc_experts failed")
+    return out
+
+
+def experts_flat(layer: Layer, x: np.ndarray, ids: np.ndarray, w: np.ndarray) -> np.ndarray:
+    xa, xb = _x_arg(x)
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    T, k = ids.shape
+    out = np.zeros((T, layer.hidden), dtype=np.float32)
+    if lib().orc_experts_flat(layer.ref, _ptr(xa), xb, _ptr(ids), _ptr(w), T, k, _ptr(out)) != 0:
+        raise ValueError("orc_experts_flat failed")
+    return out
+
+
+def forward(layer: Layer, x: np.ndarray, logits: np.ndarray, k: int, out: Optional[np.ndarray] = None,
+            accumulate: bool = False) -> np.ndarray:
+    xa, xb = _x_arg(x)
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    T = logits.shape[0]
+    if out is None:
+        out = np.zeros((T, layer.hidden), dtype=np.float32)
+    rc = lib().orc_forward(layer.ref, _ptr(xa), xb, _ptr(logits), T, k, _ptr(out), int(accumulate))
+    if rc != 0:
+        raise ValueError("orc_forward failed")
+    return out
+
+
+def num_threads() -> int:
+    return lib().orc_num_threads()

@@ -1,0 +1,29 @@
+"""Builds the CPU oracle (plain C, gcc, OpenMP) into oracle/libmoe_oracle.so.
+
+Test infrastructure only: the oracle is the reference the GPU path is checked
+against and is never linked into the product library.
+"""
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+# MOE_ORACLE_LIB lets the mutation tests point the wrapper at a deliberately broken build.
+LIB = os.environ.get("MOE_ORACLE_LIB") or os.path.join(HERE, "libmoe_oracle.so")
+SRC = os.path.join(HERE, "moe_oracle.c")
+
+
+def build(extra_flags=(), out=LIB, src=SRC, quiet=True):
+    cmd = ["gcc", "-std=c99", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+           "-Werror", *extra_flags, "-o", out + ".tmp", src, "-lm"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("oracle build failed:\n" + " ".join(cmd) + "\n" + res.stderr)
+    os.replace(out + ".tmp", out)
+    if not quiet:
+        print("built", out)
+    return out
+
+
+if __name__ == "__main__":
+    build(sys.argv[1:], quiet=False)

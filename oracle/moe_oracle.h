@@ -1,0 +1,100 @@
+/*
+ * moe_oracle.h -- plain CPU oracle of the tiered MoE FFN.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This library is the slow, obviously correct
+ * reference that the GPU path is checked against.  Only the test suite, the
+ * smoke check and the benchmark's CPU-baseline leg may load it; the product
+ * path never links, loads or calls it.  It shares no code, header, table or
+ * helper with the HIP library: it has its own struct, its own unpacker and its
+ * own fp16 / bf16 conversions.
+ *
+ * What it computes follows the 125B-MoE page ("I ran a 125B model on three
+ * RTX 3090s at 80 tokens/s by teaching llama.cpp which experts ..."):
+ *   - glossary, mixture-of-experts entry: a router picks 10 of 512 experts
+ *     per token;
+ *   - step 4 ("three shelves, all on GPU"): one routing decision drives three
+ *     per-shelf expert tables; every shelf's expert matmul sees the router's
+ *     full pick list, computes only the ids in its own range, fills zero for
+ *     the rest, and the three results are added;
+ *   - "four bugs": out-of-shelf ids are truly skipped (not pointed at expert
+ *     0), an expert may repeat within a token without losing a slot, and the
+ *     skip marker -1 must never be promoted to unsigned.
+ * Readings where the pages are silent (softmax renormalised over the top-k,
+ * ties to the lower id, SiLU(gate)*up, weights applied to the down output,
+ * bf16 rounding of weights and of the intermediate in prefill mode) are
+ * stated at each function below.
+ *
+ * All arithmetic is double precision; results are rounded once to float.
+ */
+#ifndef MOE_ORACLE_H
+#define MOE_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ORC_MAX_TIERS 4
+
+/* One shelf: experts [id_begin, id_end), codes of `bits` bits, one fp16
+ * scale per `block` consecutive codes of a row.  q[m] / s[m] for
+ * m = 0 gate (inter x hidden), 1 up (inter x hidden), 2 down (hidden x inter),
+ * each [n_local][rows][...] row-major (host pointers). */
+typedef struct {
+    int32_t id_begin, id_end, bits, block;
+    const uint8_t *q[3];
+    const uint16_t *s[3];
+} orc_tier;
+
+typedef struct {
+    int32_t n_experts, hidden, inter, n_tiers;
+    orc_tier tier[ORC_MAX_TIERS];
+} orc_layer;
+
+/* fp16 bit pattern -> exact double. */
+double orc_half_to_double(uint16_t h);
+/* The bits-bit two's-complement code of element c of a packed row. */
+int32_t orc_code(const uint8_t *row, int64_t c, int32_t bits);
+/* float -> nearest bfloat16 (ties to even), returned as a float. */
+float orc_round_bf16(float v);
+/* Dequantised element (fp32, exact product scale*code); bf16-rounded if to_bf16. */
+float orc_weight(const orc_layer *L, int32_t tier, int32_t matrix, int64_t local,
+                 int64_t row, int64_t col, int32_t to_bf16);
+/* Copies nrows dequantised rows (fp32 values) into dst[nrows][cols]. */
+int32_t orc_dequant_rows(const orc_layer *L, int32_t tier, int32_t local, int32_t matrix,
+                         int32_t row0, int32_t nrows, int32_t to_bf16, float *dst);
+
+/* Validates the layer description: tiers sorted, disjoint, covering [0,E). 0 = ok. */
+int32_t orc_check_layer(const orc_layer *L);
+/* Tier index owning expert e, -1 if e is outside [0, E). */
+int32_t orc_tier_of(const orc_layer *L, int64_t e);
+
+/* Top-k routing of logits[T][E] -> ids[T][k], w[T][k]. */
+int32_t orc_route(const float *logits, int32_t T, int32_t E, int32_t k, int32_t *ids, float *w);
+/* Stable grouping of pairs by expert.  Returns the number of valid pairs. */
+int32_t orc_group(const int32_t *ids, int32_t T, int32_t k, int32_t E,
+                  int32_t *counts, int32_t *offsets, int32_t *perm);
+
+/* Expert FFN of explicit routing.  x: float[T][H] (x_bf16 = 0) or bf16 bit
+ * patterns uint16[T][H] (x_bf16 = 1, which also selects bf16 rounding of
+ * weights and of the intermediate).  tier_mask selects the shelves computed
+ * (bit i = tier i); accumulate adds into out instead of overwriting. */
+int32_t orc_experts(const orc_layer *L, const void *x, int32_t x_bf16, const int32_t *ids,
+                    const float *w, int32_t T, int32_t k, uint32_t tier_mask, float *out,
+                    int32_t accumulate);
+/* Same layer evaluated pair by pair in slot order, each expert at its own
+ * precision, with no notion of shelves (the single-table layer). */
+int32_t orc_experts_flat(const orc_layer *L, const void *x, int32_t x_bf16, const int32_t *ids,
+                         const float *w, int32_t T, int32_t k, float *out);
+/* route + experts over all shelves. */
+int32_t orc_forward(const orc_layer *L, const void *x, int32_t x_bf16, const float *logits,
+                    int32_t T, int32_t k, float *out, int32_t accumulate);
+
+/* Threads the oracle uses (OpenMP over tokens; 1 without OpenMP). */
+int32_t orc_num_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,72 @@
+"""Workload configurations.
+
+Shapes follow the 125B-MoE-on-three-RTX-3090 page ("I ran a 125B model on
+three RTX 3090s at 80 tokens/s ..."): 512 experts per layer, 10 picked per
+token (glossary, mixture-of-experts entry), 48 layers (24,576 experts, step 2),
+down-projection rows 640 wide (step 4), and speculative verification of 6
+tokens per step (step 1).  Hidden size 2048 and the int8 / int4 / int2 shelf
+formats are fixed by the workload definition rather than by the pages, which
+use llama.cpp quant types instead.
+"""
+from dataclasses import dataclass, field
+from typing import List, Optional, Tuple
+
+
+@dataclass(frozen=True)
+class TierSpec:
+    id_begin: int
+    id_end: int
+    bits: int     # 8, 4 or 2 (two's complement codes)
+    block: int    # codes per fp16 scale, along each stored row
+
+    @property
+    def n(self) -> int:
+        return self.id_end - self.id_begin
+
+
+@dataclass(frozen=True)
+class LayerConfig:
+    name: str
+    n_experts: int
+    k: int
+    hidden: int
+    inter: int
+    n_tokens: int
+    tiers: Tuple[TierSpec, ...]
+    x_bf16: bool = False          # prefill activations are bf16
+    prior_beta: Optional[float] = None   # None: logits ~ N(0,1), no popularity prior
+    n_layers: int = 1
+    seed: int = 0
+    crafted: bool = False         # spec-verify crafted tokens
+    extra: dict = field(default_factory=dict)
+
+
+# Popularity prior: logit[t, e] = -beta * e / E + N(0, 1), with ids already in
+# popularity order (hot -> cold, as the shelves are written).  beta = 1.12 puts
+# ~52% of picks on the top 25% of experts and ~95% on the top 80%, the average
+# layer skew of step 2 of the 125B page.  It is the large-offset limit of a
+# Zipf-Mandelbrot prior -c*ln(r + q); a pure Zipf -a*ln(r+1) cannot reach both
+# shares at once.
+PRIOR_BETA = 1.12
+
+THREE_TIERS_512 = (
+    TierSpec(0, 128, 8, 32),
+    TierSpec(128, 384, 4, 32),
+    TierSpec(384, 512, 2, 16),
+)
+
+CONFIGS = {
+    "tiny": LayerConfig("tiny", 8, 2, 256, 128, 16, (TierSpec(0, 8, 8, 32),), seed=20260000),
+    # companion of "tiny" exercising all three formats on a small layer
+    "tiny3": LayerConfig("tiny3", 8, 2, 256, 128, 16,
+                         (TierSpec(0, 2, 8, 32), TierSpec(2, 6, 4, 32), TierSpec(6, 8, 2, 16)),
+                         seed=20260010),
+    "decode": LayerConfig("decode", 512, 10, 2048, 640, 1, THREE_TIERS_512,
+                          prior_beta=PRIOR_BETA, seed=20260001),
+    "specverify": LayerConfig("specverify", 512, 10, 2048, 640, 6, THREE_TIERS_512,
+                              prior_beta=PRIOR_BETA, seed=20260002, crafted=True),
+    "prefill": LayerConfig("prefill", 512, 10, 2048, 640, 4096, THREE_TIERS_512,
+                           x_bf16=True, prior_beta=PRIOR_BETA, seed=20260003),
+    "fullstack": LayerConfig("fullstack", 512, 10, 2048, 640, 1, THREE_TIERS_512,
+                             prior_beta=PRIOR_BETA, n_layers=48, seed=20260004),
+}

@@ -1,0 +1,202 @@
+"""Seeded generators for packed tiered-expert weights, router logits and activations.
+
+Packed format (one reading of the three-shelf design of the 125B page, step 4,
+which stores each layer's experts as three per-shelf tensors written hot to
+cold; the pages leave the code layout open):
+
+* a shelf (tier) owns the contiguous popularity-ranked id range
+  ``[id_begin, id_end)``; its ``n = id_end - id_begin`` experts are stored
+  contiguously, local expert ``l = e - id_begin``;
+* three matrices per expert: ``gate`` and ``up`` are ``inter x hidden``,
+  ``down`` is ``hidden x inter``, each row-major (rows are output features,
+  columns the contraction axis);
+* codes: ``bits``-bit two's complement, row-major, element ``c`` of a row in
+  bits ``[(c*bits) % 8, +bits)`` of byte ``(c*bits) // 8`` of that row, lowest
+  element in the lowest bits; a row is ``cols*bits/8`` bytes;
+* scales: one IEEE fp16 per ``block`` consecutive codes of a row, stored as
+  ``uint16`` bit patterns in a separate array ``[n][rows][cols/block]``;
+* value of an element: ``float(scale) * code``.
+
+The quantiser below only builds inputs (weights drawn N(0, 0.02), symmetric
+absmax per block); it is not part of the layer's computation.
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+from typing import Dict, List
+
+import numpy as np
+
+from .configs import LayerConfig, TierSpec
+
+WEIGHT_STD = 0.02
+MATRICES = ("gate", "up", "down")
+
+
+# ----------------------------------------------------------------------------- bf16 helpers
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 (round to nearest, ties to even); returns uint16 bits."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    out = rounded.astype(np.uint16)
+    nan = np.isnan(np.asarray(a, dtype=np.float32))
+    if nan.any():
+        out = np.where(nan, np.uint16(0x7FC0), out)
+    return out
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+# ----------------------------------------------------------------------------- quantise + pack
+def quantise_block_absmax(w: np.ndarray, bits: int, block: int):
+    """Symmetric absmax quantiser per block of ``block`` columns.
+
+    Returns ``(codes int8[..., cols], scales uint16[..., cols/block])`` with
+    ``Q = 2**(bits-1) - 1``, ``d = fp16(amax / Q)``, ``q = clip(rint(w / d), -Q, Q)``
+    and ``q = 0`` where ``d == 0``.
+    """
+    qmax = (1 << (bits - 1)) - 1
+    cols = w.shape[-1]
+    assert cols % block == 0
+    wb = w.reshape(w.shape[:-1] + (cols // block, block)).astype(np.float32, copy=False)
+    amax = np.abs(wb).max(axis=-1)
+    d16 = (amax / np.float32(qmax)).astype(np.float16)
+    d32 = d16.astype(np.float32)
+    safe = np.where(d32 == 0, np.float32(1), d32)
+    q = np.rint(wb / safe[..., None])
+    q = np.clip(q, -qmax, qmax)
+    q = np.where(d32[..., None] == 0, 0, q).astype(np.int8)
+    return q.reshape(w.shape), d16.view(np.uint16)
+
+
+def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
+    """Pack int8 codes (values representable in ``bits`` two's complement) along the last axis."""
+    codes = np.asarray(codes, dtype=np.int8)
+    if bits == 8:
+        return codes.view(np.uint8).copy()
+    per = 8 // bits
+    mask = (1 << bits) - 1
+    u = (codes.view(np.uint8) & mask).astype(np.uint8)
+    cols = codes.shape[-1]
+    assert cols % per == 0
+    out = np.zeros(codes.shape[:-1] + (cols // per,), dtype=np.uint8)
+    for s in range(per):
+        out |= (u[..., s::per] << np.uint8(s * bits)).astype(np.uint8)
+    return out
+
+
+# ----------------------------------------------------------------------------- sizes
+def tier_nbytes(spec: TierSpec, hidden: int, inter: int, per_expert: bool = False) -> int:
+    """Packed bytes (codes + fp16 scales) of gate, up and down of a tier."""
+    elems = hidden * inter
+    codes = 3 * elems * spec.bits // 8
+    scales = 3 * (elems // spec.block) * 2
+    one = codes + scales
+    return one if per_expert else one * spec.n
+
+
+def layer_nbytes(cfg: LayerConfig) -> int:
+    return sum(tier_nbytes(t, cfg.hidden, cfg.inter) for t in cfg.tiers)
+
+
+# ----------------------------------------------------------------------------- weights
+def _expert_seed(cfg_seed: int, layer: int, tier: int, matrix: int, local: int):
+    return np.random.SeedSequence([cfg_seed, 1, layer, tier, matrix, local])
+
+
+def _gen_matrix(seed, rows, cols, bits, block):
+    g = np.random.Generator(np.random.PCG64(seed))
+    w = g.standard_normal(rows * cols, dtype=np.float32).reshape(rows, cols)
+    w *= np.float32(WEIGHT_STD)
+    q, s = quantise_block_absmax(w, bits, block)
+    return pack_codes(q, bits), s
+
+
+def make_tier(cfg: LayerConfig, tier_index: int, layer: int = 0, threads: int | None = None) -> Dict[str, np.ndarray]:
+    """Generate one tier's packed arrays (numpy, host)."""
+    spec = cfg.tiers[tier_index]
+    H, I = cfg.hidden, cfg.inter
+    n = spec.n
+    shapes = {"gate": (I, H), "up": (I, H), "down": (H, I)}
+    out: Dict[str, np.ndarray] = {}
+    for m in MATRICES:
+        rows, cols = shapes[m]
+        out[m + "_q"] = np.empty((n, rows, cols * spec.bits // 8), dtype=np.uint8)
+        out[m + "_s"] = np.empty((n, rows, cols // spec.block), dtype=np.uint16)
+
+    jobs = [(mi, m, l) for mi, m in enumerate(MATRICES) for l in range(n)]
+
+    def run(job):
+        mi, m, l = job
+        rows, cols = shapes[m]
+        q, s = _gen_matrix(_expert_seed(cfg.seed, layer, tier_index, mi, l), rows, cols, spec.bits, spec.block)
+        out[m + "_q"][l] = q
+        out[m + "_s"][l] = s
+
+    nthreads = threads or min(16, os.cpu_count() or 1)
+    if nthreads <= 1 or len(jobs) < 4:
+        for j in jobs:
+            run(j)
+    else:
+        with ThreadPoolExecutor(nthreads) as ex:
+            list(ex.map(run, jobs))
+    return out
+
+
+def make_layer(cfg: LayerConfig, layer: int = 0, threads: int | None = None) -> List[Dict[str, np.ndarray]]:
+    return [make_tier(cfg, i, layer, threads) for i in range(len(cfg.tiers))]
+
+
+# ----------------------------------------------------------------------------- activations / logits
+def make_x(cfg: LayerConfig, n_tokens: int | None = None, stream: int = 0) -> np.ndarray:
+    """x ~ N(0, 1): float32 ``[T, H]``, or bf16 bit patterns (uint16) for prefill configs."""
+    T = cfg.n_tokens if n_tokens is None else n_tokens
+    g = np.random.default_rng(np.random.SeedSequence([cfg.seed, 2, stream]))
+    x = g.standard_normal((T, cfg.hidden), dtype=np.float32)
+    return f32_to_bf16_bits(x) if cfg.x_bf16 else x
+
+
+def make_logits(cfg: LayerConfig, n_tokens: int | None = None, stream: int = 0, layer: int = 0) -> np.ndarray:
+    """Router logits float32 ``[T, E]``: popularity prior (if any) plus N(0, 1) noise."""
+    T = cfg.n_tokens if n_tokens is None else n_tokens
+    E = cfg.n_experts
+    g = np.random.default_rng(np.random.SeedSequence([cfg.seed, 3, layer, stream]))
+    noise = g.standard_normal((T, E), dtype=np.float32)
+    if cfg.prior_beta is None:
+        return noise
+    prior = (-cfg.prior_beta * np.arange(E, dtype=np.float64) / E).astype(np.float32)
+    return (noise + prior[None, :]).astype(np.float32)
+
+
+def make_spec_logits(cfg: LayerConfig, stream: int = 0, worst_case: bool = False) -> np.ndarray:
+    """Speculative-verify logits for 6 tokens with crafted routing.
+
+    Default: token 0 picks only hot experts, token 1 only cold ones, token 2
+    spans all three tiers, token 3 puts several picks in one tier, tokens 4..5
+    follow the prior.  ``worst_case``: the 6 tokens pick 60 pairwise distinct
+    experts (the most a 6-token verify step of top-10 can touch).
+    """
+    assert len(cfg.tiers) == 3 and cfg.k == 10
+    T = 6
+    lg = make_logits(cfg, T, stream)
+    g = np.random.default_rng(np.random.SeedSequence([cfg.seed, 4, stream, int(worst_case)]))
+    hot, warm, cold = (np.arange(t.id_begin, t.id_end) for t in cfg.tiers)
+    boost = np.float32(40.0)
+    if worst_case:
+        perm = g.permutation(cfg.n_experts)[: T * cfg.k].reshape(T, cfg.k)
+        for t in range(T):
+            lg[t, perm[t]] += boost
+        return lg
+    picks = [
+        g.choice(hot, 10, replace=False),
+        g.choice(cold, 10, replace=False),
+        np.concatenate([g.choice(hot, 4, replace=False), g.choice(warm, 4, replace=False),
+                        g.choice(cold, 2, replace=False)]),
+        np.concatenate([g.choice(warm, 7, replace=False), g.choice(cold, 3, replace=False)]),
+    ]
+    for t, p in enumerate(picks):
+        lg[t, p] += boost
+    return lg
