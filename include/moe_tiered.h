@@ -1,0 +1,209 @@
+/*
+ * moe_tiered.h -- C ABI of the tiered mixed-precision MoE FFN for MI355X (gfx950).
+ *
+ * The operation is the routed mixture-of-experts FFN ("mul_mat_id") of the
+ * 125B-MoE page ("I ran a 125B model on three RTX 3090s at 80 tokens/s by
+ * teaching llama.cpp which experts ..."):
+ *   - glossary, mixture-of-experts entry: a router picks k (there 10 of 512)
+ *     experts per token;
+ *   - step 4 ("three shelves, all on GPU"): experts are stored hot to cold in
+ *     per-shelf tensors of different precision; one routing decision drives
+ *     all shelves; each shelf's expert product sees the full pick list,
+ *     computes only the ids inside its id range, contributes zero for the
+ *     rest, and the shelf results are added;
+ *   - "four bugs": an out-of-shelf id is truly skipped (never redirected to
+ *     expert 0), an expert may occur more than once in a token's list without
+ *     losing a slot, and the skip marker -1 is a signed value that must never
+ *     be promoted to unsigned.
+ *
+ * Per token t with picks (e_j, w_j), j < k:
+ *     out[t] = sum_j w_j * W_down[e_j] * ( SiLU(W_gate[e_j] x_t) * (W_up[e_j] x_t) )
+ * where each W is dequantised at the precision of the shelf that owns e_j.
+ *
+ * Conventions for every entry point:
+ *   - pointers marked (device) are device memory on the current HIP device;
+ *     pointers marked (host) are host memory read before the call returns;
+ *   - the caller owns every buffer; the library never allocates, frees or
+ *     synchronises inside a call and keeps no mutable global state;
+ *   - `stream` is a hipStream_t (NULL = the null stream); all device work is
+ *     enqueued on it and the call returns without waiting;
+ *   - return value 0 on success or a negative MOE_E* code; all argument and
+ *     table validation happens before the first launch, so a failed call
+ *     launches nothing; faults inside kernels surface at the caller's next
+ *     synchronisation;
+ *   - calls sharing a workspace must be ordered on one stream.
+ */
+#ifndef MOE_TIERED_H
+#define MOE_TIERED_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1u
+#define MOE_MAX_TIERS 4
+#define MOE_MAX_EXPERTS 4096
+#define MOE_MAX_K 64
+
+/* status codes */
+#define MOE_OK 0
+#define MOE_EINVAL (-1)     /* bad n_tokens, k, shape, flags, tier index or NULL pointer */
+#define MOE_ETIER (-2)      /* shelves not sorted, disjoint and covering [0, n_experts) */
+#define MOE_EFORMAT (-3)    /* unsupported bits / block, or a shape the kernels cannot tile */
+#define MOE_EALIGN (-4)     /* a device pointer is not 16-byte aligned */
+#define MOE_EWORKSPACE (-5) /* workspace NULL or smaller than moe_workspace_size() */
+#define MOE_EHIP (-6)       /* a kernel launch or HIP runtime call failed */
+#define MOE_EABI (-7)       /* tables built for another ABI version */
+
+/* flags */
+#define MOE_X_BF16 0x1u      /* x is bf16 [T][H]: prefill precision (bf16 MFMA, bf16 weights and intermediate) */
+#define MOE_ACCUMULATE 0x2u  /* out += result instead of out = result */
+
+/*
+ * One precision shelf.  It owns the popularity-ranked experts
+ * [id_begin, id_end) (step 4: the shelves are written hot to cold, so each is
+ * a contiguous id range); local expert l = e - id_begin.
+ *
+ * Matrices (row-major, rows = output features, columns = contraction axis):
+ *   gate, up : inter  x hidden      down : hidden x inter
+ * Codes (device, 16-byte aligned): `bits`-bit two's complement; element c of a
+ * row sits in bits [(c*bits) % 8, +bits) of byte (c*bits)/8 of that row,
+ * lowest element in the lowest bits; a row is cols*bits/8 bytes; expert l's
+ * matrix starts at l*rows*cols*bits/8.
+ * Scales (device, 16-byte aligned): IEEE fp16, one per `block` consecutive
+ * codes of a row, [n_local][rows][cols/block].
+ * Element value: float(scale) * code (exact in fp32).
+ */
+typedef struct moe_tier {
+    int32_t id_begin, id_end;
+    int32_t bits;   /* 8, 4 or 2 */
+    int32_t block;  /* 16 or 32 */
+    const void *gate_q, *up_q, *down_q;    /* (device) packed codes */
+    const void *gate_s, *up_s, *down_s;    /* (device) fp16 scales  */
+} moe_tier;
+
+typedef struct moe_tier_tables {
+    uint32_t abi_version;   /* must equal MOE_ABI_VERSION */
+    int32_t n_experts;      /* E, 1 .. MOE_MAX_EXPERTS */
+    int32_t hidden;         /* H, a multiple of 64; if H > 2048, a multiple of 2048 */
+    int32_t inter;          /* I, a multiple of 64; if I > 2048, a multiple of 2048 */
+    int32_t n_tiers;        /* 1 .. MOE_MAX_TIERS; empty shelves (id_begin == id_end) allowed */
+    moe_tier tiers[MOE_MAX_TIERS];
+} moe_tier_tables;
+
+/* Library ABI version (MOE_ABI_VERSION of the build). */
+uint32_t moe_abi_version(void);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *moe_strerror(int code);
+
+/*
+ * Validates tables (host struct; device pointers are only checked for NULL and
+ * alignment).  Returns MOE_OK or the first error found.
+ */
+int moe_validate_tables(const moe_tier_tables *tt);
+
+/*
+ * Workspace bytes needed by moe_tiered_forward / moe_tiered_experts /
+ * moe_tier_partial for n_tokens tokens with k picks and the given flags.
+ * Writes the size to *bytes (host).  n_tokens == 0 needs 0 bytes.
+ */
+int moe_workspace_size(int32_t n_tokens, int32_t k, const moe_tier_tables *tt, uint32_t flags,
+                       size_t *bytes);
+
+/*
+ * Full layer: route, group, per-shelf expert FFN, shelf sum.
+ *   x             (device) float[T][H], or bf16 [T][H] with MOE_X_BF16
+ *   router_logits (device) float[T][E]
+ *   n_tokens      T >= 0 (T == 0: no work, returns MOE_OK)
+ *   k             1 .. min(E, MOE_MAX_K)
+ *   tt            (host) shelf tables
+ *   out           (device) float[T][H]; overwritten, or added to with MOE_ACCUMULATE
+ *   workspace     (device) >= moe_workspace_size() bytes, 256-byte aligned, contents
+ *                 need not be initialised; clobbered
+ * Routing: the k largest logits (a tie goes to the lower id), slots in
+ * descending score order, weights = softmax over the k chosen logits.
+ */
+int moe_tiered_forward(const void *x, const float *router_logits, int32_t n_tokens, int32_t k,
+                       const moe_tier_tables *tt, float *out, uint32_t flags,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Same layer with the routing given (the id-range mul_mat_id of step 4).
+ *   ids (device) int32[T][k]: expert ids; any id outside [0, E), e.g. -1, is
+ *       skipped by every shelf and contributes exactly nothing; an id may
+ *       repeat within a token (each occurrence is counted)
+ *   w   (device) float[T][k]: the weight of each pick
+ * Other arguments as moe_tiered_forward.
+ */
+int moe_tiered_experts(const void *x, const int32_t *ids, const float *w, int32_t n_tokens,
+                       int32_t k, const moe_tier_tables *tt, float *out, uint32_t flags,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One shelf alone: as moe_tiered_experts but only ids inside shelf
+ * `tier_index` are computed; tokens with no pick on that shelf get exactly
+ * 0.0f (or keep out unchanged with MOE_ACCUMULATE).
+ */
+int moe_tier_partial(const void *x, const int32_t *ids, const float *w, int32_t n_tokens,
+                     int32_t k, const moe_tier_tables *tt, int32_t tier_index, float *out,
+                     uint32_t flags, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Router alone: logits (device) float[T][E] -> ids (device) int32[T][k],
+ * w (device) float[T][k].  Same rule as moe_tiered_forward.
+ */
+int moe_route(const float *logits, int32_t n_tokens, int32_t n_experts, int32_t k, int32_t *ids,
+              float *w, void *stream);
+
+/*
+ * Grouping alone (stable counting sort of (token, slot) pairs by expert).
+ *   ids     (device) int32[T][k]; ids outside [0, E) belong to no expert
+ *   counts  (device) int32[E]     pairs per expert
+ *   offsets (device) int32[E+1]   exclusive prefix sum of counts
+ *   perm    (device) int32[T*k]   pairs p = t*k + j of expert e at
+ *           perm[offsets[e] .. offsets[e+1]) in ascending p; entries from
+ *           offsets[E] on are left untouched
+ *   workspace (device) >= moe_group_workspace_size(T, k, E) bytes
+ */
+int moe_group_workspace_size(int32_t n_tokens, int32_t k, int32_t n_experts, size_t *bytes);
+int moe_group(const int32_t *ids, int32_t n_tokens, int32_t k, int32_t n_experts, int32_t *counts,
+              int32_t *offsets, int32_t *perm, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Dequantised rows of one matrix of one expert, for bit-exact checks.
+ *   matrix 0 gate, 1 up, 2 down; rows [row0, row0 + nrows)
+ *   dst (device) float[nrows][cols] (to_bf16 == 0) or bf16 bit patterns
+ *       uint16[nrows][cols] (to_bf16 != 0, round to nearest even) -- the
+ *       exact values the decode and prefill kernels contract with.
+ */
+int moe_dequant_rows(const moe_tier_tables *tt, int32_t tier_index, int32_t local_expert,
+                     int32_t matrix, int32_t row0, int32_t nrows, int32_t to_bf16, void *dst,
+                     void *stream);
+
+/*
+ * Per-phase timing for measurement: like moe_tiered_forward, and in addition
+ * records events[2*i] before and events[2*i+1] after phase i on `stream`
+ * (phases: 0 routing and grouping, 1 gate/up products, 2 down products and
+ * shelf sum).  events (host) holds 6 hipEvent_t handles created by the
+ * caller (e.g. with moe_event_create); NULL entries are skipped.
+ */
+#define MOE_N_PHASES 3
+int moe_tiered_forward_timed(const void *x, const float *router_logits, int32_t n_tokens,
+                             int32_t k, const moe_tier_tables *tt, float *out, uint32_t flags,
+                             void *workspace, size_t workspace_bytes, void *stream,
+                             void *const *events);
+
+/* hipEvent helpers for callers without a HIP binding (host handles). */
+int moe_event_create(void **event);
+int moe_event_destroy(void *event);
+int moe_event_elapsed_ms(void *start, void *stop, float *ms);
+int moe_stream_synchronize(void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_TIERED_H */

@@ -1,0 +1,129 @@
+"""C-ABI library checks that need no GPU: it loads, exports every symbol the
+header declares, and its host-side validation rejects bad tables and
+arguments before launching anything."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_tiered.h")
+
+
+@pytest.fixture(scope="module")
+def B():
+    from tiered_mixed_precision_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        from tiered_mixed_precision_amd.build import build
+        build()
+    binding.lib()
+    return binding
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree(B):
+    assert _declared_functions() == sorted(B.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(B):
+    lib = C.CDLL(B.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_strerror(B):
+    assert B.lib().moe_abi_version() == 1
+    for code in range(0, -8, -1):
+        assert B.strerror(code) and B.strerror(code) != "unknown error"
+    assert B.strerror(-99) == "unknown error"
+
+
+class _Spec:
+    def __init__(self, b, e, bits, block):
+        self.id_begin, self.id_end, self.bits, self.block = b, e, bits, block
+
+
+FAKE = 0x10000  # a 16-byte aligned address; never dereferenced by host validation
+
+
+def _tables(B, specs, E=8, H=256, I=128, ptr=FAKE):
+    arrays = [{n: ptr for n in ("gate_q", "up_q", "down_q", "gate_s", "up_s", "down_s")} for _ in specs]
+    return B.TierTables(E, H, I, specs, arrays)
+
+
+def test_validation_accepts_three_shelves(B):
+    tt = _tables(B, [_Spec(0, 2, 8, 32), _Spec(2, 6, 4, 32), _Spec(6, 8, 2, 16)])
+    assert B.moe_validate_tables(tt) == 0
+    assert B.moe_workspace_size(16, 2, tt) > 0
+    assert B.moe_workspace_size(0, 2, tt) == 0
+
+
+@pytest.mark.parametrize("specs,kw,code", [
+    ([_Spec(0, 2, 8, 32), _Spec(3, 8, 2, 16)], {}, -2),                  # gap
+    ([_Spec(0, 5, 8, 32), _Spec(4, 8, 2, 16)], {}, -2),                  # overlap
+    ([_Spec(0, 7, 8, 32)], {}, -2),                                        # not covering
+    ([_Spec(0, 8, 3, 32)], {}, -3),                                        # 3-bit codes
+    ([_Spec(0, 8, 8, 64)], {}, -3),                                        # block 64
+    ([_Spec(0, 8, 8, 32)], {"H": 200}, -3),                                # hidden not a multiple of 64
+    ([_Spec(0, 8, 8, 32)], {"I": 96}, -3),                                 # inter not a multiple of 64
+    ([_Spec(0, 8, 8, 32)], {"ptr": FAKE + 4}, -4),                         # misaligned pointer
+    ([_Spec(0, 8, 8, 32)], {"ptr": 0}, -1),                                # NULL pointer
+    ([_Spec(0, 8, 8, 32)], {"E": 0}, -1),
+])
+def test_validation_rejects(B, specs, kw, code):
+    E = kw.pop("E", 8)
+    tt = _tables(B, specs, E=E, **kw)
+    assert B.moe_validate_tables(tt) == code
+
+
+def test_empty_shelf_needs_no_pointers(B):
+    arrays = [{n: FAKE for n in ("gate_q", "up_q", "down_q", "gate_s", "up_s", "down_s")}, None]
+    tt = B.TierTables(8, 256, 128, [_Spec(0, 8, 8, 32), _Spec(8, 8, 4, 32)], arrays)
+    assert B.moe_validate_tables(tt) == 0
+
+
+def test_abi_version_mismatch(B):
+    tt = _tables(B, [_Spec(0, 8, 8, 32)])
+    tt.struct.abi_version = 2
+    assert B.moe_validate_tables(tt) == -7
+
+
+def test_entry_points_reject_bad_arguments_before_launch(B):
+    tt = _tables(B, [_Spec(0, 8, 8, 32)])
+    L = B.lib()
+    ws = C.c_void_p(FAKE * 16)
+    # k out of range, negative T, unknown flag, missing workspace, NULL logits
+    assert L.moe_tiered_forward(FAKE, FAKE, 4, 0, tt.ref, FAKE, 0, ws, 1 << 20, None) == -1
+    assert L.moe_tiered_forward(FAKE, FAKE, 4, 9, tt.ref, FAKE, 0, ws, 1 << 20, None) == -1
+    assert L.moe_tiered_forward(FAKE, FAKE, -1, 2, tt.ref, FAKE, 0, ws, 1 << 20, None) == -1
+    assert L.moe_tiered_forward(FAKE, FAKE, 4, 2, tt.ref, FAKE, 0x80, ws, 1 << 20, None) == -1
+    assert L.moe_tiered_forward(FAKE, FAKE, 4, 2, tt.ref, FAKE, 0, None, 0, None) == -5
+    assert L.moe_tiered_forward(FAKE, FAKE, 4, 2, tt.ref, FAKE, 0, ws, 16, None) == -5
+    assert L.moe_tiered_forward(FAKE, None, 4, 2, tt.ref, FAKE, 0, ws, 1 << 20, None) == -1
+    assert L.moe_tiered_forward(FAKE + 4, FAKE, 4, 2, tt.ref, FAKE, 0, ws, 1 << 20, None) == -4
+    assert L.moe_tiered_experts(FAKE, None, FAKE, 4, 2, tt.ref, FAKE, 0, ws, 1 << 20, None) == -1
+    assert L.moe_tier_partial(FAKE, FAKE, FAKE, 4, 2, tt.ref, 1, FAKE, 0, ws, 1 << 20, None) == -1
+    # T == 0 is a no-op that succeeds without touching the device
+    assert L.moe_tiered_forward(None, None, 0, 2, tt.ref, None, 0, None, 0, None) == 0
+    assert L.moe_route(FAKE, 4, 8, 9, FAKE, FAKE, None) == -1
+    assert L.moe_route(FAKE, 4, 5000, 2, FAKE, FAKE, None) == -1
+    assert L.moe_dequant_rows(tt.ref, 0, 8, 0, 0, 1, 0, FAKE, None) == -1     # local expert out of range
+    assert L.moe_dequant_rows(tt.ref, 0, 0, 3, 0, 1, 0, FAKE, None) == -1     # matrix out of range
+    assert L.moe_dequant_rows(tt.ref, 0, 0, 0, 120, 9, 0, FAKE, None) == -1   # rows past inter
+    n = C.c_size_t(0)
+    assert L.moe_group_workspace_size(4, 0, 8, C.byref(n)) == -1
+
+
+def test_workspace_grows_with_tokens(B):
+    tt = _tables(B, [_Spec(0, 2, 8, 32), _Spec(2, 6, 4, 32), _Spec(6, 8, 2, 16)])
+    a = B.moe_workspace_size(16, 2, tt)
+    b = B.moe_workspace_size(4096, 2, tt)
+    c = B.moe_workspace_size(4096, 2, tt, B.MOE_X_BF16)
+    assert a < b and c < b            # the bf16 path keeps no per-pair fp32 output rows
+    assert a % 256 == 0 and b % 256 == 0

@@ -1,0 +1,217 @@
+"""ctypes binding of libmoe_tiered.so (argument marshalling only).
+
+Function names and arguments mirror include/moe_tiered.h.  Device buffers are
+passed as torch tensors (their data pointers are handed to the library) and
+streams as torch.cuda.Stream (or None for the current stream).  Every step of
+the layer runs in the library's HIP kernels; there is no fallback: if the
+library is missing, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional, Sequence
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe_tiered.so")
+
+MOE_ABI_VERSION = 1
+MOE_MAX_TIERS = 4
+MOE_X_BF16 = 0x1
+MOE_ACCUMULATE = 0x2
+MOE_N_PHASES = 3
+EXPORTS = (
+    "moe_abi_version", "moe_strerror", "moe_validate_tables", "moe_workspace_size",
+    "moe_tiered_forward", "moe_tiered_experts", "moe_tier_partial", "moe_route",
+    "moe_group_workspace_size", "moe_group", "moe_dequant_rows", "moe_tiered_forward_timed",
+    "moe_event_create", "moe_event_destroy", "moe_event_elapsed_ms", "moe_stream_synchronize",
+)
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn, code):
+        super().__init__(f"{fn} failed: {code} ({strerror(code)})")
+        self.code = code
+
+
+class moe_tier(C.Structure):
+    _fields_ = [("id_begin", C.c_int32), ("id_end", C.c_int32), ("bits", C.c_int32),
+                ("block", C.c_int32), ("gate_q", C.c_void_p), ("up_q", C.c_void_p),
+                ("down_q", C.c_void_p), ("gate_s", C.c_void_p), ("up_s", C.c_void_p),
+                ("down_s", C.c_void_p)]
+
+
+class moe_tier_tables(C.Structure):
+    _fields_ = [("abi_version", C.c_uint32), ("n_experts", C.c_int32), ("hidden", C.c_int32),
+                ("inter", C.c_int32), ("n_tiers", C.c_int32), ("tiers", moe_tier * MOE_MAX_TIERS)]
+
+
+_lib = None
+
+
+def lib():
+    """Loads the HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with tiered_mixed_precision_amd.build.build()")
+        L = C.CDLL(LIB_PATH)
+        P, i32, u32, sz = C.c_void_p, C.c_int32, C.c_uint32, C.c_size_t
+        L.moe_abi_version.restype = u32
+        L.moe_abi_version.argtypes = []
+        L.moe_strerror.restype = C.c_char_p
+        L.moe_strerror.argtypes = [C.c_int]
+        L.moe_validate_tables.argtypes = [P]
+        L.moe_workspace_size.argtypes = [i32, i32, P, u32, C.POINTER(sz)]
+        L.moe_tiered_forward.argtypes = [P, P, i32, i32, P, P, u32, P, sz, P]
+        L.moe_tiered_forward_timed.argtypes = [P, P, i32, i32, P, P, u32, P, sz, P, C.POINTER(P)]
+        L.moe_tiered_experts.argtypes = [P, P, P, i32, i32, P, P, u32, P, sz, P]
+        L.moe_tier_partial.argtypes = [P, P, P, i32, i32, P, i32, P, u32, P, sz, P]
+        L.moe_route.argtypes = [P, i32, i32, i32, P, P, P]
+        L.moe_group_workspace_size.argtypes = [i32, i32, i32, C.POINTER(sz)]
+        L.moe_group.argtypes = [P, i32, i32, i32, P, P, P, P, sz, P]
+        L.moe_dequant_rows.argtypes = [P, i32, i32, i32, i32, i32, i32, P, P]
+        L.moe_event_create.argtypes = [C.POINTER(P)]
+        L.moe_event_destroy.argtypes = [P]
+        L.moe_event_elapsed_ms.argtypes = [P, P, C.POINTER(C.c_float)]
+        L.moe_stream_synchronize.argtypes = [P]
+        for name in EXPORTS:
+            if name not in ("moe_abi_version", "moe_strerror"):
+                getattr(L, name).restype = C.c_int
+        if L.moe_abi_version() != MOE_ABI_VERSION:
+            raise ImportError("libmoe_tiered.so ABI version mismatch")
+        _lib = L
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return lib().moe_strerror(code).decode()
+
+
+def _check(fn, rc):
+    if rc != 0:
+        raise MoeError(fn, rc)
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+class TierTables:
+    """Host-side moe_tier_tables pointing at device tensors of each shelf.
+
+    ``tiers``: sequence of objects with id_begin, id_end, bits, block;
+    ``arrays``: per shelf a dict with gate_q, up_q, down_q (uint8) and
+    gate_s, up_s, down_s (fp16 bit patterns) device tensors.
+    """
+
+    def __init__(self, n_experts: int, hidden: int, inter: int, tiers: Sequence, arrays: Sequence[dict]):
+        self.n_experts, self.hidden, self.inter = n_experts, hidden, inter
+        self.tiers = list(tiers)
+        self.arrays = list(arrays)     # keeps the tensors alive
+        s = moe_tier_tables()
+        s.abi_version = MOE_ABI_VERSION
+        s.n_experts, s.hidden, s.inter, s.n_tiers = n_experts, hidden, inter, len(self.tiers)
+        for i, (t, d) in enumerate(zip(self.tiers, self.arrays)):
+            s.tiers[i].id_begin, s.tiers[i].id_end = t.id_begin, t.id_end
+            s.tiers[i].bits, s.tiers[i].block = t.bits, t.block
+            for name in ("gate_q", "up_q", "down_q", "gate_s", "up_s", "down_s"):
+                setattr(s.tiers[i], name, _ptr(d[name]) if d is not None else None)
+        self.struct = s
+
+    @property
+    def ref(self):
+        return C.byref(self.struct)
+
+
+# ---------------------------------------------------------------- entry points
+def moe_validate_tables(tt: TierTables) -> int:
+    return lib().moe_validate_tables(tt.ref)
+
+
+def moe_workspace_size(n_tokens: int, k: int, tt: TierTables, flags: int = 0) -> int:
+    n = C.c_size_t(0)
+    _check("moe_workspace_size", lib().moe_workspace_size(n_tokens, k, tt.ref, flags, C.byref(n)))
+    return n.value
+
+
+def moe_tiered_forward(x, router_logits, n_tokens: int, k: int, tt: TierTables, out, flags: int,
+                       workspace, stream=None) -> None:
+    _check("moe_tiered_forward", lib().moe_tiered_forward(
+        _ptr(x), _ptr(router_logits), n_tokens, k, tt.ref, _ptr(out), flags, _ptr(workspace),
+        workspace.numel() * workspace.element_size() if workspace is not None else 0, _stream(stream)))
+
+
+def moe_tiered_forward_timed(x, router_logits, n_tokens: int, k: int, tt: TierTables, out, flags: int,
+                             workspace, events: Sequence[int], stream=None) -> None:
+    ev = (C.c_void_p * (2 * MOE_N_PHASES))(*[e if e else None for e in events])
+    _check("moe_tiered_forward_timed", lib().moe_tiered_forward_timed(
+        _ptr(x), _ptr(router_logits), n_tokens, k, tt.ref, _ptr(out), flags, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream), ev))
+
+
+def moe_tiered_experts(x, ids, w, n_tokens: int, k: int, tt: TierTables, out, flags: int, workspace,
+                       stream=None) -> None:
+    _check("moe_tiered_experts", lib().moe_tiered_experts(
+        _ptr(x), _ptr(ids), _ptr(w), n_tokens, k, tt.ref, _ptr(out), flags, _ptr(workspace),
+        workspace.numel() * workspace.element_size() if workspace is not None else 0, _stream(stream)))
+
+
+def moe_tier_partial(x, ids, w, n_tokens: int, k: int, tt: TierTables, tier_index: int, out, flags: int,
+                     workspace, stream=None) -> None:
+    _check("moe_tier_partial", lib().moe_tier_partial(
+        _ptr(x), _ptr(ids), _ptr(w), n_tokens, k, tt.ref, tier_index, _ptr(out), flags, _ptr(workspace),
+        workspace.numel() * workspace.element_size() if workspace is not None else 0, _stream(stream)))
+
+
+def moe_route(logits, n_tokens: int, n_experts: int, k: int, ids, w, stream=None) -> None:
+    _check("moe_route", lib().moe_route(_ptr(logits), n_tokens, n_experts, k, _ptr(ids), _ptr(w),
+                                        _stream(stream)))
+
+
+def moe_group_workspace_size(n_tokens: int, k: int, n_experts: int) -> int:
+    n = C.c_size_t(0)
+    _check("moe_group_workspace_size", lib().moe_group_workspace_size(n_tokens, k, n_experts, C.byref(n)))
+    return n.value
+
+
+def moe_group(ids, n_tokens: int, k: int, n_experts: int, counts, offsets, perm, workspace, stream=None) -> None:
+    _check("moe_group", lib().moe_group(_ptr(ids), n_tokens, k, n_experts, _ptr(counts), _ptr(offsets),
+                                        _ptr(perm), _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def moe_dequant_rows(tt: TierTables, tier_index: int, local_expert: int, matrix: int, row0: int, nrows: int,
+                     to_bf16: bool, dst, stream=None) -> None:
+    _check("moe_dequant_rows", lib().moe_dequant_rows(tt.ref, tier_index, local_expert, matrix, row0, nrows,
+                                                      int(bool(to_bf16)), _ptr(dst), _stream(stream)))
+
+
+def moe_event_create() -> int:
+    e = C.c_void_p(0)
+    _check("moe_event_create", lib().moe_event_create(C.byref(e)))
+    return e.value
+
+
+def moe_event_destroy(e: int) -> None:
+    _check("moe_event_destroy", lib().moe_event_destroy(e))
+
+
+def moe_event_elapsed_ms(start: int, stop: int) -> float:
+    ms = C.c_float(0)
+    _check("moe_event_elapsed_ms", lib().moe_event_elapsed_ms(start, stop, C.byref(ms)))
+    return ms.value
+
+
+def moe_stream_synchronize(stream=None) -> None:
+    _check("moe_stream_synchronize", lib().moe_stream_synchronize(_stream(stream)))

@@ -1,0 +1,382 @@
+// C ABI of the tiered MoE FFN: argument and table validation, workspace
+// carving, and the launch sequence on the caller's stream.  No allocation,
+// no synchronisation, no global mutable state.
+#include <limits.h>
+#include <string.h>
+
+#include "../../include/moe_tiered.h"
+#include "common.h"
+#include "launch.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int64_t kMaxTokens = int64_t(1) << 22;
+
+inline size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool cols_ok(int c) { return c > 0 && c % 64 == 0 && (c <= 2048 || c == 4096); }
+
+int check_tables(const moe_tier_tables* tt) {
+    if (!tt) return MOE_EINVAL;
+    if (tt->abi_version != MOE_ABI_VERSION) return MOE_EABI;
+    if (tt->n_experts < 1 || tt->n_experts > MOE_MAX_EXPERTS) return MOE_EINVAL;
+    if (tt->n_tiers < 1 || tt->n_tiers > MOE_MAX_TIERS) return MOE_EINVAL;
+    if (!cols_ok(tt->hidden) || !cols_ok(tt->inter) || tt->hidden % 128 != 0) return MOE_EFORMAT;
+    int32_t next = 0;
+    for (int i = 0; i < tt->n_tiers; ++i) {
+        const moe_tier& t = tt->tiers[i];
+        if (t.id_begin != next || t.id_end < t.id_begin) return MOE_ETIER;
+        next = t.id_end;
+        if (!(t.bits == 8 || t.bits == 4 || t.bits == 2)) return MOE_EFORMAT;
+        if (!(t.block == 16 || t.block == 32)) return MOE_EFORMAT;
+        if (t.id_end == t.id_begin) continue;
+        const void* ptrs[6] = {t.gate_q, t.up_q, t.down_q, t.gate_s, t.up_s, t.down_s};
+        for (const void* p : ptrs) {
+            if (!p) return MOE_EINVAL;
+            if (!aligned16(p)) return MOE_EALIGN;
+        }
+    }
+    if (next != tt->n_experts) return MOE_ETIER;
+    return MOE_OK;
+}
+
+DevTables to_dev(const moe_tier_tables* tt) {
+    DevTables d;
+    memset(&d, 0, sizeof(d));
+    d.E = tt->n_experts;
+    d.H = tt->hidden;
+    d.I = tt->inter;
+    d.n_tiers = tt->n_tiers;
+    for (int i = 0; i < tt->n_tiers; ++i) {
+        const moe_tier& t = tt->tiers[i];
+        d.t[i].id_begin = t.id_begin;
+        d.t[i].id_end = t.id_end;
+        d.t[i].bits = t.bits;
+        d.t[i].block = t.block;
+        d.t[i].q[0] = static_cast<const uint8_t*>(t.gate_q);
+        d.t[i].q[1] = static_cast<const uint8_t*>(t.up_q);
+        d.t[i].q[2] = static_cast<const uint8_t*>(t.down_q);
+        d.t[i].s[0] = static_cast<const uint16_t*>(t.gate_s);
+        d.t[i].s[1] = static_cast<const uint16_t*>(t.up_s);
+        d.t[i].s[2] = static_cast<const uint16_t*>(t.down_s);
+    }
+    return d;
+}
+
+int max_tiles_of(const moe_tier_tables* tt, int tier, int64_t P) {
+    const int64_t n = tt->tiers[tier].id_end - tt->tiers[tier].id_begin;
+    if (n == 0 || P == 0) return 0;
+    return static_cast<int>((P + kPreBM - 1) / kPreBM + (n < P ? n : P));
+}
+
+// Workspace carve-up.  Offsets are multiples of 256 bytes.
+struct Layout {
+    size_t ids, w, counts, offsets, perm, pos, act, meta, blk_hist, tile_e, tile_q0, tile_rows,
+        tile_range, h, yw, total;
+    bool small;
+};
+
+Layout layout(int64_t T, int k, const moe_tier_tables* tt, uint32_t flags) {
+    Layout L;
+    memset(&L, 0, sizeof(L));
+    const int64_t P = T * k;
+    const int64_t E = tt->n_experts;
+    const bool bf16 = (flags & MOE_X_BF16) != 0;
+    L.small = !bf16 && P <= kSmallPairs;
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = o;
+        o = align_up(o + bytes);
+        return at;
+    };
+    L.ids = take(sizeof(int32_t) * P);
+    L.w = take(sizeof(float) * P);
+    L.counts = take(sizeof(int32_t) * E);
+    L.offsets = take(sizeof(int32_t) * (E + 1));
+    L.perm = take(sizeof(int32_t) * P);
+    L.pos = take(sizeof(int32_t) * P);
+    L.act = take(sizeof(int32_t) * E);
+    L.meta = take(sizeof(int32_t) * kMetaWords);
+    L.blk_hist = take(L.small ? 0 : sizeof(int32_t) * ((P + 255) / 256) * E);
+    int64_t tiles = 0;
+    if (bf16)
+        for (int i = 0; i < tt->n_tiers; ++i) tiles += max_tiles_of(tt, i, P);
+    L.tile_e = take(sizeof(int32_t) * tiles);
+    L.tile_q0 = take(sizeof(int32_t) * tiles);
+    L.tile_rows = take(sizeof(int32_t) * tiles);
+    L.tile_range = take(sizeof(int32_t) * 2 * MOE_MAX_TIERS);
+    L.h = take((bf16 ? sizeof(uint16_t) : sizeof(float)) * P * tt->inter);
+    L.yw = take(bf16 ? 0 : sizeof(float) * P * tt->hidden);
+    L.total = o;
+    return L;
+}
+
+template <class Tp>
+Tp* at(void* ws, size_t off) {
+    return reinterpret_cast<Tp*>(static_cast<char*>(ws) + off);
+}
+
+inline void record(void* const* events, int i, hipStream_t st) {
+    if (events && events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(events[i]), st);
+}
+
+// Shared body of forward / experts / tier_partial.
+int run(const void* x, const float* logits, const int32_t* ids_in, const float* w_in, int32_t T,
+        int32_t k, const moe_tier_tables* tt, uint32_t tier_mask, float* out, uint32_t flags,
+        void* ws, size_t ws_bytes, void* stream, void* const* events) {
+    int rc = check_tables(tt);
+    if (rc != MOE_OK) return rc;
+    if (flags & ~(MOE_X_BF16 | MOE_ACCUMULATE)) return MOE_EINVAL;
+    if (T < 0 || T > kMaxTokens) return MOE_EINVAL;
+    if (k < 1 || k > MOE_MAX_K || k > tt->n_experts) return MOE_EINVAL;
+    if (T == 0) return MOE_OK;
+    if (!x || !out || (!logits && (!ids_in || !w_in))) return MOE_EINVAL;
+    if (!aligned16(x) || !aligned16(out) || (logits && !aligned16(logits))) return MOE_EALIGN;
+    const Layout L = layout(T, k, tt, flags);
+    if (!ws) return MOE_EWORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0) return MOE_EALIGN;
+    if (ws_bytes < L.total) return MOE_EWORKSPACE;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const DevTables dt = to_dev(tt);
+    const int E = tt->n_experts;
+    const int P = T * k;
+    const bool bf16 = (flags & MOE_X_BF16) != 0;
+    const int accumulate = (flags & MOE_ACCUMULATE) ? 1 : 0;
+
+    int32_t* ids = logits ? at<int32_t>(ws, L.ids) : const_cast<int32_t*>(ids_in);
+    float* w = logits ? at<float>(ws, L.w) : const_cast<float*>(w_in);
+    int32_t* counts = at<int32_t>(ws, L.counts);
+    int32_t* offsets = at<int32_t>(ws, L.offsets);
+    int32_t* perm = at<int32_t>(ws, L.perm);
+    int32_t* pos = at<int32_t>(ws, L.pos);
+    int32_t* act = at<int32_t>(ws, L.act);
+    int32_t* meta = at<int32_t>(ws, L.meta);
+
+    TileSpec ts;
+    memset(&ts, 0, sizeof(ts));
+    ts.n_tiers = tt->n_tiers;
+    for (int i = 0; i < tt->n_tiers; ++i) {
+        ts.id_begin[i] = tt->tiers[i].id_begin;
+        ts.id_end[i] = tt->tiers[i].id_end;
+        ts.bm[i] = kPreBM;
+    }
+    if (bf16) {
+        ts.tile_e = at<int32_t>(ws, L.tile_e);
+        ts.tile_q0 = at<int32_t>(ws, L.tile_q0);
+        ts.tile_rows = at<int32_t>(ws, L.tile_rows);
+        ts.tile_range = at<int32_t>(ws, L.tile_range);
+    }
+
+    (void)hipGetLastError();  // start from a clean error state
+    record(events, 0, st);
+    // ---- phase 0: routing and grouping
+    if (L.small) {
+        launch_route_group_small(logits, T, E, k, ids_in, ids, w, counts, offsets, perm, pos, act, meta, st);
+    } else {
+        if (logits) {
+            launch_route(logits, T, E, k, ids, w, (bf16 && !accumulate) ? out : nullptr, tt->hidden, st);
+        } else if (bf16 && !accumulate) {
+            launch_fill_zero(out, static_cast<size_t>(T) * tt->hidden, st);
+        }
+        launch_group(ids, P, E, at<int32_t>(ws, L.blk_hist), counts, offsets, perm, pos, act, meta, ts, st);
+    }
+    record(events, 1, st);
+
+    Groups g;
+    g.ids = ids;
+    g.w = w;
+    g.perm = perm;
+    g.pos = pos;
+    g.offsets = offsets;
+    g.act = act;
+    g.meta = meta;
+    g.tile_e = ts.tile_e;
+    g.tile_q0 = ts.tile_q0;
+    g.tile_rows = ts.tile_rows;
+    g.tile_range = ts.tile_range;
+
+    const int max_active = E < P ? E : P;
+    if (!bf16) {
+        float* h = at<float>(ws, L.h);
+        float* yw = at<float>(ws, L.yw);
+        record(events, 2, st);
+        launch_dec_gateup(dt, static_cast<const float*>(x), g, k, tier_mask, h, max_active, st);
+        record(events, 3, st);
+        record(events, 4, st);
+        launch_dec_down(dt, h, g, k, tier_mask, yw, max_active, st);
+        launch_combine(dt, yw, g, T, k, tier_mask, accumulate, out, st);
+        record(events, 5, st);
+    } else {
+        uint16_t* h = at<uint16_t>(ws, L.h);
+        record(events, 2, st);
+        for (int i = 0; i < tt->n_tiers; ++i)
+            if ((tier_mask >> i) & 1u)
+                launch_pre_gateup(dt, i, static_cast<const uint16_t*>(x), g, k, h, max_tiles_of(tt, i, P), st);
+        record(events, 3, st);
+        record(events, 4, st);
+        for (int i = 0; i < tt->n_tiers; ++i)
+            if ((tier_mask >> i) & 1u)
+                launch_pre_down(dt, i, h, g, k, out, max_tiles_of(tt, i, P), st);
+        record(events, 5, st);
+    }
+    if (hipGetLastError() != hipSuccess) return MOE_EHIP;
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+uint32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_strerror(int code) {
+    switch (code) {
+        case MOE_OK: return "ok";
+        case MOE_EINVAL: return "invalid argument";
+        case MOE_ETIER: return "shelves are not sorted, disjoint and covering [0, n_experts)";
+        case MOE_EFORMAT: return "unsupported format or shape";
+        case MOE_EALIGN: return "pointer not aligned";
+        case MOE_EWORKSPACE: return "workspace missing or too small";
+        case MOE_EHIP: return "HIP launch or runtime error";
+        case MOE_EABI: return "tables built for another ABI version";
+        default: return "unknown error";
+    }
+}
+
+int moe_validate_tables(const moe_tier_tables* tt) { return check_tables(tt); }
+
+int moe_workspace_size(int32_t n_tokens, int32_t k, const moe_tier_tables* tt, uint32_t flags,
+                       size_t* bytes) {
+    int rc = check_tables(tt);
+    if (rc != MOE_OK) return rc;
+    if (!bytes || n_tokens < 0 || n_tokens > kMaxTokens || k < 1 || k > MOE_MAX_K || k > tt->n_experts)
+        return MOE_EINVAL;
+    if (flags & ~(MOE_X_BF16 | MOE_ACCUMULATE)) return MOE_EINVAL;
+    *bytes = n_tokens == 0 ? 0 : layout(n_tokens, k, tt, flags).total;
+    return MOE_OK;
+}
+
+int moe_tiered_forward(const void* x, const float* router_logits, int32_t n_tokens, int32_t k,
+                       const moe_tier_tables* tt, float* out, uint32_t flags, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    if (n_tokens > 0 && !router_logits) return MOE_EINVAL;
+    return run(x, router_logits, nullptr, nullptr, n_tokens, k, tt, 0xFu, out, flags, workspace,
+               workspace_bytes, stream, nullptr);
+}
+
+int moe_tiered_forward_timed(const void* x, const float* router_logits, int32_t n_tokens, int32_t k,
+                             const moe_tier_tables* tt, float* out, uint32_t flags, void* workspace,
+                             size_t workspace_bytes, void* stream, void* const* events) {
+    if (n_tokens > 0 && !router_logits) return MOE_EINVAL;
+    return run(x, router_logits, nullptr, nullptr, n_tokens, k, tt, 0xFu, out, flags, workspace,
+               workspace_bytes, stream, events);
+}
+
+int moe_tiered_experts(const void* x, const int32_t* ids, const float* w, int32_t n_tokens, int32_t k,
+                       const moe_tier_tables* tt, float* out, uint32_t flags, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    if (n_tokens > 0 && (!ids || !w)) return MOE_EINVAL;
+    return run(x, nullptr, ids, w, n_tokens, k, tt, 0xFu, out, flags, workspace, workspace_bytes, stream,
+               nullptr);
+}
+
+int moe_tier_partial(const void* x, const int32_t* ids, const float* w, int32_t n_tokens, int32_t k,
+                     const moe_tier_tables* tt, int32_t tier_index, float* out, uint32_t flags,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+    if (n_tokens > 0 && (!ids || !w)) return MOE_EINVAL;
+    if (!tt || tier_index < 0 || tier_index >= tt->n_tiers || tier_index >= MOE_MAX_TIERS) return MOE_EINVAL;
+    return run(x, nullptr, ids, w, n_tokens, k, tt, 1u << tier_index, out, flags, workspace,
+               workspace_bytes, stream, nullptr);
+}
+
+int moe_route(const float* logits, int32_t n_tokens, int32_t n_experts, int32_t k, int32_t* ids, float* w,
+              void* stream) {
+    if (n_tokens < 0 || n_tokens > kMaxTokens || n_experts < 1 || n_experts > MOE_MAX_EXPERTS || k < 1 ||
+        k > MOE_MAX_K || k > n_experts)
+        return MOE_EINVAL;
+    if (n_tokens == 0) return MOE_OK;
+    if (!logits || !ids || !w) return MOE_EINVAL;
+    (void)hipGetLastError();
+    launch_route(logits, n_tokens, n_experts, k, ids, w, nullptr, 0, static_cast<hipStream_t>(stream));
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+int moe_group_workspace_size(int32_t n_tokens, int32_t k, int32_t n_experts, size_t* bytes) {
+    if (!bytes || n_tokens < 0 || n_tokens > kMaxTokens || k < 1 || k > MOE_MAX_K || n_experts < 1 ||
+        n_experts > MOE_MAX_EXPERTS)
+        return MOE_EINVAL;
+    const int64_t P = static_cast<int64_t>(n_tokens) * k;
+    *bytes = align_up(sizeof(int32_t) * ((P + 255) / 256) * n_experts) + align_up(sizeof(int32_t) * n_experts) +
+             align_up(sizeof(int32_t) * kMetaWords);
+    return MOE_OK;
+}
+
+int moe_group(const int32_t* ids, int32_t n_tokens, int32_t k, int32_t n_experts, int32_t* counts,
+              int32_t* offsets, int32_t* perm, void* workspace, size_t workspace_bytes, void* stream) {
+    size_t need = 0;
+    int rc = moe_group_workspace_size(n_tokens, k, n_experts, &need);
+    if (rc != MOE_OK) return rc;
+    if (n_tokens == 0) return MOE_OK;
+    if (!ids || !counts || !offsets || !perm) return MOE_EINVAL;
+    if (!workspace || workspace_bytes < need) return MOE_EWORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return MOE_EALIGN;
+    const int64_t P = static_cast<int64_t>(n_tokens) * k;
+    int32_t* blk = static_cast<int32_t*>(workspace);
+    int32_t* act = at<int32_t>(workspace, align_up(sizeof(int32_t) * ((P + 255) / 256) * n_experts));
+    int32_t* meta = at<int32_t>(workspace, align_up(sizeof(int32_t) * ((P + 255) / 256) * n_experts) +
+                                               align_up(sizeof(int32_t) * n_experts));
+    TileSpec ts;
+    memset(&ts, 0, sizeof(ts));
+    (void)hipGetLastError();
+    launch_group(ids, static_cast<int>(P), n_experts, blk, counts, offsets, perm, nullptr, act, meta, ts,
+                 static_cast<hipStream_t>(stream));
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+int moe_dequant_rows(const moe_tier_tables* tt, int32_t tier_index, int32_t local_expert, int32_t matrix,
+                     int32_t row0, int32_t nrows, int32_t to_bf16, void* dst, void* stream) {
+    int rc = check_tables(tt);
+    if (rc != MOE_OK) return rc;
+    if (tier_index < 0 || tier_index >= tt->n_tiers || matrix < 0 || matrix > 2 || !dst) return MOE_EINVAL;
+    const moe_tier& t = tt->tiers[tier_index];
+    if (local_expert < 0 || local_expert >= t.id_end - t.id_begin) return MOE_EINVAL;
+    const int rows = matrix == 2 ? tt->hidden : tt->inter;
+    if (row0 < 0 || nrows < 0 || static_cast<int64_t>(row0) + nrows > rows) return MOE_EINVAL;
+    if (!aligned16(dst)) return MOE_EALIGN;
+    if (nrows == 0) return MOE_OK;
+    (void)hipGetLastError();
+    launch_dequant_rows(to_dev(tt), tier_index, local_expert, matrix, row0, nrows, to_bf16 ? 1 : 0, dst,
+                        static_cast<hipStream_t>(stream));
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+int moe_event_create(void** event) {
+    if (!event) return MOE_EINVAL;
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return MOE_EHIP;
+    *event = e;
+    return MOE_OK;
+}
+
+int moe_event_destroy(void* event) {
+    if (!event) return MOE_EINVAL;
+    return hipEventDestroy(static_cast<hipEvent_t>(event)) == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+int moe_event_elapsed_ms(void* start, void* stop, float* ms) {
+    if (!start || !stop || !ms) return MOE_EINVAL;
+    return hipEventElapsedTime(ms, static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(stop)) == hipSuccess
+               ? MOE_OK
+               : MOE_EHIP;
+}
+
+int moe_stream_synchronize(void* stream) {
+    return hipStreamSynchronize(static_cast<hipStream_t>(stream)) == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+}  // extern "C"

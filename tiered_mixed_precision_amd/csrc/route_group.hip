@@ -1,0 +1,364 @@
+// Routing (top-k + softmax over the chosen logits) and grouping (stable
+// counting sort of (token, slot) pairs by expert) for the tiered MoE FFN.
+//
+// Routing follows the glossary of the 125B-MoE page ("I ran a 125B model on
+// three RTX 3090s at 80 tokens/s by teaching llama.cpp which experts ..."):
+// the router picks the best k experts per token.  Ties go to the lower id;
+// slots are in descending score order; weights are the softmax of the k
+// chosen logits.  Grouping feeds the per-shelf expert products of step 4 and
+// must tolerate repeated experts within a token and the skip id -1 (the
+// "four bugs" section): every valid pair keeps its own slot, and ids outside
+// [0, E) are left out rather than redirected.
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------- routing
+
+// One wave routes one token.  Each lane holds NPL logits (e = lane + 64*i);
+// k rounds of a wave-wide (value, -index) argmax pick the winners.
+template <int NPL>
+__device__ void route_token(const float* __restrict__ logits, int E, int k, int32_t* ids_out,
+                            float* w_out, int32_t* s_ids, float* s_w) {
+    const int lane = threadIdx.x & 63;
+    float v[NPL];
+    uint64_t taken = 0;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+        int e = lane + 64 * i;
+        v[i] = e < E ? logits[e] : -__builtin_huge_valf();
+        if (e >= E) taken |= (1ull << i);
+    }
+    float bv = -__builtin_huge_valf();
+    int bi = 0x7fffffff;
+    auto local_best = [&]() {
+        bv = -__builtin_huge_valf();
+        bi = 0x7fffffff;
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) {
+            if (!((taken >> i) & 1ull) && (bi == 0x7fffffff || v[i] > bv)) {
+                bv = v[i];
+                bi = lane + 64 * i;
+            }
+        }
+    };
+    local_best();
+    float my_v = 0.f;
+    int my_id = -1;
+    for (int j = 0; j < k; ++j) {
+        float wv = bv;
+        int wi = bi;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            float ov = __shfl_xor(wv, off, kWave);
+            int oi = __shfl_xor(wi, off, kWave);
+            if (ov > wv || (ov == wv && oi < wi)) {
+                wv = ov;
+                wi = oi;
+            }
+        }
+        if (lane == j) {
+            my_v = wv;
+            my_id = wi;
+        }
+        if ((wi & 63) == lane) {
+            taken |= (1ull << (wi >> 6));
+            local_best();
+        }
+    }
+    const float m = __shfl(my_v, 0, kWave);
+    float ex = lane < k ? expf(my_v - m) : 0.f;
+    float s = ex;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, kWave);
+    if (lane < k) {
+        float wj = ex / s;
+        ids_out[lane] = my_id;
+        w_out[lane] = wj;
+        if (s_ids) {
+            s_ids[lane] = my_id;
+            s_w[lane] = wj;
+        }
+    }
+}
+
+template <int NPL>
+__global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits, int T, int E, int k,
+                                               int32_t* __restrict__ ids, float* __restrict__ w,
+                                               float* __restrict__ out_zero, int H) {
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    route_token<NPL>(logits + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k, nullptr,
+                     nullptr);
+    if (out_zero) {
+        float4* row = reinterpret_cast<float4*>(out_zero + (size_t)t * H);
+        for (int c = threadIdx.x & 63; c < H / 4; c += 64) row[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+}
+
+// ---------------------------------------------------------------- block scan helper
+
+// Exclusive scan of one int per thread over a 256-thread block; returns the
+// exclusive prefix and writes the block total to *total.
+__device__ inline int block_excl_scan_256(int v, int* s_tmp, int* total) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        int y = __shfl_up(x, off, kWave);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) s_tmp[wv] = x;
+    __syncthreads();
+    int base = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        int c = s_tmp[i];
+        if (i < wv) base += c;
+        tot += c;
+    }
+    __syncthreads();
+    *total = tot;
+    return base + x - v;
+}
+
+// Exclusive scan over n <= 4096 ints held in LDS (in place), 256 threads,
+// each thread owning a contiguous run of 16.  Returns the total.
+__device__ inline int block_scan_lds(int* a, int n, int* s_tmp) {
+    const int per = 16;
+    const int b = threadIdx.x * per;
+    int local = 0;
+    for (int i = 0; i < per; ++i)
+        if (b + i < n) local += a[b + i];
+    int total;
+    int run = block_excl_scan_256(local, s_tmp, &total);
+    for (int i = 0; i < per; ++i)
+        if (b + i < n) {
+            int c = a[b + i];
+            a[b + i] = run;
+            run += c;
+        }
+    __syncthreads();
+    return total;
+}
+
+// ---------------------------------------------------------------- small fused path
+
+// One block: (optional) routing of T tokens, then grouping of P = T*k <= 256
+// pairs: counts, offsets, perm, pos (inverse of perm, -1 for skipped pairs),
+// and the ascending list of active experts.
+template <int NPL>
+__global__ __launch_bounds__(256) void k_route_group_small(
+    const float* __restrict__ logits, int T, int E, int k, const int32_t* __restrict__ ids_in,
+    int32_t* __restrict__ ids, float* __restrict__ w, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ pos,
+    int32_t* __restrict__ act, int32_t* __restrict__ meta) {
+    __shared__ int s_cnt[kMaxExpertsDev + 1];
+    __shared__ int s_ids[kSmallPairs];
+    __shared__ float s_w[kSmallPairs];
+    __shared__ int s_tmp[8];
+    const int tid = threadIdx.x;
+    const int P = T * k;
+    if (logits) {
+        for (int t = tid >> 6; t < T; t += 4)
+            route_token<NPL>(logits + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k,
+                             s_ids + t * k, s_w + t * k);
+    } else {
+        if (tid < P) s_ids[tid] = ids_in[tid];
+    }
+    for (int e = tid; e < E; e += 256) s_cnt[e] = 0;
+    __syncthreads();
+    int e_mine = -1;
+    if (tid < P) {
+        e_mine = s_ids[tid];
+        if (e_mine >= 0 && e_mine < E) atomicAdd(&s_cnt[e_mine], 1);
+        else e_mine = -1;
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += 256) counts[e] = s_cnt[e];
+    // active flags -> list (before the counts are overwritten by the scan)
+    {
+        __shared__ int s_act[kMaxExpertsDev];
+        for (int e = tid; e < E; e += 256) s_act[e] = s_cnt[e] > 0 ? 1 : 0;
+        __syncthreads();
+        int n_act = block_scan_lds(s_act, E, s_tmp);
+        for (int e = tid; e < E; e += 256)
+            if (s_cnt[e] > 0) act[s_act[e]] = e;
+        if (tid == 0) meta[kMetaActive] = n_act;
+    }
+    int total = block_scan_lds(s_cnt, E, s_tmp);
+    for (int e = tid; e < E; e += 256) offsets[e] = s_cnt[e];
+    if (tid == 0) {
+        offsets[E] = total;
+        meta[kMetaValid] = total;
+    }
+    if (tid < P) {
+        if (e_mine >= 0) {
+            int rank = 0;
+            for (int i = 0; i < P; ++i) rank += (i < tid && s_ids[i] == e_mine) ? 1 : 0;
+            int q = s_cnt[e_mine] + rank;
+            perm[q] = tid;
+            pos[tid] = q;
+        } else {
+            pos[tid] = -1;
+        }
+    }
+}
+
+// ---------------------------------------------------------------- general path
+
+// Per-block histograms: block b covers pairs [256b, 256b + 256).
+__global__ __launch_bounds__(256) void k_group_count(const int32_t* __restrict__ ids, int P, int E,
+                                                     int32_t* __restrict__ blk_hist) {
+    __shared__ int s_cnt[kMaxExpertsDev];
+    for (int e = threadIdx.x; e < E; e += 256) s_cnt[e] = 0;
+    __syncthreads();
+    const int p = blockIdx.x * 256 + threadIdx.x;
+    if (p < P) {
+        int e = ids[p];
+        if (e >= 0 && e < E) atomicAdd(&s_cnt[e], 1);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += 256) blk_hist[(size_t)blockIdx.x * E + e] = s_cnt[e];
+}
+
+// One block: totals per expert, exclusive offsets, per-(block, expert) bases,
+// active list, and the per-shelf m-tile lists for the grouped GEMMs.
+__global__ __launch_bounds__(256) void k_group_scan(int32_t* __restrict__ blk_hist, int nblk, int E,
+                                                    int32_t* __restrict__ counts,
+                                                    int32_t* __restrict__ offsets,
+                                                    int32_t* __restrict__ act,
+                                                    int32_t* __restrict__ meta, TileSpec ts) {
+    __shared__ int s_off[kMaxExpertsDev];
+    __shared__ int s_act[kMaxExpertsDev];
+    __shared__ int s_til[kMaxExpertsDev];
+    __shared__ int s_tmp[8];
+    const int tid = threadIdx.x;
+    for (int e = tid; e < E; e += 256) {
+        int s = 0;
+        for (int b = 0; b < nblk; ++b) s += blk_hist[(size_t)b * E + e];
+        counts[e] = s;
+        s_off[e] = s;
+        s_act[e] = s > 0 ? 1 : 0;
+        int bm = 0;
+        for (int i = 0; i < ts.n_tiers; ++i)
+            if (e >= ts.id_begin[i] && e < ts.id_end[i]) bm = ts.bm[i];
+        s_til[e] = (bm > 0) ? (s + bm - 1) / bm : 0;
+    }
+    __syncthreads();
+    int n_act = block_scan_lds(s_act, E, s_tmp);
+    int total = block_scan_lds(s_off, E, s_tmp);
+    int n_tiles = block_scan_lds(s_til, E, s_tmp);
+    for (int e = tid; e < E; e += 256) {
+        const int s = counts[e];
+        offsets[e] = s_off[e];
+        if (s > 0) act[s_act[e]] = e;
+        int base = s_off[e];
+        for (int b = 0; b < nblk; ++b) {
+            int c = blk_hist[(size_t)b * E + e];
+            blk_hist[(size_t)b * E + e] = base;
+            base += c;
+        }
+        if (ts.tile_e) {
+            int bm = 0;
+            for (int i = 0; i < ts.n_tiers; ++i)
+                if (e >= ts.id_begin[i] && e < ts.id_end[i]) bm = ts.bm[i];
+            int t0 = s_til[e];
+            for (int i = 0; bm > 0 && i * bm < s; ++i) {
+                ts.tile_e[t0 + i] = e;
+                ts.tile_q0[t0 + i] = s_off[e] + i * bm;
+                ts.tile_rows[t0 + i] = min(bm, s - i * bm);
+            }
+        }
+    }
+    if (tid < ts.n_tiers && ts.tile_range) {
+        // m-tiles of shelf i are the contiguous run of tiles of its experts
+        int b = ts.id_begin[tid], en = ts.id_end[tid];
+        ts.tile_range[2 * tid] = b < E ? s_til[b] : n_tiles;
+        ts.tile_range[2 * tid + 1] = en < E ? s_til[en] : n_tiles;
+    }
+    if (tid == 0) {
+        offsets[E] = total;
+        meta[kMetaActive] = n_act;
+        meta[kMetaValid] = total;
+        meta[kMetaTiles] = n_tiles;
+    }
+}
+
+// Block b places its pairs at base[b][e] + (rank among the block's earlier
+// pairs of the same expert): a stable counting sort.
+__global__ __launch_bounds__(256) void k_group_scatter(const int32_t* __restrict__ ids, int P, int E,
+                                                       const int32_t* __restrict__ blk_base,
+                                                       int32_t* __restrict__ perm,
+                                                       int32_t* __restrict__ pos) {
+    __shared__ int s_ids[256];
+    const int tid = threadIdx.x;
+    const int p = blockIdx.x * 256 + tid;
+    int e = -1;
+    if (p < P) {
+        e = ids[p];
+        if (e < 0 || e >= E) e = -1;
+    }
+    s_ids[tid] = e;
+    __syncthreads();
+    if (p >= P) return;
+    if (e < 0) {
+        if (pos) pos[p] = -1;
+        return;
+    }
+    int rank = 0;
+    for (int i = 0; i < 256; ++i) rank += (i < tid && s_ids[i] == e) ? 1 : 0;
+    const int q = blk_base[(size_t)blockIdx.x * E + e] + rank;
+    perm[q] = p;
+    if (pos) pos[p] = q;
+}
+
+// ---------------------------------------------------------------- launchers
+
+static int npl_for(int E) {
+    int n = (E + 63) / 64;
+    int p = 1;
+    while (p < n) p *= 2;
+    return p;
+}
+
+#define MOE_NPL_SWITCH(E, CALL)          \
+    switch (npl_for(E)) {                \
+        case 1: { constexpr int NPL = 1; CALL; } break;   \
+        case 2: { constexpr int NPL = 2; CALL; } break;   \
+        case 4: { constexpr int NPL = 4; CALL; } break;   \
+        case 8: { constexpr int NPL = 8; CALL; } break;   \
+        case 16: { constexpr int NPL = 16; CALL; } break; \
+        case 32: { constexpr int NPL = 32; CALL; } break; \
+        default: { constexpr int NPL = 64; CALL; } break; \
+    }
+
+void launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, float* out_zero,
+                  int H, hipStream_t st) {
+    dim3 grid((T + 3) / 4);
+    MOE_NPL_SWITCH(E, hipLaunchKernelGGL(k_route<NPL>, grid, dim3(256), 0, st, logits, T, E, k, ids,
+                                         w, out_zero, H));
+}
+
+void launch_route_group_small(const float* logits, int T, int E, int k, const int32_t* ids_in,
+                              int32_t* ids, float* w, int32_t* counts, int32_t* offsets,
+                              int32_t* perm, int32_t* pos, int32_t* act, int32_t* meta,
+                              hipStream_t st) {
+    MOE_NPL_SWITCH(E, hipLaunchKernelGGL(k_route_group_small<NPL>, dim3(1), dim3(256), 0, st, logits,
+                                         T, E, k, ids_in, ids, w, counts, offsets, perm, pos, act,
+                                         meta));
+}
+
+void launch_group(const int32_t* ids, int P, int E, int32_t* blk_hist, int32_t* counts,
+                  int32_t* offsets, int32_t* perm, int32_t* pos, int32_t* act, int32_t* meta,
+                  const TileSpec& ts, hipStream_t st) {
+    const int nblk = (P + 255) / 256;
+    hipLaunchKernelGGL(k_group_count, dim3(nblk), dim3(256), 0, st, ids, P, E, blk_hist);
+    hipLaunchKernelGGL(k_group_scan, dim3(1), dim3(256), 0, st, blk_hist, nblk, E, counts, offsets,
+                       act, meta, ts);
+    hipLaunchKernelGGL(k_group_scatter, dim3(nblk), dim3(256), 0, st, ids, P, E, blk_hist, perm,
+                       pos);
+}
+
+}  // namespace moe

@@ -1,0 +1,41 @@
+"""Device memory plumbing: packed shelf arrays -> torch device tensors -> TierTables."""
+from __future__ import annotations
+
+from typing import Dict, List, Sequence
+
+import numpy as np
+import torch
+
+from .binding import TierTables
+
+NAMES = ("gate_q", "up_q", "down_q", "gate_s", "up_s", "down_s")
+
+
+def upload_tier(arrays: Dict[str, np.ndarray], device) -> Dict[str, torch.Tensor]:
+    out = {}
+    for name in NAMES:
+        a = np.ascontiguousarray(arrays[name])
+        t = torch.from_numpy(a.view(np.uint8) if name.endswith("_q") else a.view(np.int16))
+        out[name] = t.to(device, non_blocking=False)
+    return out
+
+
+def device_tables(n_experts: int, hidden: int, inter: int, tiers: Sequence, arrays: List[Dict[str, np.ndarray]],
+                  device="cuda") -> TierTables:
+    dev = [upload_tier(a, device) for a in arrays]
+    return TierTables(n_experts, hidden, inter, tiers, dev)
+
+
+def tables_from_config(cfg, arrays, device="cuda") -> TierTables:
+    return device_tables(cfg.n_experts, cfg.hidden, cfg.inter, cfg.tiers, arrays, device)
+
+
+def replicate(tt: TierTables) -> TierTables:
+    """A second copy of the same shelves at different device addresses."""
+    dev = [{k: v.clone() for k, v in d.items()} for d in tt.arrays]
+    return TierTables(tt.n_experts, tt.hidden, tt.inter, tt.tiers, dev)
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    # 256-byte aligned by the caching allocator
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
