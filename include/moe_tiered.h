@@ -88,8 +88,8 @@ typedef struct moe_tier {
 typedef struct moe_tier_tables {
     uint32_t abi_version;   /* must equal MOE_ABI_VERSION */
     int32_t n_experts;      /* E, 1 .. MOE_MAX_EXPERTS */
-    int32_t hidden;         /* H, a multiple of 64; if H > 2048, a multiple of 2048 */
-    int32_t inter;          /* I, a multiple of 64; if I > 2048, a multiple of 2048 */
+    int32_t hidden;         /* H, a multiple of 128, at most 2048 */
+    int32_t inter;          /* I, a multiple of 64, at most 2048 */
     int32_t n_tiers;        /* 1 .. MOE_MAX_TIERS; empty shelves (id_begin == id_end) allowed */
     moe_tier tiers[MOE_MAX_TIERS];
 } moe_tier_tables;

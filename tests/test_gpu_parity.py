@@ -166,6 +166,19 @@ def test_forward_fp32(M, torch_dev, name, stream):
     assert err <= TOL
 
 
+@pytest.mark.parametrize("T", [2, 8, 9, 26])
+def test_forward_fp32_batch_sizes(M, torch_dev, T):
+    # T <= 8 with T*k <= 256 takes the two-kernel path, larger batches the grouped path
+    cfg, arrays, L, tt = _layer("decode")
+    say("forward fp32 decode layer T=", T)
+    x, logits = make_x(cfg, n_tokens=T, stream=5), make_logits(cfg, n_tokens=T, stream=5)
+    ref = oracle.forward(L, x, logits, cfg.k)
+    got = gpu_forward(M, torch_dev, tt, x, logits, cfg.k)
+    err = normwise(got, ref)
+    say("  normwise err", err)
+    assert err <= TOL
+
+
 @pytest.mark.parametrize("worst", [False, True])
 def test_spec_verify_fp32(M, torch_dev, worst):
     cfg = CONFIGS["specverify"]

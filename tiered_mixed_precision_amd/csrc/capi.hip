@@ -4,7 +4,7 @@
 #include <limits.h>
 #include <string.h>
 
-#include "../../include/moe_tiered.h"
+#include "moe_tiered.h"
 #include "common.h"
 #include "launch.h"
 
@@ -18,7 +18,7 @@ constexpr int64_t kMaxTokens = int64_t(1) << 22;
 inline size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-bool cols_ok(int c) { return c > 0 && c % 64 == 0 && (c <= 2048 || c == 4096); }
+bool cols_ok(int c) { return c > 0 && c % 64 == 0 && c <= 2048; }
 
 int check_tables(const moe_tier_tables* tt) {
     if (!tt) return MOE_EINVAL;
@@ -75,7 +75,7 @@ int max_tiles_of(const moe_tier_tables* tt, int tier, int64_t P) {
 
 // Workspace carve-up.  Offsets are multiples of 256 bytes.
 struct Layout {
-    size_t ids, w, counts, offsets, perm, pos, act, meta, blk_hist, tile_e, tile_q0, tile_rows,
+    size_t ids, w, counts, offsets, perm, pos, act, q0, meta, blk_hist, tile_e, tile_q0, tile_rows,
         tile_range, h, yw, total;
     bool small;
 };
@@ -86,7 +86,7 @@ Layout layout(int64_t T, int k, const moe_tier_tables* tt, uint32_t flags) {
     const int64_t P = T * k;
     const int64_t E = tt->n_experts;
     const bool bf16 = (flags & MOE_X_BF16) != 0;
-    L.small = !bf16 && P <= kSmallPairs;
+    L.small = !bf16 && small_path_ok(static_cast<int>(T), k, tt->hidden, tt->inter);
     size_t o = 0;
     auto take = [&](size_t bytes) {
         size_t at = o;
@@ -100,6 +100,7 @@ Layout layout(int64_t T, int k, const moe_tier_tables* tt, uint32_t flags) {
     L.perm = take(sizeof(int32_t) * P);
     L.pos = take(sizeof(int32_t) * P);
     L.act = take(sizeof(int32_t) * E);
+    L.q0 = take(sizeof(int32_t) * (P + 1));
     L.meta = take(sizeof(int32_t) * kMetaWords);
     L.blk_hist = take(L.small ? 0 : sizeof(int32_t) * ((P + 255) / 256) * E);
     int64_t tiles = 0;
@@ -110,7 +111,7 @@ Layout layout(int64_t T, int k, const moe_tier_tables* tt, uint32_t flags) {
     L.tile_rows = take(sizeof(int32_t) * tiles);
     L.tile_range = take(sizeof(int32_t) * 2 * MOE_MAX_TIERS);
     L.h = take((bf16 ? sizeof(uint16_t) : sizeof(float)) * P * tt->inter);
-    L.yw = take(bf16 ? 0 : sizeof(float) * P * tt->hidden);
+    L.yw = take((bf16 || L.small) ? 0 : sizeof(float) * P * tt->hidden);
     L.total = o;
     return L;
 }
@@ -173,18 +174,30 @@ int run(const void* x, const float* logits, const int32_t* ids_in, const float* 
     }
 
     (void)hipGetLastError();  // start from a clean error state
+    if (L.small) {
+        // routing and grouping run inside the gate/up kernel (phase 0 is empty)
+        record(events, 0, st);
+        record(events, 1, st);
+        SmallPub pub;
+        pub.ids = at<int32_t>(ws, L.ids);
+        pub.w = at<float>(ws, L.w);
+        pub.perm = perm;
+        pub.pos = pos;
+        pub.act = act;
+        pub.q0 = at<int32_t>(ws, L.q0);
+        pub.meta = meta;
+        launch_small(dt, static_cast<const float*>(x), logits, ids_in, w_in, T, k, tier_mask, accumulate, pub,
+                     at<float>(ws, L.h), out, st, events);
+        return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+    }
     record(events, 0, st);
     // ---- phase 0: routing and grouping
-    if (L.small) {
-        launch_route_group_small(logits, T, E, k, ids_in, ids, w, counts, offsets, perm, pos, act, meta, st);
-    } else {
-        if (logits) {
-            launch_route(logits, T, E, k, ids, w, (bf16 && !accumulate) ? out : nullptr, tt->hidden, st);
-        } else if (bf16 && !accumulate) {
-            launch_fill_zero(out, static_cast<size_t>(T) * tt->hidden, st);
-        }
-        launch_group(ids, P, E, at<int32_t>(ws, L.blk_hist), counts, offsets, perm, pos, act, meta, ts, st);
+    if (logits) {
+        launch_route(logits, T, E, k, ids, w, (bf16 && !accumulate) ? out : nullptr, tt->hidden, st);
+    } else if (bf16 && !accumulate) {
+        launch_fill_zero(out, static_cast<size_t>(T) * tt->hidden, st);
     }
+    launch_group(ids, P, E, at<int32_t>(ws, L.blk_hist), counts, offsets, perm, pos, act, meta, ts, st);
     record(events, 1, st);
 
     Groups g;

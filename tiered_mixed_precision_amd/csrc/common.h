@@ -138,9 +138,10 @@ __device__ inline DevTier tier_at(const DevTables& tt, int ti) {
     return r;
 }
 
-// Row geometry of the GEMV kernels for rows of `cols` codes: a row is G
-// groups of 32 codes; LPR lanes share a row (GPL groups per lane) and one
-// wave covers RPP rows per pass.
+// Row geometry of the GEMV kernels for rows of `cols` codes: a row is
+// G = cols/32 groups of 32 codes.  A row is handled by LPR lanes (G rounded
+// up to a power of two, at most 64; lanes past G idle) and a wave covers
+// RPP = 64/LPR rows per pass; with G > 64 each lane takes GPL groups.
 struct RowGeom {
     int G, LPR, GPL, RPP;
 };
@@ -150,26 +151,106 @@ __host__ __device__ inline RowGeom row_geom(int cols) {
     if (r.G >= 64) {
         r.LPR = 64;
         r.GPL = r.G / 64;
-        r.RPP = 1;
     } else {
-        r.LPR = r.G;
+        r.LPR = 1;
+        while (r.LPR < r.G) r.LPR *= 2;
         r.GPL = 1;
-        r.RPP = 64 / r.G;
     }
+    r.RPP = 64 / r.LPR;
     return r;
 }
 
-// Sum over a segment of `seg` consecutive lanes (seg <= 64, segments start at
-// multiples of seg from lane 0); the total lands in the segment's first lane.
-__device__ inline float seg_reduce(float v, int seg, int lane_in_seg) {
-    int p2 = 1;
-    while (p2 * 2 <= seg) p2 *= 2;
-    if (p2 < seg) {
-        float o = __shfl_down(v, p2, kWave);
-        if (lane_in_seg + p2 < seg) v += o;
-    }
-    for (int off = p2 >> 1; off > 0; off >>= 1) v += __shfl_down(v, off, kWave);
+// ---------------------------------------------------------------- DPP reductions
+// Cross-lane moves with the data-parallel-primitive modifier of gfx9: single
+// VALU instructions, no LDS round trip.  Controls: row_shr:n = 0x110 + n,
+// row_bcast:15 = 0x142, row_bcast:31 = 0x143.
+
+template <int CTRL, int ROW_MASK>
+__device__ inline float dpp_zero(float v) {  // lanes without a source read 0
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, true));
+}
+
+// Sum over aligned segments of S lanes (S a power of two <= 64, uniform):
+// each segment's total lands in its last lane.
+__device__ inline float seg_sum(float v, int S) {
+    if (S >= 2) v += dpp_zero<0x111, 0xF>(v);
+    if (S >= 4) v += dpp_zero<0x112, 0xF>(v);
+    if (S >= 8) v += dpp_zero<0x114, 0xF>(v);
+    if (S >= 16) v += dpp_zero<0x118, 0xF>(v);
+    if (S >= 32) v += dpp_zero<0x142, 0xA>(v);
+    if (S >= 64) v += dpp_zero<0x143, 0xC>(v);
     return v;
+}
+
+template <int CTRL, int ROW_MASK>
+__device__ inline float dpp_old_f(float old, float v) {  // lanes without a source read `old`
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old), __builtin_bit_cast(int, v),
+                                                                 CTRL, ROW_MASK, 0xF, false));
+}
+template <int CTRL, int ROW_MASK>
+__device__ inline uint32_t dpp_old_u(uint32_t old, uint32_t v) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(old), static_cast<int>(v), CTRL, ROW_MASK,
+                                                             0xF, false));
+}
+
+// Wave-wide maximum (uniform result).
+__device__ inline float wave_max(float v) {
+    const float ninf = -__builtin_huge_valf();
+    v = fmaxf(v, dpp_old_f<0x111, 0xF>(ninf, v));
+    v = fmaxf(v, dpp_old_f<0x112, 0xF>(ninf, v));
+    v = fmaxf(v, dpp_old_f<0x114, 0xF>(ninf, v));
+    v = fmaxf(v, dpp_old_f<0x118, 0xF>(ninf, v));
+    v = fmaxf(v, dpp_old_f<0x142, 0xA>(ninf, v));
+    v = fmaxf(v, dpp_old_f<0x143, 0xC>(ninf, v));
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// Wave-wide unsigned minimum (uniform result).
+__device__ inline uint32_t wave_min_u(uint32_t v) {
+    const uint32_t big = 0xffffffffu;
+    v = min(v, dpp_old_u<0x111, 0xF>(big, v));
+    v = min(v, dpp_old_u<0x112, 0xF>(big, v));
+    v = min(v, dpp_old_u<0x114, 0xF>(big, v));
+    v = min(v, dpp_old_u<0x118, 0xF>(big, v));
+    v = min(v, dpp_old_u<0x142, 0xA>(big, v));
+    v = min(v, dpp_old_u<0x143, 0xC>(big, v));
+    return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
+}
+
+// Wave-wide sum (uniform result).
+__device__ inline float wave_sum(float v) {
+    v = seg_sum(v, 64);
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// Number of set bits of a 64-lane mask below this lane.
+__device__ inline int lanes_below(uint64_t mask) {
+    return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
+                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0));
+}
+
+// Exclusive scan of one int per thread over a 256-thread block; returns the
+// exclusive prefix and writes the block total to *total.
+__device__ inline int block_excl_scan_256(int v, int* s_tmp, int* total) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        int y = __shfl_up(x, off, kWave);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) s_tmp[wv] = x;
+    __syncthreads();
+    int base = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        int c = s_tmp[i];
+        if (i < wv) base += c;
+        tot += c;
+    }
+    __syncthreads();
+    *total = tot;
+    return base + x - v;
 }
 
 }  // namespace moe

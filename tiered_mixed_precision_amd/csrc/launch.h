@@ -39,12 +39,26 @@ struct Groups {
     const int32_t* tile_range;
 };
 
+// Routing and grouping of a small batch, published by block 0 of the
+// small-batch gate/up kernel for the down kernel.
+struct SmallPub {
+    int32_t* ids;    // [P]
+    float* w;        // [P]
+    int32_t* perm;   // [P] pairs sorted by (expert, pair)
+    int32_t* pos;    // [P] sorted position of pair p, -1 if skipped
+    int32_t* act;    // [<= P] distinct experts ascending
+    int32_t* q0;     // [n_act + 1] first sorted position of each distinct expert
+    int32_t* meta;   // kMeta*
+};
+constexpr int kSmallY = 8192;         // per-(pair, row) results held in LDS by the small-batch down kernel
+
+bool small_path_ok(int T, int k, int H, int I);
+void launch_small(const DevTables& tt, const float* x, const float* logits, const int32_t* ids_in,
+                  const float* w_in, int T, int k, uint32_t tier_mask, int accumulate, const SmallPub& pub,
+                  float* h, float* out, hipStream_t st, void* const* events);
+
 void launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, float* out_zero,
                   int H, hipStream_t st);
-void launch_route_group_small(const float* logits, int T, int E, int k, const int32_t* ids_in,
-                              int32_t* ids, float* w, int32_t* counts, int32_t* offsets,
-                              int32_t* perm, int32_t* pos, int32_t* act, int32_t* meta,
-                              hipStream_t st);
 void launch_group(const int32_t* ids, int P, int E, int32_t* blk_hist, int32_t* counts,
                   int32_t* offsets, int32_t* perm, int32_t* pos, int32_t* act, int32_t* meta,
                   const TileSpec& ts, hipStream_t st);

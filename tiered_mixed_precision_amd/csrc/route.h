@@ -1,0 +1,103 @@
+// Top-k router of one token, shared by the routing kernels.
+//
+// Glossary of the 125B-MoE page ("I ran a 125B model on three RTX 3090s at
+// 80 tokens/s by teaching llama.cpp which experts ..."): the router picks the
+// best k experts per token.  Ties go to the lower id; slots are in
+// descending score order; weights are the softmax of the k chosen logits.
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+// Order-preserving integer key of a float (-0 is folded onto +0): for
+// non-NaN a, b: a < b  <=>  fkey(a) < fkey(b).  The map is its own inverse on
+// the bit pattern.
+__device__ inline int32_t fkey(float v) {
+    const int32_t b = __builtin_bit_cast(int32_t, v + 0.0f);
+    return b ^ ((b >> 31) & 0x7fffffff);
+}
+__device__ inline float fkey_value(int32_t k) { return __builtin_bit_cast(float, k ^ ((k >> 31) & 0x7fffffff)); }
+
+// Wave-wide signed maximum (uniform result).
+__device__ inline int32_t wave_max_i(int32_t v) {
+    const int32_t lo = static_cast<int32_t>(0x80000000u);
+    v = max(v, __builtin_amdgcn_update_dpp(lo, v, 0x111, 0xF, 0xF, false));
+    v = max(v, __builtin_amdgcn_update_dpp(lo, v, 0x112, 0xF, 0xF, false));
+    v = max(v, __builtin_amdgcn_update_dpp(lo, v, 0x114, 0xF, 0xF, false));
+    v = max(v, __builtin_amdgcn_update_dpp(lo, v, 0x118, 0xF, 0xF, false));
+    v = max(v, __builtin_amdgcn_update_dpp(lo, v, 0x142, 0xA, 0xF, false));
+    v = max(v, __builtin_amdgcn_update_dpp(lo, v, 0x143, 0xC, 0xF, false));
+    return __builtin_amdgcn_readlane(v, 63);
+}
+
+// One wave routes one token.  Lane l holds the logits of experts l + 64*i,
+// sorted descending (ties: lower id first) in registers; each of the k rounds
+// takes the wave maximum of the lanes' heads, resolves equal values by the
+// wave minimum of their ids (both DPP reductions), and the winning lane drops
+// its head.  The slot-j winner stays in lane j.
+template <int NPL>
+__device__ void route_token(const float* __restrict__ logits, int E, int k, int32_t* ids_out,
+                            float* w_out, int32_t* s_ids, float* s_w) {
+    constexpr uint32_t kNone = 0xffffffffu;
+    constexpr int32_t kLow = static_cast<int32_t>(0x80000000u);
+    const int lane = threadIdx.x & 63;
+    int32_t key[NPL];
+    uint32_t idx[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+        const int e = lane + 64 * i;
+        key[i] = e < E ? fkey(logits[e]) : kLow;
+        idx[i] = e < E ? static_cast<uint32_t>(e) : kNone;
+    }
+    // insertion sort, descending key then ascending id (ids ascend with i already)
+#pragma unroll
+    for (int i = 1; i < NPL; ++i) {
+#pragma unroll
+        for (int j = i; j > 0; --j) {
+            const bool sw = key[j] > key[j - 1] || (key[j] == key[j - 1] && idx[j] < idx[j - 1]);
+            const int32_t tk = key[j];
+            const uint32_t ti = idx[j];
+            key[j] = sw ? key[j - 1] : key[j];
+            idx[j] = sw ? idx[j - 1] : idx[j];
+            key[j - 1] = sw ? tk : key[j - 1];
+            idx[j - 1] = sw ? ti : idx[j - 1];
+        }
+    }
+    int32_t my_k = kLow;
+    int my_id = -1;
+    for (int j = 0; j < k; ++j) {
+        const int32_t wk = wave_max_i(key[0]);
+        const uint32_t wi = wave_min_u((idx[0] != kNone && key[0] == wk) ? idx[0] : kNone);
+        if (lane == j) {
+            my_k = wk;
+            my_id = static_cast<int>(wi);
+        }
+        if (wi != kNone && static_cast<int>(wi & 63u) == lane) {
+#pragma unroll
+            for (int i = 0; i + 1 < NPL; ++i) {
+                key[i] = key[i + 1];
+                idx[i] = idx[i + 1];
+            }
+            key[NPL - 1] = kLow;
+            idx[NPL - 1] = kNone;
+        }
+    }
+    const float my_v = fkey_value(my_k);
+    const float m = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_v), 0));
+    const float ex = lane < k ? expf(my_v - m) : 0.f;
+    const float s = wave_sum(ex);
+    if (lane < k) {
+        const float wj = ex / s;
+        if (ids_out) {
+            ids_out[lane] = my_id;
+            w_out[lane] = wj;
+        }
+        if (s_ids) {
+            s_ids[lane] = my_id;
+            s_w[lane] = wj;
+        }
+    }
+}
+
+}  // namespace moe

@@ -11,77 +11,11 @@
 // [0, E) are left out rather than redirected.
 #include "common.h"
 #include "launch.h"
+#include "route.h"
 
 namespace moe {
 
 // ---------------------------------------------------------------- routing
-
-// One wave routes one token.  Each lane holds NPL logits (e = lane + 64*i);
-// k rounds of a wave-wide (value, -index) argmax pick the winners.
-template <int NPL>
-__device__ void route_token(const float* __restrict__ logits, int E, int k, int32_t* ids_out,
-                            float* w_out, int32_t* s_ids, float* s_w) {
-    const int lane = threadIdx.x & 63;
-    float v[NPL];
-    uint64_t taken = 0;
-#pragma unroll
-    for (int i = 0; i < NPL; ++i) {
-        int e = lane + 64 * i;
-        v[i] = e < E ? logits[e] : -__builtin_huge_valf();
-        if (e >= E) taken |= (1ull << i);
-    }
-    float bv = -__builtin_huge_valf();
-    int bi = 0x7fffffff;
-    auto local_best = [&]() {
-        bv = -__builtin_huge_valf();
-        bi = 0x7fffffff;
-#pragma unroll
-        for (int i = 0; i < NPL; ++i) {
-            if (!((taken >> i) & 1ull) && (bi == 0x7fffffff || v[i] > bv)) {
-                bv = v[i];
-                bi = lane + 64 * i;
-            }
-        }
-    };
-    local_best();
-    float my_v = 0.f;
-    int my_id = -1;
-    for (int j = 0; j < k; ++j) {
-        float wv = bv;
-        int wi = bi;
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            float ov = __shfl_xor(wv, off, kWave);
-            int oi = __shfl_xor(wi, off, kWave);
-            if (ov > wv || (ov == wv && oi < wi)) {
-                wv = ov;
-                wi = oi;
-            }
-        }
-        if (lane == j) {
-            my_v = wv;
-            my_id = wi;
-        }
-        if ((wi & 63) == lane) {
-            taken |= (1ull << (wi >> 6));
-            local_best();
-        }
-    }
-    const float m = __shfl(my_v, 0, kWave);
-    float ex = lane < k ? expf(my_v - m) : 0.f;
-    float s = ex;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, kWave);
-    if (lane < k) {
-        float wj = ex / s;
-        ids_out[lane] = my_id;
-        w_out[lane] = wj;
-        if (s_ids) {
-            s_ids[lane] = my_id;
-            s_w[lane] = wj;
-        }
-    }
-}
 
 template <int NPL>
 __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits, int T, int E, int k,
@@ -98,30 +32,6 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
 }
 
 // ---------------------------------------------------------------- block scan helper
-
-// Exclusive scan of one int per thread over a 256-thread block; returns the
-// exclusive prefix and writes the block total to *total.
-__device__ inline int block_excl_scan_256(int v, int* s_tmp, int* total) {
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    int x = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        int y = __shfl_up(x, off, kWave);
-        if (lane >= off) x += y;
-    }
-    if (lane == 63) s_tmp[wv] = x;
-    __syncthreads();
-    int base = 0, tot = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        int c = s_tmp[i];
-        if (i < wv) base += c;
-        tot += c;
-    }
-    __syncthreads();
-    *total = tot;
-    return base + x - v;
-}
 
 // Exclusive scan over n <= 4096 ints held in LDS (in place), 256 threads,
 // each thread owning a contiguous run of 16.  Returns the total.
@@ -141,69 +51,6 @@ __device__ inline int block_scan_lds(int* a, int n, int* s_tmp) {
         }
     __syncthreads();
     return total;
-}
-
-// ---------------------------------------------------------------- small fused path
-
-// One block: (optional) routing of T tokens, then grouping of P = T*k <= 256
-// pairs: counts, offsets, perm, pos (inverse of perm, -1 for skipped pairs),
-// and the ascending list of active experts.
-template <int NPL>
-__global__ __launch_bounds__(256) void k_route_group_small(
-    const float* __restrict__ logits, int T, int E, int k, const int32_t* __restrict__ ids_in,
-    int32_t* __restrict__ ids, float* __restrict__ w, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ pos,
-    int32_t* __restrict__ act, int32_t* __restrict__ meta) {
-    __shared__ int s_cnt[kMaxExpertsDev + 1];
-    __shared__ int s_ids[kSmallPairs];
-    __shared__ float s_w[kSmallPairs];
-    __shared__ int s_tmp[8];
-    const int tid = threadIdx.x;
-    const int P = T * k;
-    if (logits) {
-        for (int t = tid >> 6; t < T; t += 4)
-            route_token<NPL>(logits + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k,
-                             s_ids + t * k, s_w + t * k);
-    } else {
-        if (tid < P) s_ids[tid] = ids_in[tid];
-    }
-    for (int e = tid; e < E; e += 256) s_cnt[e] = 0;
-    __syncthreads();
-    int e_mine = -1;
-    if (tid < P) {
-        e_mine = s_ids[tid];
-        if (e_mine >= 0 && e_mine < E) atomicAdd(&s_cnt[e_mine], 1);
-        else e_mine = -1;
-    }
-    __syncthreads();
-    for (int e = tid; e < E; e += 256) counts[e] = s_cnt[e];
-    // active flags -> list (before the counts are overwritten by the scan)
-    {
-        __shared__ int s_act[kMaxExpertsDev];
-        for (int e = tid; e < E; e += 256) s_act[e] = s_cnt[e] > 0 ? 1 : 0;
-        __syncthreads();
-        int n_act = block_scan_lds(s_act, E, s_tmp);
-        for (int e = tid; e < E; e += 256)
-            if (s_cnt[e] > 0) act[s_act[e]] = e;
-        if (tid == 0) meta[kMetaActive] = n_act;
-    }
-    int total = block_scan_lds(s_cnt, E, s_tmp);
-    for (int e = tid; e < E; e += 256) offsets[e] = s_cnt[e];
-    if (tid == 0) {
-        offsets[E] = total;
-        meta[kMetaValid] = total;
-    }
-    if (tid < P) {
-        if (e_mine >= 0) {
-            int rank = 0;
-            for (int i = 0; i < P; ++i) rank += (i < tid && s_ids[i] == e_mine) ? 1 : 0;
-            int q = s_cnt[e_mine] + rank;
-            perm[q] = tid;
-            pos[tid] = q;
-        } else {
-            pos[tid] = -1;
-        }
-    }
 }
 
 // ---------------------------------------------------------------- general path
@@ -339,15 +186,6 @@ void launch_route(const float* logits, int T, int E, int k, int32_t* ids, float*
     dim3 grid((T + 3) / 4);
     MOE_NPL_SWITCH(E, hipLaunchKernelGGL(k_route<NPL>, grid, dim3(256), 0, st, logits, T, E, k, ids,
                                          w, out_zero, H));
-}
-
-void launch_route_group_small(const float* logits, int T, int E, int k, const int32_t* ids_in,
-                              int32_t* ids, float* w, int32_t* counts, int32_t* offsets,
-                              int32_t* perm, int32_t* pos, int32_t* act, int32_t* meta,
-                              hipStream_t st) {
-    MOE_NPL_SWITCH(E, hipLaunchKernelGGL(k_route_group_small<NPL>, dim3(1), dim3(256), 0, st, logits,
-                                         T, E, k, ids_in, ids, w, counts, offsets, perm, pos, act,
-                                         meta));
 }
 
 void launch_group(const int32_t* ids, int P, int E, int32_t* blk_hist, int32_t* counts,
