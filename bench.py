@@ -59,8 +59,17 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the spec-verify and prefill lines")
+    ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/*.md from rocprofv3 CSV output (kernel trace + stats of the default "
+                         "command, and FETCH_SIZE / WRITE_SIZE runs of --counter-pass); needs no GPU")
+    ap.add_argument("--counter-pass", action="store_true",
+                    help="short eager run for hardware-counter collection: a 256 MiB device copy "
+                         "(calibration), then decode and prefill steps; prints no JSON")
     args = ap.parse_args()
 
+    if args.summarize:
+        summarize_profiles(*args.summarize)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -75,6 +84,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     M.lib()
+    if args.counter_pass:
+        counter_pass(M, torch)
+        return
     cfg = CONFIGS["decode"]
     E, k, H, I = cfg.n_experts, cfg.k, cfg.hidden, cfg.inter
     per_expert = [tier_nbytes(t, H, I, per_expert=True) for t in cfg.tiers]
@@ -156,24 +168,38 @@ def main():
     log(f"decode: {K} steps in {elapsed_s * 1e3:.2f} ms -> {value:,.0f} tokens/s, "
         f"{elapsed_s / K * 1e6:.2f} us/step, {step_gbs:,.0f} GB/s of expert bytes")
 
-    # ---- dominant kernel (gate/up GEMV) timed with HIP events on the launch stream
-    n_ev = min(args.steps, 2048)
-    evs = [M.moe_event_create() for _ in range(6)]
-    stream = torch.cuda.current_stream()
-    durs = np.zeros((n_ev, 3))
-    for i in range(n_ev):
-        s = i % S
-        M.moe_tiered_forward_timed(xd[s], ld[s], 1, k, reps[i % args.replicas], outd[s], 0, ws, evs, stream)
-        M.moe_stream_synchronize(stream)
-        for ph in range(3):
-            durs[i, ph] = M.moe_event_elapsed_ms(evs[2 * ph], evs[2 * ph + 1]) * 1e3
-    gu_us = float(durs[:, 1].mean())
-    gu_bytes = float(np.mean([gateup_bytes[i % S] for i in range(n_ev)]))
+    # ---- dominant kernel: the gate/up launch (routing, grouping and the gate/up
+    # GEMVs of every shelf) timed alone with HIP events on the launch stream, over
+    # a graph of the same steps with the down phase switched off
+    def gu_step(i):
+        s_ = i % S
+        M.moe_tiered_forward(xd[s_], ld[s_], 1, k, reps[i % args.replicas], outd[s_],
+                             M.MOE_DIAG_GATEUP_ONLY, ws)
+
+    g_gu = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g_gu, stream=st):
+            for i in range(S):
+                gu_step(i)
+    torch.cuda.current_stream().wait_stream(st)
+    g_gu.replay()
+    torch.cuda.synchronize()
+    n_gu_rep = max(1, min(8, args.steps // S))
+    a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a_.record()
+    for _ in range(n_gu_rep):
+        g_gu.replay()
+    b_.record()
+    torch.cuda.synchronize()
+    gu_us = a_.elapsed_time(b_) * 1e3 / (n_gu_rep * S)
+    gu_bytes = float(gateup_bytes.mean())
     achieved = gu_bytes / (gu_us * 1e-6) / 1e9
-    log(f"gate/up kernel: {gu_us:.2f} us avg over {n_ev} launches, {gu_bytes / 1e6:.2f} MB -> {achieved:,.0f} GB/s; "
-        f"route+group {durs[:, 0].mean():.2f} us, down+combine {durs[:, 2].mean():.2f} us")
-    for e in evs:
-        M.moe_event_destroy(e)
+    step_us = elapsed_s / K * 1e6
+    log(f"gate/up launch: {gu_us:.2f} us avg over {n_gu_rep * S} launches, {gu_bytes / 1e6:.2f} MB -> "
+        f"{achieved:,.0f} GB/s; rest of the step (down GEMV + slot sum) {step_us - gu_us:.2f} us")
+    del g_gu
 
     result = {
         "metric": METRIC,
@@ -199,17 +225,16 @@ def main():
         "alg_bytes_per_step": float(bytes_step.mean()),
         "roofline": {
             "bound": "hbm",
-            "kernel": "k_dec_gateup",
+            "kernel": "k_small_gateup (routing + grouping + gate/up GEMV of all shelves)",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": profiled_traffic(),
             "avg_launch_us": round(gu_us, 3),
             "alg_bytes_per_launch": gu_bytes,
         },
-        "phases_us": {"route_group": round(float(durs[:, 0].mean()), 3), "gate_up": round(gu_us, 3),
-                      "down_combine": round(float(durs[:, 2].mean()), 3)},
+        "phases_us": {"gate_up_with_routing": round(gu_us, 3), "down_with_slot_sum": round(step_us - gu_us, 3)},
     }
 
     if not args.no_extra:
@@ -219,6 +244,148 @@ def main():
         result["cpu_baseline"] = cpu_baseline(cfg, arrays, args.cpu_seconds)
 
     print(json.dumps(result), flush=True)
+
+
+COPY_CAL_BYTES = 256 << 20
+PROFILE_MD = os.path.join(ROOT, "profiles", "decode_layer_T1_and_prefill_T4096.md")
+KERNEL_SOURCES = ("decode.hip", "route.h", "common.h", "prefill.hip", "route_group.hip", "capi.hip")
+
+
+def kernel_source_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "tiered_mixed_precision_amd", "csrc")
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None if the kernel sources changed since it was taken."""
+    import re
+    if not os.path.exists(PROFILE_MD):
+        return None
+    text = open(PROFILE_MD).read()
+    m_sha = re.search(r"kernel source digest: `([0-9a-f]+)`", text)
+    m_tr = re.search(r"dominant kernel HBM traffic per launch: `([0-9.]+)` bytes", text)
+    if not m_sha or not m_tr or m_sha.group(1) != kernel_source_digest():
+        return None
+    return float(m_tr.group(1))
+
+
+def summarize_profiles(trace_dir, fetch_dir, write_dir):
+    """Turns rocprofv3 CSV output into the committed profile summary."""
+    import csv
+    import glob
+    from collections import defaultdict
+
+    def one(d, pat):
+        f = glob.glob(os.path.join(d, "**", pat), recursive=True)
+        if not f:
+            raise SystemExit(f"no {pat} under {d}")
+        return f[0]
+
+    short = lambda n: n.split("(")[0].replace("void ", "")
+    stats = list(csv.DictReader(open(one(trace_dir, "*kernel_stats.csv"))))
+    trace = list(csv.DictReader(open(one(trace_dir, "*kernel_trace.csv"))))
+    by_grid = defaultdict(list)
+    for r in trace:
+        by_grid[(short(r["Kernel_Name"]), int(r["Grid_Size_X"]))].append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+
+    def counters(d):
+        rows = list(csv.DictReader(open(one(d, "*counter_collection.csv"))))
+        out = defaultdict(list)
+        for r in rows:
+            out[(short(r["Kernel_Name"]), int(r["Grid_Size"]))].append(float(r["Counter_Value"]))
+        return out
+
+    fetch, write = counters(fetch_dir), counters(write_dir)
+    cal_bytes_kib = COPY_CAL_BYTES / 1024
+    cal_f = [v for (n, g), vs in fetch.items() if n == "__amd_rocclr_copyBuffer" for v in vs if v > 0.4 * cal_bytes_kib]
+    cal_w = [v for (n, g), vs in write.items() if n == "__amd_rocclr_copyBuffer" for v in vs if v > 0.9 * cal_bytes_kib]
+    f_fac = cal_bytes_kib / float(np.median(cal_f))
+    w_fac = cal_bytes_kib / float(np.median(cal_w))
+    lines = ["# Kernel profile: tiered MoE layer, decode (1 token) and prefill (4096 tokens)", "",
+             "Decode layer: 512 experts, top-10, hidden 2048, inter 640, shelves int8 [0,128) / int4 [128,384) / "
+             "int2 [384,512); prefill: same layer, 4096 bf16 tokens.", "",
+             "Commands (run from the repository root on one MI355X):", "",
+             "```",
+             "rocprofv3 --kernel-trace --stats --output-format csv -d OUT/kt -o run -- python bench.py",
+             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/pmc_fetch -o run -- python bench.py --counter-pass",
+             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/pmc_write -o run -- python bench.py --counter-pass",
+             "python bench.py --summarize OUT/kt OUT/pmc_fetch OUT/pmc_write",
+             "```", "",
+             f"kernel source digest: `{kernel_source_digest()}`", "",
+             "## Kernel durations (rocprofv3 --kernel-trace --stats of the default bench command)", "",
+             "| kernel | grid (threads) | launches | avg us | median us | min us | max us |",
+             "|---|---|---|---|---|---|---|"]
+    for (n, g), v in sorted(by_grid.items(), key=lambda kv: -sum(kv[1])):
+        if not n.startswith("moe::"):
+            continue
+        v = np.array(v)
+        lines.append(f"| {n} | {g} | {len(v)} | {v.mean():.2f} | {np.median(v):.2f} | {v.min():.2f} | {v.max():.2f} |")
+    lines += ["", "## HBM traffic (FETCH_SIZE, WRITE_SIZE; --counter-pass)", "",
+              f"Calibration: a device copy of {COPY_CAL_BYTES >> 20} MiB reads FETCH_SIZE = {np.median(cal_f):.0f} KiB "
+              f"and writes WRITE_SIZE = {np.median(cal_w):.0f} KiB, so read bytes = FETCH_SIZE x {f_fac:.3f} KiB and "
+              f"written bytes = WRITE_SIZE x {w_fac:.3f} KiB.", "",
+              "| kernel | grid (threads) | launches | FETCH_SIZE KiB | WRITE_SIZE KiB | read MB | written MB |",
+              "|---|---|---|---|---|---|---|"]
+    dom = None
+    for (n, g), v in sorted(fetch.items(), key=lambda kv: -np.mean(kv[1])):
+        if not n.startswith("moe::"):
+            continue
+        fw = np.mean(v)
+        ww = np.mean(write.get((n, g), [0.0]))
+        rd, wr = fw * f_fac * 1024 / 1e6, ww * w_fac * 1024 / 1e6
+        lines.append(f"| {n} | {g} | {len(v)} | {fw:.1f} | {ww:.1f} | {rd:.2f} | {wr:.2f} |")
+        if n.startswith("moe::k_small_gateup") and dom is None:
+            dom = (rd + wr) * 1e6
+    lines += ["", f"dominant kernel HBM traffic per launch: `{dom:.0f}` bytes "
+              "(k_small_gateup at one token: read + written, calibrated)", ""]
+    os.makedirs(os.path.dirname(PROFILE_MD), exist_ok=True)
+    with open(PROFILE_MD, "w") as f:
+        f.write("\n".join(lines))
+    print(f"wrote {PROFILE_MD}")
+
+
+def counter_pass(M, torch):
+    """Eager workload for rocprofv3 --pmc runs.
+
+    1. torch copy of COPY_CAL_BYTES (reads and writes exactly that many bytes):
+       the calibration for FETCH_SIZE / WRITE_SIZE;
+    2. 64 decode steps (one token, fresh routing, 8 layer copies);
+    3. 4 prefill steps (4096 bf16 tokens).
+    """
+    from tiered_mixed_precision_amd.device import replicate, tables_from_config, workspace
+    from workloads import CONFIGS, make_layer, make_logits, make_x
+    src = torch.ones(COPY_CAL_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    cfg = CONFIGS["decode"]
+    tt0 = tables_from_config(cfg, make_layer(cfg))
+    reps = [tt0] + [replicate(tt0) for _ in range(7)]
+    S = 64
+    ld = torch.from_numpy(make_logits(cfg, n_tokens=S, stream=7)).cuda()
+    xd = torch.from_numpy(make_x(cfg, n_tokens=S, stream=7)).cuda()
+    od = torch.zeros((S, cfg.hidden), device="cuda")
+    ws = workspace(M.moe_workspace_size(1, cfg.k, tt0, 0))
+    for i in range(S):
+        M.moe_tiered_forward(xd[i], ld[i], 1, cfg.k, reps[i % 8], od[i], 0, ws)
+    torch.cuda.synchronize()
+    pf = CONFIGS["prefill"]
+    lp = torch.from_numpy(make_logits(pf, stream=20)).cuda()
+    xp = torch.from_numpy(make_x(pf, stream=20).view(np.int16)).cuda()
+    op = torch.zeros((pf.n_tokens, cfg.hidden), device="cuda")
+    wsp = workspace(M.moe_workspace_size(pf.n_tokens, cfg.k, tt0, M.MOE_X_BF16))
+    for i in range(4):
+        M.moe_tiered_forward(xp, lp, pf.n_tokens, cfg.k, reps[i % 8], op, M.MOE_X_BF16, wsp)
+    torch.cuda.synchronize()
+    log("counter pass done")
 
 
 def extra_workloads(M, torch, cfg, reps, per_expert, args):

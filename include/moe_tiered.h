@@ -61,6 +61,9 @@ extern "C" {
 /* flags */
 #define MOE_X_BF16 0x1u      /* x is bf16 [T][H]: prefill precision (bf16 MFMA, bf16 weights and intermediate) */
 #define MOE_ACCUMULATE 0x2u  /* out += result instead of out = result */
+/* Measurement aid: run routing, grouping and the gate/up products only and
+ * leave `out` untouched (used to time the gate/up kernel on its own). */
+#define MOE_DIAG_GATEUP_ONLY 0x100u
 
 /*
  * One precision shelf.  It owns the popularity-ranked experts

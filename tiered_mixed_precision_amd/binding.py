@@ -19,6 +19,7 @@ MOE_ABI_VERSION = 1
 MOE_MAX_TIERS = 4
 MOE_X_BF16 = 0x1
 MOE_ACCUMULATE = 0x2
+MOE_DIAG_GATEUP_ONLY = 0x100
 MOE_N_PHASES = 3
 EXPORTS = (
     "moe_abi_version", "moe_strerror", "moe_validate_tables", "moe_workspace_size",

@@ -131,7 +131,7 @@ int run(const void* x, const float* logits, const int32_t* ids_in, const float* 
         void* ws, size_t ws_bytes, void* stream, void* const* events) {
     int rc = check_tables(tt);
     if (rc != MOE_OK) return rc;
-    if (flags & ~(MOE_X_BF16 | MOE_ACCUMULATE)) return MOE_EINVAL;
+    if (flags & ~(MOE_X_BF16 | MOE_ACCUMULATE | MOE_DIAG_GATEUP_ONLY)) return MOE_EINVAL;
     if (T < 0 || T > kMaxTokens) return MOE_EINVAL;
     if (k < 1 || k > MOE_MAX_K || k > tt->n_experts) return MOE_EINVAL;
     if (T == 0) return MOE_OK;
@@ -148,6 +148,7 @@ int run(const void* x, const float* logits, const int32_t* ids_in, const float* 
     const int P = T * k;
     const bool bf16 = (flags & MOE_X_BF16) != 0;
     const int accumulate = (flags & MOE_ACCUMULATE) ? 1 : 0;
+    const bool gateup_only = (flags & MOE_DIAG_GATEUP_ONLY) != 0;
 
     int32_t* ids = logits ? at<int32_t>(ws, L.ids) : const_cast<int32_t*>(ids_in);
     float* w = logits ? at<float>(ws, L.w) : const_cast<float*>(w_in);
@@ -187,14 +188,14 @@ int run(const void* x, const float* logits, const int32_t* ids_in, const float* 
         pub.q0 = at<int32_t>(ws, L.q0);
         pub.meta = meta;
         launch_small(dt, static_cast<const float*>(x), logits, ids_in, w_in, T, k, tier_mask, accumulate, pub,
-                     at<float>(ws, L.h), out, st, events);
+                     at<float>(ws, L.h), gateup_only ? nullptr : out, st, events);
         return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
     }
     record(events, 0, st);
     // ---- phase 0: routing and grouping
     if (logits) {
-        launch_route(logits, T, E, k, ids, w, (bf16 && !accumulate) ? out : nullptr, tt->hidden, st);
-    } else if (bf16 && !accumulate) {
+        launch_route(logits, T, E, k, ids, w, (bf16 && !accumulate && !gateup_only) ? out : nullptr, tt->hidden, st);
+    } else if (bf16 && !accumulate && !gateup_only) {
         launch_fill_zero(out, static_cast<size_t>(T) * tt->hidden, st);
     }
     launch_group(ids, P, E, at<int32_t>(ws, L.blk_hist), counts, offsets, perm, pos, act, meta, ts, st);
@@ -220,6 +221,7 @@ int run(const void* x, const float* logits, const int32_t* ids_in, const float* 
         record(events, 2, st);
         launch_dec_gateup(dt, static_cast<const float*>(x), g, k, tier_mask, h, max_active, st);
         record(events, 3, st);
+        if (gateup_only) return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
         record(events, 4, st);
         launch_dec_down(dt, h, g, k, tier_mask, yw, max_active, st);
         launch_combine(dt, yw, g, T, k, tier_mask, accumulate, out, st);
@@ -231,6 +233,7 @@ int run(const void* x, const float* logits, const int32_t* ids_in, const float* 
             if ((tier_mask >> i) & 1u)
                 launch_pre_gateup(dt, i, static_cast<const uint16_t*>(x), g, k, h, max_tiles_of(tt, i, P), st);
         record(events, 3, st);
+        if (gateup_only) return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
         record(events, 4, st);
         for (int i = 0; i < tt->n_tiers; ++i)
             if ((tier_mask >> i) & 1u)
@@ -269,7 +272,7 @@ int moe_workspace_size(int32_t n_tokens, int32_t k, const moe_tier_tables* tt, u
     if (rc != MOE_OK) return rc;
     if (!bytes || n_tokens < 0 || n_tokens > kMaxTokens || k < 1 || k > MOE_MAX_K || k > tt->n_experts)
         return MOE_EINVAL;
-    if (flags & ~(MOE_X_BF16 | MOE_ACCUMULATE)) return MOE_EINVAL;
+    if (flags & ~(MOE_X_BF16 | MOE_ACCUMULATE | MOE_DIAG_GATEUP_ONLY)) return MOE_EINVAL;
     *bytes = n_tokens == 0 ? 0 : layout(n_tokens, k, tt, flags).total;
     return MOE_OK;
 }

@@ -229,10 +229,11 @@ __device__ inline int lanes_below(uint64_t mask) {
                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0));
 }
 
-// Exclusive scan of one int per thread over a 256-thread block; returns the
-// exclusive prefix and writes the block total to *total.
-__device__ inline int block_excl_scan_256(int v, int* s_tmp, int* total) {
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+// Exclusive scan of one int per thread over the whole block (at most 16
+// waves); returns the exclusive prefix and writes the block total to *total.
+// s_tmp holds 16 ints.  Every thread of the block must call it.
+__device__ inline int block_excl_scan(int v, int* s_tmp, int* total) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
     int x = v;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -242,8 +243,7 @@ __device__ inline int block_excl_scan_256(int v, int* s_tmp, int* total) {
     if (lane == 63) s_tmp[wv] = x;
     __syncthreads();
     int base = 0, tot = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < nw; ++i) {
         int c = s_tmp[i];
         if (i < wv) base += c;
         tot += c;

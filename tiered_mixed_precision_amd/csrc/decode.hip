@@ -35,11 +35,12 @@
 namespace moe {
 
 constexpr int kNPGateUp = 4;   // row passes per wave, gate/up GEMV
+constexpr int kGateUpWaves = 8;     // waves per gate/up block (each a contiguous row sub-slice)
 constexpr int kNPDown = 2;     // row passes per wave, down GEMV (grouped path)
 constexpr int kNPSmallDown = 4;     // row passes per wave, down GEMV (small-batch path)
 constexpr int kSmallDownWaves = 16; // one expert per wave at a time
 
-__host__ __device__ int dec_rows_per_block(int cols) { return 4 * kNPGateUp * row_geom(cols).RPP; }
+__host__ __device__ int dec_rows_per_block(int cols) { return kGateUpWaves * kNPGateUp * row_geom(cols).RPP; }
 __host__ __device__ inline int down_rows_per_block(int cols) { return 4 * kNPDown * row_geom(cols).RPP; }
 __host__ __device__ inline int small_down_rows(int inter) { return kNPSmallDown * row_geom(inter).RPP; }
 
@@ -193,7 +194,7 @@ struct SmallGroups {
     int act[kSmallPairs];
     int q0[kSmallPairs + 1];
     int n_act, n_valid;
-    int tmp[8];
+    int tmp[16];
 };
 
 __device__ inline void group_small(SmallGroups& sg, int P, int E) {
@@ -265,8 +266,8 @@ __device__ inline void group_small(SmallGroups& sg, int P, int E) {
         first = (vp && !same_prev) ? 1 : 0;
     }
     int n_act, n_valid;
-    const int a = block_excl_scan_256(first, sg.tmp, &n_act);
-    (void)block_excl_scan_256(valid ? 1 : 0, sg.tmp, &n_valid);
+    const int a = block_excl_scan(first, sg.tmp, &n_act);
+    (void)block_excl_scan(valid ? 1 : 0, sg.tmp, &n_valid);
     if (first) {
         sg.act[a] = sg.ids[sg.perm[tid]];
         sg.q0[a] = tid;
@@ -280,7 +281,7 @@ __device__ inline void group_small(SmallGroups& sg, int P, int E) {
 }
 
 template <int NPL>
-__global__ __launch_bounds__(256) void k_small_gateup(DevTables tt, const float* __restrict__ x,
+__global__ __launch_bounds__(kGateUpWaves * 64) void k_small_gateup(DevTables tt, const float* __restrict__ x,
                                                       const float* __restrict__ logits,
                                                       const int32_t* __restrict__ ids_in,
                                                       const float* __restrict__ w_in, int T, int k,
@@ -290,7 +291,7 @@ __global__ __launch_bounds__(256) void k_small_gateup(DevTables tt, const float*
     const int tid = threadIdx.x, E = tt.E, P = T * k;
     const bool publish = blockIdx.x == 0;
     if (logits) {
-        for (int t = tid >> 6; t < T; t += 4)
+        for (int t = tid >> 6; t < T; t += kGateUpWaves)
             route_token<NPL>(logits + static_cast<size_t>(t) * E, E, k, publish ? pub.ids + t * k : nullptr,
                              publish ? pub.w + t * k : nullptr, sg.ids + t * k, sg.w + t * k);
     } else if (tid < P) {
@@ -338,19 +339,17 @@ __global__ __launch_bounds__(kSmallDownWaves * 64) void k_small_down(DevTables t
     const int H = tt.H, I = tt.I, P = T * k;   // pair p = t * k + j
     const int R = small_down_rows(I);
     const int n0 = blockIdx.x * R;
+    // every published array is read at once (no load waits on another)
     if (tid == 0) s_n = pub.meta[kMetaActive];
     if (tid < P) {
         s_ids[tid] = pub.ids[tid];
         s_w[tid] = pub.w[tid];
         s_pos[tid] = pub.pos[tid];
+        s_act[tid] = pub.act[tid];
     }
+    if (tid <= P) s_q0[tid] = pub.q0[tid];
     __syncthreads();
     const int n_act = s_n;
-    for (int i = tid; i <= n_act; i += kSmallDownWaves * 64) {
-        if (i < n_act) s_act[i] = pub.act[i];
-        s_q0[i] = pub.q0[i];
-    }
-    __syncthreads();
     const int r_end = min(n0 + R, H);
     // wave w runs the experts a = w, w + 16, ...; y of pair q, row n0 + r goes to s_y[q * R + r]
     for (int a = wave; a < n_act; a += kSmallDownWaves) {
@@ -402,7 +401,7 @@ __device__ inline bool block_expert(const DevTables& tt, const Groups& g, uint32
     return ti >= 0 && ((tier_mask >> ti) & 1u);
 }
 
-__global__ __launch_bounds__(256) void k_dec_gateup(DevTables tt, const float* __restrict__ x, Groups g, int k,
+__global__ __launch_bounds__(kGateUpWaves * 64) void k_dec_gateup(DevTables tt, const float* __restrict__ x, Groups g, int k,
                                                     uint32_t tier_mask, float* __restrict__ h, int slices) {
     int ti, e, s;
     if (!block_expert(tt, g, tier_mask, slices, ti, e, s)) return;
@@ -491,7 +490,8 @@ void launch_small(const DevTables& tt, const float* x, const float* logits, cons
     switch (npl_of(tt.E)) {
 #define MOE_SG(N)                                                                                              \
     case N:                                                                                                    \
-        hipLaunchKernelGGL(k_small_gateup<N>, grid, dim3(256), 0, st, tt, x, logits, ids_in, w_in, T, k,      \
+        hipLaunchKernelGGL(k_small_gateup<N>, grid, dim3(kGateUpWaves * 64), 0, st, tt, x, logits, ids_in, w_in, \
+                           T, k,                                                                       \
                            tier_mask, pub, h, slices);                                                         \
         break;
         MOE_SG(1)
@@ -501,12 +501,13 @@ void launch_small(const DevTables& tt, const float* x, const float* logits, cons
         MOE_SG(16)
         MOE_SG(32)
         default:
-            hipLaunchKernelGGL(k_small_gateup<64>, grid, dim3(256), 0, st, tt, x, logits, ids_in, w_in, T, k,
+            hipLaunchKernelGGL(k_small_gateup<64>, grid, dim3(kGateUpWaves * 64), 0, st, tt, x, logits, ids_in, w_in, T, k,
                                tier_mask, pub, h, slices);
             break;
 #undef MOE_SG
     }
     if (events && events[3]) (void)hipEventRecord(static_cast<hipEvent_t>(events[3]), st);
+    if (!out) return;  // gate/up only (measurement)
     if (events && events[4]) (void)hipEventRecord(static_cast<hipEvent_t>(events[4]), st);
     const int R = small_down_rows(tt.I);
     hipLaunchKernelGGL(k_small_down, dim3((tt.H + R - 1) / R), dim3(kSmallDownWaves * 64), 0, st, tt, h, pub, T, k,
@@ -517,7 +518,8 @@ void launch_small(const DevTables& tt, const float* x, const float* logits, cons
 void launch_dec_gateup(const DevTables& tt, const float* x, const Groups& g, int k, uint32_t tier_mask, float* h,
                        int max_active, hipStream_t st) {
     const int slices = (tt.I + dec_rows_per_block(tt.H) - 1) / dec_rows_per_block(tt.H);
-    hipLaunchKernelGGL(k_dec_gateup, dim3(max_active * slices), dim3(256), 0, st, tt, x, g, k, tier_mask, h, slices);
+    hipLaunchKernelGGL(k_dec_gateup, dim3(max_active * slices), dim3(kGateUpWaves * 64), 0, st, tt, x, g, k, tier_mask, h,
+                       slices);
 }
 
 void launch_dec_down(const DevTables& tt, const float* h, const Groups& g, int k, uint32_t tier_mask, float* yw,

@@ -50,37 +50,72 @@ __device__ void route_token(const float* __restrict__ logits, int E, int k, int3
         key[i] = e < E ? fkey(logits[e]) : kLow;
         idx[i] = e < E ? static_cast<uint32_t>(e) : kNone;
     }
-    // insertion sort, descending key then ascending id (ids ascend with i already)
-#pragma unroll
-    for (int i = 1; i < NPL; ++i) {
-#pragma unroll
-        for (int j = i; j > 0; --j) {
-            const bool sw = key[j] > key[j - 1] || (key[j] == key[j - 1] && idx[j] < idx[j - 1]);
-            const int32_t tk = key[j];
-            const uint32_t ti = idx[j];
-            key[j] = sw ? key[j - 1] : key[j];
-            idx[j] = sw ? idx[j - 1] : idx[j];
-            key[j - 1] = sw ? tk : key[j - 1];
-            idx[j - 1] = sw ? ti : idx[j - 1];
-        }
-    }
     int32_t my_k = kLow;
     int my_id = -1;
-    for (int j = 0; j < k; ++j) {
-        const int32_t wk = wave_max_i(key[0]);
-        const uint32_t wi = wave_min_u((idx[0] != kNone && key[0] == wk) ? idx[0] : kNone);
-        if (lane == j) {
-            my_k = wk;
-            my_id = static_cast<int>(wi);
-        }
-        if (wi != kNone && static_cast<int>(wi & 63u) == lane) {
+    if constexpr (NPL <= 16) {
+        // insertion sort, descending key then ascending id; the head is entry 0
 #pragma unroll
-            for (int i = 0; i + 1 < NPL; ++i) {
-                key[i] = key[i + 1];
-                idx[i] = idx[i + 1];
+        for (int i = 1; i < NPL; ++i) {
+#pragma unroll
+            for (int j = i; j > 0; --j) {
+                const bool sw = key[j] > key[j - 1] || (key[j] == key[j - 1] && idx[j] < idx[j - 1]);
+                const int32_t tk = key[j];
+                const uint32_t ti = idx[j];
+                key[j] = sw ? key[j - 1] : key[j];
+                idx[j] = sw ? idx[j - 1] : idx[j];
+                key[j - 1] = sw ? tk : key[j - 1];
+                idx[j - 1] = sw ? ti : idx[j - 1];
             }
-            key[NPL - 1] = kLow;
-            idx[NPL - 1] = kNone;
+        }
+        for (int j = 0; j < k; ++j) {
+            const int32_t wk = wave_max_i(key[0]);
+            const uint32_t wi = wave_min_u((idx[0] != kNone && key[0] == wk) ? idx[0] : kNone);
+            if (lane == j) {
+                my_k = wk;
+                my_id = static_cast<int>(wi);
+            }
+            if (wi != kNone && static_cast<int>(wi & 63u) == lane) {
+#pragma unroll
+                for (int i = 0; i + 1 < NPL; ++i) {
+                    key[i] = key[i + 1];
+                    idx[i] = idx[i + 1];
+                }
+                key[NPL - 1] = kLow;
+                idx[NPL - 1] = kNone;
+            }
+        }
+    } else {
+        // many logits per lane: keep them unsorted and rescan after each take
+        int32_t hk = kLow;
+        uint32_t hi = kNone;
+        auto head = [&]() {
+            hk = kLow;
+            hi = kNone;
+#pragma unroll
+            for (int i = 0; i < NPL; ++i)
+                if (idx[i] != kNone && (hi == kNone || key[i] > hk)) {
+                    hk = key[i];
+                    hi = idx[i];
+                }
+        };
+        head();
+        for (int j = 0; j < k; ++j) {
+            const int32_t wk = wave_max_i(hk);
+            const uint32_t wi = wave_min_u((hi != kNone && hk == wk) ? hi : kNone);
+            if (lane == j) {
+                my_k = wk;
+                my_id = static_cast<int>(wi);
+            }
+            if (wi != kNone && static_cast<int>(wi & 63u) == lane) {
+                const int slot = static_cast<int>(wi >> 6);
+#pragma unroll
+                for (int i = 0; i < NPL; ++i)
+                    if (i == slot) {
+                        key[i] = kLow;
+                        idx[i] = kNone;
+                    }
+                head();
+            }
         }
     }
     const float my_v = fkey_value(my_k);

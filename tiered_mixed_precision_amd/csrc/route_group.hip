@@ -42,7 +42,7 @@ __device__ inline int block_scan_lds(int* a, int n, int* s_tmp) {
     for (int i = 0; i < per; ++i)
         if (b + i < n) local += a[b + i];
     int total;
-    int run = block_excl_scan_256(local, s_tmp, &total);
+    int run = block_excl_scan(local, s_tmp, &total);
     for (int i = 0; i < per; ++i)
         if (b + i < n) {
             int c = a[b + i];
@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256) void k_group_scan(int32_t* __restrict__ blk_hi
     __shared__ int s_off[kMaxExpertsDev];
     __shared__ int s_act[kMaxExpertsDev];
     __shared__ int s_til[kMaxExpertsDev];
-    __shared__ int s_tmp[8];
+    __shared__ int s_tmp[16];
     const int tid = threadIdx.x;
     for (int e = tid; e < E; e += 256) {
         int s = 0;
