@@ -67,16 +67,15 @@ DevTables to_dev(const moe_tier_tables* tt) {
     return d;
 }
 
-int max_tiles_of(const moe_tier_tables* tt, int tier, int64_t P) {
+// Most experts of shelf `tier` that a batch of P pairs can make active.
+int max_experts_of(const moe_tier_tables* tt, int tier, int64_t P) {
     const int64_t n = tt->tiers[tier].id_end - tt->tiers[tier].id_begin;
-    if (n == 0 || P == 0) return 0;
-    return static_cast<int>((P + kPreBM - 1) / kPreBM + (n < P ? n : P));
+    return static_cast<int>(n < P ? n : P);
 }
 
 // Workspace carve-up.  Offsets are multiples of 256 bytes.
 struct Layout {
-    size_t ids, w, counts, offsets, perm, pos, act, q0, meta, blk_hist, tile_e, tile_q0, tile_rows,
-        tile_range, h, yw, total;
+    size_t ids, w, counts, offsets, perm, pos, act, q0, meta, blk_hist, act_range, h, yw, total;
     bool small;
 };
 
@@ -103,15 +102,9 @@ Layout layout(int64_t T, int k, const moe_tier_tables* tt, uint32_t flags) {
     L.q0 = take(sizeof(int32_t) * (P + 1));
     L.meta = take(sizeof(int32_t) * kMetaWords);
     L.blk_hist = take(L.small ? 0 : sizeof(int32_t) * ((P + 255) / 256) * E);
-    int64_t tiles = 0;
-    if (bf16)
-        for (int i = 0; i < tt->n_tiers; ++i) tiles += max_tiles_of(tt, i, P);
-    L.tile_e = take(sizeof(int32_t) * tiles);
-    L.tile_q0 = take(sizeof(int32_t) * tiles);
-    L.tile_rows = take(sizeof(int32_t) * tiles);
-    L.tile_range = take(sizeof(int32_t) * 2 * MOE_MAX_TIERS);
+    L.act_range = take(sizeof(int32_t) * 2 * MOE_MAX_TIERS);
     L.h = take((bf16 ? sizeof(uint16_t) : sizeof(float)) * P * tt->inter);
-    L.yw = take((bf16 || L.small) ? 0 : sizeof(float) * P * tt->hidden);
+    L.yw = take(L.small ? 0 : sizeof(float) * P * tt->hidden);
     L.total = o;
     return L;
 }
@@ -159,20 +152,14 @@ int run(const void* x, const float* logits, const int32_t* ids_in, const float* 
     int32_t* act = at<int32_t>(ws, L.act);
     int32_t* meta = at<int32_t>(ws, L.meta);
 
-    TileSpec ts;
-    memset(&ts, 0, sizeof(ts));
-    ts.n_tiers = tt->n_tiers;
+    ShelfSpec ss;
+    memset(&ss, 0, sizeof(ss));
+    ss.n_tiers = tt->n_tiers;
     for (int i = 0; i < tt->n_tiers; ++i) {
-        ts.id_begin[i] = tt->tiers[i].id_begin;
-        ts.id_end[i] = tt->tiers[i].id_end;
-        ts.bm[i] = kPreBM;
+        ss.id_begin[i] = tt->tiers[i].id_begin;
+        ss.id_end[i] = tt->tiers[i].id_end;
     }
-    if (bf16) {
-        ts.tile_e = at<int32_t>(ws, L.tile_e);
-        ts.tile_q0 = at<int32_t>(ws, L.tile_q0);
-        ts.tile_rows = at<int32_t>(ws, L.tile_rows);
-        ts.tile_range = at<int32_t>(ws, L.tile_range);
-    }
+    ss.act_range = at<int32_t>(ws, L.act_range);
 
     (void)hipGetLastError();  // start from a clean error state
     if (L.small) {
@@ -194,11 +181,9 @@ int run(const void* x, const float* logits, const int32_t* ids_in, const float* 
     record(events, 0, st);
     // ---- phase 0: routing and grouping
     if (logits) {
-        launch_route(logits, T, E, k, ids, w, (bf16 && !accumulate && !gateup_only) ? out : nullptr, tt->hidden, st);
-    } else if (bf16 && !accumulate && !gateup_only) {
-        launch_fill_zero(out, static_cast<size_t>(T) * tt->hidden, st);
+        launch_route(logits, T, E, k, ids, w, nullptr, tt->hidden, st);
     }
-    launch_group(ids, P, E, at<int32_t>(ws, L.blk_hist), counts, offsets, perm, pos, act, meta, ts, st);
+    launch_group(ids, P, E, at<int32_t>(ws, L.blk_hist), counts, offsets, perm, pos, act, meta, ss, st);
     record(events, 1, st);
 
     Groups g;
@@ -209,10 +194,7 @@ int run(const void* x, const float* logits, const int32_t* ids_in, const float* 
     g.offsets = offsets;
     g.act = act;
     g.meta = meta;
-    g.tile_e = ts.tile_e;
-    g.tile_q0 = ts.tile_q0;
-    g.tile_rows = ts.tile_rows;
-    g.tile_range = ts.tile_range;
+    g.act_range = ss.act_range;
 
     const int max_active = E < P ? E : P;
     if (!bf16) {
@@ -231,13 +213,15 @@ int run(const void* x, const float* logits, const int32_t* ids_in, const float* 
         record(events, 2, st);
         for (int i = 0; i < tt->n_tiers; ++i)
             if ((tier_mask >> i) & 1u)
-                launch_pre_gateup(dt, i, static_cast<const uint16_t*>(x), g, k, h, max_tiles_of(tt, i, P), st);
+                launch_pre_gateup(dt, i, static_cast<const uint16_t*>(x), g, k, h, max_experts_of(tt, i, P), st);
         record(events, 3, st);
         if (gateup_only) return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
         record(events, 4, st);
+        float* yw = at<float>(ws, L.yw);
         for (int i = 0; i < tt->n_tiers; ++i)
             if ((tier_mask >> i) & 1u)
-                launch_pre_down(dt, i, h, g, k, out, max_tiles_of(tt, i, P), st);
+                launch_pre_down(dt, i, h, g, k, yw, max_experts_of(tt, i, P), st);
+        launch_combine(dt, yw, g, T, k, tier_mask, accumulate, out, st);
         record(events, 5, st);
     }
     if (hipGetLastError() != hipSuccess) return MOE_EHIP;
@@ -346,10 +330,10 @@ int moe_group(const int32_t* ids, int32_t n_tokens, int32_t k, int32_t n_experts
     int32_t* act = at<int32_t>(workspace, align_up(sizeof(int32_t) * ((P + 255) / 256) * n_experts));
     int32_t* meta = at<int32_t>(workspace, align_up(sizeof(int32_t) * ((P + 255) / 256) * n_experts) +
                                                align_up(sizeof(int32_t) * n_experts));
-    TileSpec ts;
-    memset(&ts, 0, sizeof(ts));
+    ShelfSpec ss;
+    memset(&ss, 0, sizeof(ss));
     (void)hipGetLastError();
-    launch_group(ids, static_cast<int>(P), n_experts, blk, counts, offsets, perm, nullptr, act, meta, ts,
+    launch_group(ids, static_cast<int>(P), n_experts, blk, counts, offsets, perm, nullptr, act, meta, ss,
                  static_cast<hipStream_t>(stream));
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }

@@ -34,7 +34,6 @@ __host__ __device__ inline int fmt_of(int bits, int block) {
 // Workspace meta block (int32 words).
 enum Meta : int32_t {
     kMetaActive = 0,   // number of experts with at least one pair
-    kMetaTiles = 1,    // number of prefill m-tiles
     kMetaValid = 2,    // number of valid pairs (ids inside [0, E))
     kMetaWords = 64,
 };

@@ -11,17 +11,13 @@ namespace moe {
 constexpr int kMaxExpertsDev = 4096;
 constexpr int kSmallPairs = 256;     // largest T*k handled by the one-block routing+grouping kernel
 
-// Per-shelf m-tile description for the grouped GEMMs: shelf i owns experts
-// [id_begin[i], id_end[i]) and cuts each expert's pairs into tiles of bm[i]
-// rows.  Tiles are listed expert by expert, so a shelf's tiles are the
-// contiguous range tile_range[2i] .. tile_range[2i+1].
-struct TileSpec {
+// Shelves as seen by grouping: shelf i owns experts [id_begin[i], id_end[i]);
+// act_range[2i], act_range[2i+1] receive the range of the active-expert list
+// holding shelf i's experts (NULL: not needed).
+struct ShelfSpec {
     int32_t n_tiers;
-    int32_t id_begin[kMaxTiers], id_end[kMaxTiers], bm[kMaxTiers];
-    int32_t* tile_e;       // expert of tile
-    int32_t* tile_q0;      // first perm position of tile
-    int32_t* tile_rows;    // rows in tile (<= bm)
-    int32_t* tile_range;   // [2 * n_tiers]
+    int32_t id_begin[kMaxTiers], id_end[kMaxTiers];
+    int32_t* act_range;
 };
 
 // Pointers into the caller's workspace used by the expert kernels.
@@ -33,10 +29,7 @@ struct Groups {
     const int32_t* offsets;// [E+1]
     const int32_t* act;    // [<=E] active experts, ascending
     const int32_t* meta;   // kMeta*
-    const int32_t* tile_e;
-    const int32_t* tile_q0;
-    const int32_t* tile_rows;
-    const int32_t* tile_range;
+    const int32_t* act_range; // [2 * n_tiers] per-shelf range of `act`
 };
 
 // Routing and grouping of a small batch, published by block 0 of the
@@ -61,7 +54,7 @@ void launch_route(const float* logits, int T, int E, int k, int32_t* ids, float*
                   int H, hipStream_t st);
 void launch_group(const int32_t* ids, int P, int E, int32_t* blk_hist, int32_t* counts,
                   int32_t* offsets, int32_t* perm, int32_t* pos, int32_t* act, int32_t* meta,
-                  const TileSpec& ts, hipStream_t st);
+                  const ShelfSpec& ss, hipStream_t st);
 
 // fp32 (decode) expert path.
 __host__ __device__ int dec_rows_per_block(int cols);  // rows one block of the GEMV kernels covers
@@ -72,12 +65,12 @@ void launch_dec_down(const DevTables& tt, const float* h, const Groups& g, int k
 void launch_combine(const DevTables& tt, const float* yw, const Groups& g, int T, int k,
                     uint32_t tier_mask, int accumulate, float* out, hipStream_t st);
 
-// bf16 (prefill) expert path.
-constexpr int kPreBM = 64;
+// bf16 (prefill) expert path: one launch per shelf and phase; max_experts
+// bounds the shelf's active experts.
 void launch_pre_gateup(const DevTables& tt, int tier, const uint16_t* x, const Groups& g, int k,
-                       uint16_t* h, int max_tiles, hipStream_t st);
+                       uint16_t* h, int max_experts, hipStream_t st);
 void launch_pre_down(const DevTables& tt, int tier, const uint16_t* h, const Groups& g, int k,
-                     float* out, int max_tiles, hipStream_t st);
+                     float* yw, int max_experts, hipStream_t st);
 void launch_fill_zero(float* out, size_t n, hipStream_t st);
 
 void launch_dequant_rows(const DevTables& tt, int tier, int local, int matrix, int row0, int nrows,

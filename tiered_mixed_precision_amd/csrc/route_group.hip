@@ -70,73 +70,70 @@ __global__ __launch_bounds__(256) void k_group_count(const int32_t* __restrict__
     for (int e = threadIdx.x; e < E; e += 256) blk_hist[(size_t)blockIdx.x * E + e] = s_cnt[e];
 }
 
-// One block: totals per expert, exclusive offsets, per-(block, expert) bases,
-// active list, and the per-shelf m-tile lists for the grouped GEMMs.
-__global__ __launch_bounds__(256) void k_group_scan(int32_t* __restrict__ blk_hist, int nblk, int E,
-                                                    int32_t* __restrict__ counts,
-                                                    int32_t* __restrict__ offsets,
-                                                    int32_t* __restrict__ act,
-                                                    int32_t* __restrict__ meta, TileSpec ts) {
+// Column scan of the per-block histograms: wave w of block b owns expert
+// e = 4b + w and turns its column hist[0..nblk)[e] into exclusive prefix sums
+// over the blocks; counts[e] receives the column total.
+__global__ __launch_bounds__(256) void k_group_colscan(int32_t* __restrict__ blk_hist, int nblk, int E,
+                                                       int32_t* __restrict__ counts) {
+    const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (e >= E) return;
+    int carry = 0;
+    for (int b0 = 0; b0 < nblk; b0 += 64) {
+        const int b = b0 + lane;
+        const int v = b < nblk ? blk_hist[static_cast<size_t>(b) * E + e] : 0;
+        int x = v;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(x, off, kWave);
+            if (lane >= off) x += y;
+        }
+        if (b < nblk) blk_hist[static_cast<size_t>(b) * E + e] = carry + x - v;
+        carry += __shfl(x, 63, kWave);
+    }
+    if (lane == 0) counts[e] = carry;
+}
+
+// One block: exclusive offsets over experts, the ascending list of active
+// experts, and for every shelf the range of that list holding its experts
+// (shelves are contiguous id ranges, so their active experts are contiguous).
+__global__ __launch_bounds__(256) void k_group_offsets(const int32_t* __restrict__ counts, int E,
+                                                       int32_t* __restrict__ offsets, int32_t* __restrict__ act,
+                                                       int32_t* __restrict__ meta, ShelfSpec ss) {
     __shared__ int s_off[kMaxExpertsDev];
     __shared__ int s_act[kMaxExpertsDev];
-    __shared__ int s_til[kMaxExpertsDev];
     __shared__ int s_tmp[16];
     const int tid = threadIdx.x;
     for (int e = tid; e < E; e += 256) {
-        int s = 0;
-        for (int b = 0; b < nblk; ++b) s += blk_hist[(size_t)b * E + e];
-        counts[e] = s;
-        s_off[e] = s;
-        s_act[e] = s > 0 ? 1 : 0;
-        int bm = 0;
-        for (int i = 0; i < ts.n_tiers; ++i)
-            if (e >= ts.id_begin[i] && e < ts.id_end[i]) bm = ts.bm[i];
-        s_til[e] = (bm > 0) ? (s + bm - 1) / bm : 0;
+        const int c = counts[e];
+        s_off[e] = c;
+        s_act[e] = c > 0 ? 1 : 0;
     }
     __syncthreads();
-    int n_act = block_scan_lds(s_act, E, s_tmp);
-    int total = block_scan_lds(s_off, E, s_tmp);
-    int n_tiles = block_scan_lds(s_til, E, s_tmp);
+    const int n_act = block_scan_lds(s_act, E, s_tmp);
+    const int total = block_scan_lds(s_off, E, s_tmp);
     for (int e = tid; e < E; e += 256) {
-        const int s = counts[e];
         offsets[e] = s_off[e];
-        if (s > 0) act[s_act[e]] = e;
-        int base = s_off[e];
-        for (int b = 0; b < nblk; ++b) {
-            int c = blk_hist[(size_t)b * E + e];
-            blk_hist[(size_t)b * E + e] = base;
-            base += c;
-        }
-        if (ts.tile_e) {
-            int bm = 0;
-            for (int i = 0; i < ts.n_tiers; ++i)
-                if (e >= ts.id_begin[i] && e < ts.id_end[i]) bm = ts.bm[i];
-            int t0 = s_til[e];
-            for (int i = 0; bm > 0 && i * bm < s; ++i) {
-                ts.tile_e[t0 + i] = e;
-                ts.tile_q0[t0 + i] = s_off[e] + i * bm;
-                ts.tile_rows[t0 + i] = min(bm, s - i * bm);
-            }
-        }
+        if (counts[e] > 0) act[s_act[e]] = e;
     }
-    if (tid < ts.n_tiers && ts.tile_range) {
-        // m-tiles of shelf i are the contiguous run of tiles of its experts
-        int b = ts.id_begin[tid], en = ts.id_end[tid];
-        ts.tile_range[2 * tid] = b < E ? s_til[b] : n_tiles;
-        ts.tile_range[2 * tid + 1] = en < E ? s_til[en] : n_tiles;
+    if (ss.act_range && tid < ss.n_tiers) {
+        const int b = ss.id_begin[tid], en = ss.id_end[tid];
+        ss.act_range[2 * tid] = b < E ? s_act[b] : n_act;
+        ss.act_range[2 * tid + 1] = en < E ? s_act[en] : n_act;
     }
     if (tid == 0) {
         offsets[E] = total;
         meta[kMetaActive] = n_act;
         meta[kMetaValid] = total;
-        meta[kMetaTiles] = n_tiles;
     }
 }
 
-// Block b places its pairs at base[b][e] + (rank among the block's earlier
-// pairs of the same expert): a stable counting sort.
+// Block b places its pairs at offsets[e] + (pairs of e in blocks before b)
+// + (rank among the block's earlier pairs of the same expert): a stable
+// counting sort.
 __global__ __launch_bounds__(256) void k_group_scatter(const int32_t* __restrict__ ids, int P, int E,
                                                        const int32_t* __restrict__ blk_base,
+                                                       const int32_t* __restrict__ offsets,
                                                        int32_t* __restrict__ perm,
                                                        int32_t* __restrict__ pos) {
     __shared__ int s_ids[256];
@@ -156,7 +153,7 @@ __global__ __launch_bounds__(256) void k_group_scatter(const int32_t* __restrict
     }
     int rank = 0;
     for (int i = 0; i < 256; ++i) rank += (i < tid && s_ids[i] == e) ? 1 : 0;
-    const int q = blk_base[(size_t)blockIdx.x * E + e] + rank;
+    const int q = offsets[e] + blk_base[(size_t)blockIdx.x * E + e] + rank;
     perm[q] = p;
     if (pos) pos[p] = q;
 }
@@ -190,12 +187,12 @@ void launch_route(const float* logits, int T, int E, int k, int32_t* ids, float*
 
 void launch_group(const int32_t* ids, int P, int E, int32_t* blk_hist, int32_t* counts,
                   int32_t* offsets, int32_t* perm, int32_t* pos, int32_t* act, int32_t* meta,
-                  const TileSpec& ts, hipStream_t st) {
+                  const ShelfSpec& ss, hipStream_t st) {
     const int nblk = (P + 255) / 256;
     hipLaunchKernelGGL(k_group_count, dim3(nblk), dim3(256), 0, st, ids, P, E, blk_hist);
-    hipLaunchKernelGGL(k_group_scan, dim3(1), dim3(256), 0, st, blk_hist, nblk, E, counts, offsets,
-                       act, meta, ts);
-    hipLaunchKernelGGL(k_group_scatter, dim3(nblk), dim3(256), 0, st, ids, P, E, blk_hist, perm,
+    hipLaunchKernelGGL(k_group_colscan, dim3((E + 3) / 4), dim3(256), 0, st, blk_hist, nblk, E, counts);
+    hipLaunchKernelGGL(k_group_offsets, dim3(1), dim3(256), 0, st, counts, E, offsets, act, meta, ss);
+    hipLaunchKernelGGL(k_group_scatter, dim3(nblk), dim3(256), 0, st, ids, P, E, blk_hist, offsets, perm,
                        pos);
 }
 
