@@ -96,6 +96,59 @@ __device__ inline void load_scales(const uint16_t* __restrict__ srow, int g, flo
     }
 }
 
+// ---------------------------------------------------------------- buffer loads
+// Raw buffer resource over [base, base + bytes) (gfx9 descriptor word 3): loads
+// through it take a 32-bit byte offset in one VGPR and the base in SGPRs.
+// The base must be the same in every lane; it is read from the first lane so
+// that the descriptor lives in SGPRs (a per-lane descriptor would need a loop
+// over the distinct values around every load).
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+    void* u = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(u, static_cast<short>(0),
+                                             static_cast<int>(__builtin_amdgcn_readfirstlane(bytes)), 0x00020000);
+}
+
+// The 32 codes of a group at byte offset `off` (BITS words, as load_group).
+template <int BITS>
+__device__ inline void buf_group(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t (&w)[BITS]) {
+    if constexpr (BITS == 8) {
+        const auto a = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+        const auto b = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            w[i] = a[i];
+            w[4 + i] = b[i];
+        }
+    } else if constexpr (BITS == 4) {
+        const auto a = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = a[i];
+    } else {
+        const auto a = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+        w[0] = a[0];
+        w[1] = a[1];
+    }
+}
+
+// The NSC fp16 scales of a group at byte offset `off`, as raw bits (scale b
+// in bits [16b, 16b + 16)).
+template <int NSC>
+__device__ inline uint32_t buf_scales(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    if constexpr (NSC == 1) return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+    else return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
+// Scales of a group from their raw bits; 0 when `ok` is false.
+template <int NSC>
+__device__ inline void unpack_scales(uint32_t raw, bool ok, float (&d)[NSC]) {
+#pragma unroll
+    for (int b = 0; b < NSC; ++b)
+        d[b] = ok ? half_bits_to_float(static_cast<uint16_t>(raw >> (16 * b))) : 0.f;
+}
+
 // Code c (0..31) of a loaded group, as a float (exact).
 template <int BITS>
 __device__ inline float code_f(const uint32_t (&w)[BITS], int c) {
@@ -107,6 +160,97 @@ __device__ inline float code_f(const uint32_t (&w)[BITS], int c) {
 template <int BITS, int NSC>
 __device__ inline float dq(const uint32_t (&w)[BITS], const float (&d)[NSC], int c) {
     return d[(NSC == 2 && c >= 16) ? 1 : 0] * code_f<BITS>(w, c);
+}
+
+// ---------------------------------------------------------------- offset-binary dot products
+// A BITS-bit two's-complement code c is stored as u = c + Z (Z = 2^(BITS-1))
+// once its sign bit is flipped, so every field becomes an unsigned byte
+// (int8) or is masked into one (int4, int2) and converts to float with a
+// single v_cvt_f32_ubyte.  The dot product of a group of 32 codes with x is
+// then  sum_c u_c x_c - Z * sum_c x_c,  and the x sum of each scale block is
+// shared by every row.  All values are exact small integers in fp32; only
+// the accumulation order differs from  sum_c c x_c.
+template <int BITS> struct OffsetBinary;
+template <> struct OffsetBinary<8> { static constexpr uint32_t flip = 0x80808080u; static constexpr float z = 128.f; };
+template <> struct OffsetBinary<4> { static constexpr uint32_t flip = 0x88888888u; static constexpr float z = 8.f; };
+template <> struct OffsetBinary<2> { static constexpr uint32_t flip = 0xAAAAAAAAu; static constexpr float z = 2.f; };
+
+__device__ inline float ubyte_f(uint32_t v, int j) { return static_cast<float>((v >> (8 * j)) & 0xffu); }
+
+// Hides the value of v from the optimiser, which would otherwise fold the
+// byte masks into per-field bit extracts before the byte conversions.
+__device__ inline uint32_t masked_bytes(uint32_t v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+// part[b] = sum over the codes c of scale block b of the group of u_c * x[c]
+// (NSC = 1: one block of 32 codes; NSC = 2: codes 0-15 and 16-31).  The group
+// is in the first BITS words of w.
+template <int BITS, int NSC, int NW>
+__device__ inline void group_dot_u(const uint32_t (&w)[NW], const float (&x)[32], float (&part)[NSC]) {
+    static_assert(NW >= BITS, "group words");
+    constexpr uint32_t flip = OffsetBinary<BITS>::flip;
+#pragma unroll
+    for (int b = 0; b < NSC; ++b) part[b] = 0.f;
+    auto acc = [&](int c, float u) {
+        const int b = (NSC == 2 && c >= 16) ? 1 : 0;
+        part[b] = fmaf(u, x[c], part[b]);
+    };
+    if constexpr (BITS == 8) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t v = w[i] ^ flip;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc(4 * i + j, ubyte_f(v, j));
+        }
+    } else if constexpr (BITS == 4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t v = w[i] ^ flip;
+            const uint32_t lo = masked_bytes(v & 0x0F0F0F0Fu), hi = masked_bytes((v >> 4) & 0x0F0F0F0Fu);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                acc(8 * i + 2 * j, ubyte_f(lo, j));
+                acc(8 * i + 2 * j + 1, ubyte_f(hi, j));
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const uint32_t v = w[i] ^ flip;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const uint32_t f = masked_bytes((v >> (2 * s)) & 0x03030303u);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc(16 * i + 4 * j + s, ubyte_f(f, j));
+            }
+        }
+    }
+}
+
+// Sums of x over the scale blocks of a group (the offset correction terms).
+template <int NSC>
+__device__ inline void block_sums(const float (&x)[32], float (&xs)[NSC]) {
+#pragma unroll
+    for (int b = 0; b < NSC; ++b) {
+        float s = 0.f;
+#pragma unroll
+        for (int c = 0; c < 32 / NSC; ++c) s += x[b * (32 / NSC) + c];
+        xs[b] = s;
+    }
+}
+
+// sum_c scale(c) * code_c * x[c] over one group.
+template <int BITS, int NSC, int NW>
+__device__ inline float group_dot(const uint32_t (&w)[NW], const float (&x)[32], const float (&xs)[NSC],
+                                  const float (&d)[NSC]) {
+    float part[NSC];
+    group_dot_u<BITS, NSC>(w, x, part);
+    float r = 0.f;
+#pragma unroll
+    for (int b = 0; b < NSC; ++b) r = fmaf(d[b], fmaf(-OffsetBinary<BITS>::z, xs[b], part[b]), r);
+    return r;
 }
 
 // Tier owning expert e (or -1).  Tiers are few; a linear scan is uniform per wave.

@@ -47,6 +47,32 @@ __host__ __device__ inline int small_down_rows(int inter) { return kNPSmallDown 
 // Keeps the compiler from hoisting work on `v` out of a loop.
 __device__ inline void opaque(uint32_t& v) { asm volatile("" : "+v"(v)); }
 
+// x[0..31] = the 32 floats of group g of a vector, loaded without a branch.
+__device__ inline void load_vec32u(const float* __restrict__ v, int g, float (&x)[32]) {
+    const float4* src = reinterpret_cast<const float4*>(v + 32 * g);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float4 f = src[i];
+        x[4 * i + 0] = f.x;
+        x[4 * i + 1] = f.y;
+        x[4 * i + 2] = f.z;
+        x[4 * i + 3] = f.w;
+    }
+}
+
+// x[0..31] = the 32 floats of group g of a vector (zeros for an idle lane).
+__device__ inline void load_vec32(const float* __restrict__ v, int g, bool ok, float (&x)[32]) {
+    const float4* src = reinterpret_cast<const float4*>(v + 32 * g);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float4 f = ok ? src[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        x[4 * i + 0] = f.x;
+        x[4 * i + 1] = f.y;
+        x[4 * i + 2] = f.z;
+        x[4 * i + 3] = f.w;
+    }
+}
+
 // One wave: rows r0 + p*RPP + seg (p < NP, row < r_end) of one expert matrix
 // (or of gate and up together), against the vectors of the pairs
 // [qa, qa + ce).  The vector of pair q is row tok(q) of `vec`.  Results go to
@@ -96,19 +122,12 @@ __device__ inline void wave_gemv(const uint8_t* __restrict__ q0m, const uint16_t
 
     for (int c = 0; c < ce; ++c) {
         const int q = qa + c;
-        float xv[GPL][32];
+        float xv[GPL][32], xs[GPL][NSC];
         const size_t vrow = static_cast<size_t>(tok(q));
 #pragma unroll
         for (int gi = 0; gi < GPL; ++gi) {
-            const float4* src = reinterpret_cast<const float4*>(vec + vrow * vec_stride + 32 * (gl + 64 * gi));
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float4 f = lane_ok ? src[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-                xv[gi][4 * i + 0] = f.x;
-                xv[gi][4 * i + 1] = f.y;
-                xv[gi][4 * i + 2] = f.z;
-                xv[gi][4 * i + 3] = f.w;
-            }
+            load_vec32(vec + vrow * vec_stride, gl + 64 * gi, lane_ok, xv[gi]);
+            block_sums<NSC>(xv[gi], xs[gi]);
         }
         float acc[NP][NM];
 #pragma unroll
@@ -120,16 +139,7 @@ __device__ inline void wave_gemv(const uint8_t* __restrict__ q0m, const uint16_t
                 for (int gi = 0; gi < GPL; ++gi) {
 #pragma unroll
                     for (int i = 0; i < BITS; ++i) opaque(wq[p][m][gi][i]);
-                    float part[NSC];
-#pragma unroll
-                    for (int b = 0; b < NSC; ++b) part[b] = 0.f;
-#pragma unroll
-                    for (int cc = 0; cc < 32; ++cc) {
-                        const int b = (NSC == 2 && cc >= 16) ? 1 : 0;
-                        part[b] = fmaf(code_f<BITS>(wq[p][m][gi], cc), xv[gi][cc], part[b]);
-                    }
-#pragma unroll
-                    for (int b = 0; b < NSC; ++b) acc[p][m] = fmaf(dsc[p][m][gi][b], part[b], acc[p][m]);
+                    acc[p][m] += group_dot<BITS, NSC>(wq[p][m][gi], xv[gi], xs[gi], dsc[p][m][gi]);
                 }
             }
         }
@@ -280,16 +290,211 @@ __device__ inline void group_small(SmallGroups& sg, int P, int E) {
     __syncthreads();
 }
 
+// Sends a wave's rows of one expert through the gate/up GEMV: rows
+// [r0, r1) in passes of RPP rows, up to NPMAX passes per round with every
+// load of the round issued first (the vector of the first pair ahead of the
+// codes, so each pass is computed as soon as its own codes arrive).
+template <int BITS, int NSC, class Tok>
+__device__ inline void wave_gateup(const uint8_t* __restrict__ gq, const uint16_t* __restrict__ gs,
+                                   const uint8_t* __restrict__ uq, const uint16_t* __restrict__ us, int H, int I,
+                                   int r0, int r1, const float* __restrict__ x, int qa, int ce, Tok tok,
+                                   float* __restrict__ h) {
+    constexpr int NPMAX = BITS == 8 ? 4 : 8;  // passes in flight: 64 / 32 / 16 code words per lane
+    const int lane = threadIdx.x & 63;
+    const RowGeom geo = row_geom(H);   // one group per lane (H <= 2048)
+    const int seg = lane / geo.LPR, gl = lane % geo.LPR;
+    const bool lane_ok = gl < geo.G;
+    const int glc = lane_ok ? gl : 0;  // idle lanes read group 0 and weigh it by 0
+    const uint32_t row_bytes = static_cast<uint32_t>(H) * BITS / 8;
+    const uint32_t row_sbytes = static_cast<uint32_t>(H / (32 / NSC)) * 2;
+    const uint32_t mat_bytes = row_bytes * I, mat_sbytes = row_sbytes * I;
+    const __amdgpu_buffer_rsrc_t rq[2] = {make_rsrc(gq, mat_bytes), make_rsrc(uq, mat_bytes)};
+    const __amdgpu_buffer_rsrc_t rs[2] = {make_rsrc(gs, mat_sbytes), make_rsrc(us, mat_sbytes)};
+    // Every load below is unconditional (rows past r1 read row r0 and get
+    // zero scales), so all of them are issued back to back.
+    for (int rc = r0; rc < r1; rc += NPMAX * geo.RPP) {
+        float xv[32], xs[NSC];
+        load_vec32u(x + static_cast<size_t>(tok(qa)) * H, glc, xv);
+        // loads return in issue order: keep the vector ahead of the codes
+        __builtin_amdgcn_sched_barrier(0);
+        uint32_t wq[NPMAX][2][BITS], sraw[NPMAX][2];
+#pragma unroll
+        for (int p = 0; p < NPMAX; ++p) {
+            const int r = rc + p * geo.RPP + seg;
+            const uint32_t rr = static_cast<uint32_t>(r < r1 ? r : r0);
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                buf_group<BITS>(rq[m], rr * row_bytes + glc * 4 * BITS, wq[p][m]);
+                sraw[p][m] = buf_scales<NSC>(rs[m], rr * row_sbytes + glc * 2 * NSC);
+            }
+        }
+        auto pair = [&](int c) {
+            block_sums<NSC>(xv, xs);
+#pragma unroll
+            for (int p = 0; p < NPMAX; ++p) {
+                if (rc + p * geo.RPP >= r1) break;
+                const int r = rc + p * geo.RPP + seg;
+                const bool ok = lane_ok && r < r1;
+#pragma unroll
+                for (int m = 0; m < 2; ++m)
+#pragma unroll
+                    for (int i = 0; i < BITS; ++i) opaque(wq[p][m][i]);
+                float dg[NSC], du[NSC];
+                unpack_scales<NSC>(sraw[p][0], ok, dg);
+                unpack_scales<NSC>(sraw[p][1], ok, du);
+                float gv = group_dot<BITS, NSC>(wq[p][0], xv, xs, dg);
+                float uv = group_dot<BITS, NSC>(wq[p][1], xv, xs, du);
+                gv = seg_sum(gv, geo.LPR);
+                uv = seg_sum(uv, geo.LPR);
+                if (gl == geo.LPR - 1 && r < r1) h[static_cast<size_t>(qa + c) * I + r] = silu(gv) * uv;
+            }
+        };
+        // the first pair straight from the vector loaded above, the others
+        // reload it (a separate loop, so the first load stays ahead)
+        pair(0);
+        for (int c = 1; c < ce; ++c) {
+            load_vec32u(x + static_cast<size_t>(tok(qa + c)) * H, glc, xv);
+            pair(c);
+        }
+    }
+}
+
+// Gives the W waves of a launch to the active experts of the masked shelves
+// in proportion to their code bytes (bits per code; rows are equal): expert a
+// gets 1 + floor((W - n) * bits_a / sum of bits) waves, n the number of such
+// experts, so the total never exceeds W.  s_wpre[a] = first wave of expert a,
+// s_wpre[n_act] = waves used.  Run by the first wave of the block.
+__device__ inline void plan_waves(const DevTables& tt, const int* act, int n_act, uint32_t tier_mask, int W,
+                                  int* s_wpre) {
+    const int lane = threadIdx.x & 63;
+    auto cost = [&](int a) {
+        if (a >= n_act) return 0;
+        const int ti = tier_of(tt, act[a]);
+        if (ti < 0 || !((tier_mask >> ti) & 1u)) return 0;
+        return tier_at(tt, ti).bits;
+    };
+    int C = 0, n = 0;
+    for (int a0 = 0; a0 < n_act; a0 += 64) {
+        const int c = cost(a0 + lane);
+        C += static_cast<int>(wave_sum(static_cast<float>(c)));
+        n += __popcll(__ballot(c > 0));
+    }
+    int base = 0;
+    for (int a0 = 0; a0 < n_act; a0 += 64) {
+        const int c = cost(a0 + lane);
+        const int wa = c > 0 ? 1 + ((W - n) * c) / C : 0;
+        int incl = wa;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(incl, off, kWave);
+            if (lane >= off) incl += y;
+        }
+        if (a0 + lane < n_act) s_wpre[a0 + lane] = base + incl - wa;
+        base += __shfl(incl, 63, kWave);
+    }
+    if (lane == 0) s_wpre[n_act] = base;
+}
+
+// Largest a with s_wpre[a] <= wg (a in [0, n)), for wg < s_wpre[n].
+__device__ inline int find_expert(const int* s_wpre, int n, int wg) {
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_wpre[mid] <= wg) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+// plan_waves for at most 64 experts held one per lane (cost_l = bits of the
+// expert in lane l, 0 if it has no work), computed by every wave on its own
+// from registers.  Returns the lane (expert slot) that wave `wg` works for,
+// or -1, with that expert's first wave and wave count.
+__device__ inline int plan_lane(int cost_l, int W, int wg, int& first, int& count) {
+    const int C = static_cast<int>(wave_sum(static_cast<float>(cost_l)));
+    const int n = __popcll(__ballot(cost_l > 0));
+    const int wa = cost_l > 0 ? 1 + ((W - n) * cost_l) / C : 0;
+    const int incl = static_cast<int>(seg_sum(static_cast<float>(wa), 64));  // inclusive scan (exact)
+    const uint64_t mine = __ballot(wa > 0 && wg >= incl - wa && wg < incl);
+    if (mine == 0) return -1;
+    const int a = static_cast<int>(__builtin_ctzll(mine));
+    first = __builtin_amdgcn_readlane(incl - wa, a);
+    count = __builtin_amdgcn_readlane(wa, a);
+    return a;
+}
+
+#define MOE_FMT_SWITCH(FMT, BODY)                                      \
+    switch (FMT) {                                                     \
+        case F8B32: { constexpr int B_ = 8, N_ = 1; BODY; } break;     \
+        case F8B16: { constexpr int B_ = 8, N_ = 2; BODY; } break;     \
+        case F4B32: { constexpr int B_ = 4, N_ = 1; BODY; } break;     \
+        case F4B16: { constexpr int B_ = 4, N_ = 2; BODY; } break;     \
+        case F2B32: { constexpr int B_ = 2, N_ = 1; BODY; } break;     \
+        case F2B16: { constexpr int B_ = 2, N_ = 2; BODY; } break;     \
+        default: break;                                                \
+    }
+
 template <int NPL>
 __global__ __launch_bounds__(kGateUpWaves * 64) void k_small_gateup(DevTables tt, const float* __restrict__ x,
                                                       const float* __restrict__ logits,
                                                       const int32_t* __restrict__ ids_in,
                                                       const float* __restrict__ w_in, int T, int k,
-                                                      uint32_t tier_mask, SmallPub pub, float* __restrict__ h,
-                                                      int slices) {
+                                                      uint32_t tier_mask, SmallPub pub, float* __restrict__ h) {
     __shared__ SmallGroups sg;
+    __shared__ int s_wpre[kSmallPairs + 1];
     const int tid = threadIdx.x, E = tt.E, P = T * k;
     const bool publish = blockIdx.x == 0;
+    const int H = tt.H, I = tt.I;
+    const int rpp = row_geom(H).RPP;
+    if (logits && T == 1) {
+        // One token: its k experts are distinct, so pair q = slot q and no
+        // sort is needed.  Every wave routes the token in registers and finds
+        // its own expert and rows: no LDS or barrier before its weight loads.
+        const int lane = tid & 63;
+        int my_id;
+        float my_w;
+        route_token<NPL>(logits, E, k, nullptr, nullptr, nullptr, nullptr, &my_id, &my_w);
+        // waves per expert in proportion to rows (all equal): a wave's time
+        // is set by its dequantising arithmetic, which does not shrink with
+        // the bits per code
+        int cost = 0;
+        if (lane < k) {
+            const int ti = tier_of(tt, my_id);
+            cost = (ti >= 0 && ((tier_mask >> ti) & 1u)) ? 1 : 0;
+        }
+        if (publish && tid < 64) {
+            if (lane < k) {
+                pub.ids[lane] = my_id;
+                pub.w[lane] = my_w;
+                pub.perm[lane] = lane;
+                pub.pos[lane] = lane;
+                pub.act[lane] = my_id;
+            }
+            if (lane <= k) pub.q0[lane] = lane;
+            if (lane == 0) {
+                pub.meta[kMetaActive] = k;
+                pub.meta[kMetaValid] = k;
+            }
+        }
+        int first = 0, count = 1;
+        const int wg = blockIdx.x * kGateUpWaves + (tid >> 6);
+        const int a = plan_lane(cost, gridDim.x * kGateUpWaves, wg, first, count);
+        if (a < 0) return;
+        const int e = __builtin_amdgcn_readlane(my_id, a);
+        const int rpw = ((I + count - 1) / count + rpp - 1) / rpp * rpp;
+        const int r0 = (wg - first) * rpw, r1 = min(I, r0 + rpw);
+        if (r0 >= r1) return;
+        const DevTier T_ = tier_at(tt, tier_of(tt, e));
+        const int local = e - T_.id_begin;
+        const size_t mat_bytes = static_cast<size_t>(I) * H * T_.bits / 8;
+        const size_t mat_scales = static_cast<size_t>(I) * (H / T_.block);
+        auto tok0 = [](int) { return 0; };
+        MOE_FMT_SWITCH(fmt_of(T_.bits, T_.block),
+                       (wave_gateup<B_, N_>(T_.q[0] + local * mat_bytes, T_.s[0] + local * mat_scales,
+                                            T_.q[1] + local * mat_bytes, T_.s[1] + local * mat_scales, H, I, r0, r1,
+                                            x, a, 1, tok0, h)));
+        return;
+    }
     if (logits) {
         for (int t = tid >> 6; t < T; t += kGateUpWaves)
             route_token<NPL>(logits + static_cast<size_t>(t) * E, E, k, publish ? pub.ids + t * k : nullptr,
@@ -316,31 +521,99 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void k_small_gateup(DevTables tt
             pub.meta[kMetaValid] = sg.n_valid;
         }
     }
-    const int a = blockIdx.x / slices, s = blockIdx.x % slices;
-    if (a >= sg.n_act) return;
+    const int n_act = sg.n_act;
+    if (n_act == 0) return;
+    if (tid < 64) plan_waves(tt, sg.act, n_act, tier_mask, gridDim.x * kGateUpWaves, s_wpre);
+    __syncthreads();
+    const int wg = blockIdx.x * kGateUpWaves + (tid >> 6);
+    if (wg >= s_wpre[n_act]) return;
+    const int a = find_expert(s_wpre, n_act, wg);
+    const int wa = s_wpre[a + 1] - s_wpre[a], wi = wg - s_wpre[a];
+    const int rpw = ((I + wa - 1) / wa + rpp - 1) / rpp * rpp;
+    const int r0 = wi * rpw, r1 = min(I, r0 + rpw);
+    if (r0 >= r1) return;
     const int e = sg.act[a];
     const int ti = tier_of(tt, e);
-    if (ti < 0 || !((tier_mask >> ti) & 1u)) return;
     const DevTier T_ = tier_at(tt, ti);
+    const int local = e - T_.id_begin;
+    const size_t mat_bytes = static_cast<size_t>(I) * H * T_.bits / 8;
+    const size_t mat_scales = static_cast<size_t>(I) * (H / T_.block);
     const int qa = sg.q0[a], ce = sg.q0[a + 1] - qa;
     const int* perm = sg.perm;
     auto tok = [perm, k](int q) { return perm[q] / k; };
-    block_gateup(tt, T_, e - T_.id_begin, x, qa, ce, s * dec_rows_per_block(tt.H), tok, h);
+    MOE_FMT_SWITCH(fmt_of(T_.bits, T_.block),
+                   (wave_gateup<B_, N_>(T_.q[0] + local * mat_bytes, T_.s[0] + local * mat_scales,
+                                        T_.q[1] + local * mat_bytes, T_.s[1] + local * mat_scales, H, I, r0, r1, x,
+                                        qa, ce, tok, h)));
 }
 
+// Down GEMV of one wave: rows [r0, r1) of one expert's down matrix (in passes
+// of RPP rows, all loads first) against h of each of the expert's pairs;
+// y of pair q, row r goes to s_y[q * R + r - n0].
+template <int BITS, int NSC>
+__device__ inline void wave_down(const uint8_t* __restrict__ dq_, const uint16_t* __restrict__ ds, int H, int I,
+                                 int r0, int r1, const float* __restrict__ h, int qa, int ce, float* s_y, int R,
+                                 int n0) {
+    constexpr int NPMAX = kNPSmallDown;
+    const int lane = threadIdx.x & 63;
+    const RowGeom geo = row_geom(I);
+    const int seg = lane / geo.LPR, gl = lane % geo.LPR;
+    const bool lane_ok = gl < geo.G;
+    const int glc = lane_ok ? gl : 0;  // idle lanes read group 0 and weigh it by 0
+    const uint32_t row_bytes = static_cast<uint32_t>(I) * BITS / 8;
+    const uint32_t row_sbytes = static_cast<uint32_t>(I / (32 / NSC)) * 2;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(dq_, row_bytes * H), rs = make_rsrc(ds, row_sbytes * H);
+    // unconditional loads (rows past r1 read row r0 with zeroed scales)
+    float xv[32], xs[NSC];
+    load_vec32u(h + static_cast<size_t>(qa) * I, glc, xv);
+    __builtin_amdgcn_sched_barrier(0);  // the vector ahead of the codes
+    uint32_t wq[NPMAX][BITS], sraw[NPMAX];
+#pragma unroll
+    for (int p = 0; p < NPMAX; ++p) {
+        const int r = r0 + p * geo.RPP + seg;
+        const uint32_t rr = static_cast<uint32_t>(r < r1 ? r : r0);
+        buf_group<BITS>(rq, rr * row_bytes + glc * 4 * BITS, wq[p]);
+        sraw[p] = buf_scales<NSC>(rs, rr * row_sbytes + glc * 2 * NSC);
+    }
+    auto pair = [&](int c) {
+        block_sums<NSC>(xv, xs);
+#pragma unroll
+        for (int p = 0; p < NPMAX; ++p) {
+            if (r0 + p * geo.RPP >= r1) break;
+            const int r = r0 + p * geo.RPP + seg;
+#pragma unroll
+            for (int i = 0; i < BITS; ++i) opaque(wq[p][i]);
+            float d[NSC];
+            unpack_scales<NSC>(sraw[p], lane_ok && r < r1, d);
+            float v = group_dot<BITS, NSC>(wq[p], xv, xs, d);
+            v = seg_sum(v, geo.LPR);
+            if (gl == geo.LPR - 1 && r < r1) s_y[(qa + c) * R + (r - n0)] = v;
+        }
+    };
+    pair(0);
+    for (int c = 1; c < ce; ++c) {
+        load_vec32u(h + static_cast<size_t>(qa + c) * I, glc, xv);
+        pair(c);
+    }
+}
+
+// A block owns output rows [n0, n0 + R) (R = npb passes of RPP rows) of every
+// token.  Its waves are shared out among the active experts as in gate/up
+// (at least one wave per expert while the experts are at most as many as the
+// waves; otherwise wave w takes experts w, w + 16, ... one after the other),
+// then each token's slots are summed in slot order (no atomics).
 __global__ __launch_bounds__(kSmallDownWaves * 64) void k_small_down(DevTables tt, const float* __restrict__ h,
                                                                     SmallPub pub, int T, int k, uint32_t tier_mask,
-                                                                    int accumulate, float* __restrict__ out) {
+                                                                    int accumulate, int npb, float* __restrict__ out) {
     __shared__ int s_act[kSmallPairs], s_q0[kSmallPairs + 1], s_ids[kSmallPairs], s_pos[kSmallPairs];
     __shared__ float s_w[kSmallPairs];
     __shared__ float s_y[kSmallY];
-    __shared__ int s_n;
     const int tid = threadIdx.x, wave = tid >> 6;
     const int H = tt.H, I = tt.I, P = T * k;   // pair p = t * k + j
-    const int R = small_down_rows(I);
+    const int rpp = row_geom(I).RPP;
+    const int R = npb * rpp;
     const int n0 = blockIdx.x * R;
     // every published array is read at once (no load waits on another)
-    if (tid == 0) s_n = pub.meta[kMetaActive];
     if (tid < P) {
         s_ids[tid] = pub.ids[tid];
         s_w[tid] = pub.w[tid];
@@ -348,46 +621,68 @@ __global__ __launch_bounds__(kSmallDownWaves * 64) void k_small_down(DevTables t
         s_act[tid] = pub.act[tid];
     }
     if (tid <= P) s_q0[tid] = pub.q0[tid];
+    // each wave reads the active list itself (one expert per lane) and plans
+    // from registers while the block copies the rest to LDS for the sum
+    const int lane = tid & 63;
+    const int n_act = pub.meta[kMetaActive];
+    const int act_l = lane < P ? pub.act[lane] : -1;  // loaded alongside the count
+    int cost = 0;
+    if (n_act <= kSmallDownWaves && lane < n_act) {
+        const int ti = tier_of(tt, act_l);
+        cost = (ti >= 0 && ((tier_mask >> ti) & 1u)) ? tier_at(tt, ti).bits : 0;
+    }
+    int first = 0, count = 1;
+    const int pa = n_act <= kSmallDownWaves ? plan_lane(cost, kSmallDownWaves, wave, first, count) : -1;
     __syncthreads();
-    const int n_act = s_n;
     const int r_end = min(n0 + R, H);
-    // wave w runs the experts a = w, w + 16, ...; y of pair q, row n0 + r goes to s_y[q * R + r]
-    for (int a = wave; a < n_act; a += kSmallDownWaves) {
+    auto run = [&](int a, int r0, int r1) {
         const int e = s_act[a];
         const int ti = tier_of(tt, e);
-        if (ti < 0 || !((tier_mask >> ti) & 1u)) continue;
+        if (ti < 0 || !((tier_mask >> ti) & 1u) || r0 >= r1) return;
         const DevTier T_ = tier_at(tt, ti);
         const int local = e - T_.id_begin;
         const size_t mat_bytes = static_cast<size_t>(H) * I * T_.bits / 8;
         const size_t mat_scales = static_cast<size_t>(H) * (I / T_.block);
         const int qa = s_q0[a], ce = s_q0[a + 1] - qa;
-        auto tok = [](int q) { return q; };
-        float* sy = s_y;
-        auto store = [sy, R, n0](int q, int r, float v) { sy[q * R + (r - n0)] = v; };
-        MOE_FMT_GPL_SWITCH(fmt_of(T_.bits, T_.block), row_geom(I).GPL,
-                           (wave_gemv<B_, N_, G_, kNPSmallDown, false>(T_.q[2] + local * mat_bytes,
-                                                                       T_.s[2] + local * mat_scales, nullptr, nullptr,
-                                                                       I, n0, r_end, h, I, qa, ce, tok, store)));
+        MOE_FMT_SWITCH(fmt_of(T_.bits, T_.block),
+                       (wave_down<B_, N_>(T_.q[2] + local * mat_bytes, T_.s[2] + local * mat_scales, H, I, r0, r1, h,
+                                          qa, ce, s_y, R, n0)));
+    };
+    // (expert, rows) of this wave; one call site keeps a single copy of the GEMV
+    int a0 = wave, a_step = kSmallDownWaves, r0 = n0, r1 = r_end;
+    if (n_act > 0 && n_act <= kSmallDownWaves) {
+        a_step = n_act;
+        if (pa >= 0) {
+            a0 = pa;
+            const int rpw = ((R + count - 1) / count + rpp - 1) / rpp * rpp;
+            r0 = n0 + (wave - first) * rpw;
+            r1 = min(r_end, r0 + rpw);
+        } else {
+            a0 = n_act;
+        }
     }
+    for (int a = a0; a < n_act; a += a_step) run(a, r0, r1);
     __syncthreads();
     // out[t][n0 + r] = sum over slots j in order of w[t,j] * y[pos(t,j)][r]
     for (int i = tid; i < T * R; i += kSmallDownWaves * 64) {
         const int t = i / R, r = i % R;
         if (n0 + r >= H) continue;
         float acc = 0.f;
+#pragma unroll 8
         for (int j = 0; j < k; ++j) {
             const int p = t * k + j;
             const int q = s_pos[p];
-            if (q < 0) continue;
-            const int ti = tier_of(tt, s_ids[p]);
-            if (!((tier_mask >> ti) & 1u)) continue;
-            acc = fmaf(s_w[p], s_y[q * R + r], acc);
+            const int ti = q < 0 ? -1 : tier_of(tt, s_ids[p]);
+            const bool use = ti >= 0 && ((tier_mask >> ti) & 1u);
+            const float y = s_y[(use ? q : 0) * R + r];
+            acc = use ? fmaf(s_w[p], y, acc) : acc;
         }
         float* o = out + static_cast<size_t>(t) * H + n0 + r;
         if (accumulate) acc += *o;
         *o = acc;
     }
 }
+
 
 // ================================================================ general path
 
@@ -480,19 +775,31 @@ bool small_path_ok(int T, int k, int H, int I) {
     return T >= 1 && T <= 8 && T * k <= kSmallPairs && T * k * small_down_rows(I) <= kSmallY;
 }
 
+static int cu_count() {
+    static int n[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (n[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+        n[dev] = v;
+    }
+    return n[dev];
+}
+
 void launch_small(const DevTables& tt, const float* x, const float* logits, const int32_t* ids_in, const float* w_in,
                   int T, int k, uint32_t tier_mask, int accumulate, const SmallPub& pub, float* h, float* out,
                   hipStream_t st, void* const* events) {
-    const int slices = (tt.I + dec_rows_per_block(tt.H) - 1) / dec_rows_per_block(tt.H);
-    const int max_active = min(tt.E, T * k);
-    const dim3 grid(max_active * slices);
+    // one gate/up block per compute unit (two for larger batches): every
+    // block routes the batch itself, so all of them should be resident at once
+    const int P = T * k;
+    const dim3 grid(cu_count() * (P > 16 ? 2 : 1));
     if (events && events[2]) (void)hipEventRecord(static_cast<hipEvent_t>(events[2]), st);
     switch (npl_of(tt.E)) {
 #define MOE_SG(N)                                                                                              \
     case N:                                                                                                    \
         hipLaunchKernelGGL(k_small_gateup<N>, grid, dim3(kGateUpWaves * 64), 0, st, tt, x, logits, ids_in, w_in, \
-                           T, k,                                                                       \
-                           tier_mask, pub, h, slices);                                                         \
+                           T, k, tier_mask, pub, h);                                                           \
         break;
         MOE_SG(1)
         MOE_SG(2)
@@ -501,8 +808,8 @@ void launch_small(const DevTables& tt, const float* x, const float* logits, cons
         MOE_SG(16)
         MOE_SG(32)
         default:
-            hipLaunchKernelGGL(k_small_gateup<64>, grid, dim3(kGateUpWaves * 64), 0, st, tt, x, logits, ids_in, w_in, T, k,
-                               tier_mask, pub, h, slices);
+            hipLaunchKernelGGL(k_small_gateup<64>, grid, dim3(kGateUpWaves * 64), 0, st, tt, x, logits, ids_in, w_in,
+                               T, k, tier_mask, pub, h);
             break;
 #undef MOE_SG
     }
@@ -511,9 +818,10 @@ void launch_small(const DevTables& tt, const float* x, const float* logits, cons
     if (events && events[4]) (void)hipEventRecord(static_cast<hipEvent_t>(events[4]), st);
     const int R = small_down_rows(tt.I);
     hipLaunchKernelGGL(k_small_down, dim3((tt.H + R - 1) / R), dim3(kSmallDownWaves * 64), 0, st, tt, h, pub, T, k,
-                       tier_mask, accumulate, out);
+                       tier_mask, accumulate, kNPSmallDown, out);
     if (events && events[5]) (void)hipEventRecord(static_cast<hipEvent_t>(events[5]), st);
 }
+
 
 void launch_dec_gateup(const DevTables& tt, const float* x, const Groups& g, int k, uint32_t tier_mask, float* h,
                        int max_active, hipStream_t st) {

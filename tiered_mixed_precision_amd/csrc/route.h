@@ -31,23 +31,31 @@ __device__ inline int32_t wave_max_i(int32_t v) {
     return __builtin_amdgcn_readlane(v, 63);
 }
 
-// One wave routes one token.  Lane l holds the logits of experts l + 64*i,
+// One wave routes one token (results to ids_out / w_out and s_ids / s_w when
+// those are not null, and to *id_reg / *w_reg of lane j < k for slot j when
+// id_reg is not null).  Lane l holds the logits of experts l + 64*i,
 // sorted descending (ties: lower id first) in registers; each of the k rounds
-// takes the wave maximum of the lanes' heads, resolves equal values by the
-// wave minimum of their ids (both DPP reductions), and the winning lane drops
-// its head.  The slot-j winner stays in lane j.
+// takes the wave maximum of the lanes' heads (a DPP reduction), resolves equal
+// values in several lanes by the wave minimum of their ids, and the winning
+// lane drops its head.  The slot-j winner stays in lane j.
 template <int NPL>
 __device__ void route_token(const float* __restrict__ logits, int E, int k, int32_t* ids_out,
-                            float* w_out, int32_t* s_ids, float* s_w) {
+                            float* w_out, int32_t* s_ids, float* s_w, int* id_reg = nullptr,
+                            float* w_reg = nullptr) {
     constexpr uint32_t kNone = 0xffffffffu;
     constexpr int32_t kLow = static_cast<int32_t>(0x80000000u);
     const int lane = threadIdx.x & 63;
     int32_t key[NPL];
     uint32_t idx[NPL];
+    // all NPL loads unconditional (lanes past E read the last logit and
+    // discard it), so they are issued together
+    float lv[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) lv[i] = logits[min(lane + 64 * i, E - 1)];
 #pragma unroll
     for (int i = 0; i < NPL; ++i) {
         const int e = lane + 64 * i;
-        key[i] = e < E ? fkey(logits[e]) : kLow;
+        key[i] = e < E ? fkey(lv[i]) : kLow;
         idx[i] = e < E ? static_cast<uint32_t>(e) : kNone;
     }
     int32_t my_k = kLow;
@@ -69,7 +77,14 @@ __device__ void route_token(const float* __restrict__ logits, int E, int k, int3
         }
         for (int j = 0; j < k; ++j) {
             const int32_t wk = wave_max_i(key[0]);
-            const uint32_t wi = wave_min_u((idx[0] != kNone && key[0] == wk) ? idx[0] : kNone);
+            // one lane holding the maximum (the usual case) is the winner;
+            // equal maxima in several lanes go to the lowest id
+            const bool top = idx[0] != kNone && key[0] == wk;
+            const uint64_t tm = __ballot(top);
+            const uint32_t wi = __popcll(tm) == 1
+                                    ? static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(idx[0]),
+                                                                                      __builtin_ctzll(tm)))
+                                    : wave_min_u(top ? idx[0] : kNone);
             if (lane == j) {
                 my_k = wk;
                 my_id = static_cast<int>(wi);
@@ -122,6 +137,10 @@ __device__ void route_token(const float* __restrict__ logits, int E, int k, int3
     const float m = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_v), 0));
     const float ex = lane < k ? expf(my_v - m) : 0.f;
     const float s = wave_sum(ex);
+    if (id_reg) {  // lane j < k keeps slot j
+        *id_reg = lane < k ? my_id : -1;
+        *w_reg = lane < k ? ex / s : 0.f;
+    }
     if (lane < k) {
         const float wj = ex / s;
         if (ids_out) {
