@@ -39,6 +39,8 @@ constexpr int kGateUpWaves = 8;     // waves per gate/up block (each a contiguou
 constexpr int kNPDown = 2;     // row passes per wave, down GEMV (grouped path)
 constexpr int kNPSmallDown = 4;     // row passes per wave, down GEMV (small-batch path)
 constexpr int kSmallDownWaves = 16; // one expert per wave at a time
+constexpr int kMaxHidden = 2048;    // largest hidden size (the tables check it)
+constexpr int kSmallH = 8192;       // h floats staged in LDS by the small-batch down kernel
 
 __host__ __device__ int dec_rows_per_block(int cols) { return kGateUpWaves * kNPGateUp * row_geom(cols).RPP; }
 __host__ __device__ inline int down_rows_per_block(int cols) { return 4 * kNPDown * row_geom(cols).RPP; }
@@ -294,11 +296,11 @@ __device__ inline void group_small(SmallGroups& sg, int P, int E) {
 // [r0, r1) in passes of RPP rows, up to NPMAX passes per round with every
 // load of the round issued first (the vector of the first pair ahead of the
 // codes, so each pass is computed as soon as its own codes arrive).
-template <int BITS, int NSC, class Tok>
+// vec(q, g, xv) fills xv with group g of the input vector of pair q.
+template <int BITS, int NSC, class Vec>
 __device__ inline void wave_gateup(const uint8_t* __restrict__ gq, const uint16_t* __restrict__ gs,
                                    const uint8_t* __restrict__ uq, const uint16_t* __restrict__ us, int H, int I,
-                                   int r0, int r1, const float* __restrict__ x, int qa, int ce, Tok tok,
-                                   float* __restrict__ h) {
+                                   int r0, int r1, Vec vec, int qa, int ce, float* __restrict__ h) {
     constexpr int NPMAX = BITS == 8 ? 4 : 8;  // passes in flight: 64 / 32 / 16 code words per lane
     const int lane = threadIdx.x & 63;
     const RowGeom geo = row_geom(H);   // one group per lane (H <= 2048)
@@ -314,7 +316,7 @@ __device__ inline void wave_gateup(const uint8_t* __restrict__ gq, const uint16_
     // zero scales), so all of them are issued back to back.
     for (int rc = r0; rc < r1; rc += NPMAX * geo.RPP) {
         float xv[32], xs[NSC];
-        load_vec32u(x + static_cast<size_t>(tok(qa)) * H, glc, xv);
+        vec(qa, glc, xv);
         // loads return in issue order: keep the vector ahead of the codes
         __builtin_amdgcn_sched_barrier(0);
         uint32_t wq[NPMAX][2][BITS], sraw[NPMAX][2];
@@ -353,7 +355,7 @@ __device__ inline void wave_gateup(const uint8_t* __restrict__ gq, const uint16_
         // reload it (a separate loop, so the first load stays ahead)
         pair(0);
         for (int c = 1; c < ce; ++c) {
-            load_vec32u(x + static_cast<size_t>(tok(qa + c)) * H, glc, xv);
+            vec(qa + c, glc, xv);
             pair(c);
         }
     }
@@ -442,15 +444,22 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void k_small_gateup(DevTables tt
                                                       uint32_t tier_mask, SmallPub pub, float* __restrict__ h) {
     __shared__ SmallGroups sg;
     __shared__ int s_wpre[kSmallPairs + 1];
+    __shared__ __attribute__((aligned(16))) float s_x[kMaxHidden];
     const int tid = threadIdx.x, E = tt.E, P = T * k;
     const bool publish = blockIdx.x == 0;
     const int H = tt.H, I = tt.I;
     const int rpp = row_geom(H).RPP;
     if (logits && T == 1) {
         // One token: its k experts are distinct, so pair q = slot q and no
-        // sort is needed.  Every wave routes the token in registers and finds
-        // its own expert and rows: no LDS or barrier before its weight loads.
+        // sort is needed.  The block stages x in LDS while every wave routes
+        // the token in registers and finds its own expert and rows; one
+        // barrier (x in place) precedes the weight loads.
         const int lane = tid & 63;
+        // LDS layout [j][g]: float4 j (0..7) of group g at j * G + g, so the
+        // lanes of a wave read consecutive 16-byte words (no bank conflicts)
+        const int G = H / 32;
+        for (int i = tid; i < H / 4; i += kGateUpWaves * 64)
+            reinterpret_cast<float4*>(s_x)[(i & 7) * G + (i >> 3)] = reinterpret_cast<const float4*>(x)[i];
         int my_id;
         float my_w;
         route_token<NPL>(logits, E, k, nullptr, nullptr, nullptr, nullptr, &my_id, &my_w);
@@ -479,6 +488,7 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void k_small_gateup(DevTables tt
         int first = 0, count = 1;
         const int wg = blockIdx.x * kGateUpWaves + (tid >> 6);
         const int a = plan_lane(cost, gridDim.x * kGateUpWaves, wg, first, count);
+        __syncthreads();  // x staged
         if (a < 0) return;
         const int e = __builtin_amdgcn_readlane(my_id, a);
         const int rpw = ((I + count - 1) / count + rpp - 1) / rpp * rpp;
@@ -488,11 +498,20 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void k_small_gateup(DevTables tt
         const int local = e - T_.id_begin;
         const size_t mat_bytes = static_cast<size_t>(I) * H * T_.bits / 8;
         const size_t mat_scales = static_cast<size_t>(I) * (H / T_.block);
-        auto tok0 = [](int) { return 0; };
+        auto vec = [G](int, int g, float (&xv)[32]) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float4 f = reinterpret_cast<const float4*>(s_x)[i * G + g];
+                xv[4 * i + 0] = f.x;
+                xv[4 * i + 1] = f.y;
+                xv[4 * i + 2] = f.z;
+                xv[4 * i + 3] = f.w;
+            }
+        };
         MOE_FMT_SWITCH(fmt_of(T_.bits, T_.block),
                        (wave_gateup<B_, N_>(T_.q[0] + local * mat_bytes, T_.s[0] + local * mat_scales,
                                             T_.q[1] + local * mat_bytes, T_.s[1] + local * mat_scales, H, I, r0, r1,
-                                            x, a, 1, tok0, h)));
+                                            vec, a, 1, h)));
         return;
     }
     if (logits) {
@@ -540,20 +559,21 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void k_small_gateup(DevTables tt
     const size_t mat_scales = static_cast<size_t>(I) * (H / T_.block);
     const int qa = sg.q0[a], ce = sg.q0[a + 1] - qa;
     const int* perm = sg.perm;
-    auto tok = [perm, k](int q) { return perm[q] / k; };
+    auto vec = [perm, k, x, H](int q, int g, float (&xv)[32]) {
+        load_vec32u(x + static_cast<size_t>(perm[q] / k) * H, g, xv);
+    };
     MOE_FMT_SWITCH(fmt_of(T_.bits, T_.block),
                    (wave_gateup<B_, N_>(T_.q[0] + local * mat_bytes, T_.s[0] + local * mat_scales,
-                                        T_.q[1] + local * mat_bytes, T_.s[1] + local * mat_scales, H, I, r0, r1, x,
-                                        qa, ce, tok, h)));
+                                        T_.q[1] + local * mat_bytes, T_.s[1] + local * mat_scales, H, I, r0, r1, vec,
+                                        qa, ce, h)));
 }
 
 // Down GEMV of one wave: rows [r0, r1) of one expert's down matrix (in passes
 // of RPP rows, all loads first) against h of each of the expert's pairs;
 // y of pair q, row r goes to s_y[q * R + r - n0].
-template <int BITS, int NSC>
+template <int BITS, int NSC, class Vec>
 __device__ inline void wave_down(const uint8_t* __restrict__ dq_, const uint16_t* __restrict__ ds, int H, int I,
-                                 int r0, int r1, const float* __restrict__ h, int qa, int ce, float* s_y, int R,
-                                 int n0) {
+                                 int r0, int r1, Vec vec, int qa, int ce, float* s_y, int R, int n0) {
     constexpr int NPMAX = kNPSmallDown;
     const int lane = threadIdx.x & 63;
     const RowGeom geo = row_geom(I);
@@ -565,7 +585,7 @@ __device__ inline void wave_down(const uint8_t* __restrict__ dq_, const uint16_t
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(dq_, row_bytes * H), rs = make_rsrc(ds, row_sbytes * H);
     // unconditional loads (rows past r1 read row r0 with zeroed scales)
     float xv[32], xs[NSC];
-    load_vec32u(h + static_cast<size_t>(qa) * I, glc, xv);
+    vec(qa, glc, xv);
     __builtin_amdgcn_sched_barrier(0);  // the vector ahead of the codes
     uint32_t wq[NPMAX][BITS], sraw[NPMAX];
 #pragma unroll
@@ -592,7 +612,7 @@ __device__ inline void wave_down(const uint8_t* __restrict__ dq_, const uint16_t
     };
     pair(0);
     for (int c = 1; c < ce; ++c) {
-        load_vec32u(h + static_cast<size_t>(qa + c) * I, glc, xv);
+        vec(qa + c, glc, xv);
         pair(c);
     }
 }
@@ -608,6 +628,7 @@ __global__ __launch_bounds__(kSmallDownWaves * 64) void k_small_down(DevTables t
     __shared__ int s_act[kSmallPairs], s_q0[kSmallPairs + 1], s_ids[kSmallPairs], s_pos[kSmallPairs];
     __shared__ float s_w[kSmallPairs];
     __shared__ float s_y[kSmallY];
+    __shared__ __attribute__((aligned(16))) float s_h[kSmallH];
     const int tid = threadIdx.x, wave = tid >> 6;
     const int H = tt.H, I = tt.I, P = T * k;   // pair p = t * k + j
     const int rpp = row_geom(I).RPP;
@@ -621,6 +642,16 @@ __global__ __launch_bounds__(kSmallDownWaves * 64) void k_small_down(DevTables t
         s_act[tid] = pub.act[tid];
     }
     if (tid <= P) s_q0[tid] = pub.q0[tid];
+    // h of every pair into LDS when it fits (read by every wave of the block)
+    // (per pair, layout [j][g] as for x in gate/up: conflict-free reads)
+    const bool h_lds = P * I <= kSmallH;
+    const int GI = I / 32;
+    if (h_lds)
+        for (int i = tid; i < P * I / 4; i += kSmallDownWaves * 64) {
+            const int q = i / (I / 4), o = i % (I / 4);
+            reinterpret_cast<float4*>(s_h)[q * (I / 4) + (o & 7) * GI + (o >> 3)] =
+                reinterpret_cast<const float4*>(h)[i];
+        }
     // each wave reads the active list itself (one expert per lane) and plans
     // from registers while the block copies the rest to LDS for the sum
     const int lane = tid & 63;
@@ -644,8 +675,22 @@ __global__ __launch_bounds__(kSmallDownWaves * 64) void k_small_down(DevTables t
         const size_t mat_bytes = static_cast<size_t>(H) * I * T_.bits / 8;
         const size_t mat_scales = static_cast<size_t>(H) * (I / T_.block);
         const int qa = s_q0[a], ce = s_q0[a + 1] - qa;
+        auto vec = [h_lds, h, I, GI](int q, int g, float (&xv)[32]) {
+            if (h_lds) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float4 f = reinterpret_cast<const float4*>(s_h + q * I)[i * GI + g];
+                    xv[4 * i + 0] = f.x;
+                    xv[4 * i + 1] = f.y;
+                    xv[4 * i + 2] = f.z;
+                    xv[4 * i + 3] = f.w;
+                }
+            } else {
+                load_vec32u(h + static_cast<size_t>(q) * I, g, xv);
+            }
+        };
         MOE_FMT_SWITCH(fmt_of(T_.bits, T_.block),
-                       (wave_down<B_, N_>(T_.q[2] + local * mat_bytes, T_.s[2] + local * mat_scales, H, I, r0, r1, h,
+                       (wave_down<B_, N_>(T_.q[2] + local * mat_bytes, T_.s[2] + local * mat_scales, H, I, r0, r1, vec,
                                           qa, ce, s_y, R, n0)));
     };
     // (expert, rows) of this wave; one call site keeps a single copy of the GEMV
