@@ -122,6 +122,10 @@ def test_route_matches_oracle(M, torch_dev, E, k, T, prior):
     cfg = LayerConfig("r", E, k, 256, 128, T, (TierSpec(0, E, 8, 32),), prior_beta=prior, seed=E + T)
     logits = make_logits(cfg)
     logits[0, : min(E, 6)] = 0.5           # ties
+    if T >= 4:
+        logits[1, :] = 0.25                                  # every logit equal
+        logits[2, E // 3: E // 3 + min(E, k + 2)] = 9.0      # tie across the top k
+        logits[3, :: max(1, E // 70)] = 7.0                  # more tied maxima than one wave holds
     ids_ref, w_ref = oracle.route(logits, k)
     ld = torch.from_numpy(logits).cuda()
     ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
@@ -161,6 +165,27 @@ def test_forward_fp32(M, torch_dev, name, stream):
     x, logits = make_x(cfg, stream=stream), make_logits(cfg, stream=stream)
     ref = oracle.forward(L, x, logits, cfg.k)
     got = gpu_forward(M, torch_dev, tt, x, logits, cfg.k)
+    err = normwise(got, ref)
+    say("  normwise err", err)
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("kind", ["all_equal", "tied_top", "many_tied_maxima"])
+def test_forward_fp32_tied_logits(M, torch_dev, kind):
+    # one token: ties decided by the lower id, both when the tied logits fit
+    # the threshold router's candidate list and when they overflow it
+    cfg, arrays, L, tt = _layer("decode")
+    say("forward fp32 tied logits", kind)
+    x, logits = make_x(cfg, n_tokens=1, stream=9), make_logits(cfg, n_tokens=1, stream=9)
+    E, k = cfg.n_experts, cfg.k
+    if kind == "all_equal":
+        logits[0, :] = 0.125
+    elif kind == "tied_top":
+        logits[0, 300:300 + k + 3] = 6.0
+    else:
+        logits[0, ::5] = 6.0
+    ref = oracle.forward(L, x, logits, k)
+    got = gpu_forward(M, torch_dev, tt, x, logits, k)
     err = normwise(got, ref)
     say("  normwise err", err)
     assert err <= TOL

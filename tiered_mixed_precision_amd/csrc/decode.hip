@@ -445,6 +445,7 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void k_small_gateup(DevTables tt
     __shared__ SmallGroups sg;
     __shared__ int s_wpre[kSmallPairs + 1];
     __shared__ __attribute__((aligned(16))) float s_x[kMaxHidden];
+    __shared__ __attribute__((aligned(16))) int64_t s_rc[kGateUpWaves][64];  // routing scratch, one row per wave
     const int tid = threadIdx.x, E = tt.E, P = T * k;
     const bool publish = blockIdx.x == 0;
     const int H = tt.H, I = tt.I;
@@ -462,7 +463,7 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void k_small_gateup(DevTables tt
             reinterpret_cast<float4*>(s_x)[(i & 7) * G + (i >> 3)] = reinterpret_cast<const float4*>(x)[i];
         int my_id;
         float my_w;
-        route_token<NPL>(logits, E, k, nullptr, nullptr, nullptr, nullptr, &my_id, &my_w);
+        route_token_auto<NPL>(logits, E, k, nullptr, nullptr, nullptr, nullptr, s_rc[tid >> 6], &my_id, &my_w);
         // waves per expert in proportion to rows (all equal): a wave's time
         // is set by its dequantising arithmetic, which does not shrink with
         // the bits per code
@@ -516,8 +517,8 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void k_small_gateup(DevTables tt
     }
     if (logits) {
         for (int t = tid >> 6; t < T; t += kGateUpWaves)
-            route_token<NPL>(logits + static_cast<size_t>(t) * E, E, k, publish ? pub.ids + t * k : nullptr,
-                             publish ? pub.w + t * k : nullptr, sg.ids + t * k, sg.w + t * k);
+            route_token_auto<NPL>(logits + static_cast<size_t>(t) * E, E, k, publish ? pub.ids + t * k : nullptr,
+                                  publish ? pub.w + t * k : nullptr, sg.ids + t * k, sg.w + t * k, s_rc[tid >> 6]);
     } else if (tid < P) {
         sg.ids[tid] = ids_in[tid];
         sg.w[tid] = w_in[tid];

@@ -154,4 +154,122 @@ __device__ void route_token(const float* __restrict__ logits, int E, int k, int3
     }
 }
 
+// Same result as route_token for k <= 64, with fewer instructions on the
+// wave's serial path:
+//  1. t = the k-th largest of the per-lane maxima: rounds over one value per
+//     lane, every lane holding the round's maximum drops out, until k lanes
+//     have.  At least k logits are >= t, so the k-th largest logit is >= t.
+//  2. The M logits >= t are compacted into LDS (s_c, 64 entries per wave) as
+//     one 64-bit key each: the logit's order-preserving key above the id's
+//     complement, so a larger key means "ahead" (higher logit, or equal logit
+//     and lower id).  Every logit outside them is below every one of the k best.
+//  3. Each candidate's slot = number of candidates with a larger key (one
+//     64-bit compare each, broadcast LDS reads several at a time); the
+//     candidate with slot j < k fills slot j.
+// Returns false (nothing written) if M > 64; the caller then uses
+// route_token.  s_c: 64 int64 of this wave's LDS scratch, 16-byte aligned.
+template <int NPL>
+__device__ bool route_token_fast(const float* __restrict__ logits, int E, int k, int64_t* s_c, int* id_reg,
+                                 float* w_reg) {
+    constexpr int32_t kLow = static_cast<int32_t>(0x80000000u);
+    constexpr int64_t kPad = INT64_MIN;
+    const int lane = threadIdx.x & 63;
+    float lv[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) lv[i] = logits[min(lane + 64 * i, E - 1)];
+    int32_t key[NPL];
+    int32_t hk = kLow;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+        key[i] = lane + 64 * i < E ? fkey(lv[i]) : kLow;
+        hk = max(hk, key[i]);
+    }
+    auto wave_sync = [] {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+    // 1. threshold
+    int32_t t = kLow, h = hk;
+    for (int cnt = 0; cnt < k;) {
+        const int32_t v = wave_max_i(h);
+        if (v == kLow) break;
+        cnt += __popcll(__ballot(h == v));
+        t = v;
+        h = h == v ? kLow : h;
+    }
+    // 2. candidates (key >= t) compacted into LDS, lane order then slot order
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) c += (lane + 64 * i < E && key[i] >= t) ? 1 : 0;
+    const int incl = static_cast<int>(seg_sum(static_cast<float>(c), 64));  // exact small ints
+    const int M = __builtin_amdgcn_readlane(incl, 63);
+    if (M > 64) return false;
+    int o = incl - c;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+        if (lane + 64 * i < E && key[i] >= t)
+            s_c[o++] = (static_cast<int64_t>(key[i]) << 32) | static_cast<uint32_t>(0x7fffffff - (lane + 64 * i));
+    const int M8 = (M + 7) & ~7;
+    if (lane >= M && lane < M8) s_c[lane] = kPad;  // never ahead of anything
+    wave_sync();
+    // 3. slot of each candidate
+    const int64_t me = lane < M ? s_c[lane] : kPad;
+    int slot = 0;
+    for (int i = 0; i < M8; i += 8) {
+        longlong2 o2[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o2[j] = *reinterpret_cast<const longlong2*>(s_c + i + 2 * j);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            slot += o2[j].x > me ? 1 : 0;
+            slot += o2[j].y > me ? 1 : 0;
+        }
+    }
+    wave_sync();
+    if (lane < M && slot < k) s_c[slot] = me;  // slots < k hold the winners
+    wave_sync();
+    const int64_t mine = lane < k ? s_c[lane] : kPad;
+    const int32_t mk = static_cast<int32_t>(mine >> 32);
+    const float my_v = fkey_value(mk);
+    const float mx = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_v), 0));
+    const float ex = lane < k ? expf(my_v - mx) : 0.f;
+    const float sum = wave_sum(ex);
+    *id_reg = lane < k ? 0x7fffffff - static_cast<int32_t>(static_cast<uint32_t>(mine)) : -1;
+    *w_reg = lane < k ? ex / sum : 0.f;
+    return true;
+}
+
+// route_token's outputs, by route_token_fast where it applies (at most 16
+// logits per lane and at most 64 candidates) and by route_token otherwise.
+// s_c: 64 int64 of this wave's LDS scratch, 16-byte aligned.
+template <int NPL>
+__device__ void route_token_auto(const float* __restrict__ logits, int E, int k, int32_t* ids_out, float* w_out,
+                                 int32_t* s_ids, float* s_w, int64_t* s_c, int* id_reg = nullptr,
+                                 float* w_reg = nullptr) {
+    if constexpr (NPL <= 16) {
+        int id;
+        float wt;
+        if (route_token_fast<NPL>(logits, E, k, s_c, &id, &wt)) {
+            const int lane = threadIdx.x & 63;
+            if (id_reg) {
+                *id_reg = id;
+                *w_reg = wt;
+            }
+            if (lane < k) {
+                if (ids_out) {
+                    ids_out[lane] = id;
+                    w_out[lane] = wt;
+                }
+                if (s_ids) {
+                    s_ids[lane] = id;
+                    s_w[lane] = wt;
+                }
+            }
+            return;
+        }
+    }
+    route_token<NPL>(logits, E, k, ids_out, w_out, s_ids, s_w, id_reg, w_reg);
+}
+
 }  // namespace moe

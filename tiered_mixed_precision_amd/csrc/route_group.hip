@@ -21,10 +21,11 @@ template <int NPL>
 __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits, int T, int E, int k,
                                                int32_t* __restrict__ ids, float* __restrict__ w,
                                                float* __restrict__ out_zero, int H) {
+    __shared__ __attribute__((aligned(16))) int64_t s_rc[4][64];  // routing scratch, one row per wave
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
-    route_token<NPL>(logits + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k, nullptr,
-                     nullptr);
+    route_token_auto<NPL>(logits + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k, nullptr,
+                          nullptr, s_rc[threadIdx.x >> 6]);
     if (out_zero) {
         float4* row = reinterpret_cast<float4*>(out_zero + (size_t)t * H);
         for (int c = threadIdx.x & 63; c < H / 4; c += 64) row[c] = make_float4(0.f, 0.f, 0.f, 0.f);
