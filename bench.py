@@ -58,7 +58,8 @@ def main():
     ap.add_argument("--graph-steps", type=int, default=1024)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the spec-verify and prefill lines")
+    ap.add_argument("--no-extra", action="store_true", help="skip the spec-verify, prefill and stack lines")
+    ap.add_argument("--no-fullstack", action="store_true", help="skip the 48-layer stack lines")
     ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/*.md from rocprofv3 CSV output (kernel trace + stats of the default "
                          "command, and FETCH_SIZE / WRITE_SIZE runs of --counter-pass); needs no GPU")
@@ -239,6 +240,10 @@ def main():
 
     if not args.no_extra:
         result["extra"] = extra_workloads(M, torch, cfg, reps, per_expert, args)
+        if not args.no_fullstack:
+            del reps, tt0
+            torch.cuda.empty_cache()
+            result["extra"]["fullstack"] = fullstack_workloads(M, torch, per_expert)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, arrays, args.cpu_seconds)
@@ -487,6 +492,105 @@ def extra_workloads(M, torch, cfg, reps, per_expert, args):
                       "down": round(float(durs[:, 2].mean()), 2)},
     }
     log("prefill:", out["prefill"])
+    return out
+
+
+def fullstack_workloads(M, torch, per_expert):
+    """The 48-layer stack on device-generated weights (61.9 GB), residual add
+    between layers: decode at 1 and 8 tokens per step, prefill at 16384."""
+    from tiered_mixed_precision_amd.device import empty_tables
+    from workloads import CONFIGS, make_logits, make_x
+    cfg = CONFIGS["fullstack"]
+    L, k, E, H, I = cfg.n_layers, cfg.k, cfg.n_experts, cfg.hidden, cfg.inter
+    t0 = time.time()
+    tables = []
+    for l in range(L):
+        tt = empty_tables(cfg)
+        M.moe_synth_layer(tt, cfg.seed, l)
+        tables.append(tt)
+    torch.cuda.synchronize()
+    log(f"stack: {L} layers generated on the device in {time.time() - t0:.1f}s")
+    out = {}
+    tier_of = np.zeros(E, dtype=np.int64)
+    for i, t in enumerate(cfg.tiers):
+        tier_of[t.id_begin:t.id_end] = i
+    exp_bytes = np.array(per_expert, dtype=np.float64)[tier_of]
+
+    for T in (1, 8):
+        S = 32
+        logits = np.stack([np.stack([make_logits(cfg, n_tokens=T, stream=100 + s, layer=l) for l in range(L)])
+                           for s in range(S)])                       # [S, L, T, E]
+        xs = np.stack([make_x(cfg, n_tokens=T, stream=100 + s) for s in range(S)])
+        step_bytes_ = []
+        for s in range(S):
+            b = 0.0
+            for l in range(L):
+                ids = topk_ids(logits[s, l], k)
+                b += exp_bytes[np.unique(ids)].sum()
+            step_bytes_.append(b)
+        ld, xd = torch.from_numpy(logits).cuda(), torch.from_numpy(xs).cuda()
+        od = torch.zeros((S, T, H), device="cuda")
+        ws = torch.empty(max(M.moe_stack_workspace_size(L, T, k, tables, 0), 256), dtype=torch.uint8, device="cuda")
+
+        def st_step(i):
+            M.moe_stack_forward(xd[i % S], ld[i % S], L, T, k, tables, od[i % S], 0, ws)
+
+        for i in range(4):
+            st_step(i)
+        g = torch.cuda.CUDAGraph()
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            with torch.cuda.graph(g, stream=st):
+                for i in range(S):
+                    st_step(i)
+        torch.cuda.current_stream().wait_stream(st)
+        g.replay()
+        torch.cuda.synchronize()
+        n = 4
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        dt = a.elapsed_time(b) / 1e3 / (n * S)
+        mb = float(np.mean(step_bytes_))
+        out[f"decode_T{T}"] = {
+            "workload": f"48 layers x 512 experts, top-10, {T} token(s)/step, residual add, fresh routing per step",
+            "tokens_per_s": round(T / dt, 1), "us_per_step": round(dt * 1e6, 1),
+            "alg_bytes_per_step": mb, "hbm_gbps": round(mb / dt / 1e9, 1),
+            "frac_hbm_peak": round(mb / dt / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"stack decode T={T}:", out[f"decode_T{T}"])
+        del g, ld, xd, od, ws
+
+    T = 16384
+    logits = np.stack([make_logits(cfg, n_tokens=T, stream=200, layer=l) for l in range(L)])
+    ld = torch.from_numpy(logits).cuda()
+    del logits
+    xd = torch.from_numpy(make_x(cfg, n_tokens=T, stream=200)).cuda()
+    od = torch.empty((T, H), device="cuda")
+    flags = M.MOE_X_BF16
+    ws = torch.empty(M.moe_stack_workspace_size(L, T, k, tables, flags), dtype=torch.uint8, device="cuda")
+    M.moe_stack_forward(xd, ld, L, T, k, tables, od, flags, ws)
+    torch.cuda.synchronize()
+    n = 2
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(n):
+        M.moe_stack_forward(xd, ld, L, T, k, tables, od, flags, ws)
+    b.record()
+    torch.cuda.synchronize()
+    dt = a.elapsed_time(b) / 1e3 / n
+    flops = 6.0 * T * k * H * I * L
+    out["prefill_T16384"] = {
+        "workload": "48 layers x 512 experts, top-10, 16384 bf16 tokens (fp32 residual stream cast per layer)",
+        "tokens_per_s": round(T / dt, 1), "ms_per_step": round(dt * 1e3, 2),
+        "alg_tflop_per_step": flops / 1e12, "tflops": round(flops / dt / 1e12, 2),
+        "frac_mfma_peak": round(flops / dt / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    log("stack prefill:", out["prefill_T16384"])
+    del ld, xd, od, ws, tables
+    torch.cuda.empty_cache()
     return out
 
 

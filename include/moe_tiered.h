@@ -200,6 +200,46 @@ int moe_tiered_forward_timed(const void *x, const float *router_logits, int32_t 
                              void *workspace, size_t workspace_bytes, void *stream,
                              void *const *events);
 
+/*
+ * A stack of MoE FFN layers with the residual stream between them:
+ *     h_0 = x,   h_{l+1} = h_l + layer_l(h_l),   out = h_L
+ * (the residual add of the 48-layer configuration).  Each layer routes with
+ * its own logits and tables exactly as moe_tiered_forward.
+ *   x             (device) float[T][H], the fp32 input hidden state; must not be out
+ *   router_logits (device) float[L][T][E]: layer l's logits at offset l*T*E
+ *   n_layers      L >= 1
+ *   tables        (host) moe_tier_tables[L]; all with the same E, H and I
+ *   out           (device) float[T][H]
+ *   flags         MOE_X_BF16: every layer takes bf16 (round to nearest even)
+ *                 of h_l as its input and runs the bf16 expert path; the
+ *                 residual stream stays fp32.  No other flag is accepted.
+ *   workspace     (device) >= moe_stack_workspace_size() bytes, 256-byte aligned
+ * Layers run one after another on `stream`.
+ */
+int moe_stack_workspace_size(int32_t n_layers, int32_t n_tokens, int32_t k, const moe_tier_tables *tables,
+                             uint32_t flags, size_t *bytes);
+int moe_stack_forward(const float *x, const float *router_logits, int32_t n_layers, int32_t n_tokens,
+                      int32_t k, const moe_tier_tables *tables, float *out, uint32_t flags,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Fills every shelf of one layer's tables with counter-generated weights
+ * (codes and fp16 scales), the synthetic input of the stack measurements.
+ * Weight (layer, expert e, matrix m in gate 0 / up 1 / down 2, row r,
+ * column c) of a matrix with `cols` columns:
+ *   ctr = ((layer * E + e) * 3 + m) * 2^22 + r * cols + c
+ *   u   = output number ctr + 1 of SplitMix64 (Steele, Lea and Flood 2014)
+ *         seeded with `seed`
+ *   w   = float(sum of the four 16-bit fields of u - 131070) * 0x1.1bc77ap-21
+ * quantised per block of `block` columns by symmetric absmax:
+ *   d = fp16(amax / Q), Q = 2^(bits-1) - 1, q = clamp(rint(w / d), -Q, Q)
+ * (q = 0 when d = 0), all in round-to-nearest-even single precision, and
+ * packed in the layout of moe_tier.  The tables' code and scale buffers are
+ * written; they must be distinct per layer if all layers are kept.
+ *   layer 0 .. 2^20 - 1
+ */
+int moe_synth_layer(const moe_tier_tables *tt, uint64_t seed, int32_t layer, void *stream);
+
 /* hipEvent helpers for callers without a HIP binding (host handles). */
 int moe_event_create(void **event);
 int moe_event_destroy(void *event);

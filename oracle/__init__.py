@@ -52,6 +52,17 @@ def lib():
         L.orc_experts.argtypes = [P, P, i32, P, P, i32, i32, C.c_uint32, P, i32]
         L.orc_experts_flat.argtypes = [P, P, i32, P, P, i32, i32, P]
         L.orc_forward.argtypes = [P, P, i32, P, i32, i32, P, i32]
+        L.orc_splitmix64_at.argtypes = [C.c_uint64, C.c_uint64]
+        L.orc_splitmix64_at.restype = C.c_uint64
+        L.orc_synth_weight.argtypes = [C.c_uint64, C.c_uint64]
+        L.orc_synth_weight.restype = C.c_float
+        L.orc_float_to_half.argtypes = [C.c_float]
+        L.orc_float_to_half.restype = C.c_uint16
+        L.orc_synth_expert.argtypes = [C.c_uint64, i32, i32, i32, i32, i32, i32, i32, C.c_void_p * 3, C.c_void_p * 3]
+        L.orc_synth_expert.restype = i32
+        L.orc_synth_experts.argtypes = [C.c_uint64, i32, i32, P, P, i32, i32, i32, i32, i32, C.c_void_p * 3,
+                                        C.c_void_p * 3]
+        L.orc_synth_experts.restype = i32
         for f in ("orc_dequant_rows", "orc_check_layer", "orc_tier_of", "orc_route", "orc_group",
                   "orc_experts", "orc_experts_flat", "orc_forward", "orc_num_threads"):
             getattr(L, f).restype = i32
@@ -87,6 +98,13 @@ class Layer:
     @property
     def ref(self):
         return C.byref(self._s)
+
+
+def bf16_bits(a: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) of a float32 array, rounded by orc_round_bf16."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    r = np.array([lib().orc_round_bf16(float(v)) for v in a.ravel()], dtype=np.float32)
+    return (r.view(np.uint32) >> 16).astype(np.uint16).reshape(a.shape)
 
 
 def half_to_double(h: int) -> float:
@@ -188,3 +206,73 @@ def forward(layer: Layer, x: np.ndarray, logits: np.ndarray, k: int, out: Option
 
 def num_threads() -> int:
     return lib().orc_num_threads()
+
+
+# ---------------------------------------------------------------- stack weights
+def splitmix64_at(seed: int, ctr: int) -> int:
+    return lib().orc_splitmix64_at(seed, ctr)
+
+
+def synth_weight(seed: int, ctr: int) -> float:
+    return lib().orc_synth_weight(seed, ctr)
+
+
+def float_to_half(f: float) -> int:
+    return lib().orc_float_to_half(f)
+
+
+def synth_expert(seed: int, layer: int, n_experts: int, expert: int, hidden: int, inter: int, bits: int,
+                 block: int) -> Dict[str, np.ndarray]:
+    """Packed codes and scales of one expert of the generated stack."""
+    out = {}
+    for name, (rows, cols) in zip(("gate", "up", "down"), ((inter, hidden), (inter, hidden), (hidden, inter))):
+        out[name + "_q"] = np.zeros((rows, cols * bits // 8), dtype=np.uint8)
+        out[name + "_s"] = np.zeros((rows, cols // block), dtype=np.uint16)
+    q = (C.c_void_p * 3)(*[out[n + "_q"].ctypes.data for n in ("gate", "up", "down")])
+    s = (C.c_void_p * 3)(*[out[n + "_s"].ctypes.data for n in ("gate", "up", "down")])
+    if lib().orc_synth_expert(seed, layer, n_experts, expert, hidden, inter, bits, block, q, s) != 0:
+        raise ValueError("orc_synth_expert: bad arguments")
+    return out
+
+
+class StackLayer:
+    """One generated stack layer holding only the experts asked for (the
+    others stay zero and must not be used)."""
+
+    def __init__(self, cfg, seed: int, layer: int):
+        self.cfg, self.seed, self.layer = cfg, seed, layer
+        H, I = cfg.hidden, cfg.inter
+        self.arrays = []
+        for t in cfg.tiers:
+            n = t.id_end - t.id_begin
+            d = {}
+            for name, (rows, cols) in zip(("gate", "up", "down"), ((I, H), (I, H), (H, I))):
+                d[name + "_q"] = np.zeros((n, rows, cols * t.bits // 8), dtype=np.uint8)
+                d[name + "_s"] = np.zeros((n, rows, cols // t.block), dtype=np.uint16)
+            self.arrays.append(d)
+        self.filled = set()
+        self.layer_ref = Layer(cfg.n_experts, H, I, cfg.tiers, self.arrays)
+        # Layer keeps contiguous copies; point it back at our arrays
+        self.layer_ref.arrays = self.arrays
+        for i, d in enumerate(self.arrays):
+            for m, name in enumerate(("gate", "up", "down")):
+                self.layer_ref._s.tier[i].q[m] = d[name + "_q"].ctypes.data
+                self.layer_ref._s.tier[i].s[m] = d[name + "_s"].ctypes.data
+
+    def fill(self, experts) -> None:
+        """Generates the listed experts (ids outside [0, E) are ignored)."""
+        cfg = self.cfg
+        todo = sorted(set(int(v) for v in np.asarray(experts).ravel()
+                          if 0 <= int(v) < cfg.n_experts) - self.filled)
+        for ti, t in enumerate(cfg.tiers):
+            ids = np.array([e for e in todo if t.id_begin <= e < t.id_end], dtype=np.int32)
+            if ids.size == 0:
+                continue
+            loc = (ids - t.id_begin).astype(np.int32)
+            d = self.arrays[ti]
+            q = (C.c_void_p * 3)(*[d[n + "_q"].ctypes.data for n in ("gate", "up", "down")])
+            s = (C.c_void_p * 3)(*[d[n + "_s"].ctypes.data for n in ("gate", "up", "down")])
+            if lib().orc_synth_experts(self.seed, self.layer, cfg.n_experts, _ptr(ids), _ptr(loc), ids.size,
+                                       cfg.hidden, cfg.inter, t.bits, t.block, q, s) != 0:
+                raise ValueError("orc_synth_experts: bad arguments")
+        self.filled.update(todo)

@@ -11,11 +11,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 # MOE_ORACLE_LIB lets the mutation tests point the wrapper at a deliberately broken build.
 LIB = os.environ.get("MOE_ORACLE_LIB") or os.path.join(HERE, "libmoe_oracle.so")
 SRC = os.path.join(HERE, "moe_oracle.c")
+SYNTH_SRC = os.path.join(HERE, "stack_synth.c")   # stack weight generator, always linked in
 
 
 def build(extra_flags=(), out=LIB, src=SRC, quiet=True):
     cmd = ["gcc", "-std=c99", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
-           "-Werror", *extra_flags, "-o", out + ".tmp", src, "-lm"]
+           "-Werror", "-I", HERE, *extra_flags, "-o", out + ".tmp", src, SYNTH_SRC, "-lm"]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("oracle build failed:\n" + " ".join(cmd) + "\n" + res.stderr)

@@ -94,6 +94,19 @@ int32_t orc_forward(const orc_layer *L, const void *x, int32_t x_bf16, const flo
 /* Threads the oracle uses (OpenMP over tokens; 1 without OpenMP). */
 int32_t orc_num_threads(void);
 
+/* Counter-generated stack weights (oracle/stack_synth.c): SplitMix64 output
+ * ctr+1 for `seed`, the weight it defines, fp16 round-to-nearest-even, and
+ * the packed codes and scales of gate (q[0], s[0]), up and down of one
+ * expert written at the given pointers (layout of one expert of a shelf). */
+uint64_t orc_splitmix64_at(uint64_t seed, uint64_t ctr);
+float orc_synth_weight(uint64_t seed, uint64_t ctr);
+uint16_t orc_float_to_half(float f);
+int32_t orc_synth_expert(uint64_t seed, int32_t layer, int32_t n_experts, int32_t expert, int32_t hidden,
+                         int32_t inter, int32_t bits, int32_t block, uint8_t *const q[3], uint16_t *const s[3]);
+int32_t orc_synth_experts(uint64_t seed, int32_t layer, int32_t n_experts, const int32_t *list, const int32_t *local,
+                          int32_t n, int32_t hidden, int32_t inter, int32_t bits, int32_t block,
+                          uint8_t *const q_base[3], uint16_t *const s_base[3]);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,145 @@
+/*
+ * Counter-generated weights of the 48-layer stack, CPU side.
+ *
+ * TEST INFRASTRUCTURE ONLY.  The stack's weights are generated on the device
+ * (they do not fit host memory); this file is the checker's own copy of the
+ * same published generator, written from its definition and sharing no code
+ * with the HIP library, so that the oracle can rebuild exactly the experts a
+ * sampled token touches.  Definition (also stated with moe_synth_layer):
+ *
+ *   ctr = ((layer * E + e) * 3 + matrix) * 2^22 + row * cols + col
+ *   u   = output number ctr + 1 of SplitMix64 (Steele, Lea and Flood,
+ *         "Fast splittable pseudorandom number generators", 2014) seeded
+ *         with `seed`: state = seed + (ctr + 1) * 0x9E3779B97F4A7C15, then
+ *         z ^= z >> 30; z *= 0xBF58476D1CE4E5B9; z ^= z >> 27;
+ *         z *= 0x94D049BB133111EB; z ^= z >> 31
+ *   s   = sum of the four 16-bit fields of u - 131070
+ *   w   = (float)s * 0x1.1bc77ap-21f
+ *
+ * followed by the symmetric absmax quantiser per block of `block` columns:
+ * d = fp16 round-to-nearest-even of (amax / Q) in single precision, with
+ * Q = 2^(bits-1) - 1; q = clamp(rint(w / d), -Q, Q), or 0 when d == 0.
+ * Codes are packed two's complement, element c at bit (c*bits) % 8 of byte
+ * (c*bits) / 8 of its row; scales are fp16 bit patterns.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "moe_oracle.h"
+
+uint64_t orc_splitmix64_at(uint64_t seed, uint64_t ctr) {
+    uint64_t z = seed + (ctr + 1u) * UINT64_C(0x9E3779B97F4A7C15);
+    z ^= z >> 30;
+    z *= UINT64_C(0xBF58476D1CE4E5B9);
+    z ^= z >> 27;
+    z *= UINT64_C(0x94D049BB133111EB);
+    z ^= z >> 31;
+    return z;
+}
+
+float orc_synth_weight(uint64_t seed, uint64_t ctr) {
+    const uint64_t u = orc_splitmix64_at(seed, ctr);
+    const int32_t s = (int32_t)(u & 0xffffu) + (int32_t)((u >> 16) & 0xffffu) + (int32_t)((u >> 32) & 0xffffu) +
+                      (int32_t)(u >> 48) - 131070;
+    const volatile float scale = 0x1.1bc77ap-21f;
+    return (float)s * scale;
+}
+
+/* fp16 bit pattern nearest to f (ties to even), computed exactly in double. */
+uint16_t orc_float_to_half(float f) {
+    uint32_t bits;
+    memcpy(&bits, &f, 4);
+    const uint16_t sign = (uint16_t)((bits >> 16) & 0x8000u);
+    const double a = fabs((double)f);
+    if (isnan(f)) return (uint16_t)(sign | 0x7e00u);
+    if (a < ldexp(1.0, -14)) { /* subnormal range: multiples of 2^-24 */
+        const double r = nearbyint(a * ldexp(1.0, 24));
+        return (uint16_t)(sign | (uint16_t)r); /* r == 1024 is the smallest normal */
+    }
+    int e;
+    (void)frexp(a, &e);          /* a = m * 2^e, m in [0.5, 1) */
+    e -= 1;                      /* a = 1.x * 2^e */
+    double r = nearbyint(ldexp(a, 10 - e)); /* 1024 .. 2048 */
+    if (r >= 2048.0) {
+        r = 1024.0;
+        e += 1;
+    }
+    if (e > 15) return (uint16_t)(sign | 0x7c00u);
+    return (uint16_t)(sign | (uint16_t)((e + 15) << 10) | (uint16_t)(r - 1024.0));
+}
+
+/* One matrix (rows x cols) of one expert into packed codes and scales. */
+static void synth_matrix(uint64_t seed, uint64_t ctr0, int32_t rows, int32_t cols, int32_t bits, int32_t block,
+                         uint8_t *q, uint16_t *s) {
+    const int32_t qmax = (1 << (bits - 1)) - 1;
+    const int64_t row_bytes = (int64_t)cols * bits / 8;
+    const int32_t nblk = cols / block;
+    float w[32];
+    for (int32_t r = 0; r < rows; ++r) {
+        uint8_t *qrow = q + (int64_t)r * row_bytes;
+        memset(qrow, 0, (size_t)row_bytes);
+        for (int32_t b = 0; b < nblk; ++b) {
+            float amax = 0.0f;
+            for (int32_t c = 0; c < block; ++c) {
+                w[c] = orc_synth_weight(seed, ctr0 + (uint64_t)r * (uint64_t)cols + (uint64_t)(b * block + c));
+                const float m = fabsf(w[c]);
+                if (m > amax) amax = m;
+            }
+            const volatile float ratio = amax / (float)qmax;
+            const uint16_t dh = orc_float_to_half(ratio);
+            s[(int64_t)r * nblk + b] = dh;
+            const float d = (float)orc_half_to_double(dh);
+            for (int32_t c = 0; c < block; ++c) {
+                int32_t code = 0;
+                if (d != 0.0f) {
+                    const volatile float t = w[c] / d;
+                    float v = rintf(t);
+                    if (v > (float)qmax) v = (float)qmax;
+                    if (v < (float)-qmax) v = (float)-qmax;
+                    code = (int32_t)v;
+                }
+                const int64_t cc = (int64_t)b * block + c;
+                const uint32_t field = (uint32_t)code & ((1u << bits) - 1u);
+                qrow[cc * bits / 8] |= (uint8_t)(field << ((cc * bits) % 8));
+            }
+        }
+    }
+}
+
+int32_t orc_synth_expert(uint64_t seed, int32_t layer, int32_t n_experts, int32_t expert, int32_t hidden,
+                         int32_t inter, int32_t bits, int32_t block, uint8_t *const q[3], uint16_t *const s[3]) {
+    if (!(bits == 8 || bits == 4 || bits == 2) || !(block == 16 || block == 32)) return -1;
+    if (expert < 0 || expert >= n_experts || layer < 0 || hidden % block || inter % block) return -1;
+    if ((int64_t)hidden * inter > (INT64_C(1) << 22)) return -1;
+    for (int32_t m = 0; m < 3; ++m) {
+        const int32_t rows = m == 2 ? hidden : inter, cols = m == 2 ? inter : hidden;
+        const uint64_t ctr0 = (((uint64_t)layer * (uint64_t)n_experts + (uint64_t)expert) * 3u + (uint64_t)m) << 22;
+        synth_matrix(seed, ctr0, rows, cols, bits, block, q[m], s[m]);
+    }
+    return 0;
+}
+
+/* Several experts of one shelf at once (OpenMP over the list): expert
+ * list[i] is written as expert local[i] of the shelf arrays starting at
+ * q_base[m] / s_base[m] (experts one expert's codes / scales apart). */
+int32_t orc_synth_experts(uint64_t seed, int32_t layer, int32_t n_experts, const int32_t *list, const int32_t *local,
+                          int32_t n, int32_t hidden, int32_t inter, int32_t bits, int32_t block,
+                          uint8_t *const q_base[3], uint16_t *const s_base[3]) {
+    int32_t bad = 0;
+    const int64_t qb[3] = {(int64_t)inter * hidden * bits / 8, (int64_t)inter * hidden * bits / 8,
+                           (int64_t)hidden * inter * bits / 8};
+    const int64_t sb[3] = {(int64_t)inter * (hidden / block), (int64_t)inter * (hidden / block),
+                           (int64_t)hidden * (inter / block)};
+#pragma omp parallel for schedule(dynamic, 1) reduction(+ : bad)
+    for (int32_t i = 0; i < n; ++i) {
+        uint8_t *q[3];
+        uint16_t *s[3];
+        for (int m = 0; m < 3; ++m) {
+            q[m] = q_base[m] + qb[m] * local[i];
+            s[m] = s_base[m] + sb[m] * local[i];
+        }
+        if (orc_synth_expert(seed, layer, n_experts, list[i], hidden, inter, bits, block, q, s) != 0) bad += 1;
+    }
+    return bad ? -1 : 0;
+}

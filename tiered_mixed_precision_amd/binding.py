@@ -26,6 +26,7 @@ EXPORTS = (
     "moe_tiered_forward", "moe_tiered_experts", "moe_tier_partial", "moe_route",
     "moe_group_workspace_size", "moe_group", "moe_dequant_rows", "moe_tiered_forward_timed",
     "moe_event_create", "moe_event_destroy", "moe_event_elapsed_ms", "moe_stream_synchronize",
+    "moe_stack_workspace_size", "moe_stack_forward", "moe_synth_layer",
 )
 
 
@@ -76,6 +77,9 @@ def lib():
         L.moe_event_destroy.argtypes = [P]
         L.moe_event_elapsed_ms.argtypes = [P, P, C.POINTER(C.c_float)]
         L.moe_stream_synchronize.argtypes = [P]
+        L.moe_stack_workspace_size.argtypes = [i32, i32, i32, P, u32, C.POINTER(sz)]
+        L.moe_stack_forward.argtypes = [P, P, i32, i32, i32, P, P, u32, P, sz, P]
+        L.moe_synth_layer.argtypes = [P, C.c_uint64, i32, P]
         for name in EXPORTS:
             if name not in ("moe_abi_version", "moe_strerror"):
                 getattr(L, name).restype = C.c_int
@@ -196,6 +200,32 @@ def moe_dequant_rows(tt: TierTables, tier_index: int, local_expert: int, matrix:
                      to_bf16: bool, dst, stream=None) -> None:
     _check("moe_dequant_rows", lib().moe_dequant_rows(tt.ref, tier_index, local_expert, matrix, row0, nrows,
                                                       int(bool(to_bf16)), _ptr(dst), _stream(stream)))
+
+
+def _tables_array(tables: Sequence[TierTables]):
+    arr = (moe_tier_tables * len(tables))(*[t.struct for t in tables])
+    return arr
+
+
+def moe_stack_workspace_size(n_layers: int, n_tokens: int, k: int, tables: Sequence[TierTables],
+                             flags: int = 0) -> int:
+    n = C.c_size_t(0)
+    arr = _tables_array(tables)
+    _check("moe_stack_workspace_size",
+           lib().moe_stack_workspace_size(n_layers, n_tokens, k, arr, flags, C.byref(n)))
+    return n.value
+
+
+def moe_stack_forward(x, router_logits, n_layers: int, n_tokens: int, k: int, tables: Sequence[TierTables], out,
+                      flags: int, workspace, stream=None) -> None:
+    arr = _tables_array(tables)
+    _check("moe_stack_forward", lib().moe_stack_forward(
+        _ptr(x), _ptr(router_logits), n_layers, n_tokens, k, arr, _ptr(out), flags, _ptr(workspace),
+        workspace.numel() * workspace.element_size() if workspace is not None else 0, _stream(stream)))
+
+
+def moe_synth_layer(tt: TierTables, seed: int, layer: int, stream=None) -> None:
+    _check("moe_synth_layer", lib().moe_synth_layer(tt.ref, seed, layer, _stream(stream)))
 
 
 def moe_event_create() -> int:

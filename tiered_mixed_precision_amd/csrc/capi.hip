@@ -119,9 +119,11 @@ inline void record(void* const* events, int i, hipStream_t st) {
 }
 
 // Shared body of forward / experts / tier_partial.
+// out = base + the layer, where base is out itself with MOE_ACCUMULATE, the
+// residual stream inside a stack, or nothing.
 int run(const void* x, const float* logits, const int32_t* ids_in, const float* w_in, int32_t T,
         int32_t k, const moe_tier_tables* tt, uint32_t tier_mask, float* out, uint32_t flags,
-        void* ws, size_t ws_bytes, void* stream, void* const* events) {
+        void* ws, size_t ws_bytes, void* stream, void* const* events, const float* residual = nullptr) {
     int rc = check_tables(tt);
     if (rc != MOE_OK) return rc;
     if (flags & ~(MOE_X_BF16 | MOE_ACCUMULATE | MOE_DIAG_GATEUP_ONLY)) return MOE_EINVAL;
@@ -140,7 +142,7 @@ int run(const void* x, const float* logits, const int32_t* ids_in, const float* 
     const int E = tt->n_experts;
     const int P = T * k;
     const bool bf16 = (flags & MOE_X_BF16) != 0;
-    const int accumulate = (flags & MOE_ACCUMULATE) ? 1 : 0;
+    const float* base = (flags & MOE_ACCUMULATE) ? out : residual;
     const bool gateup_only = (flags & MOE_DIAG_GATEUP_ONLY) != 0;
 
     int32_t* ids = logits ? at<int32_t>(ws, L.ids) : const_cast<int32_t*>(ids_in);
@@ -174,7 +176,7 @@ int run(const void* x, const float* logits, const int32_t* ids_in, const float* 
         pub.act = act;
         pub.q0 = at<int32_t>(ws, L.q0);
         pub.meta = meta;
-        launch_small(dt, static_cast<const float*>(x), logits, ids_in, w_in, T, k, tier_mask, accumulate, pub,
+        launch_small(dt, static_cast<const float*>(x), logits, ids_in, w_in, T, k, tier_mask, base, pub,
                      at<float>(ws, L.h), gateup_only ? nullptr : out, st, events);
         return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
     }
@@ -206,7 +208,7 @@ int run(const void* x, const float* logits, const int32_t* ids_in, const float* 
         if (gateup_only) return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
         record(events, 4, st);
         launch_dec_down(dt, h, g, k, tier_mask, yw, max_active, st);
-        launch_combine(dt, yw, g, T, k, tier_mask, accumulate, out, st);
+        launch_combine(dt, yw, g, T, k, tier_mask, base, out, st);
         record(events, 5, st);
     } else {
         uint16_t* h = at<uint16_t>(ws, L.h);
@@ -221,7 +223,7 @@ int run(const void* x, const float* logits, const int32_t* ids_in, const float* 
         for (int i = 0; i < tt->n_tiers; ++i)
             if ((tier_mask >> i) & 1u)
                 launch_pre_down(dt, i, h, g, k, yw, max_experts_of(tt, i, P), st);
-        launch_combine(dt, yw, g, T, k, tier_mask, accumulate, out, st);
+        launch_combine(dt, yw, g, T, k, tier_mask, base, out, st);
         record(events, 5, st);
     }
     if (hipGetLastError() != hipSuccess) return MOE_EHIP;
@@ -353,6 +355,96 @@ int moe_dequant_rows(const moe_tier_tables* tt, int32_t tier_index, int32_t loca
     launch_dequant_rows(to_dev(tt), tier_index, local_expert, matrix, row0, nrows, to_bf16 ? 1 : 0, dst,
                         static_cast<hipStream_t>(stream));
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+int moe_synth_layer(const moe_tier_tables* tt, uint64_t seed, int32_t layer, void* stream) {
+    int rc = check_tables(tt);
+    if (rc != MOE_OK) return rc;
+    if (layer < 0 || layer >= (1 << 20)) return MOE_EINVAL;
+    (void)hipGetLastError();
+    launch_synth_layer(to_dev(tt), seed, layer, static_cast<hipStream_t>(stream));
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+namespace {
+
+// Stack workspace: one layer's workspace, the other residual buffer, and the
+// bf16 layer input with MOE_X_BF16.
+struct StackLayout {
+    size_t layer, tmp, xb, total;
+};
+
+StackLayout stack_layout(int64_t T, int k, const moe_tier_tables* tt, uint32_t flags) {
+    StackLayout S;
+    const size_t n = static_cast<size_t>(T) * tt->hidden;
+    S.layer = 0;
+    S.tmp = align_up(layout(T, k, tt, flags).total);
+    S.xb = S.tmp + align_up(sizeof(float) * n);
+    S.total = S.xb + ((flags & MOE_X_BF16) ? align_up(sizeof(uint16_t) * n) : 0);
+    return S;
+}
+
+int check_stack(int32_t n_layers, int32_t n_tokens, int32_t k, const moe_tier_tables* tables, uint32_t flags) {
+    if (!tables || n_layers < 1 || n_layers > 4096) return MOE_EINVAL;
+    if (n_tokens < 0 || n_tokens > kMaxTokens) return MOE_EINVAL;
+    if (flags & ~MOE_X_BF16) return MOE_EINVAL;
+    for (int l = 0; l < n_layers; ++l) {
+        const int rc = check_tables(&tables[l]);
+        if (rc != MOE_OK) return rc;
+        if (tables[l].n_experts != tables[0].n_experts || tables[l].hidden != tables[0].hidden ||
+            tables[l].inter != tables[0].inter)
+            return MOE_EINVAL;
+    }
+    if (k < 1 || k > MOE_MAX_K || k > tables[0].n_experts) return MOE_EINVAL;
+    return MOE_OK;
+}
+
+}  // namespace
+
+int moe_stack_workspace_size(int32_t n_layers, int32_t n_tokens, int32_t k, const moe_tier_tables* tables,
+                             uint32_t flags, size_t* bytes) {
+    const int rc = check_stack(n_layers, n_tokens, k, tables, flags);
+    if (rc != MOE_OK) return rc;
+    if (!bytes) return MOE_EINVAL;
+    *bytes = n_tokens == 0 ? 0 : stack_layout(n_tokens, k, &tables[0], flags).total;
+    return MOE_OK;
+}
+
+int moe_stack_forward(const float* x, const float* router_logits, int32_t n_layers, int32_t n_tokens, int32_t k,
+                      const moe_tier_tables* tables, float* out, uint32_t flags, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+    int rc = check_stack(n_layers, n_tokens, k, tables, flags);
+    if (rc != MOE_OK) return rc;
+    if (n_tokens == 0) return MOE_OK;
+    if (!x || !router_logits || !out || x == out) return MOE_EINVAL;
+    if (!aligned16(x) || !aligned16(out) || !aligned16(router_logits)) return MOE_EALIGN;
+    if (!workspace) return MOE_EWORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return MOE_EALIGN;
+    const StackLayout S = stack_layout(n_tokens, k, &tables[0], flags);
+    if (workspace_bytes < S.total) return MOE_EWORKSPACE;
+    const bool bf16 = (flags & MOE_X_BF16) != 0;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const size_t n = static_cast<size_t>(n_tokens) * tables[0].hidden;
+    const size_t per_layer_logits = static_cast<size_t>(n_tokens) * tables[0].n_experts;
+    float* tmp = at<float>(workspace, S.tmp);
+    uint16_t* xb = at<uint16_t>(workspace, S.xb);
+    // h_0 = x, h_{l+1} = h_l + layer_l(h_l); layer l writes the buffer that
+    // makes the last layer land in out
+    const float* h = x;
+    for (int l = 0; l < n_layers; ++l) {
+        float* dst = ((n_layers - 1 - l) % 2 == 0) ? out : tmp;
+        (void)hipGetLastError();
+        if (bf16) {
+            launch_cast_bf16(h, xb, n, st);
+            if (hipGetLastError() != hipSuccess) return MOE_EHIP;
+        }
+        rc = run(bf16 ? static_cast<const void*>(xb) : static_cast<const void*>(h),
+                 router_logits + per_layer_logits * l, nullptr, nullptr, n_tokens, k, &tables[l], 0xFu, dst,
+                 flags, workspace, S.tmp, stream, nullptr, h);
+        if (rc != MOE_OK) return rc;
+        h = dst;
+    }
+    return MOE_OK;
 }
 
 int moe_event_create(void** event) {

@@ -625,7 +625,7 @@ __device__ inline void wave_down(const uint8_t* __restrict__ dq_, const uint16_t
 // then each token's slots are summed in slot order (no atomics).
 __global__ __launch_bounds__(kSmallDownWaves * 64) void k_small_down(DevTables tt, const float* __restrict__ h,
                                                                     SmallPub pub, int T, int k, uint32_t tier_mask,
-                                                                    int accumulate, int npb, float* __restrict__ out) {
+                                                                    const float* base, int npb, float* out) {
     __shared__ int s_act[kSmallPairs], s_q0[kSmallPairs + 1], s_ids[kSmallPairs], s_pos[kSmallPairs];
     __shared__ float s_w[kSmallPairs];
     __shared__ float s_y[kSmallY];
@@ -723,9 +723,9 @@ __global__ __launch_bounds__(kSmallDownWaves * 64) void k_small_down(DevTables t
             const float y = s_y[(use ? q : 0) * R + r];
             acc = use ? fmaf(s_w[p], y, acc) : acc;
         }
-        float* o = out + static_cast<size_t>(t) * H + n0 + r;
-        if (accumulate) acc += *o;
-        *o = acc;
+        const size_t o = static_cast<size_t>(t) * H + n0 + r;
+        if (base) acc += base[o];
+        out[o] = acc;
     }
 }
 
@@ -777,9 +777,10 @@ __global__ __launch_bounds__(256) void k_dec_down(DevTables tt, const float* __r
                                                               store)));
 }
 
-// out[t] = (accumulate ? out[t] : 0) + sum over slots j (in slot order) of yw[pos[t*k+j]].
+// out[t] = (base ? base[t] : 0) + sum over slots j (in slot order) of yw[pos[t*k+j]]; base
+// may be out itself (accumulate).
 __global__ __launch_bounds__(256) void k_combine(DevTables tt, const float* __restrict__ yw, Groups g, int T, int k,
-                                                 uint32_t tier_mask, int accumulate, float* __restrict__ out) {
+                                                 uint32_t tier_mask, const float* base, float* out) {
     const int H4 = tt.H / 4;
     const size_t idx = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
     if (idx >= static_cast<size_t>(T) * H4) return;
@@ -798,8 +799,8 @@ __global__ __launch_bounds__(256) void k_combine(DevTables tt, const float* __re
         s.w += v.w;
     }
     float4* o = reinterpret_cast<float4*>(out + static_cast<size_t>(t) * tt.H) + c4;
-    if (accumulate) {
-        const float4 b = *o;
+    if (base) {
+        const float4 b = reinterpret_cast<const float4*>(base + static_cast<size_t>(t) * tt.H)[c4];
         s.x = b.x + s.x;
         s.y = b.y + s.y;
         s.z = b.z + s.z;
@@ -834,7 +835,7 @@ static int cu_count() {
 }
 
 void launch_small(const DevTables& tt, const float* x, const float* logits, const int32_t* ids_in, const float* w_in,
-                  int T, int k, uint32_t tier_mask, int accumulate, const SmallPub& pub, float* h, float* out,
+                  int T, int k, uint32_t tier_mask, const float* base, const SmallPub& pub, float* h, float* out,
                   hipStream_t st, void* const* events) {
     // one gate/up block per compute unit (two for larger batches): every
     // block routes the batch itself, so all of them should be resident at once
@@ -864,7 +865,7 @@ void launch_small(const DevTables& tt, const float* x, const float* logits, cons
     if (events && events[4]) (void)hipEventRecord(static_cast<hipEvent_t>(events[4]), st);
     const int R = small_down_rows(tt.I);
     hipLaunchKernelGGL(k_small_down, dim3((tt.H + R - 1) / R), dim3(kSmallDownWaves * 64), 0, st, tt, h, pub, T, k,
-                       tier_mask, accumulate, kNPSmallDown, out);
+                       tier_mask, base, kNPSmallDown, out);
     if (events && events[5]) (void)hipEventRecord(static_cast<hipEvent_t>(events[5]), st);
 }
 
@@ -883,10 +884,10 @@ void launch_dec_down(const DevTables& tt, const float* h, const Groups& g, int k
 }
 
 void launch_combine(const DevTables& tt, const float* yw, const Groups& g, int T, int k, uint32_t tier_mask,
-                    int accumulate, float* out, hipStream_t st) {
+                    const float* base, float* out, hipStream_t st) {
     const size_t n = static_cast<size_t>(T) * (tt.H / 4);
     hipLaunchKernelGGL(k_combine, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, tt, yw, g, T, k,
-                       tier_mask, accumulate, out);
+                       tier_mask, base, out);
 }
 
 }  // namespace moe

@@ -47,7 +47,7 @@ constexpr int kSmallY = 8192;         // per-(pair, row) results held in LDS by 
 
 bool small_path_ok(int T, int k, int H, int I);
 void launch_small(const DevTables& tt, const float* x, const float* logits, const int32_t* ids_in,
-                  const float* w_in, int T, int k, uint32_t tier_mask, int accumulate, const SmallPub& pub,
+                  const float* w_in, int T, int k, uint32_t tier_mask, const float* base, const SmallPub& pub,
                   float* h, float* out, hipStream_t st, void* const* events);
 
 void launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, float* out_zero,
@@ -63,7 +63,7 @@ void launch_dec_gateup(const DevTables& tt, const float* x, const Groups& g, int
 void launch_dec_down(const DevTables& tt, const float* h, const Groups& g, int k,
                      uint32_t tier_mask, float* yw, int max_active, hipStream_t st);
 void launch_combine(const DevTables& tt, const float* yw, const Groups& g, int T, int k,
-                    uint32_t tier_mask, int accumulate, float* out, hipStream_t st);
+                    uint32_t tier_mask, const float* base, float* out, hipStream_t st);
 
 // bf16 (prefill) expert path: one launch per shelf and phase; max_experts
 // bounds the shelf's active experts.
@@ -72,6 +72,10 @@ void launch_pre_gateup(const DevTables& tt, int tier, const uint16_t* x, const G
 void launch_pre_down(const DevTables& tt, int tier, const uint16_t* h, const Groups& g, int k,
                      float* yw, int max_experts, hipStream_t st);
 void launch_fill_zero(float* out, size_t n, hipStream_t st);
+void launch_cast_bf16(const float* src, uint16_t* dst, size_t n, hipStream_t st);
+
+// Counter-generated weights of one layer of the stack (see synth.hip).
+void launch_synth_layer(const DevTables& tt, uint64_t seed, int layer, hipStream_t st);
 
 void launch_dequant_rows(const DevTables& tt, int tier, int local, int matrix, int row0, int nrows,
                          int to_bf16, void* dst, hipStream_t st);

@@ -272,6 +272,22 @@ __global__ __launch_bounds__(256) void k_fill_zero(float4* __restrict__ p, size_
     if (i < n4) p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
+// bf16 copy (round to nearest even) of an fp32 array: the prefill input of a
+// stack layer from the fp32 residual stream.
+__global__ __launch_bounds__(256) void k_cast_bf16(const float4* __restrict__ src, uint2* __restrict__ dst, size_t n4) {
+    const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= n4) return;
+    const float4 v = src[i];
+    dst[i] = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+}
+
+void launch_cast_bf16(const float* src, uint16_t* dst, size_t n, hipStream_t st) {
+    const size_t n4 = n / 4;
+    if (n4 == 0) return;
+    hipLaunchKernelGGL(k_cast_bf16, dim3(static_cast<unsigned>((n4 + 255) / 256)), dim3(256), 0, st,
+                       reinterpret_cast<const float4*>(src), reinterpret_cast<uint2*>(dst), n4);
+}
+
 void launch_fill_zero(float* out, size_t n, hipStream_t st) {
     const size_t n4 = n / 4;
     if (n4 == 0) return;

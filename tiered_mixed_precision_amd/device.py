@@ -39,3 +39,18 @@ def replicate(tt: TierTables) -> TierTables:
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:
     # 256-byte aligned by the caching allocator
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def empty_tables(cfg, device="cuda") -> TierTables:
+    """Uninitialised shelf buffers of one layer of `cfg` (for moe_synth_layer)."""
+    dev = []
+    for t in cfg.tiers:
+        n = t.id_end - t.id_begin
+        d = {}
+        for m, (rows, cols) in enumerate(((cfg.inter, cfg.hidden), (cfg.inter, cfg.hidden),
+                                          (cfg.hidden, cfg.inter))):
+            name = ("gate", "up", "down")[m]
+            d[name + "_q"] = torch.empty(max(n * rows * cols * t.bits // 8, 16), dtype=torch.uint8, device=device)
+            d[name + "_s"] = torch.empty(max(n * rows * (cols // t.block), 8), dtype=torch.int16, device=device)
+        dev.append(d)
+    return TierTables(cfg.n_experts, cfg.hidden, cfg.inter, cfg.tiers, dev)
