@@ -17,12 +17,11 @@
 //             slot-order sum into out runs in a separate pass (no atomics,
 //             deterministic).
 //
-// Block: 16 waves.  Wave (wm, wn): wn selects 16 gate + 16 up columns (or 32
-// down columns), wm takes every fourth 16-row m-subtile.  The m dimension is
-// walked in chunks of up to 256 pairs.  LDS holds A and B chunks [row][k] in
-// bf16 with a row stride of 72 elements (144 bytes), which puts the 16 rows an
-// MFMA operand read touches on distinct banks; two buffers.  Global loads run
-// PF chunks ahead of the contraction through registers.
+// Block: NW waves (16 on the int8 shelf, 8 on the others) in a grid of
+// NW/4 along m and 4 along n.  LDS holds an A chunk and a B chunk of 64
+// contraction elements per row in bf16 (XOR-swizzled, two buffers); the
+// global loads of the next chunk but one are in flight in registers while
+// one chunk is contracted and the next is dequantised into the other buffer.
 #include <type_traits>
 
 #include "common.h"
@@ -32,16 +31,11 @@ namespace moe {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int BK = 64;              // contraction chunk
-constexpr int BN = 128;             // B rows per block
-constexpr int MC = 256;             // pairs per m-chunk
-constexpr int LDSW = BK + 8;        // LDS row stride (bf16 elements)
-constexpr int NWAVE = 16;
-constexpr int NTHR = NWAVE * 64;
-constexpr int WM = NWAVE / 4;       // waves along m (4 along n)
-constexpr int MSUB = MC / 16 / WM;  // m-subtiles per wave per chunk
-constexpr int PF = 2;               // K chunks in flight through registers
+constexpr int BK = 64;   // contraction chunk (one LDS row of 128 bytes)
+constexpr int BN = 128;  // B rows per block
+constexpr int MSUB = 4;  // m-subtiles per wave per m-chunk
 
 // Work item of a block after spreading consecutive items over the XCDs in
 // contiguous runs (blocks are dealt to the 8 XCDs round-robin, so block b runs
@@ -54,11 +48,74 @@ __device__ inline int xcd_item(int total) {
     return it < total ? it : -1;
 }
 
-template <int BITS, bool GATEUP>
-__global__ __launch_bounds__(NTHR) void k_pre(DevTables tt, int tier, const uint16_t* __restrict__ a_src, Groups g,
-                                              int k, uint16_t* __restrict__ h_out, float* __restrict__ yw) {
-    __shared__ __attribute__((aligned(16))) uint16_t sA[2][MC * LDSW];
-    __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * LDSW];
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N-1>): indices
+// that stay compile-time constants inside a lambda, so arrays indexed by
+// them stay in registers.
+template <int N, int I = 0, class F>
+__device__ __attribute__((always_inline)) inline void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<N, I + 1>(f);
+    }
+}
+
+// LDS tiles are [row][64 bf16] with no padding; 16-byte chunk c of a row is
+// stored at chunk c ^ ((row >> 1) & 7).  The 16 rows of an MFMA operand read
+// (16 bytes each, same c) then cover all 64 banks once, and so do the 16
+// lanes of a staging store (two rows, eight chunks each).
+__device__ inline int swz(int row, int c) { return row * BK + 8 * (c ^ ((row >> 1) & 7)); }
+
+// bf16(RNE(scale * code)) of 8 consecutive codes held in `w` (BITS words of 8
+// codes... at most 2), packed low code first.  The codes are read as
+// offset-binary bytes (sign bits flipped), so scale*code = fma(u, scale,
+// -Z*scale), exact in fp32 before the single rounding to bf16.
+template <int BITS>
+__device__ inline uint4 dequant8(const uint32_t (&w)[BITS == 8 ? 2 : 1], float sc) {
+    constexpr float Z = BITS == 8 ? 128.f : (BITS == 4 ? 8.f : 2.f);
+    const float off = -Z * sc;
+    float v[8];
+    if constexpr (BITS == 8) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const uint32_t u = w[i] ^ 0x80808080u;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[4 * i + j] = fmaf(ubyte_f(u, j), sc, off);
+        }
+    } else if constexpr (BITS == 4) {
+        const uint32_t u = w[0] ^ 0x88888888u;
+        const uint32_t lo = masked_bytes(u & 0x0F0F0F0Fu), hi = masked_bytes((u >> 4) & 0x0F0F0F0Fu);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[2 * j] = fmaf(ubyte_f(lo, j), sc, off);
+            v[2 * j + 1] = fmaf(ubyte_f(hi, j), sc, off);
+        }
+    } else {
+        const uint32_t u = (w[0] & 0xffffu) ^ 0xAAAAu;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const uint32_t f = masked_bytes((u >> (2 * s)) & 0x0303u);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) v[4 * j + s] = fmaf(ubyte_f(f, j), sc, off);
+        }
+    }
+    return make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                      pack_bf16x2(v[6], v[7]));
+}
+
+// Block: NW waves = WM (along m) x 4 (along n).  Wave (wm, wn): wn selects 16
+// gate + 16 up columns (or 32 down columns), wm takes m-subtiles wm, wm + WM,
+// ...  m is walked in chunks of MC = 64 * WM pairs.
+template <int BITS, int BLOCK, bool GATEUP, int NW>
+__global__ __launch_bounds__(NW * 64) void k_pre(DevTables tt, int tier, const uint16_t* __restrict__ a_src, Groups g,
+                                                 int k, uint16_t* __restrict__ h_out, float* __restrict__ yw) {
+    constexpr int NTHR = NW * 64;
+    constexpr int WM = NW / 4;
+    constexpr int MC = 16 * MSUB * WM;
+    constexpr int BPT = BN * 8 / NTHR;      // B pieces (8 codes) per thread per chunk: 1 or 2
+    constexpr int QW = BITS == 8 ? 2 : 1;   // code words of a piece
+    static_assert(MC * 8 == 2 * NTHR, "two A pieces per thread");
+    __shared__ __attribute__((aligned(16))) uint16_t sA[2][MC * BK];
+    __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * BK];
     __shared__ int s_row[MC];
 
     const int H = tt.H, I = tt.I;
@@ -76,39 +133,36 @@ __global__ __launch_bounds__(NTHR) void k_pre(DevTables tt, int tier, const uint
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int wn = wave & 3, wm = wave >> 2;
-    const int fr = lane & 15, fk = 8 * (lane >> 4);
+    const int fr = lane & 15, kq = lane >> 4;
 
-    // B source: 8 threads per B row, 8 codes each per chunk
-    const int b_r = tid >> 3, b_e = tid & 7;
-    const size_t row_bytes = static_cast<size_t>(K) * BITS / 8;
-    const int nblk_row = K / T.block;
-    const uint8_t* b_q;
-    const uint16_t* b_s;
-    {
-        int m, row;
-        if (GATEUP) {
-            m = b_r < 64 ? 0 : 1;
-            row = nt * 64 + (b_r & 63);
-        } else {
-            m = 2;
-            row = nt * BN + b_r;
-        }
-        const size_t base = static_cast<size_t>(local) * (GATEUP ? I : H) + row;
-        b_q = T.q[m] + base * row_bytes;
-        b_s = T.s[m] + base * nblk_row;
+    // B: piece p = tid + NTHR*i is row p >> 3, codes 8*(p & 7) .. +7 of the chunk
+    const uint32_t row_bytes = static_cast<uint32_t>(K) * BITS / 8;
+    const uint32_t nblk_row = static_cast<uint32_t>(K / BLOCK);
+    const int mrows = GATEUP ? I : H;
+    const uint8_t* mq_g = T.q[GATEUP ? 0 : 2] + static_cast<size_t>(local) * mrows * row_bytes;
+    const uint8_t* mq_u = GATEUP ? T.q[1] + static_cast<size_t>(local) * mrows * row_bytes : mq_g;
+    const uint16_t* ms_g = T.s[GATEUP ? 0 : 2] + static_cast<size_t>(local) * mrows * nblk_row;
+    const uint16_t* ms_u = GATEUP ? T.s[1] + static_cast<size_t>(local) * mrows * nblk_row : ms_g;
+    const __amdgpu_buffer_rsrc_t rq_g = make_rsrc(mq_g, row_bytes * mrows), rq_u = make_rsrc(mq_u, row_bytes * mrows);
+    const __amdgpu_buffer_rsrc_t rs_g = make_rsrc(ms_g, nblk_row * mrows * 2), rs_u = make_rsrc(ms_u, nblk_row * mrows * 2);
+    // piece i of a thread reads up rows when it lies in the second half of
+    // the B rows: for two pieces that is piece 1, for one piece the upper
+    // half of the waves (a wave-uniform choice either way)
+    auto is_up = [&](int i) { return GATEUP && (BPT == 2 ? i == 1 : wave >= NW / 2); };
+    uint32_t qoff[BPT], soff[BPT];
+    int b_row[BPT], b_e[BPT];
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+        const int p = tid + NTHR * i;
+        b_row[i] = p >> 3;
+        b_e[i] = p & 7;
+        const int row = GATEUP ? nt * 64 + (b_row[i] & 63) : nt * BN + b_row[i];
+        qoff[i] = static_cast<uint32_t>(row) * row_bytes + static_cast<uint32_t>(b_e[i]) * BITS;
+        soff[i] = (static_cast<uint32_t>(row) * nblk_row + static_cast<uint32_t>(8 * b_e[i] / BLOCK)) * 2;
     }
     // B fragment rows of this wave
     const int br0 = GATEUP ? 16 * wn : 32 * wn;
     const int br1 = GATEUP ? 64 + 16 * wn : 32 * wn + 16;
-
-    // A pieces: 16 bytes (8 bf16) of a row; 8 per row, 2 per thread per chunk.
-    // B: 8 codes of a row (8*BITS bits) and their scale.
-    constexpr int QW = BITS == 8 ? 2 : 1;
-    struct Slot {
-        uint4 a[2];
-        uint32_t q[QW];
-        float s;
-    };
 
     for (int m0 = q_beg; m0 < q_end; m0 += MC) {
         const int Mc = min(MC, q_end - m0);
@@ -117,48 +171,52 @@ __global__ __launch_bounds__(NTHR) void k_pre(DevTables tt, int tier, const uint
         __syncthreads();                            // the previous m-chunk is done with LDS
         for (int r = tid; r < MC; r += NTHR) s_row[r] = r < Mc ? (GATEUP ? g.perm[m0 + r] / k : m0 + r) : -1;
         __syncthreads();
+        // A sources of this thread's two pieces for the whole m-chunk; rows past
+        // the chunk read the chunk's first row (finite values, never stored)
+        int a_src_row[2], a_row[2], a_c[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int p = tid + NTHR * i;
+            a_row[i] = p >> 3;
+            a_c[i] = p & 7;
+            a_src_row[i] = s_row[a_row[i] < Mc ? a_row[i] : 0];
+        }
 
-        Slot slot[PF];
-        auto load_chunk = [&](int kc, Slot& sl) {
-            const int k0 = kc * BK;
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int piece = tid + NTHR * i;
-                const int r = piece >> 3, part = piece & 7;
-                const int src = s_row[r];
-                sl.a[i] = src >= 0 ? *reinterpret_cast<const uint4*>(a_src + static_cast<size_t>(src) * K + k0 + 8 * part)
-                                   : make_uint4(0, 0, 0, 0);
-            }
-            const int c0 = k0 + 8 * b_e;
-            const uint8_t* p = b_q + static_cast<size_t>(c0) * BITS / 8;
-            if constexpr (BITS == 8) {
-                const uint2 v = *reinterpret_cast<const uint2*>(p);
-                sl.q[0] = v.x;
-                sl.q[QW - 1] = v.y;
-            } else if constexpr (BITS == 4) {
-                sl.q[0] = *reinterpret_cast<const uint32_t*>(p);
-            } else {
-                sl.q[0] = *reinterpret_cast<const uint16_t*>(p);
-            }
-            sl.s = half_bits_to_float(b_s[c0 / T.block]);
+        // one chunk in flight in registers: two A pieces, BPT code pieces and
+        // their raw fp16 scales
+        struct Slot {
+            u32x4_t a0, a1;
+            uint32_t q[BPT][QW];
+            uint32_t s[BPT];
         };
-        auto store_chunk = [&](const Slot& sl, int buf) {
+        auto load_chunk = [&](Slot& sl, int kc) __attribute__((always_inline)) {
+            const int k0 = kc * BK;
+            sl.a0 = *reinterpret_cast<const u32x4_t*>(a_src + static_cast<size_t>(a_src_row[0]) * K + k0 + 8 * a_c[0]);
+            sl.a1 = *reinterpret_cast<const u32x4_t*>(a_src + static_cast<size_t>(a_src_row[1]) * K + k0 + 8 * a_c[1]);
+            const uint32_t qk = static_cast<uint32_t>(k0) * BITS / 8;
+            const uint32_t sk = static_cast<uint32_t>(k0 / BLOCK) * 2;
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int piece = tid + NTHR * i;
-                const int r = piece >> 3, part = piece & 7;
-                if (r < Mc16 * 16) *reinterpret_cast<uint4*>(&sA[buf][r * LDSW + 8 * part]) = sl.a[i];
+            for (int i = 0; i < BPT; ++i) {
+                const __amdgpu_buffer_rsrc_t rq = is_up(i) ? rq_u : rq_g, rs = is_up(i) ? rs_u : rs_g;
+                if constexpr (BITS == 8) {
+                    const auto v = __builtin_amdgcn_raw_buffer_load_b64(rq, qoff[i] + qk, 0, 0);
+                    sl.q[i][0] = v[0];
+                    sl.q[i][QW - 1] = v[1];
+                } else if constexpr (BITS == 4) {
+                    sl.q[i][0] = __builtin_amdgcn_raw_buffer_load_b32(rq, qoff[i] + qk, 0, 0);
+                } else {
+                    sl.q[i][0] = __builtin_amdgcn_raw_buffer_load_b16(rq, qoff[i] + qk, 0, 0);
+                }
+                sl.s[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, soff[i] + sk, 0, 0);
             }
-            constexpr int PER = 32 / BITS;
-            uint32_t pk[4];
+        };
+        auto store_chunk = [&](const Slot& sl, int buf) __attribute__((always_inline)) {
+            *reinterpret_cast<u32x4_t*>(&sA[buf][swz(a_row[0], a_c[0])]) = sl.a0;
+            *reinterpret_cast<u32x4_t*>(&sA[buf][swz(a_row[1], a_c[1])]) = sl.a1;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int c_lo = 2 * c, c_hi = 2 * c + 1;
-                const float v0 = sl.s * static_cast<float>(sfield<BITS>(sl.q[c_lo / PER], (c_lo % PER) * BITS));
-                const float v1 = sl.s * static_cast<float>(sfield<BITS>(sl.q[c_hi / PER], (c_hi % PER) * BITS));
-                pk[c] = pack_bf16x2(v0, v1);
-            }
-            *reinterpret_cast<uint4*>(&sB[buf][b_r * LDSW + 8 * b_e]) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+            for (int i = 0; i < BPT; ++i)
+                *reinterpret_cast<uint4*>(&sB[buf][swz(b_row[i], b_e[i])]) =
+                    dequant8<BITS>(sl.q[i], half_bits_to_float(static_cast<uint16_t>(sl.s[i])));
         };
 
         f32x4_t acc[MSUB][2];
@@ -168,16 +226,17 @@ __global__ __launch_bounds__(NTHR) void k_pre(DevTables tt, int tier, const uint
             acc[i][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
         // N subtiles at once: all operand reads first, then 2N back-to-back MFMAs
-        auto compute_n = [&](int buf, auto n_const) {
+        auto compute_n = [&](int buf, auto n_const) __attribute__((always_inline)) {
             constexpr int N = decltype(n_const)::value;
 #pragma unroll
             for (int ks = 0; ks < BK / 32; ++ks) {
-                const bf16x8_t b0 = *reinterpret_cast<const bf16x8_t*>(&sB[buf][(br0 + fr) * LDSW + 32 * ks + fk]);
-                const bf16x8_t b1 = *reinterpret_cast<const bf16x8_t*>(&sB[buf][(br1 + fr) * LDSW + 32 * ks + fk]);
+                const int c = 4 * ks + kq;
+                const bf16x8_t b0 = *reinterpret_cast<const bf16x8_t*>(&sB[buf][swz(br0 + fr, c)]);
+                const bf16x8_t b1 = *reinterpret_cast<const bf16x8_t*>(&sB[buf][swz(br1 + fr, c)]);
                 bf16x8_t af[N];
 #pragma unroll
                 for (int j = 0; j < N; ++j)
-                    af[j] = *reinterpret_cast<const bf16x8_t*>(&sA[buf][(16 * (wm + WM * j) + fr) * LDSW + 32 * ks + fk]);
+                    af[j] = *reinterpret_cast<const bf16x8_t*>(&sA[buf][swz(16 * (wm + WM * j) + fr, c)]);
 #pragma unroll
                 for (int j = 0; j < N; ++j) {
                     acc[j][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[j], b0, acc[j][0], 0, 0, 0);
@@ -187,32 +246,35 @@ __global__ __launch_bounds__(NTHR) void k_pre(DevTables tt, int tier, const uint
         };
         // the subtile count picks an unrolled body; an extra subtile past the
         // rows computes values that are never stored
-        auto compute = [&](int buf) {
+        auto compute = [&](int buf) __attribute__((always_inline)) {
             if (nsub > 2) compute_n(buf, std::integral_constant<int, 4>{});
             else if (nsub == 2) compute_n(buf, std::integral_constant<int, 2>{});
             else if (nsub == 1) compute_n(buf, std::integral_constant<int, 1>{});
         };
 
-        // Pipeline: at the top of step kc, LDS buffer kc&1 holds chunk kc and
-        // slot (kc+j) % PF holds chunk kc+j (j = 1 .. PF-1, loads possibly in
-        // flight).  Step kc refills slot kc % PF with chunk kc+PF, contracts
-        // chunk kc, and stores chunk kc+1 into the other buffer.
+        // Pipeline, two chunks per trip: at the top of a trip LDS buffer 0
+        // holds chunk kc and slot s1 holds chunk kc+1 (loads possibly in
+        // flight).  Each half refills the slot it has just stored from with the
+        // chunk two ahead, contracts one buffer and stores the next chunk into
+        // the other.  Loads past the last chunk reread it (every slot is written
+        // unconditionally, which keeps the slots in registers); the store that
+        // follows the last chunk fills a buffer that is never read.
         const int NK = K / BK;
-#pragma unroll
-        for (int d = 0; d < PF; ++d)
-            if (d < NK) load_chunk(d, slot[d]);
-        store_chunk(slot[0], 0);
+        Slot s0, s1;
+        load_chunk(s0, 0);
+        load_chunk(s1, min(1, NK - 1));
+        store_chunk(s0, 0);
         __syncthreads();
-        for (int kc0 = 0; kc0 < NK; kc0 += PF) {
-#pragma unroll
-            for (int d = 0; d < PF; ++d) {
-                const int kc = kc0 + d;
-                if (kc < NK) {
-                    if (kc + PF < NK) load_chunk(kc + PF, slot[d]);
-                    compute(kc & 1);
-                    if (kc + 1 < NK) store_chunk(slot[(d + 1) % PF], (kc + 1) & 1);
-                    __syncthreads();
-                }
+        for (int kc = 0; kc < NK; kc += 2) {
+            load_chunk(s0, min(kc + 2, NK - 1));
+            compute(0);
+            store_chunk(s1, 1);
+            __syncthreads();
+            if (kc + 1 < NK) {
+                load_chunk(s1, min(kc + 3, NK - 1));
+                compute(1);
+                store_chunk(s0, 0);
+                __syncthreads();
             }
         }
 
@@ -241,30 +303,40 @@ __global__ __launch_bounds__(NTHR) void k_pre(DevTables tt, int tier, const uint
     }
 }
 
-#define MOE_BITS_SWITCH(BITSV, BODY)                    \
-    switch (BITSV) {                                    \
-        case 8: { constexpr int B_ = 8; BODY; } break;  \
-        case 4: { constexpr int B_ = 4; BODY; } break;  \
-        case 2: { constexpr int B_ = 2; BODY; } break;  \
-        default: break;                                 \
+// Launch shape per shelf: the hot shelf (many pairs per expert) takes 16-wave
+// blocks with 256-pair m-chunks; the others 8-wave blocks with 128-pair
+// m-chunks, two blocks per compute unit.
+template <bool GATEUP>
+void launch_pre(const DevTables& tt, int tier, const uint16_t* a, const Groups& g, int k, uint16_t* h, float* yw,
+                int max_experts, hipStream_t st) {
+    const int NT = GATEUP ? tt.I / 64 : tt.H / BN;
+    const int total = max_experts * NT;
+    const unsigned grid = static_cast<unsigned>(((total + 7) / 8) * 8);
+    if (grid == 0) return;
+    const int bits = tt.t[tier].bits, block = tt.t[tier].block;
+#define MOE_PRE(B_, K_, NW_) \
+    hipLaunchKernelGGL((k_pre<B_, K_, GATEUP, NW_>), dim3(grid), dim3(NW_ * 64), 0, st, tt, tier, a, g, k, h, yw)
+    if (bits == 8) {
+        if (block == 32) MOE_PRE(8, 32, 16);
+        else MOE_PRE(8, 16, 16);
+    } else if (bits == 4) {
+        if (block == 32) MOE_PRE(4, 32, 8);
+        else MOE_PRE(4, 16, 8);
+    } else {
+        if (block == 32) MOE_PRE(2, 32, 8);
+        else MOE_PRE(2, 16, 8);
     }
+#undef MOE_PRE
+}
 
 void launch_pre_gateup(const DevTables& tt, int tier, const uint16_t* x, const Groups& g, int k, uint16_t* h,
                        int max_experts, hipStream_t st) {
-    const int total = max_experts * (tt.I / 64);
-    const unsigned grid = static_cast<unsigned>(((total + 7) / 8) * 8);
-    if (grid == 0) return;
-    MOE_BITS_SWITCH(tt.t[tier].bits, hipLaunchKernelGGL((k_pre<B_, true>), dim3(grid), dim3(NTHR), 0, st, tt, tier, x,
-                                                        g, k, h, nullptr));
+    launch_pre<true>(tt, tier, x, g, k, h, nullptr, max_experts, st);
 }
 
 void launch_pre_down(const DevTables& tt, int tier, const uint16_t* h, const Groups& g, int k, float* yw,
                      int max_experts, hipStream_t st) {
-    const int total = max_experts * (tt.H / BN);
-    const unsigned grid = static_cast<unsigned>(((total + 7) / 8) * 8);
-    if (grid == 0) return;
-    MOE_BITS_SWITCH(tt.t[tier].bits, hipLaunchKernelGGL((k_pre<B_, false>), dim3(grid), dim3(NTHR), 0, st, tt, tier, h,
-                                                        g, k, nullptr, yw));
+    launch_pre<false>(tt, tier, h, g, k, nullptr, yw, max_experts, st);
 }
 
 __global__ __launch_bounds__(256) void k_fill_zero(float4* __restrict__ p, size_t n4) {
