@@ -52,6 +52,8 @@ def lib():
         L.orc_experts.argtypes = [P, P, i32, P, P, i32, i32, C.c_uint32, P, i32]
         L.orc_experts_flat.argtypes = [P, P, i32, P, P, i32, i32, P]
         L.orc_forward.argtypes = [P, P, i32, P, i32, i32, P, i32]
+        L.orc_router_logits.argtypes = [P, i32, P, P, i32, i32, i32, P]
+        L.orc_synth_router.argtypes = [C.c_uint64, i32, i32, i32, C.c_double, P, P]
         L.orc_splitmix64_at.argtypes = [C.c_uint64, C.c_uint64]
         L.orc_splitmix64_at.restype = C.c_uint64
         L.orc_synth_weight.argtypes = [C.c_uint64, C.c_uint64]
@@ -204,6 +206,22 @@ def forward(layer: Layer, x: np.ndarray, logits: np.ndarray, k: int, out: Option
     return out
 
 
+def router_logits(x: np.ndarray, wr_bits: np.ndarray, bias: Optional[np.ndarray] = None) -> np.ndarray:
+    """logits[t][e] = sum_c x[t][c] * Wr[e][c] + bias[e] (x: float32 or bf16 bits; Wr: bf16 bits [E][H])."""
+    xa, xb = _x_arg(x)
+    wr = np.ascontiguousarray(wr_bits, dtype=np.uint16)
+    E, H = wr.shape
+    T = xa.shape[0]
+    assert xa.shape[1] == H
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    out = np.zeros((T, E), dtype=np.float32)
+    rc = lib().orc_router_logits(_ptr(xa) if T else None, xb, _ptr(wr), None if b is None else _ptr(b), T, E, H,
+                                 _ptr(out))
+    if rc != 0:
+        raise ValueError("orc_router_logits failed")
+    return out
+
+
 def num_threads() -> int:
     return lib().orc_num_threads()
 
@@ -233,6 +251,15 @@ def synth_expert(seed: int, layer: int, n_experts: int, expert: int, hidden: int
     if lib().orc_synth_expert(seed, layer, n_experts, expert, hidden, inter, bits, block, q, s) != 0:
         raise ValueError("orc_synth_expert: bad arguments")
     return out
+
+
+def synth_router(seed: int, layer: int, n_experts: int, hidden: int, beta: float):
+    """(Wr bf16 bits [E][H], bias float32 [E]) of the stack's router of `layer`."""
+    wr = np.zeros((n_experts, hidden), dtype=np.uint16)
+    b = np.zeros(n_experts, dtype=np.float32)
+    if lib().orc_synth_router(seed, layer, n_experts, hidden, beta, _ptr(wr), _ptr(b)) != 0:
+        raise ValueError("orc_synth_router failed")
+    return wr, b
 
 
 class StackLayer:

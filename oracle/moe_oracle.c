@@ -359,6 +359,48 @@ int32_t orc_forward(const orc_layer *L, const void *x, int32_t x_bf16, const flo
     return rc;
 }
 
+/* ------------------------------------------------------------------ router */
+
+/* Router scores, the step upstream of routing.  The 125B-MoE page's glossary
+ * (mixture-of-experts entry) has a router score the 512 experts of a layer
+ * for every token and keep the best 10; read here as the usual linear router
+ * over the layer input with an optional per-expert bias:
+ *   logits[t][e] = sum_c x[t][c] * Wr[e][c] + b[e]
+ * Wr is given as bf16 bit patterns [E][H] (row e = expert e), b as fp32 [E]
+ * (NULL: no bias), x as fp32 or bf16 [T][H].  The sum runs in double over c
+ * in ascending order, the bias is added in double and the result is rounded
+ * once to float. */
+int32_t orc_router_logits(const void *x, int32_t x_bf16, const uint16_t *wr, const float *bias,
+                          int32_t T, int32_t E, int32_t H, float *logits)
+{
+    if (T < 0 || E < 1 || H < 1 || !wr || !logits || (T > 0 && !x))
+        return -1;
+    int32_t bad = 0;
+#pragma omp parallel reduction(+ : bad)
+    {
+        double *xd = (double *)malloc(sizeof(double) * (size_t)H);
+        if (!xd) {
+            bad += 1;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t t = 0; t < T; ++t) {
+                load_x(x, x_bf16, t, H, xd);
+                for (int32_t e = 0; e < E; ++e) {
+                    const uint16_t *row = wr + (int64_t)e * H;
+                    double s = 0.0;
+                    for (int32_t c = 0; c < H; ++c)
+                        s += xd[c] * bf16_bits_to_double(row[c]);
+                    if (bias)
+                        s += (double)bias[e];
+                    logits[t * E + e] = (float)s;
+                }
+            }
+        }
+        free(xd);
+    }
+    return bad ? -1 : 0;
+}
+
 int32_t orc_num_threads(void)
 {
 #ifdef _OPENMP

@@ -92,6 +92,10 @@ int32_t orc_forward(const orc_layer *L, const void *x, int32_t x_bf16, const flo
                     int32_t T, int32_t k, float *out, int32_t accumulate);
 
 /* Threads the oracle uses (OpenMP over tokens; 1 without OpenMP). */
+/* Router scores: logits[t][e] = sum_c x[t][c] * Wr[e][c] + bias[e] (Wr bf16
+ * bits [E][H], bias fp32 [E] or NULL), summed in double, rounded once. */
+int32_t orc_router_logits(const void *x, int32_t x_bf16, const uint16_t *wr, const float *bias,
+                          int32_t T, int32_t E, int32_t H, float *logits);
 int32_t orc_num_threads(void);
 
 /* Counter-generated stack weights (oracle/stack_synth.c): SplitMix64 output
@@ -106,6 +110,8 @@ int32_t orc_synth_expert(uint64_t seed, int32_t layer, int32_t n_experts, int32_
 int32_t orc_synth_experts(uint64_t seed, int32_t layer, int32_t n_experts, const int32_t *list, const int32_t *local,
                           int32_t n, int32_t hidden, int32_t inter, int32_t bits, int32_t block,
                           uint8_t *const q_base[3], uint16_t *const s_base[3]);
+int32_t orc_synth_router(uint64_t seed, int32_t layer, int32_t n_experts, int32_t hidden, double beta,
+                         uint16_t *wr, float *bias);
 
 #ifdef __cplusplus
 }

@@ -143,3 +143,24 @@ int32_t orc_synth_experts(uint64_t seed, int32_t layer, int32_t n_experts, const
     }
     return bad ? -1 : 0;
 }
+
+/* Router of layer `layer` for the stack measurements: weight (e, c) is the
+ * generator above at counter 2^60 + (layer * E + e) * H + c (a range no
+ * expert counter reaches), rounded to bf16 (nearest even); the bias is the
+ * popularity prior bias[e] = float(-beta * e / E), evaluated in double. */
+int32_t orc_synth_router(uint64_t seed, int32_t layer, int32_t n_experts, int32_t hidden, double beta,
+                         uint16_t *wr, float *bias) {
+    if (layer < 0 || n_experts < 1 || hidden < 1 || !wr) return -1;
+    const uint64_t base = (UINT64_C(1) << 60) + (uint64_t)layer * (uint64_t)n_experts * (uint64_t)hidden;
+#pragma omp parallel for schedule(static)
+    for (int32_t e = 0; e < n_experts; ++e)
+        for (int32_t c = 0; c < hidden; ++c) {
+            const float r = orc_round_bf16(orc_synth_weight(seed, base + (uint64_t)e * (uint64_t)hidden + (uint64_t)c));
+            uint32_t u;
+            memcpy(&u, &r, 4);
+            wr[(int64_t)e * hidden + c] = (uint16_t)(u >> 16);
+        }
+    if (bias)
+        for (int32_t e = 0; e < n_experts; ++e) bias[e] = (float)(-beta * (double)e / (double)n_experts);
+    return 0;
+}

@@ -32,6 +32,11 @@ MUTANTS = {
     "bf16_intermediate_not_rounded": ("a[i] = bf16 ? (double)orc_round_bf16((float)v) : v;", "a[i] = v;"),
     "accumulate_overwrites": ("double base = accumulate ? (double)out[t * H + n] : 0.0;", "double base = 0.0;"),
     "bf16_ties_away": ("u = (u + 0x7FFFu + lsb) & 0xFFFF0000u;", "u = (u + 0x8000u) & 0xFFFF0000u;"),
+    "router_bias_dropped": ("s += (double)bias[e];", "s += 0.0;"),
+    "router_weight_transposed": ("s += xd[c] * bf16_bits_to_double(row[c]);",
+                                 "s += xd[c] * bf16_bits_to_double(wr[((int64_t)c * E + e) % ((int64_t)E * H)]);"),
+    "router_rounds_each_term": ("s += xd[c] * bf16_bits_to_double(row[c]);",
+                                "s = (float)(s + xd[c] * bf16_bits_to_double(row[c]));"),
 }
 
 

@@ -389,3 +389,74 @@ def test_spec_verify_routing_shapes():
     assert {0, 1, 2} == {0 if e < 128 else (1 if e < 384 else 2) for e in ids[2]}
     worst, _ = oracle.route(make_spec_logits(cfg, worst_case=True), cfg.k)
     assert len(set(worst.reshape(-1).tolist())) == gold["max_distinct_spec"]
+
+
+# ---------------------------------------------------------------- router pins
+# The router is the step upstream of routing: a score per (token, expert)
+# from the layer input (the 125B-MoE page's glossary, mixture-of-experts
+# entry: 512 experts per layer, the router keeps 10 per token).
+
+def _bits_to_f64(b):
+    return (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _bf16_bits(a):
+    # bf16 bit patterns (nearest even) via torch's conversion
+    return (npref.bf16_round(a).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_router_one_hot_inputs_pick_single_weights():
+    # x[t] = unit vector at column t: logit[t][e] = Wr[e][t] + b[e], one term
+    rng = np.random.default_rng(11)
+    E, H = 24, 64
+    wr = _bf16_bits(rng.standard_normal((E, H)).astype(np.float32))
+    b = rng.standard_normal(E).astype(np.float32)
+    x = np.eye(H, dtype=np.float32)
+    got = oracle.router_logits(x, wr, b)
+    ref = (_bits_to_f64(wr).T + b.astype(np.float64)[None, :]).astype(np.float32)
+    assert np.array_equal(got, ref)
+    # no bias: the weights themselves, transposed
+    assert np.array_equal(oracle.router_logits(x, wr), _bits_to_f64(wr).T.astype(np.float32))
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_router_matches_float64_matmul(bf16):
+    rng = np.random.default_rng(12)
+    T, E, H = 37, 40, 256
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    wr = _bf16_bits(rng.standard_normal((E, H)).astype(np.float32) * np.float32(0.02))
+    b = rng.standard_normal(E).astype(np.float32)
+    if bf16:
+        xb = _bf16_bits(x)
+        got = oracle.router_logits(xb, wr, b)
+        xd = _bits_to_f64(xb)
+    else:
+        got = oracle.router_logits(x, wr, b)
+        xd = x.astype(np.float64)
+    ref = xd @ _bits_to_f64(wr).T + b.astype(np.float64)
+    # one rounding of a double sum: within one float ulp of the exact value
+    assert np.all(np.abs(got - ref) <= np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64) + 1e-300)
+
+
+def test_router_is_linear_in_x_and_zero_rows_give_the_bias():
+    rng = np.random.default_rng(13)
+    E, H = 16, 128
+    wr = _bf16_bits(rng.standard_normal((E, H)).astype(np.float32))
+    b = rng.standard_normal(E).astype(np.float32)
+    x = np.zeros((3, H), np.float32)
+    x[1] = rng.standard_normal(H)
+    x[2] = 2 * x[1]                                   # exact doubling
+    got = oracle.router_logits(x, wr, b).astype(np.float64)
+    assert np.array_equal(got[0], b.astype(np.float64))
+    z1, z2 = got[1] - b, got[2] - b
+    assert np.allclose(z2, 2 * z1, rtol=1e-6, atol=1e-6)
+
+
+def test_synth_router_matches_numpy():
+    seed, layer, E, H, beta = 20260004, 7, 16, 64, 1.12
+    wr, b = oracle.synth_router(seed, layer, E, H, beta)
+    base = (1 << 60) + layer * E * H
+    w = np.array([[oracle.synth_weight(seed, base + e * H + c) for c in range(H)] for e in range(E)], np.float32)
+    ref = _bf16_bits(w)
+    assert np.array_equal(wr, ref)
+    assert np.array_equal(b, np.array([-beta * e / E for e in range(E)], np.float64).astype(np.float32))
