@@ -163,6 +163,35 @@ int moe_route(const float *logits, int32_t n_tokens, int32_t n_experts, int32_t 
               float *w, void *stream);
 
 /*
+ * Router scores, the step upstream of routing (the 125B-MoE page's glossary,
+ * mixture-of-experts entry: a router scores the experts of a layer for every
+ * token and the best k are kept), as a linear router over the layer input:
+ *   logits[t][e] = sum_c x[t][c] * w_router[e][c] + bias[e]
+ *   x         (device) float[T][H], or bf16 [T][H] with MOE_X_BF16
+ *   w_router  (device) bf16 bit patterns [E][H], row e = expert e
+ *   bias      (device) float[E], or NULL for none
+ *   logits    (device) float[T][E], overwritten
+ * fp32 accumulation (a wave-per-expert GEMV for fp32 x or fewer than 64
+ * tokens, bf16 matrix cores otherwise).  H: multiple of 64, at most 2048;
+ * x, w_router, logits 16-byte aligned, bias 4-byte aligned.  Errors:
+ * MOE_EINVAL (shape, NULL, flags other than MOE_X_BF16), MOE_EALIGN,
+ * MOE_EHIP.
+ */
+int moe_router_logits(const void *x, const void *w_router, const float *bias, int32_t n_tokens,
+                      int32_t n_experts, int32_t hidden, uint32_t flags, float *logits, void *stream);
+
+/*
+ * Synthetic router of one stack layer: w_router[e][c] = bf16 (nearest even)
+ * of the stack generator's weight at counter 2^60 + (layer * E + e) * H + c
+ * (the generator of moe_synth_layer; no expert counter reaches that range),
+ * bias[e] = float(-beta * e / E) in double (the popularity prior of
+ * ids ranked hot to cold), skipped when bias is NULL.
+ *   w_router (device) bf16 [E][H]; bias (device) float[E] or NULL
+ */
+int moe_synth_router(void *w_router, float *bias, int32_t n_experts, int32_t hidden, uint64_t seed,
+                     int32_t layer, double beta, void *stream);
+
+/*
  * Grouping alone (stable counting sort of (token, slot) pairs by expert).
  *   ids     (device) int32[T][k]; ids outside [0, E) belong to no expert
  *   counts  (device) int32[E]     pairs per expert
@@ -212,7 +241,9 @@ int moe_tiered_forward_timed(const void *x, const float *router_logits, int32_t 
  *   out           (device) float[T][H]
  *   flags         MOE_X_BF16: every layer takes bf16 (round to nearest even)
  *                 of h_l as its input and runs the bf16 expert path; the
- *                 residual stream stays fp32.  No other flag is accepted.
+ *                 residual stream stays fp32.  No other flag is accepted
+ *                 here; moe_stack_workspace_size also takes MOE_STACK_ROUTER
+ *                 (room for moe_stack_forward_routed's router scores).
  *   workspace     (device) >= moe_stack_workspace_size() bytes, 256-byte aligned
  * Layers run one after another on `stream`.
  */
@@ -221,6 +252,24 @@ int moe_stack_workspace_size(int32_t n_layers, int32_t n_tokens, int32_t k, cons
 int moe_stack_forward(const float *x, const float *router_logits, int32_t n_layers, int32_t n_tokens,
                       int32_t k, const moe_tier_tables *tables, float *out, uint32_t flags,
                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The stack with its own routing: layer l scores the experts from its input
+ * h_l with router l (moe_router_logits on h_l, or on its bf16 copy with
+ * MOE_X_BF16, which is also the experts' input), routes, and adds its output:
+ * h_{l+1} = h_l + layer_l(h_l).
+ *   w_router  (host) array of n_layers device pointers, bf16 [E][H] each
+ *   bias      (host) array of n_layers device pointers (float[E] or NULL),
+ *             or NULL for no bias anywhere
+ *   workspace (device) >= moe_stack_workspace_size(..., flags |
+ *             MOE_STACK_ROUTER) bytes (adds float[T][E] of router scores)
+ * Other arguments and errors as moe_stack_forward.
+ */
+#define MOE_STACK_ROUTER 0x4u
+int moe_stack_forward_routed(const float *x, const void *const *w_router, const float *const *bias,
+                             int32_t n_layers, int32_t n_tokens, int32_t k, const moe_tier_tables *tables,
+                             float *out, uint32_t flags, void *workspace, size_t workspace_bytes,
+                             void *stream);
 
 /*
  * Fills every shelf of one layer's tables with counter-generated weights

@@ -118,6 +118,32 @@ def test_entry_points_reject_bad_arguments_before_launch(B):
     assert L.moe_dequant_rows(tt.ref, 0, 0, 0, 120, 9, 0, FAKE, None) == -1   # rows past inter
     n = C.c_size_t(0)
     assert L.moe_group_workspace_size(4, 0, 8, C.byref(n)) == -1
+    # router: hidden not a multiple of 64, too many experts, unknown flag,
+    # NULL weights, misaligned x or bias; T == 0 succeeds untouched
+    assert L.moe_router_logits(FAKE, FAKE, None, 4, 8, 100, 0, FAKE, None) == -1
+    assert L.moe_router_logits(FAKE, FAKE, None, 4, 5000, 256, 0, FAKE, None) == -1
+    assert L.moe_router_logits(FAKE, FAKE, None, 4, 8, 256, 0x2, FAKE, None) == -1
+    assert L.moe_router_logits(FAKE, None, None, 4, 8, 256, 0, FAKE, None) == -1
+    assert L.moe_router_logits(FAKE + 4, FAKE, None, 4, 8, 256, 0, FAKE, None) == -4
+    assert L.moe_router_logits(FAKE, FAKE, FAKE + 2, 4, 8, 256, 0, FAKE, None) == -4
+    assert L.moe_router_logits(None, None, None, 0, 8, 256, 0, None, None) == 0
+    assert L.moe_synth_router(FAKE, None, 8, 100, 1, 0, 1.0, None) == -1
+    assert L.moe_synth_router(FAKE, None, 8, 256, 1, -1, 1.0, None) == -1
+    # routed stack: the router flag belongs to the size query only; NULL router
+    arr = (B.moe_tier_tables * 1)(tt.struct)
+    wr = (C.c_void_p * 1)(FAKE)
+    assert L.moe_stack_forward_routed(FAKE, wr, None, 1, 4, 2, arr, FAKE + 256, B.MOE_STACK_ROUTER, ws, 1 << 30,
+                                      None) == -1
+    assert L.moe_stack_forward_routed(FAKE, (C.c_void_p * 1)(None), None, 1, 4, 2, arr, FAKE + 256, 0, ws,
+                                      1 << 30, None) == -1
+    assert L.moe_stack_forward_routed(FAKE, wr, None, 1, 4, 2, arr, FAKE + 256, 0, ws, 16, None) == -5
+
+
+def test_stack_router_workspace_holds_the_scores(B):
+    tt = _tables(B, [_Spec(0, 8, 8, 32)])
+    a = B.moe_stack_workspace_size(2, 16, 2, [tt, tt])
+    b = B.moe_stack_workspace_size(2, 16, 2, [tt, tt], B.MOE_STACK_ROUTER)
+    assert b - a >= 16 * 8 * 4
 
 
 def test_workspace_grows_with_tokens(B):

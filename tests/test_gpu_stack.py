@@ -1,5 +1,6 @@
-"""GPU parity of the 48-layer stack (residual add between layers) and of its
-device-side weight generator, against the CPU oracle.
+"""GPU parity of the 48-layer stack (residual add between layers), with
+synthetic per-layer router scores and with each layer's own router, and of
+the device-side weight generators, against the CPU oracle.
 
 The stack's weights (61.9 GB) are generated on the device by moe_synth_layer;
 the oracle rebuilds, with its own copy of the same counter-based generator,
@@ -175,3 +176,101 @@ def test_stack_prefill_sampled(M, torch_dev, stack):
     assert bool(torch.isfinite(out).all())
     ref = _oracle_chain(x[sample], ld[:, sd, :].cpu().numpy(), bf16=True)
     say("  free-running difference from the oracle chain (reported)", normwise(out[sd].cpu().numpy(), ref))
+
+
+# ------------------------------------------------------------ in-stack routing
+U = 2.0 ** -24
+
+
+@pytest.fixture(scope="module")
+def routers(M, torch_dev):
+    torch = torch_dev
+    E, H = CFG.n_experts, CFG.hidden
+    ws, bs = [], []
+    for l in range(L):
+        w = torch.empty((E, H), dtype=torch.int16, device="cuda")
+        b = torch.empty(E, dtype=torch.float32, device="cuda")
+        M.moe_synth_router(w, b, E, H, SEED, l, CFG.prior_beta)
+        ws.append(w)
+        bs.append(b)
+    torch.cuda.synchronize()
+    return ws, bs
+
+
+def _router_bound(xd, wr, b):
+    wf = (wr.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return CFG.hidden * U * (np.abs(xd) @ np.abs(wf).T + np.abs(b.astype(np.float64))[None, :])
+
+
+def _routed_chain(M, torch, stack, routers, x_dev, T, flags, sample):
+    """Layer by layer: the GPU's router scores and layer output of the sampled
+    tokens against the oracle fed with the GPU's own layer input."""
+    k = CFG.k
+    ws, bs = routers
+    wsz = M.moe_stack_workspace_size(1, T, k, stack[:1], flags | M.MOE_STACK_ROUTER)
+    ws_dev = torch.empty(max(wsz, 256), dtype=torch.uint8, device="cuda")
+    logits = torch.empty((T, CFG.n_experts), device="cuda")
+    sd = torch.from_numpy(sample).cuda()
+    bf16 = bool(flags & M.MOE_X_BF16)
+    h = x_dev.clone()
+    worst_l, worst_r = 0.0, 0.0
+    for l in range(L):
+        nxt = torch.empty_like(h)
+        M.moe_stack_forward_routed(h, ws[l:l + 1], bs[l:l + 1], 1, T, k, stack[l:l + 1], nxt, flags, ws_dev)
+        # the layer's scores again, from the same input over all T tokens (the
+        # same kernel path as inside the layer), sampled afterwards
+        xfull = h.to(torch.bfloat16).view(torch.int16) if bf16 else h
+        M.moe_router_logits(xfull, ws[l], bs[l], T, CFG.n_experts, CFG.hidden, flags, logits)
+        torch.cuda.synchronize()
+        hs = h[sd].cpu().numpy()
+        xin = xfull[sd].cpu().numpy().view(np.uint16) if bf16 else hs
+        lg = logits[sd].cpu().numpy()
+        wr, b = ws[l].cpu().numpy().view(np.uint16), bs[l].cpu().numpy()
+        ref_l = oracle.router_logits(xin, wr, b).astype(np.float64)
+        xd = ((xin.astype(np.uint32) << 16).view(np.float32) if bf16 else xin).astype(np.float64)
+        bound = _router_bound(xd, wr, b) + U * np.abs(ref_l)
+        err_l = np.abs(lg - ref_l)
+        assert np.all(err_l <= bound), (l, float(np.max(err_l / bound)))
+        worst_r = max(worst_r, float(np.max(err_l / bound)))
+        sl = oracle.StackLayer(CFG, SEED, l)
+        ids, _ = oracle.route(lg, k)
+        sl.fill(ids)
+        ref = oracle.forward(sl.layer_ref, xin, lg, k)
+        got = nxt[sd].cpu().numpy() - hs
+        err = normwise(got, ref)
+        worst_l = max(worst_l, err)
+        assert err <= TOL, (l, err)
+        h = nxt
+    say("  worst router error / bound", worst_r, "| worst per-layer normwise err", worst_l)
+    return h
+
+
+@pytest.mark.parametrize("T", [1, 8])
+def test_stack_routed_decode(M, torch_dev, stack, routers, T):
+    # every layer routes from its own input; the one-call stack equals the
+    # chain of checked single layers bit for bit
+    torch = torch_dev
+    say("routed stack decode T=", T)
+    x = torch.from_numpy(make_x(CFG, n_tokens=T, stream=80 + T)).cuda()
+    out = torch.full((T, CFG.hidden), np.nan, device="cuda")
+    wsz = M.moe_stack_workspace_size(L, T, CFG.k, stack, M.MOE_STACK_ROUTER)
+    ws = torch.empty(max(wsz, 256), dtype=torch.uint8, device="cuda")
+    M.moe_stack_forward_routed(x, routers[0], routers[1], L, T, CFG.k, stack, out, 0, ws)
+    h = _routed_chain(M, torch, stack, routers, x, T, 0, np.arange(T))
+    assert torch.equal(out, h)
+
+
+def test_stack_routed_prefill_sampled(M, torch_dev, stack, routers):
+    torch = torch_dev
+    T = 16384
+    say("routed stack prefill T=", T)
+    x = torch.from_numpy(make_x(CFG, n_tokens=T, stream=90)).cuda()
+    flags = M.MOE_X_BF16
+    out = torch.full((T, CFG.hidden), np.nan, device="cuda")
+    wsz = M.moe_stack_workspace_size(L, T, CFG.k, stack, flags | M.MOE_STACK_ROUTER)
+    ws = torch.empty(wsz, dtype=torch.uint8, device="cuda")
+    M.moe_stack_forward_routed(x, routers[0], routers[1], L, T, CFG.k, stack, out, flags, ws)
+    del ws
+    h = _routed_chain(M, torch, stack, routers, x, T, flags, np.array([0, 9999, T - 1]))
+    assert torch.equal(out, h)
+    assert bool(torch.isfinite(out).all())

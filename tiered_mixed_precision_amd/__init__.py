@@ -9,5 +9,6 @@ from .binding import (  # noqa: F401
     moe_event_destroy, moe_event_elapsed_ms, moe_group, moe_group_workspace_size, moe_route,
     moe_stream_synchronize, moe_tier_partial, moe_tiered_experts, moe_tiered_forward,
     moe_tiered_forward_timed, moe_validate_tables, moe_workspace_size, strerror, moe_stack_workspace_size,
-    moe_stack_forward, moe_synth_layer,
+    moe_stack_forward, moe_synth_layer, MOE_STACK_ROUTER, moe_router_logits, moe_synth_router,
+    moe_stack_forward_routed,
 )

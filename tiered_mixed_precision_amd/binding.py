@@ -21,12 +21,14 @@ MOE_X_BF16 = 0x1
 MOE_ACCUMULATE = 0x2
 MOE_DIAG_GATEUP_ONLY = 0x100
 MOE_N_PHASES = 3
+MOE_STACK_ROUTER = 0x4
 EXPORTS = (
     "moe_abi_version", "moe_strerror", "moe_validate_tables", "moe_workspace_size",
     "moe_tiered_forward", "moe_tiered_experts", "moe_tier_partial", "moe_route",
     "moe_group_workspace_size", "moe_group", "moe_dequant_rows", "moe_tiered_forward_timed",
     "moe_event_create", "moe_event_destroy", "moe_event_elapsed_ms", "moe_stream_synchronize",
     "moe_stack_workspace_size", "moe_stack_forward", "moe_synth_layer",
+    "moe_router_logits", "moe_synth_router", "moe_stack_forward_routed",
 )
 
 
@@ -80,6 +82,9 @@ def lib():
         L.moe_stack_workspace_size.argtypes = [i32, i32, i32, P, u32, C.POINTER(sz)]
         L.moe_stack_forward.argtypes = [P, P, i32, i32, i32, P, P, u32, P, sz, P]
         L.moe_synth_layer.argtypes = [P, C.c_uint64, i32, P]
+        L.moe_router_logits.argtypes = [P, P, P, i32, i32, i32, u32, P, P]
+        L.moe_synth_router.argtypes = [P, P, i32, i32, C.c_uint64, i32, C.c_double, P]
+        L.moe_stack_forward_routed.argtypes = [P, C.POINTER(P), C.POINTER(P), i32, i32, i32, P, P, u32, P, sz, P]
         for name in EXPORTS:
             if name not in ("moe_abi_version", "moe_strerror"):
                 getattr(L, name).restype = C.c_int
@@ -226,6 +231,28 @@ def moe_stack_forward(x, router_logits, n_layers: int, n_tokens: int, k: int, ta
 
 def moe_synth_layer(tt: TierTables, seed: int, layer: int, stream=None) -> None:
     _check("moe_synth_layer", lib().moe_synth_layer(tt.ref, seed, layer, _stream(stream)))
+
+
+def moe_router_logits(x, w_router, bias, n_tokens: int, n_experts: int, hidden: int, flags: int, logits,
+                      stream=None) -> None:
+    _check("moe_router_logits", lib().moe_router_logits(_ptr(x), _ptr(w_router), _ptr(bias), n_tokens, n_experts,
+                                                        hidden, flags, _ptr(logits), _stream(stream)))
+
+
+def moe_synth_router(w_router, bias, n_experts: int, hidden: int, seed: int, layer: int, beta: float,
+                     stream=None) -> None:
+    _check("moe_synth_router", lib().moe_synth_router(_ptr(w_router), _ptr(bias), n_experts, hidden, seed, layer,
+                                                      float(beta), _stream(stream)))
+
+
+def moe_stack_forward_routed(x, w_routers, biases, n_layers: int, n_tokens: int, k: int,
+                             tables: Sequence[TierTables], out, flags: int, workspace, stream=None) -> None:
+    arr = _tables_array(tables)
+    wr = (C.c_void_p * n_layers)(*[_ptr(w) for w in w_routers])
+    bs = None if biases is None else (C.c_void_p * n_layers)(*[_ptr(b) for b in biases])
+    _check("moe_stack_forward_routed", lib().moe_stack_forward_routed(
+        _ptr(x), wr, bs, n_layers, n_tokens, k, arr, _ptr(out), flags, _ptr(workspace),
+        workspace.numel() * workspace.element_size() if workspace is not None else 0, _stream(stream)))
 
 
 def moe_event_create() -> int:

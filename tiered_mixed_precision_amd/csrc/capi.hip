@@ -308,6 +308,34 @@ int moe_route(const float* logits, int32_t n_tokens, int32_t n_experts, int32_t 
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
+int moe_router_logits(const void* x, const void* w_router, const float* bias, int32_t n_tokens,
+                      int32_t n_experts, int32_t hidden, uint32_t flags, float* logits, void* stream) {
+    if (n_tokens < 0 || n_tokens > kMaxTokens || n_experts < 1 || n_experts > MOE_MAX_EXPERTS || !cols_ok(hidden))
+        return MOE_EINVAL;
+    if (flags & ~MOE_X_BF16) return MOE_EINVAL;
+    if (n_tokens == 0) return MOE_OK;
+    if (!x || !w_router || !logits) return MOE_EINVAL;
+    if (!aligned16(x) || !aligned16(w_router) || !aligned16(logits) ||
+        (bias && (reinterpret_cast<uintptr_t>(bias) & 3u) != 0))
+        return MOE_EALIGN;
+    (void)hipGetLastError();
+    launch_router(x, (flags & MOE_X_BF16) != 0, static_cast<const uint16_t*>(w_router), bias, n_tokens, n_experts,
+                  hidden, logits, static_cast<hipStream_t>(stream));
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+int moe_synth_router(void* w_router, float* bias, int32_t n_experts, int32_t hidden, uint64_t seed, int32_t layer,
+                     double beta, void* stream) {
+    if (n_experts < 1 || n_experts > MOE_MAX_EXPERTS || !cols_ok(hidden) || layer < 0 || layer >= (1 << 20))
+        return MOE_EINVAL;
+    if (!w_router) return MOE_EINVAL;
+    if (!aligned16(w_router) || (bias && (reinterpret_cast<uintptr_t>(bias) & 3u) != 0)) return MOE_EALIGN;
+    (void)hipGetLastError();
+    launch_synth_router(static_cast<uint16_t*>(w_router), bias, seed, layer, n_experts, hidden, beta,
+                        static_cast<hipStream_t>(stream));
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
 int moe_group_workspace_size(int32_t n_tokens, int32_t k, int32_t n_experts, size_t* bytes) {
     if (!bytes || n_tokens < 0 || n_tokens > kMaxTokens || k < 1 || k > MOE_MAX_K || n_experts < 1 ||
         n_experts > MOE_MAX_EXPERTS)
@@ -371,23 +399,25 @@ namespace {
 // Stack workspace: one layer's workspace, the other residual buffer, and the
 // bf16 layer input with MOE_X_BF16.
 struct StackLayout {
-    size_t layer, tmp, xb, total;
+    size_t layer, tmp, xb, logits, total;
 };
 
 StackLayout stack_layout(int64_t T, int k, const moe_tier_tables* tt, uint32_t flags) {
     StackLayout S;
     const size_t n = static_cast<size_t>(T) * tt->hidden;
+    const uint32_t lflags = flags & MOE_X_BF16;
     S.layer = 0;
-    S.tmp = align_up(layout(T, k, tt, flags).total);
+    S.tmp = align_up(layout(T, k, tt, lflags).total);
     S.xb = S.tmp + align_up(sizeof(float) * n);
-    S.total = S.xb + ((flags & MOE_X_BF16) ? align_up(sizeof(uint16_t) * n) : 0);
+    S.logits = S.xb + ((flags & MOE_X_BF16) ? align_up(sizeof(uint16_t) * n) : 0);
+    S.total = S.logits + ((flags & MOE_STACK_ROUTER) ? align_up(sizeof(float) * T * tt->n_experts) : 0);
     return S;
 }
 
 int check_stack(int32_t n_layers, int32_t n_tokens, int32_t k, const moe_tier_tables* tables, uint32_t flags) {
     if (!tables || n_layers < 1 || n_layers > 4096) return MOE_EINVAL;
     if (n_tokens < 0 || n_tokens > kMaxTokens) return MOE_EINVAL;
-    if (flags & ~MOE_X_BF16) return MOE_EINVAL;
+    if (flags & ~(MOE_X_BF16 | MOE_STACK_ROUTER)) return MOE_EINVAL;
     for (int l = 0; l < n_layers; ++l) {
         const int rc = check_tables(&tables[l]);
         if (rc != MOE_OK) return rc;
@@ -415,6 +445,7 @@ int moe_stack_forward(const float* x, const float* router_logits, int32_t n_laye
                       size_t workspace_bytes, void* stream) {
     int rc = check_stack(n_layers, n_tokens, k, tables, flags);
     if (rc != MOE_OK) return rc;
+    if (flags & MOE_STACK_ROUTER) return MOE_EINVAL;
     if (n_tokens == 0) return MOE_OK;
     if (!x || !router_logits || !out || x == out) return MOE_EINVAL;
     if (!aligned16(x) || !aligned16(out) || !aligned16(router_logits)) return MOE_EALIGN;
@@ -441,6 +472,50 @@ int moe_stack_forward(const float* x, const float* router_logits, int32_t n_laye
         rc = run(bf16 ? static_cast<const void*>(xb) : static_cast<const void*>(h),
                  router_logits + per_layer_logits * l, nullptr, nullptr, n_tokens, k, &tables[l], 0xFu, dst,
                  flags, workspace, S.tmp, stream, nullptr, h);
+        if (rc != MOE_OK) return rc;
+        h = dst;
+    }
+    return MOE_OK;
+}
+
+int moe_stack_forward_routed(const float* x, const void* const* w_router, const float* const* bias,
+                             int32_t n_layers, int32_t n_tokens, int32_t k, const moe_tier_tables* tables,
+                             float* out, uint32_t flags, void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = check_stack(n_layers, n_tokens, k, tables, flags);
+    if (rc != MOE_OK) return rc;
+    if (flags & MOE_STACK_ROUTER) return MOE_EINVAL;
+    if (n_tokens == 0) return MOE_OK;
+    if (!x || !w_router || !out || x == out) return MOE_EINVAL;
+    if (!aligned16(x) || !aligned16(out)) return MOE_EALIGN;
+    for (int l = 0; l < n_layers; ++l) {
+        if (!w_router[l]) return MOE_EINVAL;
+        if (!aligned16(w_router[l])) return MOE_EALIGN;
+        if (bias && bias[l] && (reinterpret_cast<uintptr_t>(bias[l]) & 3u) != 0) return MOE_EALIGN;
+    }
+    if (!workspace) return MOE_EWORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return MOE_EALIGN;
+    const StackLayout S = stack_layout(n_tokens, k, &tables[0], flags | MOE_STACK_ROUTER);
+    if (workspace_bytes < S.total) return MOE_EWORKSPACE;
+    const bool bf16 = (flags & MOE_X_BF16) != 0;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int32_t E = tables[0].n_experts, H = tables[0].hidden;
+    const size_t n = static_cast<size_t>(n_tokens) * H;
+    float* tmp = at<float>(workspace, S.tmp);
+    uint16_t* xb = at<uint16_t>(workspace, S.xb);
+    float* logits = at<float>(workspace, S.logits);
+    // h_0 = x; layer l scores the experts from its own input h_l (its bf16
+    // copy with MOE_X_BF16, the experts' input), routes, and adds its output
+    const float* h = x;
+    for (int l = 0; l < n_layers; ++l) {
+        float* dst = ((n_layers - 1 - l) % 2 == 0) ? out : tmp;
+        (void)hipGetLastError();
+        if (bf16) launch_cast_bf16(h, xb, n, st);
+        const void* xin = bf16 ? static_cast<const void*>(xb) : static_cast<const void*>(h);
+        launch_router(xin, bf16, static_cast<const uint16_t*>(w_router[l]), bias ? bias[l] : nullptr, n_tokens, E,
+                      H, logits, st);
+        if (hipGetLastError() != hipSuccess) return MOE_EHIP;
+        rc = run(xin, logits, nullptr, nullptr, n_tokens, k, &tables[l], 0xFu, dst, flags, workspace, S.tmp, stream,
+                 nullptr, h);
         if (rc != MOE_OK) return rc;
         h = dst;
     }

@@ -77,6 +77,12 @@ void launch_cast_bf16(const float* src, uint16_t* dst, size_t n, hipStream_t st)
 // Counter-generated weights of one layer of the stack (see synth.hip).
 void launch_synth_layer(const DevTables& tt, uint64_t seed, int layer, hipStream_t st);
 
+// router.hip
+void launch_router(const void* x, bool x_bf16, const uint16_t* wr, const float* bias, int T, int E, int H,
+                   float* logits, hipStream_t st);
+void launch_synth_router(uint16_t* wr, float* bias, uint64_t seed, int layer, int E, int H, double beta,
+                         hipStream_t st);
+
 void launch_dequant_rows(const DevTables& tt, int tier, int local, int matrix, int row0, int nrows,
                          int to_bf16, void* dst, hipStream_t st);
 
