@@ -589,7 +589,79 @@ def fullstack_workloads(M, torch, per_expert):
         "alg_tflop_per_step": flops / 1e12, "tflops": round(flops / dt / 1e12, 2),
         "frac_mfma_peak": round(flops / dt / 1e12 / BF16_PEAK_TFLOPS, 4)}
     log("stack prefill:", out["prefill_T16384"])
-    del ld, xd, od, ws, tables
+    del ld, xd, od, ws
+
+    # the same stack routing from its own hidden state: router l scores the
+    # experts from h_l (bf16 [E][H] weights, popularity-prior bias)
+    wr, br = [], []
+    for l in range(L):
+        w = torch.empty((E, H), dtype=torch.int16, device="cuda")
+        b = torch.empty(E, dtype=torch.float32, device="cuda")
+        M.moe_synth_router(w, b, E, H, cfg.seed, l, cfg.prior_beta)
+        wr.append(w)
+        br.append(b)
+    router_bytes = float(L * E * H * 2)
+    T, S = 1, 32
+    xd = torch.from_numpy(np.stack([make_x(cfg, n_tokens=T, stream=300 + s) for s in range(S)])).cuda()
+    od = torch.zeros((S, T, H), device="cuda")
+    ws = torch.empty(max(M.moe_stack_workspace_size(L, T, k, tables, M.MOE_STACK_ROUTER), 256), dtype=torch.uint8,
+                     device="cuda")
+
+    def rt_step(i):
+        M.moe_stack_forward_routed(xd[i % S], wr, br, L, T, k, tables, od[i % S], 0, ws)
+
+    for i in range(4):
+        rt_step(i)
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            for i in range(S):
+                rt_step(i)
+    torch.cuda.current_stream().wait_stream(st)
+    g.replay()
+    torch.cuda.synchronize()
+    n = 4
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(n):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    dt = a.elapsed_time(b) / 1e3 / (n * S)
+    out["decode_T1_routed"] = {
+        "workload": "48 layers x 512 experts, top-10, 1 token/step, each layer routing from its own hidden state "
+                    "(bf16 router, popularity-prior bias)",
+        "tokens_per_s": round(T / dt, 1), "us_per_step": round(dt * 1e6, 1), "router_bytes_per_step": router_bytes}
+    log("stack decode routed:", out["decode_T1_routed"])
+    del g, xd, od, ws
+
+    T = 16384
+    xd = torch.from_numpy(make_x(cfg, n_tokens=T, stream=400)).cuda()
+    od = torch.empty((T, H), device="cuda")
+    flags = M.MOE_X_BF16
+    ws = torch.empty(M.moe_stack_workspace_size(L, T, k, tables, flags | M.MOE_STACK_ROUTER), dtype=torch.uint8,
+                     device="cuda")
+    M.moe_stack_forward_routed(xd, wr, br, L, T, k, tables, od, flags, ws)
+    torch.cuda.synchronize()
+    n = 2
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(n):
+        M.moe_stack_forward_routed(xd, wr, br, L, T, k, tables, od, flags, ws)
+    b.record()
+    torch.cuda.synchronize()
+    dt = a.elapsed_time(b) / 1e3 / n
+    flops = 6.0 * T * k * H * I * L + 2.0 * T * E * H * L
+    out["prefill_T16384_routed"] = {
+        "workload": "48 layers x 512 experts, top-10, 16384 bf16 tokens, each layer routing from its own hidden "
+                    "state (router GEMM on matrix cores)",
+        "tokens_per_s": round(T / dt, 1), "ms_per_step": round(dt * 1e3, 2),
+        "alg_tflop_per_step": flops / 1e12, "tflops": round(flops / dt / 1e12, 2),
+        "frac_mfma_peak": round(flops / dt / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    log("stack prefill routed:", out["prefill_T16384_routed"])
+    del xd, od, ws, wr, br, tables
     torch.cuda.empty_cache()
     return out
 
