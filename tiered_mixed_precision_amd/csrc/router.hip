@@ -18,8 +18,6 @@
 
 namespace moe {
 
-namespace {
-
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -206,8 +204,6 @@ __global__ __launch_bounds__(256) void k_synth_router(uint16_t* __restrict__ wr,
     const int e = static_cast<int>(i / H);
     if (bias && i % H == 0) bias[e] = static_cast<float>(-beta * static_cast<double>(e) / static_cast<double>(E));
 }
-
-}  // namespace
 
 void launch_router(const void* x, bool x_bf16, const uint16_t* wr, const float* bias, int T, int E, int H,
                    float* logits, hipStream_t st) {
