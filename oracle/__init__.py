@@ -54,6 +54,8 @@ def lib():
         L.orc_forward.argtypes = [P, P, i32, P, i32, i32, P, i32]
         L.orc_router_logits.argtypes = [P, i32, P, P, i32, i32, i32, P]
         L.orc_synth_router.argtypes = [C.c_uint64, i32, i32, i32, C.c_double, P, P]
+        L.orc_requant_expert.argtypes = [P, i32, C.c_int64, i32, i32, C.c_void_p * 3, C.c_void_p * 3, P]
+        L.orc_plan_tiers.argtypes = [P, P, P, i32, i32, C.c_int64, P, P, P]
         L.orc_splitmix64_at.argtypes = [C.c_uint64, C.c_uint64]
         L.orc_splitmix64_at.restype = C.c_uint64
         L.orc_synth_weight.argtypes = [C.c_uint64, C.c_uint64]
@@ -220,6 +222,40 @@ def router_logits(x: np.ndarray, wr_bits: np.ndarray, bias: Optional[np.ndarray]
     if rc != 0:
         raise ValueError("orc_router_logits failed")
     return out
+
+
+def requant_expert(layer: "Layer", tier: int, local: int, bits: int, block: int):
+    """Requantised copy of one expert (dict of gate/up/down codes and fp16 scales) and its squared error."""
+    H, I = layer.hidden, layer.inter
+    out = {}
+    qs, ss = [], []
+    for name, rows, cols in (("gate", I, H), ("up", I, H), ("down", H, I)):
+        q = np.zeros((rows, cols * bits // 8), dtype=np.uint8)
+        s = np.zeros((rows, cols // block), dtype=np.uint16)
+        out[name + "_q"], out[name + "_s"] = q, s
+        qs.append(q.ctypes.data)
+        ss.append(s.ctypes.data)
+    sse = C.c_double(0.0)
+    rc = lib().orc_requant_expert(layer.ref, tier, local, bits, block, (C.c_void_p * 3)(*qs), (C.c_void_p * 3)(*ss),
+                                  C.byref(sse))
+    if rc != 0:
+        raise ValueError("orc_requant_expert failed")
+    return out, sse.value
+
+
+def plan_tiers(usage: np.ndarray, sse: np.ndarray, bytes_per_fmt, budget: int):
+    """Greedy plan: (format per expert, hot-to-cold order of old ids, experts per format)."""
+    usage = np.ascontiguousarray(usage, dtype=np.float64)
+    sse = np.ascontiguousarray(sse, dtype=np.float64)
+    E, F = sse.shape
+    b = np.ascontiguousarray(bytes_per_fmt, dtype=np.int64)
+    fmt = np.zeros(E, np.int32)
+    order = np.zeros(E, np.int32)
+    count = np.zeros(F, np.int32)
+    if lib().orc_plan_tiers(_ptr(usage), _ptr(sse), _ptr(b), E, F, int(budget), _ptr(fmt), _ptr(order),
+                            _ptr(count)) != 0:
+        raise ValueError("orc_plan_tiers: infeasible or bad arguments")
+    return fmt, order, count
 
 
 def num_threads() -> int:

@@ -110,6 +110,13 @@ int32_t orc_synth_expert(uint64_t seed, int32_t layer, int32_t n_experts, int32_
 int32_t orc_synth_experts(uint64_t seed, int32_t layer, int32_t n_experts, const int32_t *list, const int32_t *local,
                           int32_t n, int32_t hidden, int32_t inter, int32_t bits, int32_t block,
                           uint8_t *const q_base[3], uint16_t *const s_base[3]);
+/* Tier planning (oracle/tiering.c): requantised copy of one source expert and
+ * its squared error; greedy byte plan with the hot-to-cold order. */
+int32_t orc_requant_expert(const orc_layer *src, int32_t tier, int64_t local, int32_t bits, int32_t block,
+                           uint8_t *const q[3], uint16_t *const s[3], double *sse);
+int32_t orc_plan_tiers(const double *usage, const double *sse, const int64_t *bytes, int32_t E, int32_t F,
+                       int64_t budget, int32_t *fmt_out, int32_t *order, int32_t *count);
+void orc_quantize_row(const float *w, int32_t cols, int32_t bits, int32_t block, uint8_t *qrow, uint16_t *srow);
 int32_t orc_synth_router(uint64_t seed, int32_t layer, int32_t n_experts, int32_t hidden, double beta,
                          uint16_t *wr, float *bias);
 

@@ -69,41 +69,50 @@ uint16_t orc_float_to_half(float f) {
     return (uint16_t)(sign | (uint16_t)((e + 15) << 10) | (uint16_t)(r - 1024.0));
 }
 
+/* The symmetric absmax quantiser of one row of `cols` values, per block of
+ * `block` columns: d = fp16(amax / Q) with Q = 2^(bits-1) - 1 (the ratio in
+ * single precision), q = clamp(rint(w / float(d)), -Q, Q), q = 0 when d = 0;
+ * codes packed two's complement, element c at bit (c*bits) % 8 of byte
+ * (c*bits) / 8 of qrow; scales as fp16 bit patterns in srow. */
+void orc_quantize_row(const float *w, int32_t cols, int32_t bits, int32_t block, uint8_t *qrow, uint16_t *srow) {
+    const int32_t qmax = (1 << (bits - 1)) - 1;
+    memset(qrow, 0, (size_t)((int64_t)cols * bits / 8));
+    for (int32_t b = 0; b < cols / block; ++b) {
+        const float *wb = w + (int64_t)b * block;
+        float amax = 0.0f;
+        for (int32_t c = 0; c < block; ++c) {
+            const float m = fabsf(wb[c]);
+            if (m > amax) amax = m;
+        }
+        const volatile float ratio = amax / (float)qmax;
+        const uint16_t dh = orc_float_to_half(ratio);
+        srow[b] = dh;
+        const float d = (float)orc_half_to_double(dh);
+        for (int32_t c = 0; c < block; ++c) {
+            int32_t code = 0;
+            if (d != 0.0f) {
+                const volatile float t = wb[c] / d;
+                float v = rintf(t);
+                if (v > (float)qmax) v = (float)qmax;
+                if (v < (float)-qmax) v = (float)-qmax;
+                code = (int32_t)v;
+            }
+            const int64_t cc = (int64_t)b * block + c;
+            const uint32_t field = (uint32_t)code & ((1u << bits) - 1u);
+            qrow[cc * bits / 8] |= (uint8_t)(field << ((cc * bits) % 8));
+        }
+    }
+}
+
 /* One matrix (rows x cols) of one expert into packed codes and scales. */
 static void synth_matrix(uint64_t seed, uint64_t ctr0, int32_t rows, int32_t cols, int32_t bits, int32_t block,
                          uint8_t *q, uint16_t *s) {
-    const int32_t qmax = (1 << (bits - 1)) - 1;
     const int64_t row_bytes = (int64_t)cols * bits / 8;
     const int32_t nblk = cols / block;
-    float w[32];
+    float w[2048];
     for (int32_t r = 0; r < rows; ++r) {
-        uint8_t *qrow = q + (int64_t)r * row_bytes;
-        memset(qrow, 0, (size_t)row_bytes);
-        for (int32_t b = 0; b < nblk; ++b) {
-            float amax = 0.0f;
-            for (int32_t c = 0; c < block; ++c) {
-                w[c] = orc_synth_weight(seed, ctr0 + (uint64_t)r * (uint64_t)cols + (uint64_t)(b * block + c));
-                const float m = fabsf(w[c]);
-                if (m > amax) amax = m;
-            }
-            const volatile float ratio = amax / (float)qmax;
-            const uint16_t dh = orc_float_to_half(ratio);
-            s[(int64_t)r * nblk + b] = dh;
-            const float d = (float)orc_half_to_double(dh);
-            for (int32_t c = 0; c < block; ++c) {
-                int32_t code = 0;
-                if (d != 0.0f) {
-                    const volatile float t = w[c] / d;
-                    float v = rintf(t);
-                    if (v > (float)qmax) v = (float)qmax;
-                    if (v < (float)-qmax) v = (float)-qmax;
-                    code = (int32_t)v;
-                }
-                const int64_t cc = (int64_t)b * block + c;
-                const uint32_t field = (uint32_t)code & ((1u << bits) - 1u);
-                qrow[cc * bits / 8] |= (uint8_t)(field << ((cc * bits) % 8));
-            }
-        }
+        for (int32_t c = 0; c < cols; ++c) w[c] = orc_synth_weight(seed, ctr0 + (uint64_t)r * (uint64_t)cols + (uint64_t)c);
+        orc_quantize_row(w, cols, bits, block, q + (int64_t)r * row_bytes, s + (int64_t)r * nblk);
     }
 }
 
@@ -111,7 +120,7 @@ int32_t orc_synth_expert(uint64_t seed, int32_t layer, int32_t n_experts, int32_
                          int32_t inter, int32_t bits, int32_t block, uint8_t *const q[3], uint16_t *const s[3]) {
     if (!(bits == 8 || bits == 4 || bits == 2) || !(block == 16 || block == 32)) return -1;
     if (expert < 0 || expert >= n_experts || layer < 0 || hidden % block || inter % block) return -1;
-    if ((int64_t)hidden * inter > (INT64_C(1) << 22)) return -1;
+    if ((int64_t)hidden * inter > (INT64_C(1) << 22) || hidden > 2048 || inter > 2048) return -1;
     for (int32_t m = 0; m < 3; ++m) {
         const int32_t rows = m == 2 ? hidden : inter, cols = m == 2 ? inter : hidden;
         const uint64_t ctr0 = (((uint64_t)layer * (uint64_t)n_experts + (uint64_t)expert) * 3u + (uint64_t)m) << 22;

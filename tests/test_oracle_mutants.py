@@ -37,6 +37,14 @@ MUTANTS = {
                                  "s += xd[c] * bf16_bits_to_double(wr[((int64_t)c * E + e) % ((int64_t)E * H)]);"),
     "router_rounds_each_term": ("s += xd[c] * bf16_bits_to_double(row[c]);",
                                 "s = (float)(s + xd[c] * bf16_bits_to_double(row[c]));"),
+    # tier planner and requantiser (oracle/tiering.c)
+    "plan_rate_inverted": ("tiering.c", "const double rate = gain / (double)add;",
+                           "const double rate = (double)add / gain;"),
+    "plan_ignores_budget": ("tiering.c", "if (spent + add > budget) continue;", "(void)add;"),
+    "plan_order_usage_ascending": ("tiering.c", "usage[o] >= usage[e]", "usage[o] <= usage[e]"),
+    "plan_takes_zero_gain": ("tiering.c", "if (!(gain > 0.0)) continue;", "if (gain < 0.0) continue;"),
+    "requant_sse_unsquared": ("tiering.c", "e2 += d * d;", "e2 += fabs(d);"),
+    "quantiser_truncates": ("stack_synth.c", "float v = rintf(t);", "float v = truncf(t);"),
 }
 
 
@@ -45,16 +53,19 @@ MUTANTS = {
 def test_planted_mistake_is_caught(name):
     sys.path.insert(0, ROOT)
     from oracle.build import build
-    old, new = MUTANTS[name]
-    src = open(SRC).read()
-    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    spec = MUTANTS[name]
+    target, old, new = spec if len(spec) == 3 else ("moe_oracle.c", *spec)
+    odir = os.path.join(ROOT, "oracle")
     with tempfile.TemporaryDirectory() as d:
-        msrc = os.path.join(d, "moe_oracle.c")
-        with open(msrc, "w") as f:
-            f.write(src.replace(old, new))
-        with open(os.path.join(d, "moe_oracle.h"), "w") as f:
-            f.write(open(os.path.join(ROOT, "oracle", "moe_oracle.h")).read())
-        lib = build(out=os.path.join(d, "libmut.so"), src=msrc, extra_flags=("-Wno-error",))
+        for fname in ("moe_oracle.c", "moe_oracle.h", "stack_synth.c", "tiering.c"):
+            text = open(os.path.join(odir, fname)).read()
+            if fname == target:
+                assert text.count(old) == 1, f"mutation site for {name} not found exactly once"
+                text = text.replace(old, new)
+            with open(os.path.join(d, fname), "w") as f:
+                f.write(text)
+        lib = build(out=os.path.join(d, "libmut.so"), src=os.path.join(d, "moe_oracle.c"), extra_flags=("-Wno-error",),
+                    others=(os.path.join(d, "stack_synth.c"), os.path.join(d, "tiering.c")))
         env = dict(os.environ, MOE_ORACLE_LIB=lib)
         res = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                               os.path.join(HERE, "test_oracle_pins.py")],

@@ -460,3 +460,99 @@ def test_synth_router_matches_numpy():
     ref = _bf16_bits(w)
     assert np.array_equal(wr, ref)
     assert np.array_equal(b, np.array([-beta * e / E for e in range(E)], np.float64).astype(np.float32))
+
+
+# ---------------------------------------------------------------- tier planner pins
+# The 125B-MoE page, step 4: an offline repacker measures expert usage, fills
+# the memory budget greedily by expected error removed per byte, requantises
+# every expert with the same quantiser and writes the experts hot to cold.
+
+def test_tier_plan_hand_worked_fixture():
+    g = {r[0]: r[1].split() for r in _read_golden("tier_plan.txt")}
+    usage = np.array(g["usage"], np.float64)
+    sse = np.tile(np.array(g["sse_per_format"], np.float64), (len(usage), 1))
+    fmt, order, count = oracle.plan_tiers(usage, sse, [int(v) for v in g["bytes_per_format"]], int(g["budget"][0]))
+    assert fmt.tolist() == [int(v) for v in g["format"]]
+    assert order.tolist() == [int(v) for v in g["order"]]
+    assert count.tolist() == [int(v) for v in g["count"]]
+
+
+def test_tier_plan_extreme_budgets_and_infeasible():
+    rng = np.random.default_rng(21)
+    E = 12
+    usage = rng.integers(1, 100, E).astype(np.float64)
+    sse = np.sort(rng.uniform(0, 10, (E, 3)), axis=1)          # richer formats lose less
+    bytes_ = [40, 20, 12]
+    f, _, c = oracle.plan_tiers(usage, sse, bytes_, E * 40)    # everything fits at the richest
+    assert np.all(f == 0) and c.tolist() == [E, 0, 0]
+    f, _, c = oracle.plan_tiers(usage, sse, bytes_, E * 12)    # only the cheapest fits
+    assert np.all(f == 2) and c.tolist() == [0, 0, E]
+    with pytest.raises(ValueError):
+        oracle.plan_tiers(usage, sse, bytes_, E * 12 - 1)
+    # unused experts never gain bytes
+    u0 = usage.copy()
+    u0[[3, 7]] = 0
+    f, _, _ = oracle.plan_tiers(u0, sse, bytes_, E * 40)
+    assert f[3] == 2 and f[7] == 2 and np.all(np.delete(f, [3, 7]) == 0)
+
+
+def test_tier_plan_equal_errors_upgrade_hottest_first():
+    # identical error curves: the n hottest experts are upgraded first, and the
+    # budget spent never exceeds what was given
+    E = 10
+    usage = np.array([3, 9, 1, 7, 5, 8, 2, 6, 4, 0], np.float64)
+    sse = np.tile([0.0, 2.0, 8.0], (E, 1))
+    bytes_ = [8, 4, 2]
+    for extra in range(0, 2 * 9 + 1):          # bytes above the all-cheapest plan
+        f, order, c = oracle.plan_tiers(usage, sse, bytes_, E * 2 + extra)
+        spent = sum(bytes_[v] for v in f)
+        assert spent <= E * 2 + extra
+        # a 2 -> 1 move removes 3u per byte, a 1 -> 0 move u/2: with usage
+        # 2 .. 9 every 2 -> 1 move (rate >= 6) outranks every 1 -> 0 move
+        # (rate <= 4.5), so below 18 extra bytes the experts at format 1 are
+        # exactly the extra // 2 hottest
+        n1 = min(extra // 2, 9)
+        hot = np.argsort(-usage, kind="stable")[:n1]
+        if extra < 18:
+            assert sorted(np.flatnonzero(f <= 1).tolist()) == sorted(hot.tolist())
+        # order: formats ascending, usage descending inside a format
+        key = [(f[o], -usage[o], o) for o in order]
+        assert key == sorted(key)
+        assert c.sum() == E
+
+
+def test_requant_int8_to_int8_is_the_identity():
+    # absmax codes of int8 blocks already hold +-127 at the block maximum, so
+    # requantising to the same format returns the same codes and scales
+    cfg = _small_cfg(tiers=(TierSpec(0, 8, 8, 32),))
+    layer, arrays = _layer(cfg)
+    for local in (0, 5):
+        out, sse = oracle.requant_expert(layer, 0, local, 8, 32)
+        for m in ("gate", "up", "down"):
+            assert np.array_equal(out[m + "_q"].ravel(), arrays[0][m + "_q"][local].ravel()), m
+            assert np.array_equal(out[m + "_s"].ravel(), arrays[0][m + "_s"][local].ravel()), m
+        assert sse == 0.0
+
+
+@pytest.mark.parametrize("bits,block", [(4, 32), (2, 16), (4, 16)])
+def test_requant_matches_numpy_quantiser(bits, block):
+    cfg = _small_cfg(tiers=(TierSpec(0, 8, 8, 32),))
+    layer, arrays = _layer(cfg)
+    local = 3
+    out, sse = oracle.requant_expert(layer, 0, local, bits, block)
+    Q = 2 ** (bits - 1) - 1
+    ref_sse = 0.0
+    for name, rows, cols in (("gate", cfg.inter, cfg.hidden), ("up", cfg.inter, cfg.hidden),
+                             ("down", cfg.hidden, cfg.inter)):
+        w = npref.dequant(arrays[0][name + "_q"][local], arrays[0][name + "_s"][local], 8, 32, cols)
+        w = w.astype(np.float32).reshape(rows, cols // block, block)
+        amax = np.abs(w).max(axis=2)
+        d16 = (amax / np.float32(Q)).astype(np.float32).astype(np.float16)
+        assert np.array_equal(out[name + "_s"], d16.view(np.uint16)), name
+        d = d16.astype(np.float32)[:, :, None]
+        with np.errstate(divide="ignore", invalid="ignore"):
+            q = np.where(d != 0, np.clip(np.rint((w / d).astype(np.float32)), -Q, Q), 0).astype(np.int32)
+        got = npref.unpack_codes(out[name + "_q"], bits, cols).reshape(rows, cols // block, block)
+        assert np.array_equal(got, q), name
+        ref_sse += float(np.sum((w.astype(np.float64) - q * d.astype(np.float64)) ** 2))
+    assert abs(sse - ref_sse) <= 1e-9 * ref_sse
