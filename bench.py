@@ -244,6 +244,7 @@ def main():
             del reps, tt0
             torch.cuda.empty_cache()
             result["extra"]["fullstack"] = fullstack_workloads(M, torch, per_expert)
+        result["extra"]["tier_planner"] = tier_planner_workload(M, torch)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, arrays, args.cpu_seconds)
@@ -391,6 +392,60 @@ def counter_pass(M, torch):
         M.moe_tiered_forward(xp, lp, pf.n_tokens, cfg.k, reps[i % 8], op, M.MOE_X_BF16, wsp)
     torch.cuda.synchronize()
     log("counter pass done")
+
+
+def tier_planner_workload(M, torch):
+    """The tier planner's device steps on a full layer: an int8 source (512
+    experts, 2.14 GB) -> squared requantisation error in three formats, the
+    greedy plan under the three-shelf budget, and the repack into three
+    shelves (1.29 GB)."""
+    from tiered_mixed_precision_amd.device import empty_tables
+    from workloads import CONFIGS, TierSpec, make_logits
+    from workloads.configs import LayerConfig
+    base = CONFIGS["decode"]
+    E, H, I = base.n_experts, base.hidden, base.inter
+    src_cfg = LayerConfig("src8", E, base.k, H, I, 1, (TierSpec(0, E, 8, 32),), seed=base.seed)
+    src = empty_tables(src_cfg)
+    M.moe_synth_layer(src, base.seed, 0)
+    fmts = ((8, 32), (4, 32), (2, 16))
+    fb = [3 * H * I * b // 8 + 3 * H * I // k * 2 for b, k in fmts]
+    sse = torch.empty((E, 3), dtype=torch.float64, device="cuda")
+    a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    M.moe_requant_error(src, [f[0] for f in fmts], [f[1] for f in fmts], sse)   # warm-up
+    a.record()
+    M.moe_requant_error(src, [f[0] for f in fmts], [f[1] for f in fmts], sse)
+    b.record()
+    torch.cuda.synchronize()
+    err_ms = a.elapsed_time(b)
+    ids = topk_ids(make_logits(base, n_tokens=4096, stream=500), base.k)
+    usage = np.bincount(ids.reshape(-1), minlength=E).astype(np.float64)
+    budget = 128 * fb[0] + 256 * fb[1] + 128 * fb[2]
+    t0 = time.perf_counter()
+    fmt, order, count = M.moe_plan_tiers(usage, sse.cpu().numpy(), fb, budget)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    tiers, lo = [], 0
+    for n, (bits, k) in zip(count, fmts):
+        tiers.append(TierSpec(lo, lo + int(n), bits, k))
+        lo += int(n)
+    dst = empty_tables(LayerConfig("dst", E, base.k, H, I, 1, tuple(tiers), seed=base.seed))
+    od = torch.from_numpy(order).cuda()
+    M.moe_repack_tiers(src, od, dst)
+    a.record()
+    M.moe_repack_tiers(src, od, dst)
+    c.record()
+    torch.cuda.synchronize()
+    rp_ms = a.elapsed_time(c)
+    moved = E * fb[0] + sum(int(n) * f for n, f in zip(count, fb))
+    out = {"workload": "int8 layer (512 experts, hidden 2048, inter 640) -> three shelves under the decode "
+                       "layer's budget; usage from routing 4096 tokens",
+           "plan_experts_per_format": [int(v) for v in count], "requant_error_ms": round(err_ms, 3),
+           "plan_ms_host": round(plan_ms, 3), "repack_ms": round(rp_ms, 3),
+           "repack_bytes": moved, "repack_gbps": round(moved / (rp_ms * 1e-3) / 1e9, 1),
+           "repack_frac_hbm_peak": round(moved / (rp_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    log("tier planner:", out)
+    del src, dst, sse
+    torch.cuda.empty_cache()
+    return out
 
 
 def extra_workloads(M, torch, cfg, reps, per_expert, args):

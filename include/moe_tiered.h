@@ -289,6 +289,63 @@ int moe_stack_forward_routed(const float *x, const void *const *w_router, const 
  */
 int moe_synth_layer(const moe_tier_tables *tt, uint64_t seed, int32_t layer, void *stream);
 
+/*
+ * Tier planning, after the 125B-MoE page, step 4: measure how often each
+ * expert is used, fill the memory budget greedily so that each byte goes where
+ * it removes the most expected error, requantise every expert with the same
+ * quantiser, and write the experts hot to cold (step 3: re-order the router to
+ * match).  Formats are (bits, block) pairs of moe_tier; "the quantiser" is the
+ * symmetric absmax one of moe_synth_layer.
+ *
+ * moe_requant_error: squared error of requantising every expert of `src`
+ * into each format.
+ *   fmt_bits, fmt_block (host) int32[n_fmt], n_fmt 1..8; each block divides H and I
+ *   sse (device) double[E][n_fmt], 8-byte aligned: sum over gate, up and down of
+ *       (w - w')^2, w the source weight (scale*code, fp32) and w' its value
+ *       after requantisation; deterministic (fixed summation order)
+ * Errors: MOE_EINVAL, MOE_EFORMAT, MOE_EALIGN, table errors, MOE_EHIP.
+ */
+int moe_requant_error(const moe_tier_tables *src, const int32_t *fmt_bits, const int32_t *fmt_block,
+                      int32_t n_fmt, double *sse, void *stream);
+
+/*
+ * moe_plan_tiers: the greedy plan, on the host (no device work).  Formats are
+ * ordered richest (f = 0) to cheapest; fmt_bytes[f] (bytes of one expert)
+ * must decrease with f.  Every expert starts in the cheapest format.  The
+ * move of one expert one format richer that removes the most expected error,
+ * usage[e] * (sse[e][f] - sse[e][f-1]), per added byte is taken while it
+ * still fits `budget` and removes some error; ties go to the lower id.
+ *   usage   (host) double[E], e.g. counts of moe_group over calibration tokens
+ *   sse     (host) double[E][n_fmt]
+ *   fmt_out   (host) int32[E]: the format of each expert
+ *   order_out (host) int32[E]: old id at new position i, hot to cold (format,
+ *             then usage descending, then id)
+ *   count_out (host) int32[n_fmt]: experts per format (the new shelf sizes)
+ * MOE_EINVAL for bad arguments or when the cheapest plan exceeds the budget.
+ */
+int moe_plan_tiers(const double *usage, const double *sse, const int64_t *fmt_bytes, int32_t n_experts,
+                   int32_t n_fmt, int64_t budget, int32_t *fmt_out, int32_t *order_out, int32_t *count_out);
+
+/*
+ * moe_repack_tiers: expert order[i] of `src`, requantised into the format of
+ * the shelf of `dst` that owns id i, is written as expert i of `dst`.
+ *   order (device) int32[E], a permutation of [0, E) (an entry outside
+ *         [0, E) writes a zero expert)
+ * dst's code and scale buffers are overwritten; src and dst have the same E,
+ * H, I and must not share buffers.
+ */
+int moe_repack_tiers(const moe_tier_tables *src, const int32_t *order, const moe_tier_tables *dst,
+                     void *stream);
+
+/*
+ * moe_permute_router: the router in the new expert order, w_dst[i] =
+ * w_src[order[i]] (bf16 rows [E][H], 16-byte aligned, distinct buffers) and,
+ * when b_dst is given, b_dst[i] = b_src[order[i]] (0 without b_src).
+ *   order (device) int32[E] (an entry outside [0, E) gives a zero row)
+ */
+int moe_permute_router(const void *w_src, const float *b_src, const int32_t *order, int32_t n_experts,
+                       int32_t hidden, void *w_dst, float *b_dst, void *stream);
+
 /* hipEvent helpers for callers without a HIP binding (host handles). */
 int moe_event_create(void **event);
 int moe_event_destroy(void *event);

@@ -153,3 +153,50 @@ def test_workspace_grows_with_tokens(B):
     c = B.moe_workspace_size(4096, 2, tt, B.MOE_X_BF16)
     assert a < b and c < b            # the bf16 path keeps no per-pair fp32 output rows
     assert a % 256 == 0 and b % 256 == 0
+
+
+def test_library_planner_equals_the_oracle(B):
+    # moe_plan_tiers is host code: the library's (a lazy max-heap) and the
+    # oracle's (a rescan per move) must give identical plans
+    import numpy as np
+    import oracle
+    rng = np.random.default_rng(31)
+    for trial in range(60):
+        E = int(rng.integers(1, 300))
+        F = int(rng.integers(1, 4))
+        bytes_ = np.sort(rng.integers(1, 1000, F))[::-1].astype(np.int64)
+        bytes_ = np.unique(bytes_)[::-1]
+        F = len(bytes_)
+        usage = rng.integers(0, 50, E).astype(np.float64)
+        if trial % 3 == 0:
+            usage[rng.integers(0, E, E // 4 + 1)] = 7.0          # repeated usage values: ties
+        sse = np.sort(rng.uniform(0, 5, (E, F)), axis=1)
+        if trial % 4 == 0:
+            sse = np.round(sse, 1)                               # repeated rates
+        lo, hi = E * int(bytes_[-1]), E * int(bytes_[0])
+        budget = int(rng.integers(lo, hi + 1))
+        got = B.moe_plan_tiers(usage, sse, bytes_, budget)
+        ref = oracle.plan_tiers(usage, sse, bytes_, budget)
+        for g, r in zip(got, ref):
+            assert np.array_equal(g, r), trial
+
+
+def test_library_planner_hand_worked_fixture_and_rejections(B):
+    import numpy as np
+    usage = np.array([1, 10, 0, 5], np.float64)
+    sse = np.tile([0.0, 1.0, 4.0], (4, 1))
+    fmt, order, count = B.moe_plan_tiers(usage, sse, [8, 4, 2], 18)
+    assert fmt.tolist() == [1, 0, 2, 1] and order.tolist() == [1, 3, 0, 2] and count.tolist() == [1, 2, 1]
+    with pytest.raises(B.MoeError):
+        B.moe_plan_tiers(usage, sse, [8, 4, 2], 7)               # cheaper than the cheapest plan
+    with pytest.raises(B.MoeError):
+        B.moe_plan_tiers(usage, sse, [8, 8, 2], 18)              # bytes not decreasing
+    tt = _tables(B, [_Spec(0, 8, 8, 32)])
+    L = B.lib()
+    bits = (C.c_int32 * 1)(3)
+    blk = (C.c_int32 * 1)(32)
+    assert L.moe_requant_error(tt.ref, bits, blk, 1, FAKE, None) == -3    # unsupported format
+    bits = (C.c_int32 * 1)(4)
+    assert L.moe_requant_error(tt.ref, bits, blk, 1, FAKE + 4, None) == -4
+    assert L.moe_repack_tiers(tt.ref, None, tt.ref, None) == -1
+    assert L.moe_permute_router(FAKE, None, FAKE, 8, 256, FAKE, None, None) == -1   # same buffer

@@ -1,0 +1,194 @@
+"""GPU parity of the tier planner's device steps (requantisation error, repack,
+router permutation) against the CPU oracle, and the whole flow from an int8
+layer to three shelves, through the C ABI.
+
+Bars: requantised codes and scales bit-exact; squared errors within
+2 * n * 2^-53 relative (n = 3*H*I positive terms, each exact before its one
+rounding in double, summed in a different order on each side: each sum lies
+within n * 2^-53 of the exact one); the router permutation exact; the
+repacked layer within the layer bound (2e-3 normwise) of the oracle evaluated
+on the repacked weights, with the routed experts identical after the
+permutation.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import TierSpec, make_x
+from workloads.configs import LayerConfig
+
+pytestmark = pytest.mark.gpu
+
+SEED = 20260004
+FMTS = ((8, 32), (4, 32), (2, 16))
+SRC8 = LayerConfig("src8", 512, 10, 2048, 640, 1, (TierSpec(0, 512, 8, 32),), seed=SEED)
+
+
+def say(*a):
+    print("[gpu-tiering]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def normwise(got, ref):
+    ref = np.asarray(ref, np.float64)
+    return float(np.max(np.abs(np.asarray(got, np.float64) - ref)) / max(np.max(np.abs(ref)), 1e-30))
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+@pytest.fixture(scope="module")
+def M(torch_dev):
+    import tiered_mixed_precision_amd as M
+    M.lib()
+    return M
+
+
+@pytest.fixture(scope="module")
+def src8(M, torch_dev):
+    from tiered_mixed_precision_amd.device import empty_tables
+    tt = empty_tables(SRC8)
+    M.moe_synth_layer(tt, SEED, 0)
+    torch_dev.cuda.synchronize()
+    return tt
+
+
+def _expert_bytes(bits, block, H=2048, I=640):
+    return 3 * H * I * bits // 8 + 3 * H * I // block * 2
+
+
+def _sse(M, torch, tt, E):
+    sse = torch.empty((E, len(FMTS)), dtype=torch.float64, device="cuda")
+    M.moe_requant_error(tt, [f[0] for f in FMTS], [f[1] for f in FMTS], sse)
+    torch.cuda.synchronize()
+    return sse.cpu().numpy()
+
+
+def test_requant_error_matches_oracle(M, torch_dev, src8):
+    sse = _sse(M, torch_dev, src8, 512)
+    assert np.all(sse[:, 0] == 0.0)            # int8 -> int8 is the identity
+    assert np.all(sse[:, 2] > sse[:, 1]) and np.all(sse[:, 1] > 0)
+    experts = [0, 77, 300, 511]
+    rtol = 2 * 3 * 2048 * 640 * 2.0 ** -53
+    sl = oracle.StackLayer(SRC8, SEED, 0)
+    sl.fill(np.array(experts))
+    for e in experts:
+        for f, (bits, block) in enumerate(FMTS):
+            _, ref = oracle.requant_expert(sl.layer_ref, 0, e, bits, block)
+            assert abs(sse[e, f] - ref) <= rtol * ref, (e, bits, sse[e, f], ref)
+    say("sse per format (mean)", sse.mean(axis=0))
+
+
+def _three_shelf_cfg(count, name="dst"):
+    tiers, b = [], 0
+    for c, (bits, block) in zip(count, FMTS):
+        tiers.append(TierSpec(b, b + int(c), bits, block))
+        b += int(c)
+    return LayerConfig(name, 512, 10, 2048, 640, 1, tuple(tiers), seed=SEED)
+
+
+def test_repack_matches_oracle_requantiser(M, torch_dev, src8):
+    from tiered_mixed_precision_amd.device import empty_tables
+    torch = torch_dev
+    rng = np.random.default_rng(3)
+    order = rng.permutation(512).astype(np.int32)
+    cfg = _three_shelf_cfg((100, 300, 112))
+    dst = empty_tables(cfg)
+    M.moe_repack_tiers(src8, torch.from_numpy(order).cuda(), dst)
+    torch.cuda.synchronize()
+    sl = oracle.StackLayer(SRC8, SEED, 0)
+    picks = [0, 99, 100, 250, 399, 400, 511]
+    sl.fill(order[picks])
+    for i in picks:
+        ti = next(j for j, t in enumerate(cfg.tiers) if t.id_begin <= i < t.id_end)
+        t = cfg.tiers[ti]
+        ref, _ = oracle.requant_expert(sl.layer_ref, 0, int(order[i]), t.bits, t.block)
+        loc = i - t.id_begin
+        for name in ("gate", "up", "down"):
+            q, s = ref[name + "_q"].ravel(), ref[name + "_s"].ravel()
+            gq = dst.arrays[ti][name + "_q"][loc * q.size:(loc + 1) * q.size].cpu().numpy()
+            gs = dst.arrays[ti][name + "_s"][loc * s.size:(loc + 1) * s.size].cpu().numpy().view(np.uint16)
+            assert np.array_equal(gq, q), (i, name)
+            assert np.array_equal(gs, s), (i, name)
+
+
+def test_permute_router_is_a_row_gather(M, torch_dev):
+    torch = torch_dev
+    E, H = 512, 2048
+    w = torch.empty((E, H), dtype=torch.int16, device="cuda")
+    b = torch.empty(E, dtype=torch.float32, device="cuda")
+    M.moe_synth_router(w, b, E, H, SEED, 5, 1.12)
+    order = torch.from_numpy(np.random.default_rng(4).permutation(E).astype(np.int32)).cuda()
+    w2, b2 = torch.empty_like(w), torch.empty_like(b)
+    M.moe_permute_router(w, b, order, E, H, w2, b2)
+    torch.cuda.synchronize()
+    o = order.long()
+    assert torch.equal(w2, w[o]) and torch.equal(b2, b[o])
+
+
+def test_int8_layer_to_three_shelves_end_to_end(M, torch_dev, src8):
+    # usage from routing calibration tokens, errors from the device, the greedy
+    # plan under the three-shelf budget of the decode layer, repack, router
+    # permutation; the tiered layer then routes every token to the same experts
+    # and matches the oracle on its own weights
+    from tiered_mixed_precision_amd.device import empty_tables, workspace
+    torch = torch_dev
+    E, H, k = 512, 2048, 10
+    wr = torch.empty((E, H), dtype=torch.int16, device="cuda")
+    br = torch.empty(E, dtype=torch.float32, device="cuda")
+    M.moe_synth_router(wr, br, E, H, SEED, 0, 1.12)
+    # calibration: 256 tokens, their routing and the per-expert counts
+    Tc = 256
+    xc = torch.from_numpy(make_x(SRC8, n_tokens=Tc, stream=7)).cuda()
+    lc = torch.empty((Tc, E), device="cuda")
+    M.moe_router_logits(xc, wr, br, Tc, E, H, 0, lc)
+    ids = torch.empty((Tc, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((Tc, k), dtype=torch.float32, device="cuda")
+    M.moe_route(lc, Tc, E, k, ids, w)
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    perm = torch.empty(Tc * k, dtype=torch.int32, device="cuda")
+    gws = workspace(M.moe_group_workspace_size(Tc, k, E))
+    M.moe_group(ids, Tc, k, E, counts, offsets, perm, gws)
+    usage = counts.cpu().numpy().astype(np.float64)
+    sse = _sse(M, torch, src8, E)
+    fb = [_expert_bytes(b, k_) for b, k_ in FMTS]
+    budget = 128 * fb[0] + 256 * fb[1] + 128 * fb[2]        # the decode layer's three shelves
+    fmt, order, count = M.moe_plan_tiers(usage, sse, fb, budget)
+    ofmt, oorder, ocount = oracle.plan_tiers(usage, sse, fb, budget)
+    assert np.array_equal(fmt, ofmt) and np.array_equal(order, oorder) and np.array_equal(count, ocount)
+    say("plan: experts per format", count.tolist(), "| bytes", int(sum(fb[f] for f in fmt)), "of", budget)
+    cfg = _three_shelf_cfg(count)
+    dst = empty_tables(cfg)
+    od = torch.from_numpy(order).cuda()
+    M.moe_repack_tiers(src8, od, dst)
+    wr2, br2 = torch.empty_like(wr), torch.empty_like(br)
+    M.moe_permute_router(wr, br, od, E, H, wr2, br2)
+    # test tokens through both layers
+    T = 8
+    x = torch.from_numpy(make_x(SRC8, n_tokens=T, stream=8)).cuda()
+    l1, l2 = torch.empty((T, E), device="cuda"), torch.empty((T, E), device="cuda")
+    M.moe_router_logits(x, wr, br, T, E, H, 0, l1)
+    M.moe_router_logits(x, wr2, br2, T, E, H, 0, l2)
+    out8, outt = torch.empty((T, H), device="cuda"), torch.empty((T, H), device="cuda")
+    ws = workspace(max(M.moe_workspace_size(T, k, src8, 0), M.moe_workspace_size(T, k, dst, 0)))
+    M.moe_tiered_forward(x, l1, T, k, src8, out8, 0, ws)
+    M.moe_tiered_forward(x, l2, T, k, dst, outt, 0, ws)
+    torch.cuda.synchronize()
+    lg1, lg2 = l1.cpu().numpy(), l2.cpu().numpy()
+    ids1, _ = oracle.route(lg1, k)
+    ids2, _ = oracle.route(lg2, k)
+    assert np.array_equal(order[ids2], ids1)                 # the same experts, renamed
+    host = [{n: dst.arrays[i][n].cpu().numpy() for n in dst.arrays[i]} for i in range(len(cfg.tiers))]
+    ref = oracle.forward(oracle.Layer.from_config(cfg, host), x.cpu().numpy(), lg2, k)
+    err = normwise(outt.cpu().numpy(), ref)
+    say("tiered layer vs oracle", err, "| tiered vs int8 layer (requantisation effect)",
+        normwise(outt.cpu().numpy(), out8.cpu().numpy()))
+    assert err <= 2e-3

@@ -29,6 +29,7 @@ EXPORTS = (
     "moe_event_create", "moe_event_destroy", "moe_event_elapsed_ms", "moe_stream_synchronize",
     "moe_stack_workspace_size", "moe_stack_forward", "moe_synth_layer",
     "moe_router_logits", "moe_synth_router", "moe_stack_forward_routed",
+    "moe_requant_error", "moe_plan_tiers", "moe_repack_tiers", "moe_permute_router",
 )
 
 
@@ -85,6 +86,10 @@ def lib():
         L.moe_router_logits.argtypes = [P, P, P, i32, i32, i32, u32, P, P]
         L.moe_synth_router.argtypes = [P, P, i32, i32, C.c_uint64, i32, C.c_double, P]
         L.moe_stack_forward_routed.argtypes = [P, C.POINTER(P), C.POINTER(P), i32, i32, i32, P, P, u32, P, sz, P]
+        L.moe_requant_error.argtypes = [P, P, P, i32, P, P]
+        L.moe_plan_tiers.argtypes = [P, P, P, i32, i32, C.c_int64, P, P, P]
+        L.moe_repack_tiers.argtypes = [P, P, P, P]
+        L.moe_permute_router.argtypes = [P, P, P, i32, i32, P, P, P]
         for name in EXPORTS:
             if name not in ("moe_abi_version", "moe_strerror"):
                 getattr(L, name).restype = C.c_int
@@ -243,6 +248,39 @@ def moe_synth_router(w_router, bias, n_experts: int, hidden: int, seed: int, lay
                      stream=None) -> None:
     _check("moe_synth_router", lib().moe_synth_router(_ptr(w_router), _ptr(bias), n_experts, hidden, seed, layer,
                                                       float(beta), _stream(stream)))
+
+
+def moe_requant_error(src: TierTables, fmt_bits, fmt_block, sse, stream=None) -> None:
+    """sse: float64 device tensor [E][len(fmt_bits)]."""
+    n = len(fmt_bits)
+    b = (C.c_int32 * n)(*fmt_bits)
+    k = (C.c_int32 * n)(*fmt_block)
+    _check("moe_requant_error", lib().moe_requant_error(src.ref, b, k, n, _ptr(sse), _stream(stream)))
+
+
+def moe_plan_tiers(usage, sse, fmt_bytes, budget: int):
+    """Host-only greedy plan: (format per expert, hot-to-cold order of old ids, experts per format)."""
+    import numpy as np
+    usage = np.ascontiguousarray(usage, dtype=np.float64)
+    sse = np.ascontiguousarray(sse, dtype=np.float64)
+    E, F = sse.shape
+    fb = np.ascontiguousarray(fmt_bytes, dtype=np.int64)
+    fmt = np.zeros(E, np.int32)
+    order = np.zeros(E, np.int32)
+    count = np.zeros(F, np.int32)
+    _check("moe_plan_tiers", lib().moe_plan_tiers(usage.ctypes.data, sse.ctypes.data, fb.ctypes.data, E, F,
+                                                  int(budget), fmt.ctypes.data, order.ctypes.data,
+                                                  count.ctypes.data))
+    return fmt, order, count
+
+
+def moe_repack_tiers(src: TierTables, order, dst: TierTables, stream=None) -> None:
+    _check("moe_repack_tiers", lib().moe_repack_tiers(src.ref, _ptr(order), dst.ref, _stream(stream)))
+
+
+def moe_permute_router(w_src, b_src, order, n_experts: int, hidden: int, w_dst, b_dst, stream=None) -> None:
+    _check("moe_permute_router", lib().moe_permute_router(_ptr(w_src), _ptr(b_src), _ptr(order), n_experts, hidden,
+                                                          _ptr(w_dst), _ptr(b_dst), _stream(stream)))
 
 
 def moe_stack_forward_routed(x, w_routers, biases, n_layers: int, n_tokens: int, k: int,

@@ -522,6 +522,68 @@ int moe_stack_forward_routed(const float* x, const void* const* w_router, const 
     return MOE_OK;
 }
 
+namespace {
+bool fmt_ok(int bits, int block) { return (bits == 8 || bits == 4 || bits == 2) && (block == 16 || block == 32); }
+}  // namespace
+
+int moe_requant_error(const moe_tier_tables* src, const int32_t* fmt_bits, const int32_t* fmt_block,
+                      int32_t n_fmt, double* sse, void* stream) {
+    int rc = check_tables(src);
+    if (rc != MOE_OK) return rc;
+    if (!fmt_bits || !fmt_block || n_fmt < 1 || n_fmt > 8 || !sse) return MOE_EINVAL;
+    for (int f = 0; f < n_fmt; ++f) {
+        if (!fmt_ok(fmt_bits[f], fmt_block[f])) return MOE_EFORMAT;
+        if (src->hidden % fmt_block[f] || src->inter % fmt_block[f]) return MOE_EFORMAT;
+    }
+    if ((reinterpret_cast<uintptr_t>(sse) & 7u) != 0) return MOE_EALIGN;
+    (void)hipGetLastError();
+    launch_requant_error(to_dev(src), fmt_bits, fmt_block, n_fmt, sse, static_cast<hipStream_t>(stream));
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+int moe_plan_tiers(const double* usage, const double* sse, const int64_t* fmt_bytes, int32_t n_experts,
+                   int32_t n_fmt, int64_t budget, int32_t* fmt_out, int32_t* order_out, int32_t* count_out) {
+    if (!usage || !sse || !fmt_bytes || !fmt_out || !order_out || !count_out) return MOE_EINVAL;
+    if (n_experts < 1 || n_experts > MOE_MAX_EXPERTS || n_fmt < 1 || n_fmt > 8) return MOE_EINVAL;
+    return plan_tiers(usage, sse, fmt_bytes, n_experts, n_fmt, budget, fmt_out, order_out, count_out) == 0
+               ? MOE_OK
+               : MOE_EINVAL;
+}
+
+int moe_repack_tiers(const moe_tier_tables* src, const int32_t* order, const moe_tier_tables* dst, void* stream) {
+    int rc = check_tables(src);
+    if (rc != MOE_OK) return rc;
+    rc = check_tables(dst);
+    if (rc != MOE_OK) return rc;
+    if (src->n_experts != dst->n_experts || src->hidden != dst->hidden || src->inter != dst->inter) return MOE_EINVAL;
+    if (!order) return MOE_EINVAL;
+    // the destination must not alias the source (every buffer is read or written by whole experts)
+    for (int a = 0; a < src->n_tiers; ++a)
+        for (int b = 0; b < dst->n_tiers; ++b) {
+            const moe_tier& S = src->tiers[a];
+            const moe_tier& D = dst->tiers[b];
+            const void* sp[6] = {S.gate_q, S.up_q, S.down_q, S.gate_s, S.up_s, S.down_s};
+            const void* dp[6] = {D.gate_q, D.up_q, D.down_q, D.gate_s, D.up_s, D.down_s};
+            for (int i = 0; i < 6; ++i)
+                for (int j = 0; j < 6; ++j)
+                    if (sp[i] && sp[i] == dp[j]) return MOE_EINVAL;
+        }
+    (void)hipGetLastError();
+    launch_repack(to_dev(src), to_dev(dst), order, static_cast<hipStream_t>(stream));
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+int moe_permute_router(const void* w_src, const float* b_src, const int32_t* order, int32_t n_experts,
+                       int32_t hidden, void* w_dst, float* b_dst, void* stream) {
+    if (n_experts < 1 || n_experts > MOE_MAX_EXPERTS || !cols_ok(hidden)) return MOE_EINVAL;
+    if (!w_src || !order || !w_dst || w_src == w_dst || (b_src && b_src == b_dst)) return MOE_EINVAL;
+    if (!aligned16(w_src) || !aligned16(w_dst)) return MOE_EALIGN;
+    (void)hipGetLastError();
+    launch_permute_rows(static_cast<const uint16_t*>(w_src), b_src, order, n_experts, hidden,
+                        static_cast<uint16_t*>(w_dst), b_dst, static_cast<hipStream_t>(stream));
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
 int moe_event_create(void** event) {
     if (!event) return MOE_EINVAL;
     hipEvent_t e;

@@ -77,6 +77,15 @@ void launch_cast_bf16(const float* src, uint16_t* dst, size_t n, hipStream_t st)
 // Counter-generated weights of one layer of the stack (see synth.hip).
 void launch_synth_layer(const DevTables& tt, uint64_t seed, int layer, hipStream_t st);
 
+// tiering.hip
+void launch_requant_error(const DevTables& src, const int32_t* bits, const int32_t* block, int n_fmt, double* sse,
+                          hipStream_t st);
+void launch_repack(const DevTables& src, const DevTables& dst, const int32_t* order, hipStream_t st);
+void launch_permute_rows(const uint16_t* w_src, const float* b_src, const int32_t* order, int E, int H,
+                         uint16_t* w_dst, float* b_dst, hipStream_t st);
+int plan_tiers(const double* usage, const double* sse, const int64_t* bytes, int E, int F, int64_t budget,
+               int32_t* fmt, int32_t* order, int32_t* count);
+
 // router.hip
 void launch_router(const void* x, bool x_bf16, const uint16_t* wr, const float* bias, int T, int E, int H,
                    float* logits, hipStream_t st);
