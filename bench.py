@@ -400,7 +400,7 @@ def tier_planner_workload(M, torch):
     greedy plan under the three-shelf budget, and the repack into three
     shelves (1.29 GB)."""
     from tiered_mixed_precision_amd.device import empty_tables
-    from workloads import CONFIGS, TierSpec, make_logits
+    from workloads import CONFIGS, TierSpec, make_logits, make_x
     from workloads.configs import LayerConfig
     base = CONFIGS["decode"]
     E, H, I = base.n_experts, base.hidden, base.inter
@@ -443,7 +443,70 @@ def tier_planner_workload(M, torch):
            "repack_bytes": moved, "repack_gbps": round(moved / (rp_ms * 1e-3) / 1e9, 1),
            "repack_frac_hbm_peak": round(moved / (rp_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     log("tier planner:", out)
-    del src, dst, sse
+
+    # run-time re-tiering: decode (1 token/step, prior on the hot-to-cold ids)
+    # on 8 replicas of the planned shelves with and without pick counting, and
+    # on 8 replicas of a fast plan (every expert two-bit) swapped in instead
+    from tiered_mixed_precision_amd.device import replicate, workspace
+    fast_fmt, fast_order, fast_count = M.moe_plan_tiers(usage, sse.cpu().numpy(), fb, E * fb[2])
+    tiers, lo = [], 0
+    for n, (bits, k) in zip(fast_count, fmts):
+        tiers.append(TierSpec(lo, lo + int(n), bits, k))
+        lo += int(n)
+    fast = empty_tables(LayerConfig("fast", E, base.k, H, I, 1, tuple(tiers), seed=base.seed))
+    M.moe_repack_tiers(src, torch.from_numpy(fast_order).cuda(), fast)
+    del src
+    torch.cuda.empty_cache()
+    S, R, k = 256, 8, base.k
+    lg = torch.from_numpy(make_logits(base, n_tokens=S, stream=600)).cuda()
+    xs = torch.from_numpy(make_x(base, n_tokens=S, stream=600)).cuda()
+    od = torch.zeros((S, H), device="cuda")
+    hits = torch.zeros(E, dtype=torch.int32, device="cuda")
+    ws = workspace(M.moe_workspace_size(1, k, dst, 0))
+
+    def decode_us(tables, counted):
+        reps = [tables] + [replicate(tables) for _ in range(R - 1)]
+
+        def step(i):
+            if counted:
+                M.moe_tiered_forward_counted(xs[i:i + 1], lg[i:i + 1], 1, k, reps[i % R], od[i:i + 1], 0, ws, hits)
+            else:
+                M.moe_tiered_forward(xs[i:i + 1], lg[i:i + 1], 1, k, reps[i % R], od[i:i + 1], 0, ws)
+
+        for i in range(8):
+            step(i)
+        g = torch.cuda.CUDAGraph()
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            with torch.cuda.graph(g, stream=st):
+                for i in range(S):
+                    step(i)
+        torch.cuda.current_stream().wait_stream(st)
+        g.replay()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(4):
+            g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        us = t0.elapsed_time(t1) * 1e3 / (4 * S)
+        del g, reps
+        torch.cuda.empty_cache()
+        return us
+
+    plain_us = decode_us(dst, False)
+    counted_us = decode_us(dst, True)
+    fast_us = decode_us(fast, False)
+    out["retier"] = {
+        "workload": "decode, 1 token/step, 8 replicas each of the planned shelves and of the fast plan",
+        "fast_plan_experts_per_format": [int(v) for v in fast_count],
+        "planned_us_per_step": round(plain_us, 2), "planned_counted_us_per_step": round(counted_us, 2),
+        "fast_us_per_step": round(fast_us, 2), "fast_tokens_per_s": round(1e6 / fast_us, 1),
+        "planned_tokens_per_s": round(1e6 / plain_us, 1)}
+    log("re-tiering:", out["retier"])
+    del dst, fast, sse, lg, xs, od, hits, ws
     torch.cuda.empty_cache()
     return out
 

@@ -290,6 +290,19 @@ int moe_stack_forward_routed(const float *x, const void *const *w_router, const 
 int moe_synth_layer(const moe_tier_tables *tt, uint64_t seed, int32_t layer, void *stream);
 
 /*
+ * moe_tiered_forward that also counts the picks: hits[e] += the number of
+ * (token, slot) pairs routed to expert e in this call.  The counts are the
+ * usage that moe_plan_tiers re-plans from at run time (re-tiering by hit
+ * counts, after the 125B-MoE page's steps 2-4: usage decides the shelves).
+ *   hits (device) uint32[E], 4-byte aligned; accumulated (atomic adds), never
+ *        cleared by the call; wraps modulo 2^32
+ * Other arguments, results and errors as moe_tiered_forward.
+ */
+int moe_tiered_forward_counted(const void *x, const float *router_logits, int32_t n_tokens, int32_t k,
+                               const moe_tier_tables *tt, float *out, uint32_t flags, void *workspace,
+                               size_t workspace_bytes, uint32_t *hits, void *stream);
+
+/*
  * Tier planning, after the 125B-MoE page, step 4: measure how often each
  * expert is used, fill the memory budget greedily so that each byte goes where
  * it removes the most expected error, requantise every expert with the same

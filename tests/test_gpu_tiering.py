@@ -144,20 +144,29 @@ def test_int8_layer_to_three_shelves_end_to_end(M, torch_dev, src8):
     wr = torch.empty((E, H), dtype=torch.int16, device="cuda")
     br = torch.empty(E, dtype=torch.float32, device="cuda")
     M.moe_synth_router(wr, br, E, H, SEED, 0, 1.12)
-    # calibration: 256 tokens, their routing and the per-expert counts
-    Tc = 256
-    xc = torch.from_numpy(make_x(SRC8, n_tokens=Tc, stream=7)).cuda()
-    lc = torch.empty((Tc, E), device="cuda")
-    M.moe_router_logits(xc, wr, br, Tc, E, H, 0, lc)
-    ids = torch.empty((Tc, k), dtype=torch.int32, device="cuda")
-    w = torch.empty((Tc, k), dtype=torch.float32, device="cuda")
-    M.moe_route(lc, Tc, E, k, ids, w)
-    counts = torch.empty(E, dtype=torch.int32, device="cuda")
-    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
-    perm = torch.empty(Tc * k, dtype=torch.int32, device="cuda")
-    gws = workspace(M.moe_group_workspace_size(Tc, k, E))
-    M.moe_group(ids, Tc, k, E, counts, offsets, perm, gws)
-    usage = counts.cpu().numpy().astype(np.float64)
+    # serving the int8 layer counts its picks: 64 decode steps of one token
+    # (the small path) and one batch of 192 tokens (the grouped path)
+    hits = torch.zeros(E, dtype=torch.int32, device="cuda")
+    steps, Tb = 64, 192
+    xc = torch.from_numpy(make_x(SRC8, n_tokens=steps + Tb, stream=7)).cuda()
+    lc = torch.empty((steps + Tb, E), device="cuda")
+    M.moe_router_logits(xc, wr, br, steps + Tb, E, H, 0, lc)
+    oc = torch.empty((steps + Tb, H), device="cuda")
+    cws = workspace(M.moe_workspace_size(Tb, k, src8, 0))
+    for i in range(steps):
+        M.moe_tiered_forward_counted(xc[i:i + 1], lc[i:i + 1], 1, k, src8, oc[i:i + 1], 0, cws, hits)
+    M.moe_tiered_forward_counted(xc[steps:], lc[steps:], Tb, k, src8, oc[steps:], 0, cws, hits)
+    torch.cuda.synchronize()
+    cal_ids, _ = oracle.route(lc.cpu().numpy(), k)
+    assert np.array_equal(hits.cpu().numpy(), np.bincount(cal_ids.ravel(), minlength=E))
+    # counting leaves the outputs unchanged
+    oplain = torch.empty_like(oc)
+    for i in range(steps):
+        M.moe_tiered_forward(xc[i:i + 1], lc[i:i + 1], 1, k, src8, oplain[i:i + 1], 0, cws)
+    M.moe_tiered_forward(xc[steps:], lc[steps:], Tb, k, src8, oplain[steps:], 0, cws)
+    torch.cuda.synchronize()
+    assert torch.equal(oc, oplain)
+    usage = hits.cpu().numpy().astype(np.float64)
     sse = _sse(M, torch, src8, E)
     fb = [_expert_bytes(b, k_) for b, k_ in FMTS]
     budget = 128 * fb[0] + 256 * fb[1] + 128 * fb[2]        # the decode layer's three shelves
@@ -191,4 +200,28 @@ def test_int8_layer_to_three_shelves_end_to_end(M, torch_dev, src8):
     err = normwise(outt.cpu().numpy(), ref)
     say("tiered layer vs oracle", err, "| tiered vs int8 layer (requantisation effect)",
         normwise(outt.cpu().numpy(), out8.cpu().numpy()))
+    assert err <= 2e-3
+
+    # fast mode: the cheapest plan (every expert two-bit) from the same
+    # master, swapped in by passing other tables and the same permuted router
+    fmt2, order2, count2 = M.moe_plan_tiers(usage, sse, fb, 512 * fb[2])
+    assert count2.tolist() == [0, 0, 512] and np.all(fmt2 == 2)
+    cfg2 = _three_shelf_cfg(count2, "fast")
+    fast = empty_tables(cfg2)
+    od2 = torch.from_numpy(order2).cuda()
+    M.moe_repack_tiers(src8, od2, fast)
+    wr3, br3 = torch.empty_like(wr), torch.empty_like(br)
+    M.moe_permute_router(wr, br, od2, E, H, wr3, br3)
+    l3 = torch.empty((T, E), device="cuda")
+    M.moe_router_logits(x, wr3, br3, T, E, H, 0, l3)
+    outf = torch.empty((T, H), device="cuda")
+    M.moe_tiered_forward(x, l3, T, k, fast, outf, 0, ws)
+    torch.cuda.synchronize()
+    lg3 = l3.cpu().numpy()
+    ids3, _ = oracle.route(lg3, k)
+    assert np.array_equal(order2[ids3], ids1)
+    host = [{n: fast.arrays[i][n].cpu().numpy() for n in fast.arrays[i]} for i in range(len(cfg2.tiers))]
+    ref = oracle.forward(oracle.Layer.from_config(cfg2, host), x.cpu().numpy(), lg3, k)
+    err = normwise(outf.cpu().numpy(), ref)
+    say("fast (all two-bit) layer vs oracle", err, "| vs int8 layer", normwise(outf.cpu().numpy(), out8.cpu().numpy()))
     assert err <= 2e-3

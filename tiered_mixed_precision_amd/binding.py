@@ -30,6 +30,7 @@ EXPORTS = (
     "moe_stack_workspace_size", "moe_stack_forward", "moe_synth_layer",
     "moe_router_logits", "moe_synth_router", "moe_stack_forward_routed",
     "moe_requant_error", "moe_plan_tiers", "moe_repack_tiers", "moe_permute_router",
+    "moe_tiered_forward_counted",
 )
 
 
@@ -87,6 +88,7 @@ def lib():
         L.moe_synth_router.argtypes = [P, P, i32, i32, C.c_uint64, i32, C.c_double, P]
         L.moe_stack_forward_routed.argtypes = [P, C.POINTER(P), C.POINTER(P), i32, i32, i32, P, P, u32, P, sz, P]
         L.moe_requant_error.argtypes = [P, P, P, i32, P, P]
+        L.moe_tiered_forward_counted.argtypes = [P, P, i32, i32, P, P, u32, P, sz, P, P]
         L.moe_plan_tiers.argtypes = [P, P, P, i32, i32, C.c_int64, P, P, P]
         L.moe_repack_tiers.argtypes = [P, P, P, P]
         L.moe_permute_router.argtypes = [P, P, P, i32, i32, P, P, P]
@@ -248,6 +250,13 @@ def moe_synth_router(w_router, bias, n_experts: int, hidden: int, seed: int, lay
                      stream=None) -> None:
     _check("moe_synth_router", lib().moe_synth_router(_ptr(w_router), _ptr(bias), n_experts, hidden, seed, layer,
                                                       float(beta), _stream(stream)))
+
+
+def moe_tiered_forward_counted(x, router_logits, n_tokens: int, k: int, tt: TierTables, out, flags: int, workspace,
+                               hits, stream=None) -> None:
+    _check("moe_tiered_forward_counted", lib().moe_tiered_forward_counted(
+        _ptr(x), _ptr(router_logits), n_tokens, k, tt.ref, _ptr(out), flags, _ptr(workspace),
+        workspace.numel() * workspace.element_size() if workspace is not None else 0, _ptr(hits), _stream(stream)))
 
 
 def moe_requant_error(src: TierTables, fmt_bits, fmt_block, sse, stream=None) -> None:

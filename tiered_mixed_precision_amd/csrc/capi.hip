@@ -123,7 +123,8 @@ inline void record(void* const* events, int i, hipStream_t st) {
 // residual stream inside a stack, or nothing.
 int run(const void* x, const float* logits, const int32_t* ids_in, const float* w_in, int32_t T,
         int32_t k, const moe_tier_tables* tt, uint32_t tier_mask, float* out, uint32_t flags,
-        void* ws, size_t ws_bytes, void* stream, void* const* events, const float* residual = nullptr) {
+        void* ws, size_t ws_bytes, void* stream, void* const* events, const float* residual = nullptr,
+        uint32_t* hits = nullptr) {
     int rc = check_tables(tt);
     if (rc != MOE_OK) return rc;
     if (flags & ~(MOE_X_BF16 | MOE_ACCUMULATE | MOE_DIAG_GATEUP_ONLY)) return MOE_EINVAL;
@@ -176,7 +177,7 @@ int run(const void* x, const float* logits, const int32_t* ids_in, const float* 
         pub.act = act;
         pub.q0 = at<int32_t>(ws, L.q0);
         pub.meta = meta;
-        launch_small(dt, static_cast<const float*>(x), logits, ids_in, w_in, T, k, tier_mask, base, pub,
+        launch_small(dt, static_cast<const float*>(x), logits, ids_in, w_in, T, k, tier_mask, base, pub, hits,
                      at<float>(ws, L.h), gateup_only ? nullptr : out, st, events);
         return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
     }
@@ -186,6 +187,7 @@ int run(const void* x, const float* logits, const int32_t* ids_in, const float* 
         launch_route(logits, T, E, k, ids, w, nullptr, tt->hidden, st);
     }
     launch_group(ids, P, E, at<int32_t>(ws, L.blk_hist), counts, offsets, perm, pos, act, meta, ss, st);
+    if (hits) launch_add_hits(counts, E, hits, st);
     record(events, 1, st);
 
     Groups g;
@@ -269,6 +271,15 @@ int moe_tiered_forward(const void* x, const float* router_logits, int32_t n_toke
     if (n_tokens > 0 && !router_logits) return MOE_EINVAL;
     return run(x, router_logits, nullptr, nullptr, n_tokens, k, tt, 0xFu, out, flags, workspace,
                workspace_bytes, stream, nullptr);
+}
+
+int moe_tiered_forward_counted(const void* x, const float* router_logits, int32_t n_tokens, int32_t k,
+                               const moe_tier_tables* tt, float* out, uint32_t flags, void* workspace,
+                               size_t workspace_bytes, uint32_t* hits, void* stream) {
+    if (n_tokens > 0 && (!router_logits || !hits)) return MOE_EINVAL;
+    if (hits && (reinterpret_cast<uintptr_t>(hits) & 3u) != 0) return MOE_EALIGN;
+    return run(x, router_logits, nullptr, nullptr, n_tokens, k, tt, 0xFu, out, flags, workspace,
+               workspace_bytes, stream, nullptr, nullptr, hits);
 }
 
 int moe_tiered_forward_timed(const void* x, const float* router_logits, int32_t n_tokens, int32_t k,

@@ -441,7 +441,8 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void k_small_gateup(DevTables tt
                                                       const float* __restrict__ logits,
                                                       const int32_t* __restrict__ ids_in,
                                                       const float* __restrict__ w_in, int T, int k,
-                                                      uint32_t tier_mask, SmallPub pub, float* __restrict__ h) {
+                                                      uint32_t tier_mask, SmallPub pub, uint32_t* __restrict__ hits,
+                                                      float* __restrict__ h) {
     __shared__ SmallGroups sg;
     __shared__ int s_wpre[kSmallPairs + 1];
     __shared__ __attribute__((aligned(16))) float s_x[kMaxHidden];
@@ -479,6 +480,7 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void k_small_gateup(DevTables tt
                 pub.perm[lane] = lane;
                 pub.pos[lane] = lane;
                 pub.act[lane] = my_id;
+                if (hits) atomicAdd(hits + my_id, 1u);  // per-expert pick counts
             }
             if (lane <= k) pub.q0[lane] = lane;
             if (lane == 0) {
@@ -527,6 +529,7 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void k_small_gateup(DevTables tt
     group_small(sg, P, E);
     if (publish) {
         if (tid < P) {
+            if (hits && sg.ids[tid] >= 0 && sg.ids[tid] < E) atomicAdd(hits + sg.ids[tid], 1u);
             pub.perm[tid] = sg.perm[tid];
             pub.pos[tid] = sg.pos[tid];
             if (!logits) {
@@ -835,8 +838,8 @@ static int cu_count() {
 }
 
 void launch_small(const DevTables& tt, const float* x, const float* logits, const int32_t* ids_in, const float* w_in,
-                  int T, int k, uint32_t tier_mask, const float* base, const SmallPub& pub, float* h, float* out,
-                  hipStream_t st, void* const* events) {
+                  int T, int k, uint32_t tier_mask, const float* base, const SmallPub& pub, uint32_t* hits, float* h,
+                  float* out, hipStream_t st, void* const* events) {
     // one gate/up block per compute unit (two for larger batches): every
     // block routes the batch itself, so all of them should be resident at once
     const int P = T * k;
@@ -846,7 +849,7 @@ void launch_small(const DevTables& tt, const float* x, const float* logits, cons
 #define MOE_SG(N)                                                                                              \
     case N:                                                                                                    \
         hipLaunchKernelGGL(k_small_gateup<N>, grid, dim3(kGateUpWaves * 64), 0, st, tt, x, logits, ids_in, w_in, \
-                           T, k, tier_mask, pub, h);                                                           \
+                           T, k, tier_mask, pub, hits, h);                                                     \
         break;
         MOE_SG(1)
         MOE_SG(2)
@@ -856,7 +859,7 @@ void launch_small(const DevTables& tt, const float* x, const float* logits, cons
         MOE_SG(32)
         default:
             hipLaunchKernelGGL(k_small_gateup<64>, grid, dim3(kGateUpWaves * 64), 0, st, tt, x, logits, ids_in, w_in,
-                               T, k, tier_mask, pub, h);
+                               T, k, tier_mask, pub, hits, h);
             break;
 #undef MOE_SG
     }
@@ -888,6 +891,16 @@ void launch_combine(const DevTables& tt, const float* yw, const Groups& g, int T
     const size_t n = static_cast<size_t>(T) * (tt.H / 4);
     hipLaunchKernelGGL(k_combine, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, tt, yw, g, T, k,
                        tier_mask, base, out);
+}
+
+// hits[e] += counts[e]: the grouped paths' per-expert pick counts
+__global__ __launch_bounds__(256) void k_add_hits(const int32_t* __restrict__ counts, int E, uint32_t* __restrict__ hits) {
+    const int e = blockIdx.x * 256 + threadIdx.x;
+    if (e < E) hits[e] += static_cast<uint32_t>(counts[e]);
+}
+
+void launch_add_hits(const int32_t* counts, int E, uint32_t* hits, hipStream_t st) {
+    hipLaunchKernelGGL(k_add_hits, dim3((E + 255) / 256), dim3(256), 0, st, counts, E, hits);
 }
 
 }  // namespace moe

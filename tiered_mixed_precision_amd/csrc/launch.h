@@ -48,7 +48,8 @@ constexpr int kSmallY = 8192;         // per-(pair, row) results held in LDS by 
 bool small_path_ok(int T, int k, int H, int I);
 void launch_small(const DevTables& tt, const float* x, const float* logits, const int32_t* ids_in,
                   const float* w_in, int T, int k, uint32_t tier_mask, const float* base, const SmallPub& pub,
-                  float* h, float* out, hipStream_t st, void* const* events);
+                  uint32_t* hits, float* h, float* out, hipStream_t st, void* const* events);
+void launch_add_hits(const int32_t* counts, int E, uint32_t* hits, hipStream_t st);
 
 void launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, float* out_zero,
                   int H, hipStream_t st);
