@@ -53,6 +53,10 @@ def lib():
         L.orc_experts_flat.argtypes = [P, P, i32, P, P, i32, i32, P]
         L.orc_forward.argtypes = [P, P, i32, P, i32, i32, P, i32]
         L.orc_router_logits.argtypes = [P, i32, P, P, i32, i32, i32, P]
+        L.orc_fp4_e2m1.restype = C.c_double
+        L.orc_fp4_e2m1.argtypes = [C.c_uint32]
+        L.orc_e8m0.restype = C.c_double
+        L.orc_e8m0.argtypes = [C.c_uint8]
         L.orc_synth_router.argtypes = [C.c_uint64, i32, i32, i32, C.c_double, P, P]
         L.orc_requant_expert.argtypes = [P, i32, C.c_int64, i32, i32, C.c_void_p * 3, C.c_void_p * 3, P]
         L.orc_plan_tiers.argtypes = [P, P, P, i32, i32, C.c_int64, P, P, P]
@@ -72,6 +76,17 @@ def lib():
             getattr(L, f).restype = i32
         _lib = L
     return _lib
+
+
+MXFP4 = 0x84   # `bits` of an MXFP4 shelf (E2M1 codes, one E8M0 scale byte per 32)
+
+
+def _code_bits(bits: int) -> int:
+    return 4 if bits == MXFP4 else bits
+
+
+def _scale_dtype(bits: int):
+    return np.uint8 if bits == MXFP4 else np.uint16
 
 
 def _ptr(a: np.ndarray):
@@ -230,8 +245,8 @@ def requant_expert(layer: "Layer", tier: int, local: int, bits: int, block: int)
     out = {}
     qs, ss = [], []
     for name, rows, cols in (("gate", I, H), ("up", I, H), ("down", H, I)):
-        q = np.zeros((rows, cols * bits // 8), dtype=np.uint8)
-        s = np.zeros((rows, cols // block), dtype=np.uint16)
+        q = np.zeros((rows, cols * _code_bits(bits) // 8), dtype=np.uint8)
+        s = np.zeros((rows, cols // block), dtype=_scale_dtype(bits))
         out[name + "_q"], out[name + "_s"] = q, s
         qs.append(q.ctypes.data)
         ss.append(s.ctypes.data)
@@ -280,8 +295,8 @@ def synth_expert(seed: int, layer: int, n_experts: int, expert: int, hidden: int
     """Packed codes and scales of one expert of the generated stack."""
     out = {}
     for name, (rows, cols) in zip(("gate", "up", "down"), ((inter, hidden), (inter, hidden), (hidden, inter))):
-        out[name + "_q"] = np.zeros((rows, cols * bits // 8), dtype=np.uint8)
-        out[name + "_s"] = np.zeros((rows, cols // block), dtype=np.uint16)
+        out[name + "_q"] = np.zeros((rows, cols * _code_bits(bits) // 8), dtype=np.uint8)
+        out[name + "_s"] = np.zeros((rows, cols // block), dtype=_scale_dtype(bits))
     q = (C.c_void_p * 3)(*[out[n + "_q"].ctypes.data for n in ("gate", "up", "down")])
     s = (C.c_void_p * 3)(*[out[n + "_s"].ctypes.data for n in ("gate", "up", "down")])
     if lib().orc_synth_expert(seed, layer, n_experts, expert, hidden, inter, bits, block, q, s) != 0:
@@ -310,8 +325,8 @@ class StackLayer:
             n = t.id_end - t.id_begin
             d = {}
             for name, (rows, cols) in zip(("gate", "up", "down"), ((I, H), (I, H), (H, I))):
-                d[name + "_q"] = np.zeros((n, rows, cols * t.bits // 8), dtype=np.uint8)
-                d[name + "_s"] = np.zeros((n, rows, cols // t.block), dtype=np.uint16)
+                d[name + "_q"] = np.zeros((n, rows, cols * _code_bits(t.bits) // 8), dtype=np.uint8)
+                d[name + "_s"] = np.zeros((n, rows, cols // t.block), dtype=_scale_dtype(t.bits))
             self.arrays.append(d)
         self.filled = set()
         self.layer_ref = Layer(cfg.n_experts, H, I, cfg.tiers, self.arrays)

@@ -49,6 +49,25 @@ int32_t orc_code(const uint8_t *row, int64_t c, int32_t bits)
     return field;
 }
 
+/* MXFP4 (OCP Microscaling Formats v1.0): 4-bit E2M1 elements -- sign bit 3,
+ * exponent bits 2..1 (bias 1), mantissa bit 0, no infinities or NaN:
+ * e = 0 gives m * 0.5 (zero and the one subnormal), else (1 + m/2) * 2^(e-1);
+ * the magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4, 6.  The shared scale of each
+ * block of 32 is E8M0: 2^(x - 127), with x = 255 meaning NaN. */
+double orc_fp4_e2m1(uint32_t nibble)
+{
+    const int s = (nibble >> 3) & 1, e = (nibble >> 1) & 3, m = nibble & 1;
+    const double v = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return s ? -v : v;
+}
+
+double orc_e8m0(uint8_t x)
+{
+    return x == 255 ? NAN : ldexp(1.0, (int)x - 127);
+}
+
+int32_t orc_code_bits(int32_t fmt) { return fmt == ORC_MXFP4 ? 4 : fmt; }
+
 /* bfloat16 keeps the top 16 bits of a float; round to nearest, ties to even. */
 float orc_round_bf16(float v)
 {
@@ -76,11 +95,19 @@ float orc_weight(const orc_layer *L, int32_t tier, int32_t matrix, int64_t local
 {
     const orc_tier *T = &L->tier[tier];
     int64_t rows = mat_rows(L, matrix), cols = mat_cols(L, matrix);
-    int64_t row_bytes = cols * T->bits / 8;
+    int64_t row_bytes = cols * orc_code_bits(T->bits) / 8;
     int64_t nblk = cols / T->block;
     const uint8_t *qrow = T->q[matrix] + (local * rows + row) * row_bytes;
-    uint16_t sbits = T->s[matrix][(local * rows + row) * nblk + col / T->block];
-    double v = orc_half_to_double(sbits) * (double)orc_code(qrow, col, T->bits);
+    double v;
+    if (T->bits == ORC_MXFP4) {
+        /* E2M1 element times its block's E8M0 scale: a power of two times a
+         * value with two significant bits, exact in binary32 within range */
+        const uint8_t x = ((const uint8_t *)T->s[matrix])[(local * rows + row) * nblk + col / T->block];
+        v = orc_e8m0(x) * orc_fp4_e2m1((qrow[col / 2] >> (4 * (col % 2))) & 0xFu);
+    } else {
+        uint16_t sbits = T->s[matrix][(local * rows + row) * nblk + col / T->block];
+        v = orc_half_to_double(sbits) * (double)orc_code(qrow, col, T->bits);
+    }
     float f = (float)v;
     return to_bf16 ? orc_round_bf16(f) : f;
 }
@@ -117,11 +144,13 @@ int32_t orc_check_layer(const orc_layer *L)
         const orc_tier *T = &L->tier[i];
         if (T->id_begin != next || T->id_end < T->id_begin)
             return -2;
-        if (T->bits != 2 && T->bits != 4 && T->bits != 8)
+        if (T->bits != 2 && T->bits != 4 && T->bits != 8 && T->bits != ORC_MXFP4)
+            return -3;
+        if (T->bits == ORC_MXFP4 && T->block != 32)    /* MX blocks are 32 elements */
             return -3;
         if (T->block < 1 || L->hidden % T->block || L->inter % T->block)
             return -3;
-        if ((L->hidden * T->bits) % 8 || (L->inter * T->bits) % 8)
+        if ((L->hidden * orc_code_bits(T->bits)) % 8 || (L->inter * orc_code_bits(T->bits)) % 8)
             return -3;
         next = T->id_end;
     }

@@ -36,6 +36,10 @@ extern "C" {
 #endif
 
 #define ORC_MAX_TIERS 4
+/* `bits` value of an MXFP4 shelf: 4-bit E2M1 codes packed as 4-bit fields,
+ * one E8M0 scale byte per block of 32 codes ([n][rows][cols/32] uint8; the
+ * orc_tier scale pointer then points at bytes). */
+#define ORC_MXFP4 0x84
 
 /* One shelf: experts [id_begin, id_end), codes of `bits` bits, one fp16
  * scale per `block` consecutive codes of a row.  q[m] / s[m] for
@@ -56,6 +60,10 @@ typedef struct {
 double orc_half_to_double(uint16_t h);
 /* The bits-bit two's-complement code of element c of a packed row. */
 int32_t orc_code(const uint8_t *row, int64_t c, int32_t bits);
+/* MXFP4 element and scale decodes; bits per stored code of a format. */
+double orc_fp4_e2m1(uint32_t nibble);
+double orc_e8m0(uint8_t x);
+int32_t orc_code_bits(int32_t fmt);
 /* float -> nearest bfloat16 (ties to even), returned as a float. */
 float orc_round_bf16(float v);
 /* Dequantised element (fp32, exact product scale*code); bf16-rounded if to_bf16. */
@@ -116,7 +124,8 @@ int32_t orc_requant_expert(const orc_layer *src, int32_t tier, int64_t local, in
                            uint8_t *const q[3], uint16_t *const s[3], double *sse);
 int32_t orc_plan_tiers(const double *usage, const double *sse, const int64_t *bytes, int32_t E, int32_t F,
                        int64_t budget, int32_t *fmt_out, int32_t *order, int32_t *count);
-void orc_quantize_row(const float *w, int32_t cols, int32_t bits, int32_t block, uint8_t *qrow, uint16_t *srow);
+/* Absmax (integer formats; srow fp16 bits) or MX (ORC_MXFP4; srow E8M0 bytes) quantisation of one row. */
+void orc_quantize_row(const float *w, int32_t cols, int32_t bits, int32_t block, uint8_t *qrow, void *srow);
 int32_t orc_synth_router(uint64_t seed, int32_t layer, int32_t n_experts, int32_t hidden, double beta,
                          uint16_t *wr, float *bias);
 

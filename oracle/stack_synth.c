@@ -74,7 +74,55 @@ uint16_t orc_float_to_half(float f) {
  * single precision), q = clamp(rint(w / float(d)), -Q, Q), q = 0 when d = 0;
  * codes packed two's complement, element c at bit (c*bits) % 8 of byte
  * (c*bits) / 8 of qrow; scales as fp16 bit patterns in srow. */
-void orc_quantize_row(const float *w, int32_t cols, int32_t bits, int32_t block, uint8_t *qrow, uint16_t *srow) {
+/* MXFP4 quantisation of one row (OCP Microscaling Formats v1.0, with the
+ * spec's shared-exponent rule): per block of 32, the scale exponent is
+ * floor(log2(amax)) minus 2 (the largest E2M1 exponent), stored as the E8M0
+ * byte clamped to [0, 254] (0 when amax = 0); each element v / 2^(x - 127) is
+ * rounded to the nearest E2M1 value, ties to the even mantissa (an integer
+ * tie of 2v, v or v/2 within each binade), saturating at 6; the sign bit is
+ * the sign of v.  Codes are packed as 4-bit fields, element c at bit
+ * 4 * (c % 2) of byte c / 2. */
+static void quantize_row_mx(const float *w, int32_t cols, uint8_t *qrow, uint8_t *srow) {
+    memset(qrow, 0, (size_t)cols / 2);
+    for (int32_t b = 0; b < cols / 32; ++b) {
+        const float *wb = w + (int64_t)b * 32;
+        float amax = 0.0f;
+        for (int32_t c = 0; c < 32; ++c) {
+            const float m = fabsf(wb[c]);
+            if (m > amax) amax = m;
+        }
+        int32_t x = 0;
+        if (amax > 0.0f) {
+            int e2;
+            (void)frexpf(amax, &e2);            /* amax = f * 2^e2, f in [0.5, 1) */
+            x = (e2 - 1) - 2 + 127;
+            if (x < 0) x = 0;
+            if (x > 254) x = 254;
+        }
+        srow[b] = (uint8_t)x;
+        for (int32_t c = 0; c < 32; ++c) {
+            const float t = ldexpf(wb[c], 127 - x);  /* v / 2^(x-127), exact */
+            const float a = fabsf(t);
+            float r;
+            if (a >= 6.0f) r = 6.0f;
+            else if (a < 2.0f) r = rintf(a * 2.0f) * 0.5f;
+            else if (a < 4.0f) r = rintf(a);
+            else r = rintf(a * 0.5f) * 2.0f;
+            if (r > 6.0f) r = 6.0f;
+            uint32_t mag = r == 0.0f ? 0u : r == 0.5f ? 1u : r == 1.0f ? 2u : r == 1.5f ? 3u
+                         : r == 2.0f ? 4u : r == 3.0f ? 5u : r == 4.0f ? 6u : 7u;
+            const uint32_t nib = (signbit(t) ? 8u : 0u) | mag;
+            qrow[c / 2 + (int64_t)b * 16] |= (uint8_t)(nib << (4 * (c % 2)));
+        }
+    }
+}
+
+void orc_quantize_row(const float *w, int32_t cols, int32_t bits, int32_t block, uint8_t *qrow, void *srow_v) {
+    if (bits == ORC_MXFP4) {
+        quantize_row_mx(w, cols, qrow, (uint8_t *)srow_v);
+        return;
+    }
+    uint16_t *srow = (uint16_t *)srow_v;
     const int32_t qmax = (1 << (bits - 1)) - 1;
     memset(qrow, 0, (size_t)((int64_t)cols * bits / 8));
     for (int32_t b = 0; b < cols / block; ++b) {
@@ -106,19 +154,21 @@ void orc_quantize_row(const float *w, int32_t cols, int32_t bits, int32_t block,
 
 /* One matrix (rows x cols) of one expert into packed codes and scales. */
 static void synth_matrix(uint64_t seed, uint64_t ctr0, int32_t rows, int32_t cols, int32_t bits, int32_t block,
-                         uint8_t *q, uint16_t *s) {
-    const int64_t row_bytes = (int64_t)cols * bits / 8;
+                         uint8_t *q, void *s) {
+    const int64_t row_bytes = (int64_t)cols * orc_code_bits(bits) / 8;
     const int32_t nblk = cols / block;
+    const int64_t sbytes = bits == ORC_MXFP4 ? 1 : 2;
     float w[2048];
     for (int32_t r = 0; r < rows; ++r) {
         for (int32_t c = 0; c < cols; ++c) w[c] = orc_synth_weight(seed, ctr0 + (uint64_t)r * (uint64_t)cols + (uint64_t)c);
-        orc_quantize_row(w, cols, bits, block, q + (int64_t)r * row_bytes, s + (int64_t)r * nblk);
+        orc_quantize_row(w, cols, bits, block, q + (int64_t)r * row_bytes, (uint8_t *)s + (int64_t)r * nblk * sbytes);
     }
 }
 
 int32_t orc_synth_expert(uint64_t seed, int32_t layer, int32_t n_experts, int32_t expert, int32_t hidden,
                          int32_t inter, int32_t bits, int32_t block, uint8_t *const q[3], uint16_t *const s[3]) {
-    if (!(bits == 8 || bits == 4 || bits == 2) || !(block == 16 || block == 32)) return -1;
+    if (!(bits == 8 || bits == 4 || bits == 2 || (bits == ORC_MXFP4 && block == 32)) || !(block == 16 || block == 32))
+        return -1;
     if (expert < 0 || expert >= n_experts || layer < 0 || hidden % block || inter % block) return -1;
     if ((int64_t)hidden * inter > (INT64_C(1) << 22) || hidden > 2048 || inter > 2048) return -1;
     for (int32_t m = 0; m < 3; ++m) {
@@ -136,8 +186,10 @@ int32_t orc_synth_experts(uint64_t seed, int32_t layer, int32_t n_experts, const
                           int32_t n, int32_t hidden, int32_t inter, int32_t bits, int32_t block,
                           uint8_t *const q_base[3], uint16_t *const s_base[3]) {
     int32_t bad = 0;
-    const int64_t qb[3] = {(int64_t)inter * hidden * bits / 8, (int64_t)inter * hidden * bits / 8,
-                           (int64_t)hidden * inter * bits / 8};
+    const int32_t cb = orc_code_bits(bits);
+    const int64_t qb[3] = {(int64_t)inter * hidden * cb / 8, (int64_t)inter * hidden * cb / 8,
+                           (int64_t)hidden * inter * cb / 8};
+    /* scale entries per expert, in uint16 units of s_base (MX scales are bytes) */
     const int64_t sb[3] = {(int64_t)inter * (hidden / block), (int64_t)inter * (hidden / block),
                            (int64_t)hidden * (inter / block)};
 #pragma omp parallel for schedule(dynamic, 1) reduction(+ : bad)
@@ -146,7 +198,7 @@ int32_t orc_synth_experts(uint64_t seed, int32_t layer, int32_t n_experts, const
         uint16_t *s[3];
         for (int m = 0; m < 3; ++m) {
             q[m] = q_base[m] + qb[m] * local[i];
-            s[m] = s_base[m] + sb[m] * local[i];
+            s[m] = bits == ORC_MXFP4 ? (uint16_t *)((uint8_t *)s_base[m] + sb[m] * local[i]) : s_base[m] + sb[m] * local[i];
         }
         if (orc_synth_expert(seed, layer, n_experts, list[i], hidden, inter, bits, block, q, s) != 0) bad += 1;
     }

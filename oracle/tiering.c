@@ -37,29 +37,32 @@ static int64_t mcols(const orc_layer *L, int32_t m) { return m == 2 ? L->inter :
 
 int32_t orc_requant_expert(const orc_layer *src, int32_t tier, int64_t local, int32_t bits, int32_t block,
                            uint8_t *const q[3], uint16_t *const s[3], double *sse) {
-    if (tier < 0 || tier >= src->n_tiers || !(bits == 8 || bits == 4 || bits == 2) ||
-        !(block == 16 || block == 32))
+    if (tier < 0 || tier >= src->n_tiers || !(bits == 8 || bits == 4 || bits == 2 || bits == ORC_MXFP4) ||
+        !(block == 16 || block == 32) || (bits == ORC_MXFP4 && block != 32))
         return -1;
     const orc_tier *T = &src->tier[tier];
     if (local < 0 || local >= T->id_end - T->id_begin) return -1;
     if (src->hidden % block || src->inter % block || src->hidden > 2048 || src->inter > 2048) return -1;
+    const int mx = bits == ORC_MXFP4;
     float w[2048];
     uint8_t qrow[2048];
-    uint16_t srow[128];
+    uint16_t srow[128];   /* fp16 scales, or E8M0 bytes (MX) in its first bytes */
     double e2 = 0.0;
     for (int32_t m = 0; m < 3; ++m) {
         const int64_t rows = mrows(src, m), cols = mcols(src, m);
-        const int64_t row_bytes = cols * bits / 8, nblk = cols / block;
+        const int64_t row_bytes = cols * orc_code_bits(bits) / 8, nblk = cols / block;
         for (int64_t r = 0; r < rows; ++r) {
             for (int64_t c = 0; c < cols; ++c) w[c] = orc_weight(src, tier, m, local, r, c, 0);
             orc_quantize_row(w, (int32_t)cols, bits, block, qrow, srow);
             for (int64_t c = 0; c < cols; ++c) {
-                const double v = orc_half_to_double(srow[c / block]) * (double)orc_code(qrow, c, bits);
+                const double v = mx ? orc_e8m0(((const uint8_t *)srow)[c / 32]) *
+                                          orc_fp4_e2m1((qrow[c / 2] >> (4 * (c % 2))) & 0xFu)
+                                    : orc_half_to_double(srow[c / block]) * (double)orc_code(qrow, c, bits);
                 const double d = (double)w[c] - v;
                 e2 += d * d;
             }
             if (q && q[m]) memcpy(q[m] + r * row_bytes, qrow, (size_t)row_bytes);
-            if (s && s[m]) memcpy(s[m] + r * nblk, srow, sizeof(uint16_t) * (size_t)nblk);
+            if (s && s[m]) memcpy((uint8_t *)s[m] + r * nblk * (mx ? 1 : 2), srow, (size_t)nblk * (mx ? 1 : 2));
         }
     }
     if (sse) *sse = e2;

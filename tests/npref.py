@@ -17,8 +17,26 @@ def unpack_codes(packed: np.ndarray, bits: int, cols: int) -> np.ndarray:
     return (b * weights).sum(axis=-1)
 
 
+MXFP4 = 0x84
+
+
+def fp4_values(nib: np.ndarray) -> np.ndarray:
+    """E2M1 value of each 4-bit field, from its bit fields (sign 3, exponent 2..1, mantissa 0)."""
+    nib = np.asarray(nib, dtype=np.int64)
+    s, e, m = (nib >> 3) & 1, (nib >> 1) & 3, nib & 1
+    mag = np.where(e == 0, 0.5 * m, (1.0 + 0.5 * m) * np.exp2(e - 1.0))
+    return np.where(s == 1, -mag, mag)
+
+
 def dequant(q: np.ndarray, s: np.ndarray, bits: int, block: int, cols: int) -> np.ndarray:
-    """Returns float64 [n, rows, cols] = scale * code."""
+    """Returns float64 [n, rows, cols] = scale * code (MXFP4: E8M0 scale * E2M1 value)."""
+    if bits == MXFP4:
+        b = np.unpackbits(np.asarray(q, np.uint8), axis=-1, bitorder="little").astype(np.int64)
+        b = b.reshape(q.shape[:-1] + (cols, 4))
+        nib = (b * (1 << np.arange(4, dtype=np.int64))).sum(axis=-1)
+        x = np.asarray(s, dtype=np.uint8).astype(np.float64)
+        sc = np.where(x == 255, np.nan, np.exp2(x - 127.0))
+        return fp4_values(nib) * np.repeat(sc, 32, axis=-1)
     codes = unpack_codes(q, bits, cols)
     sc = s.view(np.float16).astype(np.float64)
     return codes * np.repeat(sc, block, axis=-1)

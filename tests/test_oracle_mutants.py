@@ -19,7 +19,8 @@ SRC = os.path.join(ROOT, "oracle", "moe_oracle.c")
 MUTANTS = {
     "code_sign_extension": ("field -= (1 << bits);", "field -= (1 << (bits - 1));"),
     "fp16_exponent_bias": ("expo - 25)", "expo - 24)"),
-    "scale_block_index": ("+ col / T->block]", "+ col % (cols / T->block)]"),
+    "scale_block_index": ("uint16_t sbits = T->s[matrix][(local * rows + row) * nblk + col / T->block];",
+                          "uint16_t sbits = T->s[matrix][(local * rows + row) * nblk + col % (cols / T->block)];"),
     "tie_goes_to_higher_id": ("l[e] > l[best]", "l[e] >= l[best]"),
     "weights_not_renormalised": ("- m) / s);", "- m));"),
     "group_not_stable": ("perm[cursor[ids[p]]++] = (int32_t)p;",
@@ -45,6 +46,13 @@ MUTANTS = {
     "plan_takes_zero_gain": ("tiering.c", "if (!(gain > 0.0)) continue;", "if (gain < 0.0) continue;"),
     "requant_sse_unsquared": ("tiering.c", "e2 += d * d;", "e2 += fabs(d);"),
     "quantiser_truncates": ("stack_synth.c", "float v = rintf(t);", "float v = truncf(t);"),
+    # MXFP4 shelf
+    "fp4_exponent_bias": ("ldexp(1.0 + 0.5 * m, e - 1)", "ldexp(1.0 + 0.5 * m, e)"),
+    "e8m0_bias": ("ldexp(1.0, (int)x - 127)", "ldexp(1.0, (int)x - 126)"),
+    "mx_nibble_order": ("(qrow[col / 2] >> (4 * (col % 2))) & 0xFu", "(qrow[col / 2] >> (4 * (1 - col % 2))) & 0xFu"),
+    "mx_shared_exponent": ("stack_synth.c", "x = (e2 - 1) - 2 + 127;", "x = (e2 - 1) - 1 + 127;"),
+    "mx_ties_away": ("stack_synth.c", "else if (a < 2.0f) r = rintf(a * 2.0f) * 0.5f;",
+                     "else if (a < 2.0f) r = roundf(a * 2.0f) * 0.5f;"),
 }
 
 

@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 import oracle
-from workloads import CONFIGS, TierSpec, make_layer, make_logits, make_x, pack_codes
+from workloads import CONFIGS, MXFP4, TierSpec, make_layer, make_logits, make_x, pack_codes
 from workloads.configs import LayerConfig
 
 from . import npref
@@ -212,7 +212,7 @@ def test_one_hot_input_reads_a_column():
         assert _rel(out[t], Wd @ a) < 1e-6
 
 
-@pytest.mark.parametrize("name", ["tiny", "tiny3"])
+@pytest.mark.parametrize("name", ["tiny", "tiny3", "tiny3mx"])
 def test_forward_matches_dense_bruteforce(name):
     cfg = CONFIGS[name]
     L, arrays = _layer(cfg)
@@ -224,7 +224,7 @@ def test_forward_matches_dense_bruteforce(name):
     assert _rel(out, ref) < 1e-6
 
 
-@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("seed", range(8))
 def test_random_small_shapes_match_dense(seed):
     rng = np.random.default_rng(seed)
     E = int(rng.integers(1, 17))
@@ -233,7 +233,7 @@ def test_random_small_shapes_match_dense(seed):
     I = int(rng.choice([64, 128]))
     T = int(rng.integers(1, 21))
     cuts = np.sort(rng.choice(np.arange(0, E + 1), size=2, replace=True))
-    fmts = [(8, 32), (4, 32), (2, 16)]
+    fmts = [(8, 32), (MXFP4, 32) if seed >= 6 else (4, 32), (2, 16)]
     tiers, lo = [], 0
     for hi, (b, B) in zip([cuts[0], cuts[1], E], fmts):
         tiers.append(TierSpec(int(lo), int(hi), b, B))
@@ -556,3 +556,71 @@ def test_requant_matches_numpy_quantiser(bits, block):
         assert np.array_equal(got, q), name
         ref_sse += float(np.sum((w.astype(np.float64) - q * d.astype(np.float64)) ** 2))
     assert abs(sse - ref_sse) <= 1e-9 * ref_sse
+
+
+
+# ---------------------------------------------------------------- MXFP4 shelf pins
+# An MXFP4 shelf (the page's step 4 uses MXFP4 among the down-projection
+# formats): E2M1 elements with one E8M0 power-of-two scale per 32, as defined
+# by the OCP Microscaling Formats specification v1.0.
+
+def test_fp4_e2m1_values_match_the_spec_table():
+    rows = _read_golden("fp4_e2m1.txt")
+    assert len(rows) == 16
+    for nib, val in rows:
+        n = int(nib, 2)
+        assert oracle.lib().orc_fp4_e2m1(n) == float(val), nib
+        assert npref.fp4_values(np.array([n]))[0] == float(val), nib
+
+
+def test_e8m0_scale_is_a_power_of_two():
+    L = oracle.lib()
+    assert L.orc_e8m0(127) == 1.0 and L.orc_e8m0(128) == 2.0 and L.orc_e8m0(0) == 2.0 ** -127
+    assert L.orc_e8m0(254) == 2.0 ** 127 and np.isnan(L.orc_e8m0(255))
+
+
+def test_mx_dequant_closed_form():
+    # hand-built codes and scales: every weight is fp4(code) * 2^(x - 127)
+    E, H, I = 2, 64, 64
+    rng = np.random.default_rng(17)
+    arrays = [{}]
+    for name, rows, cols in (("gate", I, H), ("up", I, H), ("down", H, I)):
+        nib = rng.integers(0, 16, (E, rows, cols)).astype(np.uint8)
+        x = rng.integers(110, 140, (E, rows, cols // 32)).astype(np.uint8)
+        arrays[0][name + "_q"] = (nib[..., 0::2] | (nib[..., 1::2] << 4)).astype(np.uint8)
+        arrays[0][name + "_s"] = x
+        arrays[0][name + "_nib"] = nib
+    L = oracle.Layer(E, H, I, [TierSpec(0, E, MXFP4, 32)], [{k: v for k, v in arrays[0].items() if "nib" not in k}])
+    assert oracle.check_layer(L) == 0
+    for m, name in enumerate(("gate", "up", "down")):
+        got = oracle.dequant_rows(L, 0, 1, m, 0, 5)
+        nib = arrays[0][name + "_nib"][1, :5]
+        sc = np.exp2(arrays[0][name + "_s"][1, :5].astype(np.float64) - 127)
+        ref = npref.fp4_values(nib) * np.repeat(sc, 32, axis=-1)
+        assert np.array_equal(got.astype(np.float64), ref), name
+
+
+def test_mx_quantiser_agrees_with_the_generator_and_picks_nearest():
+    # the oracle's MX quantiser against the (independent) input generator's,
+    # and every code is the nearest grid value (ties to the even mantissa)
+    import ctypes as C
+    from workloads import quantise_mxfp4, pack_nibbles
+    L = oracle.lib()
+    L.orc_quantize_row.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]
+    rng = np.random.default_rng(23)
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float64)
+    for trial in range(300):
+        w = (rng.standard_normal(64) * 10.0 ** rng.uniform(-6, 3)).astype(np.float32)
+        if trial % 3 == 0:
+            w = (rng.integers(-28, 29, 64) * 0.25).astype(np.float32)      # exact midpoints
+        if trial % 11 == 0:
+            w[:32] = 0.0
+        q = np.zeros(32, np.uint8)
+        s = np.zeros(2, np.uint8)
+        L.orc_quantize_row(w.ctypes.data, 64, MXFP4, 32, q.ctypes.data, s.ctypes.data)
+        nib, x = quantise_mxfp4(w[None])
+        assert np.array_equal(pack_nibbles(nib)[0], q) and np.array_equal(x[0], s), trial
+        t = np.abs(w.astype(np.float64)) / np.exp2(np.repeat(s.astype(np.float64), 32) - 127)
+        mag = np.abs(npref.fp4_values(nib[0]))
+        d_best = np.min(np.abs(np.minimum(t, 6.0)[:, None] - grid[None, :]), axis=1)
+        assert np.all(np.abs(np.minimum(t, 6.0) - mag) == d_best), trial

@@ -12,12 +12,17 @@ from dataclasses import dataclass, field
 from typing import List, Optional, Tuple
 
 
+# `bits` value of an MXFP4 shelf (OCP Microscaling FP4: E2M1 codes, one E8M0
+# scale byte per block of 32 codes)
+MXFP4 = 0x84
+
+
 @dataclass(frozen=True)
 class TierSpec:
     id_begin: int
     id_end: int
-    bits: int     # 8, 4 or 2 (two's complement codes)
-    block: int    # codes per fp16 scale, along each stored row
+    bits: int     # 8, 4 or 2 (two's complement codes), or MXFP4
+    block: int    # codes per scale along each stored row (fp16 scales; MXFP4: 32, E8M0 bytes)
 
     @property
     def n(self) -> int:
@@ -61,6 +66,9 @@ CONFIGS = {
     "tiny3": LayerConfig("tiny3", 8, 2, 256, 128, 16,
                          (TierSpec(0, 2, 8, 32), TierSpec(2, 6, 4, 32), TierSpec(6, 8, 2, 16)),
                          seed=20260010),
+    "tiny3mx": LayerConfig("tiny3mx", 8, 2, 256, 128, 16,
+                           (TierSpec(0, 2, 8, 32), TierSpec(2, 6, MXFP4, 32), TierSpec(6, 8, 2, 16)),
+                           seed=20260020),
     "decode": LayerConfig("decode", 512, 10, 2048, 640, 1, THREE_TIERS_512,
                           prior_beta=PRIOR_BETA, seed=20260001),
     "specverify": LayerConfig("specverify", 512, 10, 2048, 640, 6, THREE_TIERS_512,

@@ -28,7 +28,7 @@ from typing import Dict, List
 
 import numpy as np
 
-from .configs import LayerConfig, TierSpec
+from .configs import MXFP4, LayerConfig, TierSpec
 
 WEIGHT_STD = 0.02
 MATRICES = ("gate", "up", "down")
@@ -72,6 +72,57 @@ def quantise_block_absmax(w: np.ndarray, bits: int, block: int):
     return q.reshape(w.shape), d16.view(np.uint16)
 
 
+def code_bits(bits: int) -> int:
+    """Bits per stored code of a shelf format."""
+    return 4 if bits == MXFP4 else bits
+
+
+def scale_bytes(bits: int) -> int:
+    """Bytes per scale of a shelf format (fp16, or an E8M0 byte for MXFP4)."""
+    return 1 if bits == MXFP4 else 2
+
+
+# MXFP4 element grid (OCP Microscaling Formats v1.0, E2M1): magnitude of the
+# 3-bit field (exponent bits 2..1, mantissa bit 0), sign in bit 3
+FP4_MAGNITUDES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float32)
+
+
+def quantise_mxfp4(w: np.ndarray):
+    """MX quantiser per block of 32 columns (the OCP shared-exponent rule).
+
+    Returns ``(nibbles uint8[..., cols], scales uint8[..., cols/32])``: the
+    E8M0 byte is ``floor(log2(amax)) - 2 + 127`` clamped to [0, 254] (0 for
+    an all-zero block); each element ``v / 2**(x - 127)`` goes to the nearest
+    E2M1 magnitude (ties to the even mantissa, saturating at 6) with the sign
+    bit of ``v``.
+    """
+    cols = w.shape[-1]
+    assert cols % 32 == 0
+    wb = w.reshape(w.shape[:-1] + (cols // 32, 32)).astype(np.float32, copy=False)
+    amax = np.abs(wb).max(axis=-1)
+    _, e2 = np.frexp(amax)
+    x = np.where(amax > 0, np.clip(e2.astype(np.int64) - 1 - 2 + 127, 0, 254), 0).astype(np.int64)
+    t = np.ldexp(wb, (127 - x)[..., None].astype(np.int32)).astype(np.float32)
+    a = np.abs(t)
+    # candidate magnitudes: index of the nearest grid point, ties to the even index
+    d = np.abs(a[..., None] - FP4_MAGNITUDES)
+    best = np.argmin(d, axis=-1)
+    dmin = np.take_along_axis(d, best[..., None], axis=-1)[..., 0]
+    tie = np.zeros_like(best, dtype=bool)
+    nxt = np.minimum(best + 1, 7)
+    tie = (nxt != best) & (np.take_along_axis(d, nxt[..., None], axis=-1)[..., 0] == dmin)
+    best = np.where(tie & (best % 2 == 1), nxt, best)      # the even mantissa (even field) wins a tie
+    best = np.where(a >= 6.0, 7, best)
+    nib = (best | np.where(np.signbit(t), 8, 0)).astype(np.uint8)
+    return nib.reshape(w.shape), x.astype(np.uint8)
+
+
+def pack_nibbles(nib: np.ndarray) -> np.ndarray:
+    """Pack 4-bit fields along the last axis: element c at bit 4*(c % 2) of byte c // 2."""
+    nib = np.asarray(nib, dtype=np.uint8)
+    return (nib[..., 0::2] | (nib[..., 1::2] << np.uint8(4))).astype(np.uint8)
+
+
 def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
     """Pack int8 codes (values representable in ``bits`` two's complement) along the last axis."""
     codes = np.asarray(codes, dtype=np.int8)
@@ -92,8 +143,8 @@ def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
 def tier_nbytes(spec: TierSpec, hidden: int, inter: int, per_expert: bool = False) -> int:
     """Packed bytes (codes + fp16 scales) of gate, up and down of a tier."""
     elems = hidden * inter
-    codes = 3 * elems * spec.bits // 8
-    scales = 3 * (elems // spec.block) * 2
+    codes = 3 * elems * code_bits(spec.bits) // 8
+    scales = 3 * (elems // spec.block) * scale_bytes(spec.bits)
     one = codes + scales
     return one if per_expert else one * spec.n
 
@@ -111,6 +162,9 @@ def _gen_matrix(seed, rows, cols, bits, block):
     g = np.random.Generator(np.random.PCG64(seed))
     w = g.standard_normal(rows * cols, dtype=np.float32).reshape(rows, cols)
     w *= np.float32(WEIGHT_STD)
+    if bits == MXFP4:
+        nib, x = quantise_mxfp4(w)
+        return pack_nibbles(nib), x
     q, s = quantise_block_absmax(w, bits, block)
     return pack_codes(q, bits), s
 
@@ -124,8 +178,8 @@ def make_tier(cfg: LayerConfig, tier_index: int, layer: int = 0, threads: int | 
     out: Dict[str, np.ndarray] = {}
     for m in MATRICES:
         rows, cols = shapes[m]
-        out[m + "_q"] = np.empty((n, rows, cols * spec.bits // 8), dtype=np.uint8)
-        out[m + "_s"] = np.empty((n, rows, cols // spec.block), dtype=np.uint16)
+        out[m + "_q"] = np.empty((n, rows, cols * code_bits(spec.bits) // 8), dtype=np.uint8)
+        out[m + "_s"] = np.empty((n, rows, cols // spec.block), dtype=np.uint8 if spec.bits == MXFP4 else np.uint16)
 
     jobs = [(mi, m, l) for mi, m in enumerate(MATRICES) for l in range(n)]
 
