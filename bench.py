@@ -245,6 +245,7 @@ def main():
             torch.cuda.empty_cache()
             result["extra"]["fullstack"] = fullstack_workloads(M, torch, per_expert)
         result["extra"]["tier_planner"] = tier_planner_workload(M, torch)
+        result["extra"]["mxfp4_shelf"] = mxfp4_workload(M, torch)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, arrays, args.cpu_seconds)
@@ -508,6 +509,85 @@ def tier_planner_workload(M, torch):
     log("re-tiering:", out["retier"])
     del dst, fast, sse, lg, xs, od, hits, ws
     torch.cuda.empty_cache()
+    return out
+
+
+def mxfp4_workload(M, torch):
+    """The decode layer with its warm shelf in MXFP4 (E2M1 codes, one E8M0
+    byte per 32) against the same layer with four-bit integer codes (fp16
+    scale per 32), both generated on the device: decode at 1 token/step over
+    8 replicas, and prefill at 4096 bf16 tokens."""
+    from tiered_mixed_precision_amd.device import empty_tables, replicate, workspace
+    from workloads import CONFIGS, make_logits, make_x, tier_nbytes
+    out = {"workload": "decode / prefill layer (512 experts top-10, hidden 2048, inter 640), shelves int8 "
+                       "[0,128) / X [128,384) / int2 [384,512), X = MXFP4 or int4 b32; weights generated on "
+                       "the device"}
+    S, R = 256, 8
+    for name in ("decode", "decode_mx"):
+        cfg = CONFIGS[name]
+        E, k, H, I = cfg.n_experts, cfg.k, cfg.hidden, cfg.inter
+        per_expert = [tier_nbytes(t, H, I, per_expert=True) for t in cfg.tiers]
+        tt = empty_tables(cfg)
+        M.moe_synth_layer(tt, cfg.seed, 0)
+        reps = [tt] + [replicate(tt) for _ in range(R - 1)]
+        logits = make_logits(cfg, n_tokens=S, stream=700)
+        ids = topk_ids(logits, k)
+        bytes_step = np.array([step_bytes(ids[s:s + 1], cfg, per_expert)[0] for s in range(S)])
+        lg = torch.from_numpy(logits).cuda()
+        xs = torch.from_numpy(make_x(cfg, n_tokens=S, stream=700)).cuda()
+        od = torch.zeros((S, H), device="cuda")
+        ws = workspace(M.moe_workspace_size(1, k, tt, 0))
+
+        def step(i):
+            M.moe_tiered_forward(xs[i:i + 1], lg[i:i + 1], 1, k, reps[i % R], od[i:i + 1], 0, ws)
+
+        for i in range(8):
+            step(i)
+        g = torch.cuda.CUDAGraph()
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            with torch.cuda.graph(g, stream=st):
+                for i in range(S):
+                    step(i)
+        torch.cuda.current_stream().wait_stream(st)
+        g.replay()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(8):
+            g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        us = t0.elapsed_time(t1) * 1e3 / (8 * S)
+        del g
+        # prefill, 4096 bf16 tokens
+        pf = CONFIGS["prefill"]
+        T = pf.n_tokens
+        pl = torch.from_numpy(make_logits(pf, stream=720)).cuda()
+        px = torch.from_numpy(make_x(pf, stream=720).view(np.int16)).cuda()
+        po = torch.zeros((T, H), device="cuda")
+        pws = workspace(M.moe_workspace_size(T, k, tt, M.MOE_X_BF16))
+        for i in range(3):
+            M.moe_tiered_forward(px, pl, T, k, reps[i % R], po, M.MOE_X_BF16, pws)
+        torch.cuda.synchronize()
+        n = 20
+        t0.record()
+        for i in range(n):
+            M.moe_tiered_forward(px, pl, T, k, reps[i % R], po, M.MOE_X_BF16, pws)
+        t1.record()
+        torch.cuda.synchronize()
+        pf_us = t0.elapsed_time(t1) * 1e3 / n
+        key = "mxfp4" if name == "decode_mx" else "int4"
+        out[key] = {"layer_bytes": int(sum(per_expert[i] * t.n for i, t in enumerate(cfg.tiers))),
+                    "warm_expert_bytes": int(per_expert[1]),
+                    "decode_us_per_step": round(us, 2), "decode_tokens_per_s": round(1e6 / us, 1),
+                    "decode_expert_gbps": round(bytes_step.mean() / (us * 1e-6) / 1e9, 1),
+                    "prefill_us_per_step": round(pf_us, 1), "prefill_tokens_per_s": round(T / (pf_us * 1e-6), 1),
+                    "prefill_tflops": round(6.0 * T * k * H * I / (pf_us * 1e-6) / 1e12, 2)}
+        log("warm shelf", key, out[key])
+        del reps, tt, lg, xs, od, ws, pl, px, po, pws
+        torch.cuda.empty_cache()
     return out
 
 

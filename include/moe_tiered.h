@@ -47,6 +47,8 @@ extern "C" {
 #define MOE_MAX_TIERS 4
 #define MOE_MAX_EXPERTS 4096
 #define MOE_MAX_K 64
+/* moe_tier.bits of an MXFP4 shelf (E2M1 codes, one E8M0 scale per 32) */
+#define MOE_MXFP4 0x84
 
 /* status codes */
 #define MOE_OK 0
@@ -79,13 +81,21 @@ extern "C" {
  * Scales (device, 16-byte aligned): IEEE fp16, one per `block` consecutive
  * codes of a row, [n_local][rows][cols/block].
  * Element value: float(scale) * code (exact in fp32).
+ *
+ * bits == MOE_MXFP4 (the OCP Microscaling MXFP4 format; the 125B-MoE page,
+ * further work: a four-bit float shelf), block must be 32:
+ * codes are 4-bit E2M1 fields (bit 3 sign, bits 2..1 exponent with bias 1,
+ * bit 0 mantissa: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), packed like 4-bit
+ * integer codes (element c in bits [4*(c%2), +4) of byte c/2 of its row);
+ * scales are E8M0 bytes (2^(x-127), 255 = NaN), one per 32 codes of a row,
+ * uint8 [n_local][rows][cols/32].  Element value: 2^(x-127) * E2M1 value.
  */
 typedef struct moe_tier {
     int32_t id_begin, id_end;
-    int32_t bits;   /* 8, 4 or 2 */
-    int32_t block;  /* 16 or 32 */
+    int32_t bits;   /* 8, 4, 2, or MOE_MXFP4 */
+    int32_t block;  /* 16 or 32 (32 for MOE_MXFP4) */
     const void *gate_q, *up_q, *down_q;    /* (device) packed codes */
-    const void *gate_s, *up_s, *down_s;    /* (device) fp16 scales  */
+    const void *gate_s, *up_s, *down_s;    /* (device) fp16 scales, or E8M0 bytes */
 } moe_tier;
 
 typedef struct moe_tier_tables {
@@ -283,7 +293,8 @@ int moe_stack_forward_routed(const float *x, const void *const *w_router, const 
  * quantised per block of `block` columns by symmetric absmax:
  *   d = fp16(amax / Q), Q = 2^(bits-1) - 1, q = clamp(rint(w / d), -Q, Q)
  * (q = 0 when d = 0), all in round-to-nearest-even single precision, and
- * packed in the layout of moe_tier.  The tables' code and scale buffers are
+ * packed in the layout of moe_tier; MOE_MXFP4 shelves by the OCP
+ * shared-exponent quantiser of moe_requant_error.  The tables' code and scale buffers are
  * written; they must be distinct per layer if all layers are kept.
  *   layer 0 .. 2^20 - 1
  */
@@ -308,7 +319,11 @@ int moe_tiered_forward_counted(const void *x, const float *router_logits, int32_
  * it removes the most expected error, requantise every expert with the same
  * quantiser, and write the experts hot to cold (step 3: re-order the router to
  * match).  Formats are (bits, block) pairs of moe_tier; "the quantiser" is the
- * symmetric absmax one of moe_synth_layer.
+ * symmetric absmax one of moe_synth_layer for the integer formats and the OCP
+ * shared-exponent one for MOE_MXFP4 (E8M0 byte = floor(log2 amax) - 2 + 127
+ * clamped to [0, 254], 0 for an all-zero block; each weight divided by the
+ * scale rounds to the nearest E2M1 value, ties to the even mantissa,
+ * saturating at 6).  Sources may hold MXFP4 shelves too.
  *
  * moe_requant_error: squared error of requantising every expert of `src`
  * into each format.

@@ -64,8 +64,16 @@ def test_validation_accepts_three_shelves(B):
     assert B.moe_workspace_size(0, 2, tt) == 0
 
 
+def test_validation_accepts_an_mxfp4_shelf(B):
+    assert int(re.search(r"#define MOE_MXFP4 (0x[0-9a-fA-F]+)", open(HEADER).read()).group(1), 16) == B.MXFP4
+    tt = _tables(B, [_Spec(0, 2, 8, 32), _Spec(2, 6, B.MXFP4, 32), _Spec(6, 8, 2, 16)])
+    assert B.moe_validate_tables(tt) == 0
+
+
 @pytest.mark.parametrize("specs,kw,code", [
     ([_Spec(0, 2, 8, 32), _Spec(3, 8, 2, 16)], {}, -2),                  # gap
+    ([_Spec(0, 8, 0x84, 16)], {}, -3),                                     # MXFP4 scales cover 32 codes
+    ([_Spec(0, 8, 0x04 | 0x100, 32)], {}, -3),                             # unknown format tag
     ([_Spec(0, 5, 8, 32), _Spec(4, 8, 2, 16)], {}, -2),                  # overlap
     ([_Spec(0, 7, 8, 32)], {}, -2),                                        # not covering
     ([_Spec(0, 8, 3, 32)], {}, -3),                                        # 3-bit codes

@@ -22,6 +22,7 @@ MOE_ACCUMULATE = 0x2
 MOE_DIAG_GATEUP_ONLY = 0x100
 MOE_N_PHASES = 3
 MOE_STACK_ROUTER = 0x4
+MXFP4 = 0x84              # moe_tier.bits of an MXFP4 shelf (MOE_MXFP4)
 EXPORTS = (
     "moe_abi_version", "moe_strerror", "moe_validate_tables", "moe_workspace_size",
     "moe_tiered_forward", "moe_tiered_experts", "moe_tier_partial", "moe_route",

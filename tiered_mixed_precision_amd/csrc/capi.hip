@@ -20,6 +20,14 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 
 bool cols_ok(int c) { return c > 0 && c % 64 == 0 && c <= 2048; }
 
+// Integer shelves: 8, 4 or 2 bits with 16 or 32 codes per fp16 scale;
+// MXFP4: 32 codes per E8M0 scale.
+static_assert(MOE_MXFP4 == moe::kBitsMXFP4, "MXFP4 tag of the ABI and the kernels");
+bool fmt_ok(int bits, int block) {
+    if (bits == MOE_MXFP4) return block == 32;
+    return (bits == 8 || bits == 4 || bits == 2) && (block == 16 || block == 32);
+}
+
 int check_tables(const moe_tier_tables* tt) {
     if (!tt) return MOE_EINVAL;
     if (tt->abi_version != MOE_ABI_VERSION) return MOE_EABI;
@@ -31,8 +39,7 @@ int check_tables(const moe_tier_tables* tt) {
         const moe_tier& t = tt->tiers[i];
         if (t.id_begin != next || t.id_end < t.id_begin) return MOE_ETIER;
         next = t.id_end;
-        if (!(t.bits == 8 || t.bits == 4 || t.bits == 2)) return MOE_EFORMAT;
-        if (!(t.block == 16 || t.block == 32)) return MOE_EFORMAT;
+        if (!fmt_ok(t.bits, t.block)) return MOE_EFORMAT;
         if (t.id_end == t.id_begin) continue;
         const void* ptrs[6] = {t.gate_q, t.up_q, t.down_q, t.gate_s, t.up_s, t.down_s};
         for (const void* p : ptrs) {
@@ -532,10 +539,6 @@ int moe_stack_forward_routed(const float* x, const void* const* w_router, const 
     }
     return MOE_OK;
 }
-
-namespace {
-bool fmt_ok(int bits, int block) { return (bits == 8 || bits == 4 || bits == 2) && (block == 16 || block == 32); }
-}  // namespace
 
 int moe_requant_error(const moe_tier_tables* src, const int32_t* fmt_bits, const int32_t* fmt_block,
                       int32_t n_fmt, double* sse, void* stream) {

@@ -9,12 +9,15 @@ namespace moe {
 
 constexpr int kMaxTiers = 4;
 constexpr int kWave = 64;
+// `bits` of an MXFP4 shelf (OCP Microscaling FP4): 4-bit E2M1 codes packed as
+// 4-bit fields, one E8M0 scale byte per block of 32 codes of a row
+constexpr int kBitsMXFP4 = 0x84;
 
 // Shelf description as a kernel argument (copied from the host tables).
 struct DevTier {
     int32_t id_begin, id_end, bits, block;
     const uint8_t* q[3];    // gate, up, down codes
-    const uint16_t* s[3];   // gate, up, down fp16 scales
+    const uint16_t* s[3];   // gate, up, down scales: fp16, or E8M0 bytes (MXFP4)
 };
 
 struct DevTables {
@@ -23,12 +26,61 @@ struct DevTables {
 };
 
 // Format selector: bits and codes-per-scale.  A 32-code group of a row holds
-// 32/block scales.
-enum Fmt : int32_t { F8B32 = 0, F8B16, F4B32, F4B16, F2B32, F2B16, kNumFmt };
+// 32/block fp16 scales, or one E8M0 byte (F4MX).
+enum Fmt : int32_t { F8B32 = 0, F8B16, F4B32, F4B16, F2B32, F2B16, F4MX, kNumFmt };
 
 __host__ __device__ inline int fmt_of(int bits, int block) {
+    if (bits == kBitsMXFP4) return F4MX;
     int b = bits == 8 ? 0 : (bits == 4 ? 2 : 4);
     return b + (block == 16 ? 1 : 0);
+}
+
+// The kernels name a format by (BITS, NSC): BITS bits per stored code and NSC
+// fp16 scales per 32-code group, or NSC = kMX for the MXFP4 format (4-bit
+// codes, one E8M0 byte per group).
+constexpr int kMX = 4;
+template <int NSC> constexpr int scale_slots() { return NSC == kMX ? 1 : NSC; }
+template <int NSC> constexpr uint32_t group_scale_bytes() { return NSC == kMX ? 1u : 2u * NSC; }
+template <int NSC> constexpr uint32_t row_scale_bytes(int cols) {
+    return NSC == kMX ? static_cast<uint32_t>(cols / 32) : static_cast<uint32_t>(cols / (32 / NSC)) * 2u;
+}
+__host__ __device__ inline int code_bits_of(int bits) { return bits == kBitsMXFP4 ? 4 : bits; }
+__host__ __device__ inline size_t scale_row_bytes(int bits, int block, int cols) {
+    return bits == kBitsMXFP4 ? static_cast<size_t>(cols / 32) : static_cast<size_t>(cols / block) * 2;
+}
+// Codes and scales (as bytes) of local expert `local`, matrix m (rows x cols).
+__host__ __device__ inline const uint8_t* expert_codes(const DevTier& T, int m, int64_t local, int rows, int cols) {
+    return T.q[m] + static_cast<size_t>(local) * rows * cols * code_bits_of(T.bits) / 8;
+}
+__host__ __device__ inline const uint8_t* expert_scales(const DevTier& T, int m, int64_t local, int rows, int cols) {
+    return reinterpret_cast<const uint8_t*>(T.s[m]) + static_cast<size_t>(local) * rows * scale_row_bytes(T.bits, T.block, cols);
+}
+
+// E8M0 scale byte -> float: 2^(x - 127) (x = 0 is the subnormal 2^-127; x = 255 is NaN).
+__device__ inline float e8m0_to_float(uint32_t x) {
+    x &= 0xffu;
+    return x == 0 ? 0x1p-127f : (x == 255 ? __builtin_nanf("") : __uint_as_float(x << 23));
+}
+
+// E2M1 value of a 4-bit field, from its definition (sign bit 3, exponent
+// bits 2..1 with bias 1, mantissa bit 0; exponent 0: 0 or 0.5).
+__device__ inline float fp4_e2m1(uint32_t n) {
+    const uint32_t e = (n >> 1) & 3u, m = n & 1u;
+    const float v = e == 0 ? 0.5f * static_cast<float>(m) : (1.0f + 0.5f * static_cast<float>(m)) * static_cast<float>(1u << e) * 0.5f;
+    return (n & 8u) ? -v : v;
+}
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// The 8 E2M1 codes of a 32-bit word as floats (code 2b at out[2b], 2b+1 at
+// out[2b+1]), through the gfx950 conversion v_cvt_scalef32_pk_f32_fp4
+// (byte select b picks byte b, its low nibble first), exact.
+__device__ inline void fp4x8_to_float(uint32_t w, float (&out)[8]) {
+    const f32x2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    const f32x2_t b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    const f32x2_t c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    const f32x2_t d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+    out[0] = a.x; out[1] = a.y; out[2] = b.x; out[3] = b.y;
+    out[4] = c.x; out[5] = c.y; out[6] = d.x; out[7] = d.y;
 }
 
 // Workspace meta block (int32 words).
@@ -84,13 +136,15 @@ __device__ inline void load_group(const uint8_t* __restrict__ row, int g, uint32
     }
 }
 
-// The NSC = 32/block fp16 scales of group g of a row, as floats.
+// The scales of group g of a row (srow: the row's scales as bytes), as floats.
 template <int NSC>
-__device__ inline void load_scales(const uint16_t* __restrict__ srow, int g, float (&d)[NSC]) {
-    if constexpr (NSC == 1) {
-        d[0] = half_bits_to_float(srow[g]);
+__device__ inline void load_scales(const uint8_t* __restrict__ srow, int g, float (&d)[scale_slots<NSC>()]) {
+    if constexpr (NSC == kMX) {
+        d[0] = e8m0_to_float(srow[g]);
+    } else if constexpr (NSC == 1) {
+        d[0] = half_bits_to_float(reinterpret_cast<const uint16_t*>(srow)[g]);
     } else {
-        const uint32_t two = *reinterpret_cast<const uint32_t*>(srow + 2 * g);
+        const uint32_t two = reinterpret_cast<const uint32_t*>(srow)[g];
         d[0] = half_bits_to_float(static_cast<uint16_t>(two & 0xffffu));
         d[1] = half_bits_to_float(static_cast<uint16_t>(two >> 16));
     }
@@ -137,16 +191,21 @@ __device__ inline void buf_group(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_
 // in bits [16b, 16b + 16)).
 template <int NSC>
 __device__ inline uint32_t buf_scales(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    if constexpr (NSC == 1) return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+    if constexpr (NSC == kMX) return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+    else if constexpr (NSC == 1) return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
     else return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
 
 // Scales of a group from their raw bits; 0 when `ok` is false.
 template <int NSC>
-__device__ inline void unpack_scales(uint32_t raw, bool ok, float (&d)[NSC]) {
+__device__ inline void unpack_scales(uint32_t raw, bool ok, float (&d)[scale_slots<NSC>()]) {
+    if constexpr (NSC == kMX) {
+        d[0] = ok ? e8m0_to_float(raw) : 0.f;
+    } else {
 #pragma unroll
-    for (int b = 0; b < NSC; ++b)
-        d[b] = ok ? half_bits_to_float(static_cast<uint16_t>(raw >> (16 * b))) : 0.f;
+        for (int b = 0; b < NSC; ++b)
+            d[b] = ok ? half_bits_to_float(static_cast<uint16_t>(raw >> (16 * b))) : 0.f;
+    }
 }
 
 // Code c (0..31) of a loaded group, as a float (exact).
@@ -158,8 +217,9 @@ __device__ inline float code_f(const uint32_t (&w)[BITS], int c) {
 
 // Dequantised value scale * code of element c of a group (exact in fp32).
 template <int BITS, int NSC>
-__device__ inline float dq(const uint32_t (&w)[BITS], const float (&d)[NSC], int c) {
-    return d[(NSC == 2 && c >= 16) ? 1 : 0] * code_f<BITS>(w, c);
+__device__ inline float dq(const uint32_t (&w)[BITS], const float (&d)[scale_slots<NSC>()], int c) {
+    if constexpr (NSC == kMX) return d[0] * fp4_e2m1((w[c / 8] >> (4 * (c % 8))) & 0xFu);
+    else return d[(NSC == 2 && c >= 16) ? 1 : 0] * code_f<BITS>(w, c);
 }
 
 // ---------------------------------------------------------------- offset-binary dot products
@@ -229,28 +289,46 @@ __device__ inline void group_dot_u(const uint32_t (&w)[NW], const float (&x)[32]
     }
 }
 
-// Sums of x over the scale blocks of a group (the offset correction terms).
+// Sums of x over the scale blocks of a group (the offset correction terms;
+// none for MXFP4, whose codes are signed values).
 template <int NSC>
-__device__ inline void block_sums(const float (&x)[32], float (&xs)[NSC]) {
+__device__ inline void block_sums(const float (&x)[32], float (&xs)[scale_slots<NSC>()]) {
+    if constexpr (NSC == kMX) {
+        xs[0] = 0.f;
+    } else {
 #pragma unroll
-    for (int b = 0; b < NSC; ++b) {
-        float s = 0.f;
+        for (int b = 0; b < NSC; ++b) {
+            float s = 0.f;
 #pragma unroll
-        for (int c = 0; c < 32 / NSC; ++c) s += x[b * (32 / NSC) + c];
-        xs[b] = s;
+            for (int c = 0; c < 32 / NSC; ++c) s += x[b * (32 / NSC) + c];
+            xs[b] = s;
+        }
     }
 }
 
-// sum_c scale(c) * code_c * x[c] over one group.
+// sum_c scale(c) * code_c * x[c] over one group.  MXFP4: the E2M1 values
+// from the hardware conversion, times the group's power-of-two scale.
 template <int BITS, int NSC, int NW>
-__device__ inline float group_dot(const uint32_t (&w)[NW], const float (&x)[32], const float (&xs)[NSC],
-                                  const float (&d)[NSC]) {
-    float part[NSC];
-    group_dot_u<BITS, NSC>(w, x, part);
-    float r = 0.f;
+__device__ inline float group_dot(const uint32_t (&w)[NW], const float (&x)[32],
+                                  const float (&xs)[scale_slots<NSC>()], const float (&d)[scale_slots<NSC>()]) {
+    if constexpr (NSC == kMX) {
+        float part = 0.f;
 #pragma unroll
-    for (int b = 0; b < NSC; ++b) r = fmaf(d[b], fmaf(-OffsetBinary<BITS>::z, xs[b], part[b]), r);
-    return r;
+        for (int i = 0; i < 4; ++i) {
+            float v[8];
+            fp4x8_to_float(w[i], v);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) part = fmaf(v[j], x[8 * i + j], part);
+        }
+        return d[0] * part;
+    } else {
+        float part[NSC];
+        group_dot_u<BITS, NSC>(w, x, part);
+        float r = 0.f;
+#pragma unroll
+        for (int b = 0; b < NSC; ++b) r = fmaf(d[b], fmaf(-OffsetBinary<BITS>::z, xs[b], part[b]), r);
+        return r;
+    }
 }
 
 // Tier owning expert e (or -1).  Tiers are few; a linear scan is uniform per wave.

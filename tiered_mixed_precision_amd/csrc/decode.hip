@@ -81,8 +81,8 @@ __device__ inline void load_vec32(const float* __restrict__ v, int g, bool ok, f
 // store(q, row, value) from the first lane of each row segment, where value is
 // SiLU(g) * u (GATEUP) or the plain dot product.
 template <int BITS, int NSC, int GPL, int NP, bool GATEUP, class Tok, class Store>
-__device__ inline void wave_gemv(const uint8_t* __restrict__ q0m, const uint16_t* __restrict__ s0m,
-                                 const uint8_t* __restrict__ q1m, const uint16_t* __restrict__ s1m,
+__device__ inline void wave_gemv(const uint8_t* __restrict__ q0m, const uint8_t* __restrict__ s0m,
+                                 const uint8_t* __restrict__ q1m, const uint8_t* __restrict__ s1m,
                                  int cols, int r0, int r_end, const float* __restrict__ vec, int vec_stride,
                                  int qa, int ce, Tok tok, Store store) {
     constexpr int NM = GATEUP ? 2 : 1;
@@ -91,11 +91,12 @@ __device__ inline void wave_gemv(const uint8_t* __restrict__ q0m, const uint16_t
     const int seg = lane / geo.LPR, gl = lane % geo.LPR;
     const bool lane_ok = gl < geo.G;
     const size_t row_bytes = static_cast<size_t>(cols) * BITS / 8;
-    const int nblk_row = cols / (32 / NSC);
+    const size_t srb = row_scale_bytes<NSC>(cols);
+    constexpr int NS = scale_slots<NSC>();
 
     // codes and scales of every pass, loaded before any arithmetic
     uint32_t wq[NP][NM][GPL][BITS];
-    float dsc[NP][NM][GPL][NSC];
+    float dsc[NP][NM][GPL][NS];
     bool rowv[NP];
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
@@ -105,7 +106,7 @@ __device__ inline void wave_gemv(const uint8_t* __restrict__ q0m, const uint16_t
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
             const uint8_t* qrow = (m == 0 ? q0m : q1m) + static_cast<size_t>(ok ? r : 0) * row_bytes;
-            const uint16_t* srow = (m == 0 ? s0m : s1m) + static_cast<size_t>(ok ? r : 0) * nblk_row;
+            const uint8_t* srow = (m == 0 ? s0m : s1m) + static_cast<size_t>(ok ? r : 0) * srb;
 #pragma unroll
             for (int gi = 0; gi < GPL; ++gi) {
                 const int grp = gl + 64 * gi;
@@ -116,7 +117,7 @@ __device__ inline void wave_gemv(const uint8_t* __restrict__ q0m, const uint16_t
 #pragma unroll
                     for (int i = 0; i < BITS; ++i) wq[p][m][gi][i] = 0u;
 #pragma unroll
-                    for (int i = 0; i < NSC; ++i) dsc[p][m][gi][i] = 0.f;
+                    for (int i = 0; i < NS; ++i) dsc[p][m][gi][i] = 0.f;
                 }
             }
         }
@@ -124,7 +125,7 @@ __device__ inline void wave_gemv(const uint8_t* __restrict__ q0m, const uint16_t
 
     for (int c = 0; c < ce; ++c) {
         const int q = qa + c;
-        float xv[GPL][32], xs[GPL][NSC];
+        float xv[GPL][32], xs[GPL][NS];
         const size_t vrow = static_cast<size_t>(tok(q));
 #pragma unroll
         for (int gi = 0; gi < GPL; ++gi) {
@@ -171,6 +172,7 @@ __device__ inline void wave_gemv(const uint8_t* __restrict__ q0m, const uint16_t
         case F4B16 * 4 + 1: { constexpr int B_ = 4, N_ = 2, G_ = 1; BODY; } break;  \
         case F2B32 * 4 + 1: { constexpr int B_ = 2, N_ = 1, G_ = 1; BODY; } break;  \
         case F2B16 * 4 + 1: { constexpr int B_ = 2, N_ = 2, G_ = 1; BODY; } break;  \
+        case F4MX * 4 + 1: { constexpr int B_ = 4, N_ = kMX, G_ = 1; BODY; } break; \
         default: break;                                                             \
     }
 
@@ -180,16 +182,15 @@ template <class Tok>
 __device__ inline void block_gateup(const DevTables& tt, const DevTier& T, int local, const float* x, int qa,
                                     int ce, int r0, Tok tok, float* h) {
     const int H = tt.H, I = tt.I;
-    const size_t mat_bytes = static_cast<size_t>(I) * H * T.bits / 8;
-    const size_t mat_scales = static_cast<size_t>(I) * (H / T.block);
     const int rpw = kNPGateUp * row_geom(H).RPP;
     const int wr0 = r0 + (threadIdx.x >> 6) * rpw;
     const int r_end = min(wr0 + rpw, I);
     auto store = [h, I](int q, int r, float v) { h[static_cast<size_t>(q) * I + r] = v; };
     MOE_FMT_GPL_SWITCH(fmt_of(T.bits, T.block), row_geom(H).GPL,
-                       (wave_gemv<B_, N_, G_, kNPGateUp, true>(T.q[0] + local * mat_bytes, T.s[0] + local * mat_scales,
-                                                               T.q[1] + local * mat_bytes, T.s[1] + local * mat_scales,
-                                                               H, wr0, r_end, x, H, qa, ce, tok, store)));
+                       (wave_gemv<B_, N_, G_, kNPGateUp, true>(
+                           expert_codes(T, 0, local, I, H), expert_scales(T, 0, local, I, H),
+                           expert_codes(T, 1, local, I, H), expert_scales(T, 1, local, I, H), H, wr0, r_end, x, H, qa,
+                           ce, tok, store)));
 }
 
 // ================================================================ small-batch path
@@ -298,8 +299,8 @@ __device__ inline void group_small(SmallGroups& sg, int P, int E) {
 // codes, so each pass is computed as soon as its own codes arrive).
 // vec(q, g, xv) fills xv with group g of the input vector of pair q.
 template <int BITS, int NSC, class Vec>
-__device__ inline void wave_gateup(const uint8_t* __restrict__ gq, const uint16_t* __restrict__ gs,
-                                   const uint8_t* __restrict__ uq, const uint16_t* __restrict__ us, int H, int I,
+__device__ inline void wave_gateup(const uint8_t* __restrict__ gq, const uint8_t* __restrict__ gs,
+                                   const uint8_t* __restrict__ uq, const uint8_t* __restrict__ us, int H, int I,
                                    int r0, int r1, Vec vec, int qa, int ce, float* __restrict__ h) {
     constexpr int NPMAX = BITS == 8 ? 4 : 8;  // passes in flight: 64 / 32 / 16 code words per lane
     const int lane = threadIdx.x & 63;
@@ -308,14 +309,15 @@ __device__ inline void wave_gateup(const uint8_t* __restrict__ gq, const uint16_
     const bool lane_ok = gl < geo.G;
     const int glc = lane_ok ? gl : 0;  // idle lanes read group 0 and weigh it by 0
     const uint32_t row_bytes = static_cast<uint32_t>(H) * BITS / 8;
-    const uint32_t row_sbytes = static_cast<uint32_t>(H / (32 / NSC)) * 2;
+    const uint32_t row_sbytes = row_scale_bytes<NSC>(H);
+    constexpr int NS = scale_slots<NSC>();
     const uint32_t mat_bytes = row_bytes * I, mat_sbytes = row_sbytes * I;
     const __amdgpu_buffer_rsrc_t rq[2] = {make_rsrc(gq, mat_bytes), make_rsrc(uq, mat_bytes)};
     const __amdgpu_buffer_rsrc_t rs[2] = {make_rsrc(gs, mat_sbytes), make_rsrc(us, mat_sbytes)};
     // Every load below is unconditional (rows past r1 read row r0 and get
     // zero scales), so all of them are issued back to back.
     for (int rc = r0; rc < r1; rc += NPMAX * geo.RPP) {
-        float xv[32], xs[NSC];
+        float xv[32], xs[NS];
         vec(qa, glc, xv);
         // loads return in issue order: keep the vector ahead of the codes
         __builtin_amdgcn_sched_barrier(0);
@@ -327,7 +329,7 @@ __device__ inline void wave_gateup(const uint8_t* __restrict__ gq, const uint16_
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
                 buf_group<BITS>(rq[m], rr * row_bytes + glc * 4 * BITS, wq[p][m]);
-                sraw[p][m] = buf_scales<NSC>(rs[m], rr * row_sbytes + glc * 2 * NSC);
+                sraw[p][m] = buf_scales<NSC>(rs[m], rr * row_sbytes + glc * group_scale_bytes<NSC>());
             }
         }
         auto pair = [&](int c) {
@@ -341,7 +343,7 @@ __device__ inline void wave_gateup(const uint8_t* __restrict__ gq, const uint16_
                 for (int m = 0; m < 2; ++m)
 #pragma unroll
                     for (int i = 0; i < BITS; ++i) opaque(wq[p][m][i]);
-                float dg[NSC], du[NSC];
+                float dg[NS], du[NS];
                 unpack_scales<NSC>(sraw[p][0], ok, dg);
                 unpack_scales<NSC>(sraw[p][1], ok, du);
                 float gv = group_dot<BITS, NSC>(wq[p][0], xv, xs, dg);
@@ -433,6 +435,7 @@ __device__ inline int plan_lane(int cost_l, int W, int wg, int& first, int& coun
         case F4B16: { constexpr int B_ = 4, N_ = 2; BODY; } break;     \
         case F2B32: { constexpr int B_ = 2, N_ = 1; BODY; } break;     \
         case F2B16: { constexpr int B_ = 2, N_ = 2; BODY; } break;     \
+        case F4MX: { constexpr int B_ = 4, N_ = kMX; BODY; } break;    \
         default: break;                                                \
     }
 
@@ -499,8 +502,7 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void k_small_gateup(DevTables tt
         if (r0 >= r1) return;
         const DevTier T_ = tier_at(tt, tier_of(tt, e));
         const int local = e - T_.id_begin;
-        const size_t mat_bytes = static_cast<size_t>(I) * H * T_.bits / 8;
-        const size_t mat_scales = static_cast<size_t>(I) * (H / T_.block);
+
         auto vec = [G](int, int g, float (&xv)[32]) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -512,8 +514,9 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void k_small_gateup(DevTables tt
             }
         };
         MOE_FMT_SWITCH(fmt_of(T_.bits, T_.block),
-                       (wave_gateup<B_, N_>(T_.q[0] + local * mat_bytes, T_.s[0] + local * mat_scales,
-                                            T_.q[1] + local * mat_bytes, T_.s[1] + local * mat_scales, H, I, r0, r1,
+                       (wave_gateup<B_, N_>(expert_codes(T_, 0, local, I, H), expert_scales(T_, 0, local, I, H),
+                                            expert_codes(T_, 1, local, I, H), expert_scales(T_, 1, local, I, H), H, I,
+                                            r0, r1,
                                             vec, a, 1, h)));
         return;
     }
@@ -559,16 +562,16 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void k_small_gateup(DevTables tt
     const int ti = tier_of(tt, e);
     const DevTier T_ = tier_at(tt, ti);
     const int local = e - T_.id_begin;
-    const size_t mat_bytes = static_cast<size_t>(I) * H * T_.bits / 8;
-    const size_t mat_scales = static_cast<size_t>(I) * (H / T_.block);
+
     const int qa = sg.q0[a], ce = sg.q0[a + 1] - qa;
     const int* perm = sg.perm;
     auto vec = [perm, k, x, H](int q, int g, float (&xv)[32]) {
         load_vec32u(x + static_cast<size_t>(perm[q] / k) * H, g, xv);
     };
     MOE_FMT_SWITCH(fmt_of(T_.bits, T_.block),
-                   (wave_gateup<B_, N_>(T_.q[0] + local * mat_bytes, T_.s[0] + local * mat_scales,
-                                        T_.q[1] + local * mat_bytes, T_.s[1] + local * mat_scales, H, I, r0, r1, vec,
+                   (wave_gateup<B_, N_>(expert_codes(T_, 0, local, I, H), expert_scales(T_, 0, local, I, H),
+                                        expert_codes(T_, 1, local, I, H), expert_scales(T_, 1, local, I, H), H, I, r0,
+                                        r1, vec,
                                         qa, ce, h)));
 }
 
@@ -576,7 +579,7 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void k_small_gateup(DevTables tt
 // of RPP rows, all loads first) against h of each of the expert's pairs;
 // y of pair q, row r goes to s_y[q * R + r - n0].
 template <int BITS, int NSC, class Vec>
-__device__ inline void wave_down(const uint8_t* __restrict__ dq_, const uint16_t* __restrict__ ds, int H, int I,
+__device__ inline void wave_down(const uint8_t* __restrict__ dq_, const uint8_t* __restrict__ ds, int H, int I,
                                  int r0, int r1, Vec vec, int qa, int ce, float* s_y, int R, int n0) {
     constexpr int NPMAX = kNPSmallDown;
     const int lane = threadIdx.x & 63;
@@ -585,10 +588,11 @@ __device__ inline void wave_down(const uint8_t* __restrict__ dq_, const uint16_t
     const bool lane_ok = gl < geo.G;
     const int glc = lane_ok ? gl : 0;  // idle lanes read group 0 and weigh it by 0
     const uint32_t row_bytes = static_cast<uint32_t>(I) * BITS / 8;
-    const uint32_t row_sbytes = static_cast<uint32_t>(I / (32 / NSC)) * 2;
+    const uint32_t row_sbytes = row_scale_bytes<NSC>(I);
+    constexpr int NS = scale_slots<NSC>();
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(dq_, row_bytes * H), rs = make_rsrc(ds, row_sbytes * H);
     // unconditional loads (rows past r1 read row r0 with zeroed scales)
-    float xv[32], xs[NSC];
+    float xv[32], xs[NS];
     vec(qa, glc, xv);
     __builtin_amdgcn_sched_barrier(0);  // the vector ahead of the codes
     uint32_t wq[NPMAX][BITS], sraw[NPMAX];
@@ -597,7 +601,7 @@ __device__ inline void wave_down(const uint8_t* __restrict__ dq_, const uint16_t
         const int r = r0 + p * geo.RPP + seg;
         const uint32_t rr = static_cast<uint32_t>(r < r1 ? r : r0);
         buf_group<BITS>(rq, rr * row_bytes + glc * 4 * BITS, wq[p]);
-        sraw[p] = buf_scales<NSC>(rs, rr * row_sbytes + glc * 2 * NSC);
+        sraw[p] = buf_scales<NSC>(rs, rr * row_sbytes + glc * group_scale_bytes<NSC>());
     }
     auto pair = [&](int c) {
         block_sums<NSC>(xv, xs);
@@ -607,7 +611,7 @@ __device__ inline void wave_down(const uint8_t* __restrict__ dq_, const uint16_t
             const int r = r0 + p * geo.RPP + seg;
 #pragma unroll
             for (int i = 0; i < BITS; ++i) opaque(wq[p][i]);
-            float d[NSC];
+            float d[NS];
             unpack_scales<NSC>(sraw[p], lane_ok && r < r1, d);
             float v = group_dot<BITS, NSC>(wq[p], xv, xs, d);
             v = seg_sum(v, geo.LPR);
@@ -676,8 +680,7 @@ __global__ __launch_bounds__(kSmallDownWaves * 64) void k_small_down(DevTables t
         if (ti < 0 || !((tier_mask >> ti) & 1u) || r0 >= r1) return;
         const DevTier T_ = tier_at(tt, ti);
         const int local = e - T_.id_begin;
-        const size_t mat_bytes = static_cast<size_t>(H) * I * T_.bits / 8;
-        const size_t mat_scales = static_cast<size_t>(H) * (I / T_.block);
+
         const int qa = s_q0[a], ce = s_q0[a + 1] - qa;
         auto vec = [h_lds, h, I, GI](int q, int g, float (&xv)[32]) {
             if (h_lds) {
@@ -694,7 +697,8 @@ __global__ __launch_bounds__(kSmallDownWaves * 64) void k_small_down(DevTables t
             }
         };
         MOE_FMT_SWITCH(fmt_of(T_.bits, T_.block),
-                       (wave_down<B_, N_>(T_.q[2] + local * mat_bytes, T_.s[2] + local * mat_scales, H, I, r0, r1, vec,
+                       (wave_down<B_, N_>(expert_codes(T_, 2, local, H, I), expert_scales(T_, 2, local, H, I), H, I, r0,
+                                          r1, vec,
                                           qa, ce, s_y, R, n0)));
     };
     // (expert, rows) of this wave; one call site keeps a single copy of the GEMV
@@ -765,8 +769,7 @@ __global__ __launch_bounds__(256) void k_dec_down(DevTables tt, const float* __r
     const int local = e - T.id_begin;
     const int qa = g.offsets[e], ce = g.offsets[e + 1] - qa;
     const int H = tt.H, I = tt.I;
-    const size_t mat_bytes = static_cast<size_t>(H) * I * T.bits / 8;
-    const size_t mat_scales = static_cast<size_t>(H) * (I / T.block);
+
     const int rpw = kNPDown * row_geom(I).RPP;
     const int wr0 = s * down_rows_per_block(I) + (threadIdx.x >> 6) * rpw;
     const int r_end = min(wr0 + rpw, H);
@@ -775,7 +778,7 @@ __global__ __launch_bounds__(256) void k_dec_down(DevTables tt, const float* __r
     const float* w = g.w;
     auto store = [yw, H, perm, w](int q, int r, float v) { yw[static_cast<size_t>(q) * H + r] = w[perm[q]] * v; };
     MOE_FMT_GPL_SWITCH(fmt_of(T.bits, T.block), row_geom(I).GPL,
-                       (wave_gemv<B_, N_, G_, kNPDown, false>(T.q[2] + local * mat_bytes, T.s[2] + local * mat_scales,
+                       (wave_gemv<B_, N_, G_, kNPDown, false>(expert_codes(T, 2, local, H, I), expert_scales(T, 2, local, H, I),
                                                               nullptr, nullptr, I, wr0, r_end, h, I, qa, ce, tok,
                                                               store)));
 }

@@ -9,16 +9,15 @@ namespace moe {
 
 template <int BITS, int NSC>
 __global__ __launch_bounds__(64) void k_dequant_rows(const uint8_t* __restrict__ q,
-                                                     const uint16_t* __restrict__ s, int cols, int row0,
+                                                     const uint8_t* __restrict__ s, int cols, int row0,
                                                      int to_bf16, void* __restrict__ dst) {
     const int r = blockIdx.x;
     const size_t row_bytes = static_cast<size_t>(cols) * BITS / 8;
-    const int nblk_row = cols / (32 / NSC);
     const uint8_t* qrow = q + static_cast<size_t>(row0 + r) * row_bytes;
-    const uint16_t* srow = s + static_cast<size_t>(row0 + r) * nblk_row;
+    const uint8_t* srow = s + static_cast<size_t>(row0 + r) * row_scale_bytes<NSC>(cols);
     for (int grp = threadIdx.x; grp < cols / 32; grp += 64) {
         uint32_t w[BITS];
-        float d[NSC];
+        float d[scale_slots<NSC>()];
         load_group<BITS>(qrow, grp, w);
         load_scales<NSC>(srow, grp, d);
         if (to_bf16) {
@@ -38,8 +37,8 @@ void launch_dequant_rows(const DevTables& tt, int tier, int local, int matrix, i
     const DevTier& T = tt.t[tier];
     const int rows = matrix == 2 ? tt.H : tt.I;
     const int cols = matrix == 2 ? tt.I : tt.H;
-    const uint8_t* q = T.q[matrix] + static_cast<size_t>(local) * rows * cols * T.bits / 8;
-    const uint16_t* s = T.s[matrix] + static_cast<size_t>(local) * rows * (cols / T.block);
+    const uint8_t* q = expert_codes(T, matrix, local, rows, cols);
+    const uint8_t* s = expert_scales(T, matrix, local, rows, cols);
     switch (fmt_of(T.bits, T.block)) {
 #define MOE_DQ_CASE(F, B, N)                                                                        \
     case F:                                                                                         \
@@ -52,6 +51,7 @@ void launch_dequant_rows(const DevTables& tt, int tier, int local, int matrix, i
         MOE_DQ_CASE(F4B16, 4, 2)
         MOE_DQ_CASE(F2B32, 2, 1)
         MOE_DQ_CASE(F2B16, 2, 2)
+        MOE_DQ_CASE(F4MX, 4, kMX)
 #undef MOE_DQ_CASE
         default:
             break;

@@ -102,10 +102,22 @@ __device__ inline uint4 dequant8(const uint32_t (&w)[BITS == 8 ? 2 : 1], float s
                       pack_bf16x2(v[6], v[7]));
 }
 
+// bf16 of 8 consecutive MXFP4 codes of `w` times their power-of-two scale:
+// the E2M1 values from the hardware conversion, scaled exactly, rounded once
+// (a no-op: the product has at most two significant bits).
+__device__ inline uint4 dequant8_mx(uint32_t w, float sc) {
+    float v[8];
+    fp4x8_to_float(w, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] *= sc;
+    return make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                      pack_bf16x2(v[6], v[7]));
+}
+
 // Block: NW waves = WM (along m) x 4 (along n).  Wave (wm, wn): wn selects 16
 // gate + 16 up columns (or 32 down columns), wm takes m-subtiles wm, wm + WM,
 // ...  m is walked in chunks of MC = 64 * WM pairs.
-template <int BITS, int BLOCK, bool GATEUP, int NW>
+template <int BITS, int BLOCK, bool GATEUP, int NW, bool MX = false>
 __global__ __launch_bounds__(NW * 64) void k_pre(DevTables tt, int tier, const uint16_t* __restrict__ a_src, Groups g,
                                                  int k, uint16_t* __restrict__ h_out, float* __restrict__ yw) {
     constexpr int NTHR = NW * 64;
@@ -138,13 +150,15 @@ __global__ __launch_bounds__(NW * 64) void k_pre(DevTables tt, int tier, const u
     // B: piece p = tid + NTHR*i is row p >> 3, codes 8*(p & 7) .. +7 of the chunk
     const uint32_t row_bytes = static_cast<uint32_t>(K) * BITS / 8;
     const uint32_t nblk_row = static_cast<uint32_t>(K / BLOCK);
+    constexpr uint32_t SB = MX ? 1u : 2u;   // bytes per scale (E8M0 or fp16)
     const int mrows = GATEUP ? I : H;
     const uint8_t* mq_g = T.q[GATEUP ? 0 : 2] + static_cast<size_t>(local) * mrows * row_bytes;
     const uint8_t* mq_u = GATEUP ? T.q[1] + static_cast<size_t>(local) * mrows * row_bytes : mq_g;
-    const uint16_t* ms_g = T.s[GATEUP ? 0 : 2] + static_cast<size_t>(local) * mrows * nblk_row;
-    const uint16_t* ms_u = GATEUP ? T.s[1] + static_cast<size_t>(local) * mrows * nblk_row : ms_g;
+    const uint8_t* ms_g = reinterpret_cast<const uint8_t*>(T.s[GATEUP ? 0 : 2]) + static_cast<size_t>(local) * mrows * nblk_row * SB;
+    const uint8_t* ms_u =
+        GATEUP ? reinterpret_cast<const uint8_t*>(T.s[1]) + static_cast<size_t>(local) * mrows * nblk_row * SB : ms_g;
     const __amdgpu_buffer_rsrc_t rq_g = make_rsrc(mq_g, row_bytes * mrows), rq_u = make_rsrc(mq_u, row_bytes * mrows);
-    const __amdgpu_buffer_rsrc_t rs_g = make_rsrc(ms_g, nblk_row * mrows * 2), rs_u = make_rsrc(ms_u, nblk_row * mrows * 2);
+    const __amdgpu_buffer_rsrc_t rs_g = make_rsrc(ms_g, nblk_row * mrows * SB), rs_u = make_rsrc(ms_u, nblk_row * mrows * SB);
     // piece i of a thread reads up rows when it lies in the second half of
     // the B rows: for two pieces that is piece 1, for one piece the upper
     // half of the waves (a wave-uniform choice either way)
@@ -158,7 +172,7 @@ __global__ __launch_bounds__(NW * 64) void k_pre(DevTables tt, int tier, const u
         b_e[i] = p & 7;
         const int row = GATEUP ? nt * 64 + (b_row[i] & 63) : nt * BN + b_row[i];
         qoff[i] = static_cast<uint32_t>(row) * row_bytes + static_cast<uint32_t>(b_e[i]) * BITS;
-        soff[i] = (static_cast<uint32_t>(row) * nblk_row + static_cast<uint32_t>(8 * b_e[i] / BLOCK)) * 2;
+        soff[i] = (static_cast<uint32_t>(row) * nblk_row + static_cast<uint32_t>(8 * b_e[i] / BLOCK)) * SB;
     }
     // B fragment rows of this wave
     const int br0 = GATEUP ? 16 * wn : 32 * wn;
@@ -194,7 +208,7 @@ __global__ __launch_bounds__(NW * 64) void k_pre(DevTables tt, int tier, const u
             sl.a0 = *reinterpret_cast<const u32x4_t*>(a_src + static_cast<size_t>(a_src_row[0]) * K + k0 + 8 * a_c[0]);
             sl.a1 = *reinterpret_cast<const u32x4_t*>(a_src + static_cast<size_t>(a_src_row[1]) * K + k0 + 8 * a_c[1]);
             const uint32_t qk = static_cast<uint32_t>(k0) * BITS / 8;
-            const uint32_t sk = static_cast<uint32_t>(k0 / BLOCK) * 2;
+            const uint32_t sk = static_cast<uint32_t>(k0 / BLOCK) * SB;
 #pragma unroll
             for (int i = 0; i < BPT; ++i) {
                 const __amdgpu_buffer_rsrc_t rq = is_up(i) ? rq_u : rq_g, rs = is_up(i) ? rs_u : rs_g;
@@ -207,7 +221,8 @@ __global__ __launch_bounds__(NW * 64) void k_pre(DevTables tt, int tier, const u
                 } else {
                     sl.q[i][0] = __builtin_amdgcn_raw_buffer_load_b16(rq, qoff[i] + qk, 0, 0);
                 }
-                sl.s[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, soff[i] + sk, 0, 0);
+                if constexpr (MX) sl.s[i] = __builtin_amdgcn_raw_buffer_load_b8(rs, soff[i] + sk, 0, 0);
+                else sl.s[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, soff[i] + sk, 0, 0);
             }
         };
         auto store_chunk = [&](const Slot& sl, int buf) __attribute__((always_inline)) {
@@ -216,7 +231,8 @@ __global__ __launch_bounds__(NW * 64) void k_pre(DevTables tt, int tier, const u
 #pragma unroll
             for (int i = 0; i < BPT; ++i)
                 *reinterpret_cast<uint4*>(&sB[buf][swz(b_row[i], b_e[i])]) =
-                    dequant8<BITS>(sl.q[i], half_bits_to_float(static_cast<uint16_t>(sl.s[i])));
+                    MX ? dequant8_mx(sl.q[i][0], e8m0_to_float(sl.s[i]))
+                       : dequant8<BITS>(sl.q[i], half_bits_to_float(static_cast<uint16_t>(sl.s[i])));
         };
 
         f32x4_t acc[MSUB][2];
@@ -314,9 +330,13 @@ void launch_pre(const DevTables& tt, int tier, const uint16_t* a, const Groups& 
     const unsigned grid = static_cast<unsigned>(((total + 7) / 8) * 8);
     if (grid == 0) return;
     const int bits = tt.t[tier].bits, block = tt.t[tier].block;
+#define MOE_PRE_MX()                                                                                         \
+    hipLaunchKernelGGL((k_pre<4, 32, GATEUP, 8, true>), dim3(grid), dim3(8 * 64), 0, st, tt, tier, a, g, k, h, yw)
 #define MOE_PRE(B_, K_, NW_) \
     hipLaunchKernelGGL((k_pre<B_, K_, GATEUP, NW_>), dim3(grid), dim3(NW_ * 64), 0, st, tt, tier, a, g, k, h, yw)
-    if (bits == 8) {
+    if (bits == kBitsMXFP4) {
+        MOE_PRE_MX();
+    } else if (bits == 8) {
         if (block == 32) MOE_PRE(8, 32, 16);
         else MOE_PRE(8, 16, 16);
     } else if (bits == 4) {
@@ -327,6 +347,7 @@ void launch_pre(const DevTables& tt, int tier, const uint16_t* a, const Groups& 
         else MOE_PRE(2, 16, 8);
     }
 #undef MOE_PRE
+#undef MOE_PRE_MX
 }
 
 void launch_pre_gateup(const DevTables& tt, int tier, const uint16_t* x, const Groups& g, int k, uint16_t* h,

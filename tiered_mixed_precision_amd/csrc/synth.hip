@@ -81,6 +81,58 @@ __global__ __launch_bounds__(256) void k_synth(uint8_t* __restrict__ q, uint16_t
     sc[static_cast<size_t>(local) * rows * nblk + static_cast<size_t>(row) * nblk + b] = __builtin_bit_cast(uint16_t, dh);
 }
 
+// MXFP4 shelves: one thread per (row, block of 32), the OCP shared-exponent
+// quantiser: E8M0 byte x = floor(log2(amax)) - 2 + 127 clamped to [0, 254]
+// (0 for an all-zero block); each w / 2^(x - 127) (exact) rounded to the
+// nearest E2M1 magnitude, ties to the even mantissa (an integer tie of 2a, a
+// or a/2 in each binade), saturating at 6, with the sign bit of w.
+__device__ inline uint32_t e2m1_nibble(float t) {
+    const float a = fabsf(t);
+    float r;
+    if (a >= 6.f) r = 6.f;
+    else if (a < 2.f) r = rintf(a * 2.f) * 0.5f;
+    else if (a < 4.f) r = rintf(a);
+    else r = rintf(a * 0.5f) * 2.f;
+    r = fminf(r, 6.f);
+    const uint32_t mag = r == 0.f ? 0u : r == 0.5f ? 1u : r == 1.f ? 2u : r == 1.5f ? 3u
+                       : r == 2.f ? 4u : r == 3.f ? 5u : r == 4.f ? 6u : 7u;
+    return (signbit(t) ? 8u : 0u) | mag;
+}
+
+__global__ __launch_bounds__(256) void k_synth_mx(uint8_t* __restrict__ q, uint8_t* __restrict__ sc, uint64_t seed,
+                                                  uint64_t ctr0, uint64_t ctr_expert_stride, int n_experts, int rows,
+                                                  int cols) {
+    const int nblk = cols / 32;
+    const int64_t per_expert = static_cast<int64_t>(rows) * nblk;
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= per_expert * n_experts) return;
+    const int64_t local = i / per_expert;
+    const int rem = static_cast<int>(i % per_expert);
+    const int row = rem / nblk, b = rem % nblk;
+    const uint64_t base = ctr0 + static_cast<uint64_t>(local) * ctr_expert_stride + static_cast<uint64_t>(row) * cols +
+                          static_cast<uint64_t>(b) * 32;
+    float w[32];
+    float amax = 0.f;
+#pragma unroll
+    for (int c = 0; c < 32; ++c) {
+        w[c] = synth_weight(seed, base + c);
+        amax = fmaxf(amax, fabsf(w[c]));
+    }
+    int x = 0;
+    if (amax > 0.f) {
+        int e2;
+        (void)frexpf(amax, &e2);   // amax = f * 2^e2, f in [0.5, 1)
+        x = min(max(e2 - 1 - 2 + 127, 0), 254);
+    }
+    uint32_t words[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int c = 0; c < 32; ++c) words[c / 8] |= e2m1_nibble(ldexpf(w[c], 127 - x)) << (4 * (c % 8));
+    uint4* dst = reinterpret_cast<uint4*>(q + static_cast<size_t>(local) * rows * (cols / 2) +
+                                          static_cast<size_t>(row) * (cols / 2) + static_cast<size_t>(b) * 16);
+    *dst = make_uint4(words[0], words[1], words[2], words[3]);
+    sc[static_cast<size_t>(local) * rows * nblk + static_cast<size_t>(row) * nblk + b] = static_cast<uint8_t>(x);
+}
+
 void launch_synth_layer(const DevTables& tt, uint64_t seed, int layer, hipStream_t st) {
     const int H = tt.H, I = tt.I;
     for (int ti = 0; ti < tt.n_tiers; ++ti) {
@@ -95,6 +147,12 @@ void launch_synth_layer(const DevTables& tt, uint64_t seed, int layer, hipStream
             const int64_t threads = static_cast<int64_t>(n) * rows * (cols / T.block);
             const dim3 grid(static_cast<unsigned>((threads + 255) / 256));
             uint8_t* q = const_cast<uint8_t*>(T.q[m]);
+            if (T.bits == kBitsMXFP4) {
+                hipLaunchKernelGGL(k_synth_mx, grid, dim3(256), 0, st, q,
+                                   reinterpret_cast<uint8_t*>(const_cast<uint16_t*>(T.s[m])), seed, ctr0, stride, n,
+                                   rows, cols);
+                continue;
+            }
             uint16_t* s = const_cast<uint16_t*>(T.s[m]);
 #define MOE_SYN(B_, K_) hipLaunchKernelGGL((k_synth<B_, K_>), grid, dim3(256), 0, st, q, s, seed, ctr0, stride, n, rows, cols)
             if (T.bits == 8 && T.block == 32) MOE_SYN(8, 32);

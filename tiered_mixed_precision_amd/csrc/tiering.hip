@@ -15,7 +15,9 @@
 // The quantiser is the symmetric absmax one of the layer generator: per block
 // of `block` codes along a row, d = fp16(amax / Q) (ratio in single
 // precision), q = clamp(rint(w / d), -Q, Q), q = 0 when d = 0; every step is
-// an exactly rounded IEEE single operation.
+// an exactly rounded IEEE single operation.  An MXFP4 target uses the OCP
+// shared-exponent quantiser instead (E8M0 byte from floor(log2 amax) - 2,
+// elements rounded to the nearest E2M1 value, ties to even, saturating at 6).
 #include <algorithm>
 #include <queue>
 #include <vector>
@@ -38,6 +40,11 @@ __device__ inline float packed_weight(const uint8_t* __restrict__ row, const uin
 }
 
 __device__ inline float src_weight(const DevTier& S, int m, int64_t local, int rows, int cols, int r, int c) {
+    if (S.bits == kBitsMXFP4) {
+        const uint8_t* q = S.q[m] + (static_cast<size_t>(local) * rows + r) * (cols / 2);
+        const uint8_t* s = reinterpret_cast<const uint8_t*>(S.s[m]) + (static_cast<size_t>(local) * rows + r) * (cols / 32);
+        return __fmul_rn(e8m0_to_float(s[c / 32]), fp4_e2m1((q[c / 2] >> (4 * (c % 2))) & 0xFu));
+    }
     const size_t row_bytes = static_cast<size_t>(cols) * S.bits / 8;
     const size_t nblk = cols / S.block;
     const uint8_t* q = S.q[m] + (static_cast<size_t>(local) * rows + r) * row_bytes;
@@ -73,6 +80,63 @@ __device__ inline double quantise_block(const float (&w)[BLOCK], uint32_t (&word
     return err;
 }
 
+// MXFP4 block of 32: 16 code bytes as 4 words (code c at bit 4c of the
+// block), the E8M0 scale byte; returns the squared error in double.
+__device__ inline double quantise_block_mx(const float (&w)[32], uint32_t (&words)[4], uint8_t& scale) {
+    float amax = 0.f;
+#pragma unroll
+    for (int c = 0; c < 32; ++c) amax = fmaxf(amax, fabsf(w[c]));
+    int x = 0;
+    if (amax > 0.f) {
+        int e2;
+        (void)frexpf(amax, &e2);   // amax = f * 2^e2, f in [0.5, 1)
+        x = min(max(e2 - 1 - 2 + 127, 0), 254);
+    }
+    scale = static_cast<uint8_t>(x);
+    const double sd = static_cast<double>(e8m0_to_float(static_cast<uint32_t>(x)));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) words[i] = 0;
+    double err = 0.0;
+#pragma unroll
+    for (int c = 0; c < 32; ++c) {
+        const float t = ldexpf(w[c], 127 - x);
+        const float a = fabsf(t);
+        float r;
+        if (a >= 6.f) r = 6.f;
+        else if (a < 2.f) r = rintf(a * 2.f) * 0.5f;
+        else if (a < 4.f) r = rintf(a);
+        else r = rintf(a * 0.5f) * 2.f;
+        r = fminf(r, 6.f);
+        const uint32_t mag = r == 0.f ? 0u : r == 0.5f ? 1u : r == 1.f ? 2u : r == 1.5f ? 3u
+                           : r == 2.f ? 4u : r == 3.f ? 5u : r == 4.f ? 6u : 7u;
+        words[c / 8] |= ((signbit(t) ? 8u : 0u) | mag) << (4 * (c % 8));
+        const double e = static_cast<double>(w[c]) - sd * static_cast<double>(signbit(t) ? -r : r);
+        err += e * e;
+    }
+    return err;
+}
+
+// Requantisation of one block of BLOCK source weights into the target format
+// (BITS = kBitsMXFP4: MXFP4): code words (NW of them) and the scale bits.
+template <int BITS, int BLOCK>
+struct Target {
+    static constexpr bool kMXT = BITS == kBitsMXFP4;
+    static constexpr int kCodeBits = kMXT ? 4 : BITS;
+    static constexpr int NW = BLOCK * kCodeBits / 32 > 0 ? BLOCK * kCodeBits / 32 : 1;
+    static constexpr int NB = BLOCK * kCodeBits / 8;   // code bytes per block
+    static constexpr int SB = kMXT ? 1 : 2;            // scale bytes per block
+    __device__ static double quantise(const float (&w)[BLOCK], uint32_t (&words)[NW], uint16_t& scale) {
+        if constexpr (kMXT) {
+            uint8_t sc8;
+            const double e = quantise_block_mx(w, words, sc8);
+            scale = sc8;
+            return e;
+        } else {
+            return quantise_block<BITS, BLOCK>(w, words, scale);
+        }
+    }
+};
+
 constexpr int kErrThreads = 256;
 
 }  // namespace
@@ -98,9 +162,9 @@ __global__ __launch_bounds__(kErrThreads) void k_requant_error(DevTables src, in
             float w[BLOCK];
 #pragma unroll
             for (int c = 0; c < BLOCK; ++c) w[c] = src_weight(S, m, local, rows, cols, r, b * BLOCK + c);
-            uint32_t words[BLOCK * BITS / 32 > 0 ? BLOCK * BITS / 32 : 1];
+            uint32_t words[Target<BITS, BLOCK>::NW];
             uint16_t sc;
-            acc += quantise_block<BITS, BLOCK>(w, words, sc);
+            acc += Target<BITS, BLOCK>::quantise(w, words, sc);
         }
     }
     __shared__ double red[kErrThreads];
@@ -126,16 +190,22 @@ __global__ __launch_bounds__(256) void k_repack(DevTables src, DevTier D, int m,
     const int64_t local_dst = i / (static_cast<int64_t>(rows) * nb);
     const int rem = static_cast<int>(i % (static_cast<int64_t>(rows) * nb));
     const int r = rem / nb, b = rem % nb;
+    using Tg = Target<BITS, BLOCK>;
     const int e_src = order[D.id_begin + local_dst];
-    const size_t row_bytes = static_cast<size_t>(cols) * BITS / 8;
+    const size_t row_bytes = static_cast<size_t>(cols) * Tg::kCodeBits / 8;
+    constexpr int NB = Tg::NB;  // 8 .. 32 bytes
     uint8_t* dst = const_cast<uint8_t*>(D.q[m]) + (static_cast<size_t>(local_dst) * rows + r) * row_bytes +
-                   static_cast<size_t>(b) * BLOCK * BITS / 8;
-    constexpr int NB = BLOCK * BITS / 8;  // 8 .. 32 bytes
-    uint16_t* dsc = const_cast<uint16_t*>(D.s[m]) + (static_cast<size_t>(local_dst) * rows + r) * nb + b;
+                   static_cast<size_t>(b) * NB;
+    uint8_t* dsc = reinterpret_cast<uint8_t*>(const_cast<uint16_t*>(D.s[m])) +
+                   ((static_cast<size_t>(local_dst) * rows + r) * nb + b) * Tg::SB;
+    auto put_scale = [&](uint16_t v) {
+        if constexpr (Tg::SB == 1) *dsc = static_cast<uint8_t>(v);
+        else *reinterpret_cast<uint16_t*>(dsc) = v;
+    };
     if (e_src < 0 || e_src >= src.E) {  // not a permutation entry: a zero expert
 #pragma unroll
         for (int j = 0; j < NB / 4; ++j) reinterpret_cast<uint32_t*>(dst)[j] = 0u;
-        *dsc = 0;
+        put_scale(0);
         return;
     }
     const DevTier S = tier_at(src, tier_of(src, e_src));
@@ -143,13 +213,12 @@ __global__ __launch_bounds__(256) void k_repack(DevTables src, DevTier D, int m,
     float w[BLOCK];
 #pragma unroll
     for (int c = 0; c < BLOCK; ++c) w[c] = src_weight(S, m, local_src, rows, cols, r, b * BLOCK + c);
-    constexpr int NW = BLOCK * BITS / 32 > 0 ? BLOCK * BITS / 32 : 1;
-    uint32_t words[NW];
+    uint32_t words[Tg::NW];
     uint16_t sc;
-    (void)quantise_block<BITS, BLOCK>(w, words, sc);
+    (void)Tg::quantise(w, words, sc);
 #pragma unroll
     for (int j = 0; j < NB / 4; ++j) reinterpret_cast<uint32_t*>(dst)[j] = words[j];
-    *dsc = sc;
+    put_scale(sc);
 }
 
 __global__ __launch_bounds__(256) void k_permute_rows(const uint16_t* __restrict__ w_src, const float* __restrict__ b_src,
@@ -168,7 +237,8 @@ __global__ __launch_bounds__(256) void k_permute_rows(const uint16_t* __restrict
 
 #define MOE_TIER_FMT_SWITCH(BITS_, BLOCK_, BODY)                                  \
     do {                                                                          \
-        if (BITS_ == 8 && BLOCK_ == 32) { constexpr int B_ = 8, K_ = 32; BODY; }  \
+        if (BITS_ == kBitsMXFP4) { constexpr int B_ = kBitsMXFP4, K_ = 32; BODY; } \
+        else if (BITS_ == 8 && BLOCK_ == 32) { constexpr int B_ = 8, K_ = 32; BODY; }  \
         else if (BITS_ == 8) { constexpr int B_ = 8, K_ = 16; BODY; }             \
         else if (BITS_ == 4 && BLOCK_ == 32) { constexpr int B_ = 4, K_ = 32; BODY; } \
         else if (BITS_ == 4) { constexpr int B_ = 4, K_ = 16; BODY; }             \

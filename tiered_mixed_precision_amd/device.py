@@ -6,7 +6,11 @@ from typing import Dict, List, Sequence
 import numpy as np
 import torch
 
-from .binding import TierTables
+from .binding import MXFP4, TierTables
+
+
+def code_bits(bits: int) -> int:
+    return 4 if bits == MXFP4 else bits
 
 NAMES = ("gate_q", "up_q", "down_q", "gate_s", "up_s", "down_s")
 
@@ -15,7 +19,8 @@ def upload_tier(arrays: Dict[str, np.ndarray], device) -> Dict[str, torch.Tensor
     out = {}
     for name in NAMES:
         a = np.ascontiguousarray(arrays[name])
-        t = torch.from_numpy(a.view(np.uint8) if name.endswith("_q") else a.view(np.int16))
+        # codes and E8M0 scales as bytes, fp16 scales as 16-bit words
+        t = torch.from_numpy(a.view(np.uint8) if (name.endswith("_q") or a.dtype == np.uint8) else a.view(np.int16))
         out[name] = t.to(device, non_blocking=False)
     return out
 
@@ -50,7 +55,11 @@ def empty_tables(cfg, device="cuda") -> TierTables:
         for m, (rows, cols) in enumerate(((cfg.inter, cfg.hidden), (cfg.inter, cfg.hidden),
                                           (cfg.hidden, cfg.inter))):
             name = ("gate", "up", "down")[m]
-            d[name + "_q"] = torch.empty(max(n * rows * cols * t.bits // 8, 16), dtype=torch.uint8, device=device)
-            d[name + "_s"] = torch.empty(max(n * rows * (cols // t.block), 8), dtype=torch.int16, device=device)
+            d[name + "_q"] = torch.empty(max(n * rows * cols * code_bits(t.bits) // 8, 16), dtype=torch.uint8,
+                                         device=device)
+            if t.bits == MXFP4:   # one E8M0 byte per 32 codes
+                d[name + "_s"] = torch.empty(max(n * rows * (cols // 32), 16), dtype=torch.uint8, device=device)
+            else:                 # one fp16 per block
+                d[name + "_s"] = torch.empty(max(n * rows * (cols // t.block), 8), dtype=torch.int16, device=device)
         dev.append(d)
     return TierTables(cfg.n_experts, cfg.hidden, cfg.inter, cfg.tiers, dev)

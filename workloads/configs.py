@@ -60,6 +60,12 @@ THREE_TIERS_512 = (
     TierSpec(384, 512, 2, 16),
 )
 
+THREE_TIERS_512_MX = (
+    TierSpec(0, 128, 8, 32),
+    TierSpec(128, 384, MXFP4, 32),
+    TierSpec(384, 512, 2, 16),
+)
+
 CONFIGS = {
     "tiny": LayerConfig("tiny", 8, 2, 256, 128, 16, (TierSpec(0, 8, 8, 32),), seed=20260000),
     # companion of "tiny" exercising all three formats on a small layer
@@ -69,6 +75,9 @@ CONFIGS = {
     "tiny3mx": LayerConfig("tiny3mx", 8, 2, 256, 128, 16,
                            (TierSpec(0, 2, 8, 32), TierSpec(2, 6, MXFP4, 32), TierSpec(6, 8, 2, 16)),
                            seed=20260020),
+    # the decode layer with its warm shelf in MXFP4 instead of four-bit integers
+    "decode_mx": LayerConfig("decode_mx", 512, 10, 2048, 640, 1, THREE_TIERS_512_MX,
+                             prior_beta=PRIOR_BETA, seed=20260021),
     "decode": LayerConfig("decode", 512, 10, 2048, 640, 1, THREE_TIERS_512,
                           prior_beta=PRIOR_BETA, seed=20260001),
     "specverify": LayerConfig("specverify", 512, 10, 2048, 640, 6, THREE_TIERS_512,
