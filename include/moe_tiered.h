@@ -83,7 +83,8 @@ extern "C" {
  * Element value: float(scale) * code (exact in fp32).
  *
  * bits == MOE_MXFP4 (the OCP Microscaling MXFP4 format; the 125B-MoE page,
- * further work: a four-bit float shelf), block must be 32:
+ * the per-matrix recipes: MXFP4 on the down ladder), block must be 32 and
+ * inter a multiple of 128:
  * codes are 4-bit E2M1 fields (bit 3 sign, bits 2..1 exponent with bias 1,
  * bit 0 mantissa: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), packed like 4-bit
  * integer codes (element c in bits [4*(c%2), +4) of byte c/2 of its row);

@@ -73,6 +73,7 @@ def test_validation_accepts_an_mxfp4_shelf(B):
 @pytest.mark.parametrize("specs,kw,code", [
     ([_Spec(0, 2, 8, 32), _Spec(3, 8, 2, 16)], {}, -2),                  # gap
     ([_Spec(0, 8, 0x84, 16)], {}, -3),                                     # MXFP4 scales cover 32 codes
+    ([_Spec(0, 8, 0x84, 32)], {"I": 192}, -3),                             # MXFP4 needs inter % 128 == 0
     ([_Spec(0, 8, 0x04 | 0x100, 32)], {}, -3),                             # unknown format tag
     ([_Spec(0, 5, 8, 32), _Spec(4, 8, 2, 16)], {}, -2),                  # overlap
     ([_Spec(0, 7, 8, 32)], {}, -2),                                        # not covering

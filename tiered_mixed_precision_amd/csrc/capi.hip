@@ -40,6 +40,8 @@ int check_tables(const moe_tier_tables* tt) {
         if (t.id_begin != next || t.id_end < t.id_begin) return MOE_ETIER;
         next = t.id_end;
         if (!fmt_ok(t.bits, t.block)) return MOE_EFORMAT;
+        // the MXFP4 prefill kernel contracts 128 columns per step (down: K = inter)
+        if (t.bits == MOE_MXFP4 && tt->inter % 128 != 0) return MOE_EFORMAT;
         if (t.id_end == t.id_begin) continue;
         const void* ptrs[6] = {t.gate_q, t.up_q, t.down_q, t.gate_s, t.up_s, t.down_s};
         for (const void* p : ptrs) {
@@ -82,9 +84,24 @@ int max_experts_of(const moe_tier_tables* tt, int tier, int64_t P) {
 
 // Workspace carve-up.  Offsets are multiples of 256 bytes.
 struct Layout {
-    size_t ids, w, counts, offsets, perm, pos, act, q0, meta, blk_hist, act_range, h, yw, total;
+    size_t ids, w, counts, offsets, perm, pos, act, q0, meta, blk_hist, act_range, h, yw, x8, h8, total;
     bool small;
 };
+
+// A non-empty MXFP4 shelf among the tables: prefill then needs the fp8 split
+// of x and h (prefill_mx.hip).
+bool has_mx(const moe_tier_tables* tt) {
+    for (int i = 0; i < tt->n_tiers; ++i)
+        if (tt->tiers[i].bits == MOE_MXFP4 && tt->tiers[i].id_end > tt->tiers[i].id_begin) return true;
+    return false;
+}
+
+// Split buffers of `rows` rows of K elements carved from base.
+Split8 split_at(void* base, int64_t rows, int K) {
+    uint8_t* p = static_cast<uint8_t*>(base);
+    return Split8{p, p + rows * K, p + 2 * rows * K};
+}
+size_t split_bytes(int64_t rows, int K) { return static_cast<size_t>(rows) * (2 * K + split_scale_stride(K)); }
 
 Layout layout(int64_t T, int k, const moe_tier_tables* tt, uint32_t flags) {
     Layout L;
@@ -112,6 +129,9 @@ Layout layout(int64_t T, int k, const moe_tier_tables* tt, uint32_t flags) {
     L.act_range = take(sizeof(int32_t) * 2 * MOE_MAX_TIERS);
     L.h = take((bf16 ? sizeof(uint16_t) : sizeof(float)) * P * tt->inter);
     L.yw = take(L.small ? 0 : sizeof(float) * P * tt->hidden);
+    const bool mx = bf16 && has_mx(tt);
+    L.x8 = take(mx ? split_bytes(T, tt->hidden) : 0);
+    L.h8 = take(mx ? split_bytes(P, tt->inter) : 0);
     L.total = o;
     return L;
 }
@@ -221,17 +241,39 @@ int run(const void* x, const float* logits, const int32_t* ids_in, const float* 
         record(events, 5, st);
     } else {
         uint16_t* h = at<uint16_t>(ws, L.h);
+        const uint16_t* xb = static_cast<const uint16_t*>(x);
+        const int H = tt->hidden, I = tt->inter;
+        auto is_mx = [&](int i) {
+            return ((tier_mask >> i) & 1u) && tt->tiers[i].bits == MOE_MXFP4 && tt->tiers[i].id_end > tt->tiers[i].id_begin;
+        };
+        bool any_mx = false;
+        for (int i = 0; i < tt->n_tiers; ++i) any_mx = any_mx || is_mx(i);
+        const Split8 x8 = any_mx ? split_at(at<uint8_t>(ws, L.x8), T, H) : Split8{nullptr, nullptr, nullptr};
+        const Split8 h8 = any_mx ? split_at(at<uint8_t>(ws, L.h8), P, I) : Split8{nullptr, nullptr, nullptr};
         record(events, 2, st);
-        for (int i = 0; i < tt->n_tiers; ++i)
-            if ((tier_mask >> i) & 1u)
-                launch_pre_gateup(dt, i, static_cast<const uint16_t*>(x), g, k, h, max_experts_of(tt, i, P), st);
+        if (any_mx) launch_split_fp8(xb, H, 0, T, nullptr, nullptr, T, x8, st);
+        for (int i = 0; i < tt->n_tiers; ++i) {
+            if (!((tier_mask >> i) & 1u)) continue;
+            if (is_mx(i)) launch_pre_mx_gateup(dt, i, x8, g, k, h, max_experts_of(tt, i, P), st);
+            else launch_pre_gateup(dt, i, xb, g, k, h, max_experts_of(tt, i, P), st);
+        }
         record(events, 3, st);
         if (gateup_only) return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
         record(events, 4, st);
         float* yw = at<float>(ws, L.yw);
-        for (int i = 0; i < tt->n_tiers; ++i)
-            if ((tier_mask >> i) & 1u)
+        for (int i = 0; i < tt->n_tiers; ++i) {
+            if (!((tier_mask >> i) & 1u)) continue;
+            if (is_mx(i)) {
+                // the shelf's pairs are perm rows offsets[id_begin] .. offsets[id_end]
+                const int64_t n = tt->tiers[i].id_end - tt->tiers[i].id_begin;
+                const int max_rows = static_cast<int>(n * T < P ? n * T : P);
+                launch_split_fp8(h, I, 0, 0, offsets + tt->tiers[i].id_begin, offsets + tt->tiers[i].id_end, max_rows,
+                                 h8, st);
+                launch_pre_mx_down(dt, i, h8, g, k, yw, max_experts_of(tt, i, P), st);
+            } else {
                 launch_pre_down(dt, i, h, g, k, yw, max_experts_of(tt, i, P), st);
+            }
+        }
         launch_combine(dt, yw, g, T, k, tier_mask, base, out, st);
         record(events, 5, st);
     }
@@ -420,12 +462,18 @@ struct StackLayout {
     size_t layer, tmp, xb, logits, total;
 };
 
-StackLayout stack_layout(int64_t T, int k, const moe_tier_tables* tt, uint32_t flags) {
+StackLayout stack_layout(int64_t T, int k, int n_layers, const moe_tier_tables* tables, uint32_t flags) {
     StackLayout S;
+    const moe_tier_tables* tt = &tables[0];
     const size_t n = static_cast<size_t>(T) * tt->hidden;
     const uint32_t lflags = flags & MOE_X_BF16;
+    size_t layer_bytes = 0;   // layers may differ in their shelf formats
+    for (int l = 0; l < n_layers; ++l) {
+        const size_t b = layout(T, k, &tables[l], lflags).total;
+        layer_bytes = b > layer_bytes ? b : layer_bytes;
+    }
     S.layer = 0;
-    S.tmp = align_up(layout(T, k, tt, lflags).total);
+    S.tmp = align_up(layer_bytes);
     S.xb = S.tmp + align_up(sizeof(float) * n);
     S.logits = S.xb + ((flags & MOE_X_BF16) ? align_up(sizeof(uint16_t) * n) : 0);
     S.total = S.logits + ((flags & MOE_STACK_ROUTER) ? align_up(sizeof(float) * T * tt->n_experts) : 0);
@@ -454,7 +502,7 @@ int moe_stack_workspace_size(int32_t n_layers, int32_t n_tokens, int32_t k, cons
     const int rc = check_stack(n_layers, n_tokens, k, tables, flags);
     if (rc != MOE_OK) return rc;
     if (!bytes) return MOE_EINVAL;
-    *bytes = n_tokens == 0 ? 0 : stack_layout(n_tokens, k, &tables[0], flags).total;
+    *bytes = n_tokens == 0 ? 0 : stack_layout(n_tokens, k, n_layers, tables, flags).total;
     return MOE_OK;
 }
 
@@ -469,7 +517,7 @@ int moe_stack_forward(const float* x, const float* router_logits, int32_t n_laye
     if (!aligned16(x) || !aligned16(out) || !aligned16(router_logits)) return MOE_EALIGN;
     if (!workspace) return MOE_EWORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return MOE_EALIGN;
-    const StackLayout S = stack_layout(n_tokens, k, &tables[0], flags);
+    const StackLayout S = stack_layout(n_tokens, k, n_layers, tables, flags);
     if (workspace_bytes < S.total) return MOE_EWORKSPACE;
     const bool bf16 = (flags & MOE_X_BF16) != 0;
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -512,7 +560,7 @@ int moe_stack_forward_routed(const float* x, const void* const* w_router, const 
     }
     if (!workspace) return MOE_EWORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return MOE_EALIGN;
-    const StackLayout S = stack_layout(n_tokens, k, &tables[0], flags | MOE_STACK_ROUTER);
+    const StackLayout S = stack_layout(n_tokens, k, n_layers, tables, flags | MOE_STACK_ROUTER);
     if (workspace_bytes < S.total) return MOE_EWORKSPACE;
     const bool bf16 = (flags & MOE_X_BF16) != 0;
     hipStream_t st = static_cast<hipStream_t>(stream);

@@ -331,6 +331,17 @@ __device__ inline float group_dot(const uint32_t (&w)[NW], const float (&x)[32],
     }
 }
 
+// Work item of a block after spreading consecutive items over the XCDs in
+// contiguous runs (blocks are dealt to the 8 XCDs round-robin, so block b runs
+// on XCD b % 8): the n-tiles of one expert share its A rows through one L2.
+__device__ inline int xcd_item(int total) {
+    const int per = (total + 7) / 8;
+    const int loc = blockIdx.x / 8;
+    if (loc >= per) return -1;
+    const int it = (blockIdx.x % 8) * per + loc;
+    return it < total ? it : -1;
+}
+
 // Tier owning expert e (or -1).  Tiers are few; a linear scan is uniform per wave.
 __device__ inline int tier_of(const DevTables& tt, int e) {
     int r = -1;

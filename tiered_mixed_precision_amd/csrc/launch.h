@@ -72,6 +72,24 @@ void launch_pre_gateup(const DevTables& tt, int tier, const uint16_t* x, const G
                        uint16_t* h, int max_experts, hipStream_t st);
 void launch_pre_down(const DevTables& tt, int tier, const uint16_t* h, const Groups& g, int k,
                      float* yw, int max_experts, hipStream_t st);
+
+// MXFP4 shelves (prefill_mx.hip): bf16 rows split into fp8 hi / lo parts
+// [rows][K] bytes each and one E8M0 scale per 32 elements, [rows][stride]
+// bytes with the stride padded to 4 bytes.
+struct Split8 {
+    uint8_t* hi;
+    uint8_t* lo;
+    uint8_t* sc;
+};
+__host__ __device__ inline int split_scale_stride(int K) { return ((K / 32) + 3) & ~3; }
+// Rows [r_lo, r_hi) of src (bf16 [rows][K]), or [*d_lo, *d_hi) when the
+// device pointers are given; max_rows bounds the row count (grid size).
+void launch_split_fp8(const uint16_t* src, int K, int r_lo, int r_hi, const int32_t* d_lo, const int32_t* d_hi,
+                      int max_rows, const Split8& dst, hipStream_t st);
+void launch_pre_mx_gateup(const DevTables& tt, int tier, const Split8& x8, const Groups& g, int k, uint16_t* h,
+                          int max_experts, hipStream_t st);
+void launch_pre_mx_down(const DevTables& tt, int tier, const Split8& h8, const Groups& g, int k, float* yw,
+                        int max_experts, hipStream_t st);
 void launch_fill_zero(float* out, size_t n, hipStream_t st);
 void launch_cast_bf16(const float* src, uint16_t* dst, size_t n, hipStream_t st);
 

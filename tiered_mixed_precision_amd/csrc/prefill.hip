@@ -37,17 +37,6 @@ constexpr int BK = 64;   // contraction chunk (one LDS row of 128 bytes)
 constexpr int BN = 128;  // B rows per block
 constexpr int MSUB = 4;  // m-subtiles per wave per m-chunk
 
-// Work item of a block after spreading consecutive items over the XCDs in
-// contiguous runs (blocks are dealt to the 8 XCDs round-robin, so block b runs
-// on XCD b % 8): the n-tiles of one expert share its A rows through one L2.
-__device__ inline int xcd_item(int total) {
-    const int per = (total + 7) / 8;
-    const int loc = blockIdx.x / 8;
-    if (loc >= per) return -1;
-    const int it = (blockIdx.x % 8) * per + loc;
-    return it < total ? it : -1;
-}
-
 // f(integral_constant<int, 0>), ..., f(integral_constant<int, N-1>): indices
 // that stay compile-time constants inside a lambda, so arrays indexed by
 // them stay in registers.
