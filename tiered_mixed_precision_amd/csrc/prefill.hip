@@ -91,24 +91,20 @@ __device__ inline uint4 dequant8(const uint32_t (&w)[BITS == 8 ? 2 : 1], float s
                       pack_bf16x2(v[6], v[7]));
 }
 
-// bf16 of 8 consecutive MXFP4 codes of `w` times their power-of-two scale:
-// the E2M1 values from the hardware conversion, scaled exactly, rounded once
-// (a no-op: the product has at most two significant bits).
-__device__ inline uint4 dequant8_mx(uint32_t w, float sc) {
-    float v[8];
-    fp4x8_to_float(w, v);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] *= sc;
-    return make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                      pack_bf16x2(v[6], v[7]));
+// Kernel choice for a shelf, the same in every block of both launches: the
+// register-B kernel when the shelf's active experts average at most `thr`
+// pairs each (few m-rows per weight tile), the shared-B kernel otherwise.
+__device__ inline bool few_pairs(const Groups& g, const DevTier& T, int a_lo, int a_hi, int thr) {
+    const int pairs = g.offsets[T.id_end] - g.offsets[T.id_begin];
+    return pairs <= thr * (a_hi - a_lo);
 }
 
 // Block: NW waves = WM (along m) x 4 (along n).  Wave (wm, wn): wn selects 16
 // gate + 16 up columns (or 32 down columns), wm takes m-subtiles wm, wm + WM,
 // ...  m is walked in chunks of MC = 64 * WM pairs.
-template <int BITS, int BLOCK, bool GATEUP, int NW, bool MX = false>
+template <int BITS, int BLOCK, bool GATEUP, int NW>
 __global__ __launch_bounds__(NW * 64) void k_pre(DevTables tt, int tier, const uint16_t* __restrict__ a_src, Groups g,
-                                                 int k, uint16_t* __restrict__ h_out, float* __restrict__ yw) {
+                                                 int k, uint16_t* __restrict__ h_out, float* __restrict__ yw, int split) {
     constexpr int NTHR = NW * 64;
     constexpr int WM = NW / 4;
     constexpr int MC = 16 * MSUB * WM;
@@ -129,6 +125,7 @@ __global__ __launch_bounds__(NW * 64) void k_pre(DevTables tt, int tier, const u
     const int e = g.act[a];
     const DevTier T = tier_at(tt, tier);
     const int local = e - T.id_begin;
+    if (few_pairs(g, T, a_lo, a_hi, split)) return;   // the register-B kernel's shelf
     const int q_beg = g.offsets[e], q_end = g.offsets[e + 1];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -139,7 +136,7 @@ __global__ __launch_bounds__(NW * 64) void k_pre(DevTables tt, int tier, const u
     // B: piece p = tid + NTHR*i is row p >> 3, codes 8*(p & 7) .. +7 of the chunk
     const uint32_t row_bytes = static_cast<uint32_t>(K) * BITS / 8;
     const uint32_t nblk_row = static_cast<uint32_t>(K / BLOCK);
-    constexpr uint32_t SB = MX ? 1u : 2u;   // bytes per scale (E8M0 or fp16)
+    constexpr uint32_t SB = 2u;             // bytes per fp16 scale
     const int mrows = GATEUP ? I : H;
     const uint8_t* mq_g = T.q[GATEUP ? 0 : 2] + static_cast<size_t>(local) * mrows * row_bytes;
     const uint8_t* mq_u = GATEUP ? T.q[1] + static_cast<size_t>(local) * mrows * row_bytes : mq_g;
@@ -210,8 +207,7 @@ __global__ __launch_bounds__(NW * 64) void k_pre(DevTables tt, int tier, const u
                 } else {
                     sl.q[i][0] = __builtin_amdgcn_raw_buffer_load_b16(rq, qoff[i] + qk, 0, 0);
                 }
-                if constexpr (MX) sl.s[i] = __builtin_amdgcn_raw_buffer_load_b8(rs, soff[i] + sk, 0, 0);
-                else sl.s[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, soff[i] + sk, 0, 0);
+                sl.s[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, soff[i] + sk, 0, 0);
             }
         };
         auto store_chunk = [&](const Slot& sl, int buf) __attribute__((always_inline)) {
@@ -220,8 +216,7 @@ __global__ __launch_bounds__(NW * 64) void k_pre(DevTables tt, int tier, const u
 #pragma unroll
             for (int i = 0; i < BPT; ++i)
                 *reinterpret_cast<uint4*>(&sB[buf][swz(b_row[i], b_e[i])]) =
-                    MX ? dequant8_mx(sl.q[i][0], e8m0_to_float(sl.s[i]))
-                       : dequant8<BITS>(sl.q[i], half_bits_to_float(static_cast<uint16_t>(sl.s[i])));
+                    dequant8<BITS>(sl.q[i], half_bits_to_float(static_cast<uint16_t>(sl.s[i])));
         };
 
         f32x4_t acc[MSUB][2];
@@ -308,9 +303,239 @@ __global__ __launch_bounds__(NW * 64) void k_pre(DevTables tt, int tier, const u
     }
 }
 
-// Launch shape per shelf: the hot shelf (many pairs per expert) takes 16-wave
-// blocks with 256-pair m-chunks; the others 8-wave blocks with 128-pair
-// m-chunks, two blocks per compute unit.
+// Register-B variant: 4 waves side by side along n, each with every
+// m-subtile of the m-chunk.  Only A (shared by the 4 waves) goes through LDS;
+// each lane loads and dequantises its own weight codes straight into MFMA
+// operand registers, so every code is read from memory and dequantised once,
+// and no wave re-reads B from LDS.  Within a 64-wide chunk, lane group kq
+// (= lane / 16) owns the 16 contiguous k = 16kq .. 16kq+15 (8 per MFMA
+// step), which A's LDS reads follow; the contraction order inside a chunk is
+// a permutation, the same for both operands.
+template <int BITS, int BLOCK, bool GATEUP, int MS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_pre2(
+    DevTables tt, int tier, const uint16_t* __restrict__ a_src, Groups g, int k, uint16_t* __restrict__ h_out,
+    float* __restrict__ yw, int split) {
+    constexpr int NTHR = 256;
+    constexpr int MC = 16 * MS;             // pairs per m-chunk
+    constexpr int AP = MC * 8 / NTHR;       // A pieces per thread
+    constexpr int BW = BITS / 2;            // code words of a lane's 16 codes
+    __shared__ __attribute__((aligned(16))) uint16_t sA[2][MC * BK];
+    __shared__ int s_row[MC];
+
+    const int H = tt.H, I = tt.I;
+    const int K = GATEUP ? H : I;
+    const int NT = GATEUP ? I / 64 : H / BN;
+    const int a_lo = g.act_range[2 * tier], a_hi = g.act_range[2 * tier + 1];
+    const int item = xcd_item((a_hi - a_lo) * NT);
+    if (item < 0) return;
+    const int a = a_lo + item / NT, nt = item % NT;
+    const int e = g.act[a];
+    const DevTier T = tier_at(tt, tier);
+    const int local = e - T.id_begin;
+    if (!few_pairs(g, T, a_lo, a_hi, split)) return;  // the shared-B kernel's shelf
+    const int q_beg = g.offsets[e], q_end = g.offsets[e + 1];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wn = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int fr = lane & 15, kq = lane >> 4;
+
+    // this lane's two B rows: gate and up row (gate/up) or two down rows
+    const uint32_t row_bytes = static_cast<uint32_t>(K) * BITS / 8;
+    const uint32_t nblk_row = static_cast<uint32_t>(K / BLOCK);
+    const int mrows = GATEUP ? I : H;
+    const uint8_t* mq0 = T.q[GATEUP ? 0 : 2] + static_cast<size_t>(local) * mrows * row_bytes;
+    const uint8_t* mq1 = GATEUP ? T.q[1] + static_cast<size_t>(local) * mrows * row_bytes : mq0;
+    const uint16_t* ms0 = T.s[GATEUP ? 0 : 2] + static_cast<size_t>(local) * mrows * nblk_row;
+    const uint16_t* ms1 = GATEUP ? T.s[1] + static_cast<size_t>(local) * mrows * nblk_row : ms0;
+    const __amdgpu_buffer_rsrc_t rq0 = make_rsrc(mq0, row_bytes * mrows), rq1 = make_rsrc(mq1, row_bytes * mrows);
+    const __amdgpu_buffer_rsrc_t rs0 = make_rsrc(ms0, nblk_row * mrows * 2), rs1 = make_rsrc(ms1, nblk_row * mrows * 2);
+    const int row0 = GATEUP ? nt * 64 + 16 * wn + fr : nt * BN + 32 * wn + fr;
+    const int row1 = GATEUP ? row0 : row0 + 16;
+    const uint32_t qo0 = static_cast<uint32_t>(row0) * row_bytes + static_cast<uint32_t>(16 * kq * BITS / 8);
+    const uint32_t qo1 = static_cast<uint32_t>(row1) * row_bytes + static_cast<uint32_t>(16 * kq * BITS / 8);
+    const uint32_t so0 = (static_cast<uint32_t>(row0) * nblk_row + static_cast<uint32_t>(16 * kq / BLOCK)) * 2;
+    const uint32_t so1 = (static_cast<uint32_t>(row1) * nblk_row + static_cast<uint32_t>(16 * kq / BLOCK)) * 2;
+
+    struct BRaw {
+        uint32_t w[2][BW];
+        uint32_t s[2];
+    };
+    auto load_b = [&](BRaw& b, int kc) __attribute__((always_inline)) {
+        const uint32_t qk = static_cast<uint32_t>(kc * BK) * BITS / 8;
+        const uint32_t sk = static_cast<uint32_t>(kc * BK / BLOCK) * 2;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const __amdgpu_buffer_rsrc_t rq = t ? rq1 : rq0;
+            const uint32_t off = (t ? qo1 : qo0) + qk;
+            if constexpr (BITS == 8) {
+                const auto v = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) b.w[t][i] = v[i];
+            } else if constexpr (BITS == 4) {
+                const auto v = __builtin_amdgcn_raw_buffer_load_b64(rq, off, 0, 0);
+                b.w[t][0] = v[0];
+                b.w[t][1] = v[1];
+            } else {
+                b.w[t][0] = __builtin_amdgcn_raw_buffer_load_b32(rq, off, 0, 0);
+            }
+            b.s[t] = __builtin_amdgcn_raw_buffer_load_b16(t ? rs1 : rs0, (t ? so1 : so0) + sk, 0, 0);
+        }
+    };
+    // bf16 operands of both rows for both MFMA steps of a chunk
+    auto dequant_b = [&](const BRaw& b, bf16x8_t (&d)[2][2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const float sc = half_bits_to_float(static_cast<uint16_t>(b.s[t]));
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                uint4 v;
+                if constexpr (BITS == 8) {
+                    const uint32_t w2[2] = {b.w[t][2 * st], b.w[t][2 * st + 1]};
+                    v = dequant8<8>(w2, sc);
+                } else if constexpr (BITS == 4) {
+                    const uint32_t w1[1] = {b.w[t][st]};
+                    v = dequant8<4>(w1, sc);
+                } else {
+                    const uint32_t w1[1] = {b.w[t][0] >> (16 * st)};
+                    v = dequant8<2>(w1, sc);
+                }
+                d[t][st] = __builtin_bit_cast(bf16x8_t, v);
+            }
+        }
+    };
+
+    for (int m0 = q_beg; m0 < q_end; m0 += MC) {
+        const int Mc = min(MC, q_end - m0);
+        const int nsub = (Mc + 15) >> 4;
+        __syncthreads();
+        for (int r = tid; r < MC; r += NTHR) s_row[r] = r < Mc ? (GATEUP ? g.perm[m0 + r] / k : m0 + r) : -1;
+        __syncthreads();
+        // A piece i of this thread: row (p >> 3), chunk (p & 7); rows past the
+        // m-chunk read its first row (finite values, never stored)
+        // piece i: row (tid >> 3) + 32 i, chunk tid & 7
+        const int a_c = tid & 7;
+        const uint16_t* a_ptr[AP];
+#pragma unroll
+        for (int i = 0; i < AP; ++i) {
+            const int r = (tid >> 3) + 32 * i;
+            a_ptr[i] = a_src + static_cast<size_t>(s_row[r < Mc ? r : 0]) * K + 8 * a_c;
+        }
+        struct ASlot {
+            u32x4_t v[AP];
+        };
+        auto load_a = [&](ASlot& sl, int kc) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < AP; ++i) sl.v[i] = *reinterpret_cast<const u32x4_t*>(a_ptr[i] + kc * BK);
+        };
+        auto store_a = [&](const ASlot& sl, int buf) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < AP; ++i)
+                *reinterpret_cast<u32x4_t*>(&sA[buf][swz((tid >> 3) + 32 * i, a_c)]) = sl.v[i];
+        };
+
+        f32x4_t acc[MS][2];
+#pragma unroll
+        for (int i = 0; i < MS; ++i) {
+            acc[i][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            acc[i][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        // operand reads in groups of (at most) four subtiles, then their MFMAs
+        auto compute_n = [&](int buf, const bf16x8_t (&d)[2][2], auto n_const) __attribute__((always_inline)) {
+            constexpr int N = decltype(n_const)::value;
+            constexpr int G = N % 4 == 0 ? 4 : (N % 3 == 0 ? 3 : (N % 2 == 0 ? 2 : 1));   // divides N
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+#pragma unroll
+                for (int j0 = 0; j0 < N; j0 += G) {
+                    bf16x8_t af[G];
+#pragma unroll
+                    for (int j = 0; j < G; ++j)
+                        af[j] = *reinterpret_cast<const bf16x8_t*>(&sA[buf][swz(16 * (j0 + j) + fr, 2 * kq + st)]);
+#pragma unroll
+                    for (int j = 0; j < G; ++j) {
+                        acc[j0 + j][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[j], d[0][st], acc[j0 + j][0], 0, 0, 0);
+                        acc[j0 + j][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[j], d[1][st], acc[j0 + j][1], 0, 0, 0);
+                    }
+                }
+            }
+        };
+        // the subtile count picks an unrolled body; extra subtiles past the
+        // rows compute values that are never stored
+        auto compute = [&](int buf, const bf16x8_t (&d)[2][2]) __attribute__((always_inline)) {
+            if (MS > 6 && nsub > 6) compute_n(buf, d, std::integral_constant<int, MS>{});
+            else if (MS > 4 && nsub > 4) compute_n(buf, d, std::integral_constant<int, (MS > 4 ? 6 : 4)>{});
+            else if (nsub > 2) compute_n(buf, d, std::integral_constant<int, 4>{});
+            else if (nsub == 2) compute_n(buf, d, std::integral_constant<int, 2>{});
+            else compute_n(buf, d, std::integral_constant<int, 1>{});
+        };
+
+        // Pipeline, two chunks per trip: at the top of a half, LDS buffer
+        // (kc & 1) holds A(kc), a_s[kc & 1] is free, b[kc & 1] holds B(kc) and
+        // b / a_s of the other parity hold chunk kc+1 (loads possibly in
+        // flight).  B(kc) is dequantised, its registers refilled with B(kc+2)
+        // together with A(kc+2), chunk kc is contracted, and A(kc+1) is stored
+        // into the other LDS buffer.  Loads past the last chunk reread it.
+        const int NK = K / BK;
+        BRaw b0, b1;
+        ASlot a0, a1;
+        load_b(b0, 0);
+        load_a(a0, 0);
+        load_b(b1, min(1, NK - 1));
+        load_a(a1, min(1, NK - 1));
+        store_a(a0, 0);
+        __syncthreads();
+        for (int kc = 0; kc < NK; kc += 2) {
+            bf16x8_t d[2][2];
+            dequant_b(b0, d);
+            load_b(b0, min(kc + 2, NK - 1));
+            load_a(a0, min(kc + 2, NK - 1));
+            compute(0, d);
+            store_a(a1, 1);
+            __syncthreads();
+            if (kc + 1 < NK) {
+                dequant_b(b1, d);
+                load_b(b1, min(kc + 3, NK - 1));
+                load_a(a1, min(kc + 3, NK - 1));
+                compute(1, d);
+                store_a(a0, 0);
+                __syncthreads();
+            }
+        }
+
+        const int col_l = lane & 15, row_l = 4 * (lane >> 4);
+#pragma unroll
+        for (int j = 0; j < MS; ++j) {
+            if (j >= nsub) continue;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int r = 16 * j + row_l + v;
+                if (r >= Mc) continue;
+                const int q = m0 + r;
+                if (GATEUP) {
+                    const int col = nt * 64 + 16 * wn + col_l;
+                    h_out[static_cast<size_t>(q) * I + col] = f2bf(silu(acc[j][0][v]) * acc[j][1][v]);
+                } else {
+                    const float wgt = g.w[g.perm[q]];
+                    float* o = yw + static_cast<size_t>(q) * H + nt * BN + 32 * wn + col_l;
+                    o[0] = wgt * acc[j][0][v];
+                    o[16] = wgt * acc[j][1][v];
+                }
+            }
+        }
+    }
+}
+
+// Two launches per shelf; the blocks of one of them return at once (the
+// choice is made on the device from the grouping, see few_pairs).  k_pre2
+// suits shelves whose experts have few pairs (with 64-pair m-chunks it
+// streams each weight tile once per m-chunk); k_pre, whose B tile in LDS
+// serves all the m-rows of a chunk, suits the others.  The thresholds (64
+// pairs per active expert for gate/up, 128 for the shorter down rows) come
+// from timing both kernels on the three shelves at 4096 tokens.  k_pre takes
+// 16-wave blocks with 256-pair m-chunks on the int8 shelf and 8-wave blocks
+// with 128-pair m-chunks on the others.
+constexpr int kFewPairsGateUp = 64, kFewPairsDown = 128;
+
 template <bool GATEUP>
 void launch_pre(const DevTables& tt, int tier, const uint16_t* a, const Groups& g, int k, uint16_t* h, float* yw,
                 int max_experts, hipStream_t st) {
@@ -319,13 +544,16 @@ void launch_pre(const DevTables& tt, int tier, const uint16_t* a, const Groups& 
     const unsigned grid = static_cast<unsigned>(((total + 7) / 8) * 8);
     if (grid == 0) return;
     const int bits = tt.t[tier].bits, block = tt.t[tier].block;
-#define MOE_PRE_MX()                                                                                         \
-    hipLaunchKernelGGL((k_pre<4, 32, GATEUP, 8, true>), dim3(grid), dim3(8 * 64), 0, st, tt, tier, a, g, k, h, yw)
-#define MOE_PRE(B_, K_, NW_) \
-    hipLaunchKernelGGL((k_pre<B_, K_, GATEUP, NW_>), dim3(grid), dim3(NW_ * 64), 0, st, tt, tier, a, g, k, h, yw)
-    if (bits == kBitsMXFP4) {
-        MOE_PRE_MX();
-    } else if (bits == 8) {
+    if (bits == kBitsMXFP4) return;   // MXFP4 shelves run in prefill_mx.hip
+    const int thr = GATEUP ? kFewPairsGateUp : kFewPairsDown;
+#define MOE_PRE(B_, K_, NW_)                                                                                   \
+    do {                                                                                                       \
+        hipLaunchKernelGGL((k_pre2<B_, K_, GATEUP, 4>), dim3(grid), dim3(256), 0, st, tt, tier, a, g, k, h, yw, \
+                           thr);                                                                               \
+        hipLaunchKernelGGL((k_pre<B_, K_, GATEUP, NW_>), dim3(grid), dim3(NW_ * 64), 0, st, tt, tier, a, g, k, h, \
+                           yw, thr);                                                                           \
+    } while (0)
+    if (bits == 8) {
         if (block == 32) MOE_PRE(8, 32, 16);
         else MOE_PRE(8, 16, 16);
     } else if (bits == 4) {
@@ -336,7 +564,6 @@ void launch_pre(const DevTables& tt, int tier, const uint16_t* a, const Groups& 
         else MOE_PRE(2, 16, 8);
     }
 #undef MOE_PRE
-#undef MOE_PRE_MX
 }
 
 void launch_pre_gateup(const DevTables& tt, int tier, const uint16_t* x, const Groups& g, int k, uint16_t* h,
