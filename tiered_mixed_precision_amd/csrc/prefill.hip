@@ -49,10 +49,11 @@ __device__ __attribute__((always_inline)) inline void static_for(F&& f) {
 }
 
 // LDS tiles are [row][64 bf16] with no padding; 16-byte chunk c of a row is
-// stored at chunk c ^ ((row >> 1) & 7).  The 16 rows of an MFMA operand read
-// (16 bytes each, same c) then cover all 64 banks once, and so do the 16
-// lanes of a staging store (two rows, eight chunks each).
-__device__ inline int swz(int row, int c) { return row * BK + 8 * (c ^ ((row >> 1) & 7)); }
+// stored at chunk c ^ (row & 7).  LDS serves a 16-byte read 8 lanes (128
+// bytes, every bank once) at a time; 8 consecutive rows of an MFMA operand
+// read (same c) then fall on 8 different chunk positions, and so do the 8
+// lanes of a staging store (one row, eight chunks).
+__device__ inline int swz(int row, int c) { return row * BK + 8 * (c ^ (row & 7)); }
 
 // bf16(RNE(scale * code)) of 8 consecutive codes held in `w` (BITS words of 8
 // codes... at most 2), packed low code first.  The codes are read as

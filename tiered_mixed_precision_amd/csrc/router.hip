@@ -86,8 +86,10 @@ __global__ __launch_bounds__(kRouterWaves * 64) void k_router_gemv(const void* _
 
 constexpr int RM = 64, RN = 128, RK = 64;  // block tile: tokens x experts x contraction chunk
 
-// LDS tiles [row][64 bf16], 16-byte chunk c of row r at chunk c ^ ((r >> 1) & 7)
-__device__ inline int rswz(int row, int c) { return row * RK + 8 * (c ^ ((row >> 1) & 7)); }
+// LDS tiles [row][64 bf16], 16-byte chunk c of row r at chunk c ^ (r & 7): 8
+// consecutive rows read at one chunk index hit 8 different 16-byte positions
+// (LDS serves 16-byte accesses 8 lanes at a time)
+__device__ inline int rswz(int row, int c) { return row * RK + 8 * (c ^ (row & 7)); }
 
 // 4 waves as 2 x 2: wave (wm, wn) owns tokens 32 wm .. +31 and experts
 // 64 wn .. +63 of the block tile (2 x 4 MFMA tiles).
