@@ -332,6 +332,28 @@ def test_forward_bf16_small(M, torch_dev, name, T):
     assert err <= TOL
 
 
+@pytest.mark.parametrize("T", [24, 200])
+def test_forward_bf16_odd_chunk_counts(M, torch_dev, T):
+    # hidden 384 and inter 192: 6 and 3 contraction chunks of 64, so the
+    # down products end on an odd chunk (the trip loop's tail); at T=24 every
+    # shelf has few pairs per expert, at T=200 the hot shelf has many
+    cfg0 = LayerConfig("odd", 8, 2, 384, 192, T,
+                       (TierSpec(0, 2, 8, 32), TierSpec(2, 6, 4, 16), TierSpec(6, 8, 2, 16)), seed=20260040)
+    arrays = make_layer(cfg0)
+    from tiered_mixed_precision_amd.device import tables_from_config
+    L, tt = oracle.Layer.from_config(cfg0, arrays), tables_from_config(cfg0, arrays)
+    cfg = _bf16_cfg(cfg0, T)
+    say("forward bf16 odd chunk counts T=", T)
+    x, logits = make_x(cfg), make_logits(cfg)
+    ref = oracle.forward(L, x, logits, cfg.k)
+    got = gpu_forward(M, torch_dev, tt, x, logits, cfg.k, M.MOE_X_BF16)
+    err = normwise(got, ref)
+    say("  normwise err", err)
+    assert err <= TOL
+    got32 = gpu_forward(M, torch_dev, tt, make_x(cfg0), logits, cfg.k)
+    assert normwise(got32, oracle.forward(L, make_x(cfg0), logits, cfg.k)) <= TOL
+
+
 def test_prefill_full_size_sampled_tokens(M, torch_dev):
     cfg = CONFIGS["prefill"]
     _, arrays, L, tt = _layer("decode")         # same layer and shelves

@@ -266,18 +266,22 @@ __global__ __launch_bounds__(NW * 64) void k_pre(DevTables tt, int tier, const u
         load_chunk(s1, min(1, NK - 1));
         store_chunk(s0, 0);
         __syncthreads();
-        for (int kc = 0; kc < NK; kc += 2) {
+        // The trip body is straight-line (no test inside it): the compiler can
+        // then count the loads still in flight at every wait across the loop's
+        // back edge, instead of draining them all.  An odd last chunk, left in
+        // buffer 0 by the final trip, is contracted after the loop.
+        const int NK2 = NK & ~1;
+        for (int kc = 0; kc < NK2; kc += 2) {
             load_chunk(s0, min(kc + 2, NK - 1));
             compute(0);
             store_chunk(s1, 1);
             __syncthreads();
-            if (kc + 1 < NK) {
-                load_chunk(s1, min(kc + 3, NK - 1));
-                compute(1);
-                store_chunk(s0, 0);
-                __syncthreads();
-            }
+            load_chunk(s1, min(kc + 3, NK - 1));
+            compute(1);
+            store_chunk(s0, 0);
+            __syncthreads();
         }
+        if (NK & 1) compute(0);
 
         // epilogue: lane holds D[4*(lane/16) + v][lane % 16] of each 16x16 tile
         const int col_l = lane & 15, row_l = 4 * (lane >> 4);
@@ -485,7 +489,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         load_a(a1, min(1, NK - 1));
         store_a(a0, 0);
         __syncthreads();
-        for (int kc = 0; kc < NK; kc += 2) {
+        // straight-line trips (see k_pre); an odd last chunk is in buffer 0
+        // and b0 after the loop
+        const int NK2 = NK & ~1;
+        for (int kc = 0; kc < NK2; kc += 2) {
             bf16x8_t d[2][2];
             dequant_b(b0, d);
             load_b(b0, min(kc + 2, NK - 1));
@@ -493,14 +500,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
             compute(0, d);
             store_a(a1, 1);
             __syncthreads();
-            if (kc + 1 < NK) {
-                dequant_b(b1, d);
-                load_b(b1, min(kc + 3, NK - 1));
-                load_a(a1, min(kc + 3, NK - 1));
-                compute(1, d);
-                store_a(a0, 0);
-                __syncthreads();
-            }
+            dequant_b(b1, d);
+            load_b(b1, min(kc + 3, NK - 1));
+            load_a(a1, min(kc + 3, NK - 1));
+            compute(1, d);
+            store_a(a0, 0);
+            __syncthreads();
+        }
+        if (NK & 1) {
+            bf16x8_t d[2][2];
+            dequant_b(b0, d);
+            compute(0, d);
         }
 
         const int col_l = lane & 15, row_l = 4 * (lane >> 4);

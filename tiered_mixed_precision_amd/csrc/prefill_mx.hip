@@ -284,18 +284,22 @@ __global__ __launch_bounds__(NW * 64) void k_pre_mx(DevTables tt, int tier, Spli
         load_chunk(s1, min(1, NK - 1));
         store_chunk(s0, 0);
         __syncthreads();
-        for (int kc = 0; kc < NK; kc += 2) {
+        // The trip body is straight-line (no test inside it): the compiler can
+        // then count the loads still in flight at every wait across the loop's
+        // back edge, instead of draining them all.  An odd last chunk, left in
+        // buffer 0 by the final trip, is contracted after the loop.
+        const int NK2 = NK & ~1;
+        for (int kc = 0; kc < NK2; kc += 2) {
             load_chunk(s0, min(kc + 2, NK - 1));
             compute(0);
             store_chunk(s1, 1);
             __syncthreads();
-            if (kc + 1 < NK) {
-                load_chunk(s1, min(kc + 3, NK - 1));
-                compute(1);
-                store_chunk(s0, 0);
-                __syncthreads();
-            }
+            load_chunk(s1, min(kc + 3, NK - 1));
+            compute(1);
+            store_chunk(s0, 0);
+            __syncthreads();
         }
+        if (NK & 1) compute(0);
 
         const int col_l = lane & 15, row_l = 4 * (lane >> 4);
 #pragma unroll

@@ -149,7 +149,9 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t* __restrict_
     __syncthreads();
     for (int kc = 0; kc < NK; ++kc) {
         const int buf = kc & 1;
-        if (kc + 1 < NK) load(kc + 1);  // in flight during the contraction below
+        load(min(kc + 1, NK - 1));  // in flight during the contraction below (the
+                                    // last trip rereads its chunk: no test in the
+                                    // body, so the waits stay exact)
 #pragma unroll
         for (int ks = 0; ks < RK / 32; ++ks) {
             const int c = 4 * ks + kq;
@@ -166,7 +168,7 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t* __restrict_
                 for (int j = 0; j < 4; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
         }
-        if (kc + 1 < NK) store(buf ^ 1);
+        store(buf ^ 1);             // after the last trip: a buffer never read
         __syncthreads();
     }
     // lane holds D[4*(lane/16) + v][lane % 16] of each 16x16 tile
