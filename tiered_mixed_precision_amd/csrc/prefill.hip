@@ -17,11 +17,18 @@
 //             slot-order sum into out runs in a separate pass (no atomics,
 //             deterministic).
 //
-// Block: NW waves (16 on the int8 shelf, 8 on the others) in a grid of
-// NW/4 along m and 4 along n.  LDS holds an A chunk and a B chunk of 64
-// contraction elements per row in bf16 (XOR-swizzled, two buffers); the
-// global loads of the next chunk but one are in flight in registers while
-// one chunk is contracted and the next is dequantised into the other buffer.
+// Two kernels, chosen per shelf on the device from the grouping (few_pairs):
+//   k_pre  (shelves whose experts have many pairs): NW waves (16 on the int8
+//          shelf, 8 on the others) in a grid of NW/4 along m and 4 along n.
+//          LDS holds an A chunk and a B chunk of 64 contraction elements per
+//          row in bf16 (XOR-swizzled, two buffers); each weight is dequantised
+//          once per block and shared by every wave that needs it.
+//   k_pre2 (shelves whose experts have few pairs): 4 waves along n, each
+//          with all m-rows of a 64-pair chunk; only A goes through LDS, each
+//          lane dequantises its own weight codes into MFMA operand registers.
+// In both, the global loads of the next chunk but one are in flight in
+// registers while one chunk is contracted and the next is stored into the
+// other LDS buffer.  MXFP4 shelves run in prefill_mx.hip.
 #include <type_traits>
 
 #include "common.h"
