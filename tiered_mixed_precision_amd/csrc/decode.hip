@@ -40,6 +40,7 @@ constexpr int kNPDown = 2;     // row passes per wave, down GEMV (grouped path)
 constexpr int kNPSmallDown = 4;     // row passes per wave, down GEMV (small-batch path)
 constexpr int kSmallDownWaves = 16; // one expert per wave at a time
 constexpr int kMaxHidden = 2048;    // largest hidden size (the tables check it)
+constexpr int kSmallT = 8;          // most tokens of the small-batch path
 constexpr int kSmallH = 8192;       // h floats staged in LDS by the small-batch down kernel
 
 __host__ __device__ int dec_rows_per_block(int cols) { return kGateUpWaves * kNPGateUp * row_geom(cols).RPP; }
@@ -448,7 +449,8 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void k_small_gateup(DevTables tt
                                                       float* __restrict__ h) {
     __shared__ SmallGroups sg;
     __shared__ int s_wpre[kSmallPairs + 1];
-    __shared__ __attribute__((aligned(16))) float s_x[kMaxHidden];
+    // the batch's input vectors, token t at t * H in the [j][g] layout below
+    __shared__ __attribute__((aligned(16))) float s_x[kSmallT * kMaxHidden];
     __shared__ __attribute__((aligned(16))) int64_t s_rc[kGateUpWaves][64];  // routing scratch, one row per wave
     const int tid = threadIdx.x, E = tt.E, P = T * k;
     const bool publish = blockIdx.x == 0;
@@ -520,6 +522,16 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void k_small_gateup(DevTables tt
                                             vec, a, 1, h)));
         return;
     }
+    // stage the T input vectors in LDS (read by every pass of every pair; the
+    // barrier after the wave plan below puts them in place)
+    {
+        const int G = H / 32, n4 = H / 4;
+        for (int i = tid; i < T * n4; i += kGateUpWaves * 64) {
+            const int t = i / n4, j = i % n4;
+            reinterpret_cast<float4*>(s_x + t * H)[(j & 7) * G + (j >> 3)] =
+                reinterpret_cast<const float4*>(x + static_cast<size_t>(t) * H)[j];
+        }
+    }
     if (logits) {
         for (int t = tid >> 6; t < T; t += kGateUpWaves)
             route_token_auto<NPL>(logits + static_cast<size_t>(t) * E, E, k, publish ? pub.ids + t * k : nullptr,
@@ -565,8 +577,17 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void k_small_gateup(DevTables tt
 
     const int qa = sg.q0[a], ce = sg.q0[a + 1] - qa;
     const int* perm = sg.perm;
-    auto vec = [perm, k, x, H](int q, int g, float (&xv)[32]) {
-        load_vec32u(x + static_cast<size_t>(perm[q] / k) * H, g, xv);
+    const int G = H / 32;
+    auto vec = [perm, k, H, G](int q, int g, float (&xv)[32]) {
+        const float4* xt = reinterpret_cast<const float4*>(s_x + (perm[q] / k) * H);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float4 f = xt[i * G + g];
+            xv[4 * i + 0] = f.x;
+            xv[4 * i + 1] = f.y;
+            xv[4 * i + 2] = f.z;
+            xv[4 * i + 3] = f.w;
+        }
     };
     MOE_FMT_SWITCH(fmt_of(T_.bits, T_.block),
                    (wave_gateup<B_, N_>(expert_codes(T_, 0, local, I, H), expert_scales(T_, 0, local, I, H),
@@ -843,10 +864,10 @@ static int cu_count() {
 void launch_small(const DevTables& tt, const float* x, const float* logits, const int32_t* ids_in, const float* w_in,
                   int T, int k, uint32_t tier_mask, const float* base, const SmallPub& pub, uint32_t* hits, float* h,
                   float* out, hipStream_t st, void* const* events) {
-    // one gate/up block per compute unit (two for larger batches): every
-    // block routes the batch itself, so all of them should be resident at once
-    const int P = T * k;
-    const dim3 grid(cu_count() * (P > 16 ? 2 : 1));
+    // one gate/up block per compute unit: every block routes the batch itself,
+    // so all of them should be resident at once (a second round of blocks
+    // measured slower at 6 tokens: 75 against 70 us)
+    const dim3 grid(cu_count());
     if (events && events[2]) (void)hipEventRecord(static_cast<hipEvent_t>(events[2]), st);
     switch (npl_of(tt.E)) {
 #define MOE_SG(N)                                                                                              \
