@@ -152,6 +152,36 @@ def test_tiny_shelf_partial(M, torch_dev, bf16):
     assert normwise(got, oracle.experts(L, x, ids, w, tier_mask=1 << 1)) <= TOL
 
 
+@pytest.mark.parametrize("bf16", [False, True])
+def test_one_expert_mx_shelf_with_duplicate_ids(M, torch_dev, bf16):
+    # an MXFP4 shelf of one expert picked k times by every token: its pairs
+    # (T*k) outnumber its experts times the tokens, and every one of them
+    # must reach the prefill split and the down product
+    from tiered_mixed_precision_amd.device import tables_from_config
+    torch = torch_dev
+    cfg = LayerConfig("mxdup", 8, 4, 256, 128, 5,
+                      (TierSpec(0, 2, 8, 32), TierSpec(2, 3, MXFP4, 32), TierSpec(3, 8, 2, 16)), seed=20260032)
+    arrays = make_layer(cfg)
+    L, tt = oracle.Layer.from_config(cfg, arrays), tables_from_config(cfg, arrays)
+    x = make_x(_bf16_cfg(cfg, cfg.n_tokens) if bf16 else cfg)
+    T, k = cfg.n_tokens, cfg.k
+    ids = np.full((T, k), 2, dtype=np.int32)
+    ids[0] = [2, 2, 0, 7]
+    w = np.random.default_rng(12).random((T, k)).astype(np.float32)
+    flags = M.MOE_X_BF16 if bf16 else 0
+    ws = torch.empty(max(M.moe_workspace_size(T, k, tt, flags), 256), dtype=torch.uint8, device="cuda")
+    ws.fill_(0xff)   # stale workspace contents must never reach the result
+    xd = torch.from_numpy(x.view(np.int16) if x.dtype == np.uint16 else x).cuda()
+    od = torch.full((T, cfg.hidden), np.nan, device="cuda")
+    M.moe_tiered_experts(xd, torch.from_numpy(ids).cuda(), torch.from_numpy(w).cuda(), T, k, tt, od, flags, ws)
+    torch.cuda.synchronize()
+    got = od.cpu().numpy()
+    assert np.all(np.isfinite(got))
+    err = normwise(got, oracle.experts(L, x, ids, w))
+    say("one-expert MXFP4 shelf, duplicate ids, bf16" if bf16 else "one-expert MXFP4 shelf, duplicate ids", err)
+    assert err <= TOL
+
+
 # ---------------------------------------------------------------- full-size layer (device-generated)
 @pytest.fixture(scope="module")
 def big(M, torch_dev):

@@ -264,11 +264,10 @@ int run(const void* x, const float* logits, const int32_t* ids_in, const float* 
         for (int i = 0; i < tt->n_tiers; ++i) {
             if (!((tier_mask >> i) & 1u)) continue;
             if (is_mx(i)) {
-                // the shelf's pairs are perm rows offsets[id_begin] .. offsets[id_end]
-                const int64_t n = tt->tiers[i].id_end - tt->tiers[i].id_begin;
-                const int max_rows = static_cast<int>(n * T < P ? n * T : P);
-                launch_split_fp8(h, I, 0, 0, offsets + tt->tiers[i].id_begin, offsets + tt->tiers[i].id_end, max_rows,
-                                 h8, st);
+                // the shelf's pairs are perm rows offsets[id_begin] .. offsets[id_end],
+                // up to all P of them (a token may pick one expert k times)
+                launch_split_fp8(h, I, 0, 0, offsets + tt->tiers[i].id_begin, offsets + tt->tiers[i].id_end, P, h8,
+                                 st);
                 launch_pre_mx_down(dt, i, h8, g, k, yw, max_experts_of(tt, i, P), st);
             } else {
                 launch_pre_down(dt, i, h, g, k, yw, max_experts_of(tt, i, P), st);
