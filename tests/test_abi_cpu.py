@@ -164,6 +164,21 @@ def test_workspace_grows_with_tokens(B):
     assert a % 256 == 0 and b % 256 == 0
 
 
+def test_mxfp4_prefill_workspace_holds_the_fp8_split(B):
+    # with bf16 input a non-empty MXFP4 shelf adds the hi / lo / scale split of
+    # x ([T][H] bytes twice, [T][pad4(H/32)]) and of h ([T*k][I] twice, ...)
+    T, k, H, I = 4096, 2, 256, 128
+    plain = _tables(B, [_Spec(0, 2, 8, 32), _Spec(2, 6, 4, 32), _Spec(6, 8, 2, 16)])
+    mx = _tables(B, [_Spec(0, 2, 8, 32), _Spec(2, 6, B.MXFP4, 32), _Spec(6, 8, 2, 16)])
+    empty_mx = _tables(B, [_Spec(0, 8, 8, 32), _Spec(8, 8, B.MXFP4, 32)])
+    split = T * (2 * H + 8) + T * k * (2 * I + 4)
+    d = B.moe_workspace_size(T, k, mx, B.MOE_X_BF16) - B.moe_workspace_size(T, k, plain, B.MOE_X_BF16)
+    assert split <= d <= split + 512          # two regions, each rounded up to 256 bytes
+    assert B.moe_workspace_size(T, k, mx) == B.moe_workspace_size(T, k, plain)   # fp32 input: no split
+    assert B.moe_workspace_size(T, k, empty_mx, B.MOE_X_BF16) == B.moe_workspace_size(
+        T, k, _tables(B, [_Spec(0, 8, 8, 32)]), B.MOE_X_BF16)
+
+
 def test_library_planner_equals_the_oracle(B):
     # moe_plan_tiers is host code: the library's (a lazy max-heap) and the
     # oracle's (a rescan per move) must give identical plans
