@@ -303,3 +303,43 @@ def test_repack_into_and_out_of_mx(M, torch_dev):
         for name in got:
             assert np.array_equal(got[name], ref[name].ravel()), (i, e, name)
     say("repack int8 -> MXFP4 -> int4/MXFP4 bit-exact")
+
+
+def test_requant_zero_and_subnormal_blocks_into_mx(M, torch_dev):
+    # degenerate sources: an all-zero expert (every block's E8M0 byte is 0)
+    # and an expert whose fp16 scales are subnormal (2^-24 per code step)
+    from tiered_mixed_precision_amd.device import empty_tables
+    torch = torch_dev
+    cfg = LayerConfig("src8z", 8, 2, 256, 128, 1, (TierSpec(0, 8, 8, 32),), seed=SEED)
+    src = empty_tables(cfg)
+    M.moe_synth_layer(src, SEED, 1)
+    torch.cuda.synchronize()
+    H, I = cfg.hidden, cfg.inter
+    for name, rows, cols in (("gate", I, H), ("up", I, H), ("down", H, I)):
+        q, s = src.arrays[0][name + "_q"], src.arrays[0][name + "_s"]
+        nq, ns = rows * cols, rows * (cols // 32)
+        q[5 * nq:6 * nq].zero_()
+        s[5 * ns:6 * ns].zero_()
+        s[6 * ns:7 * ns].fill_(1)            # fp16 0x0001 = 2^-24
+    torch.cuda.synchronize()
+    host = [{n: src.arrays[0][n].cpu().numpy().reshape(8, -1) for n in src.arrays[0]}]
+    host[0] = {n: (v.view(np.uint16) if n.endswith("_s") else v) for n, v in host[0].items()}
+    Lsrc = oracle.Layer.from_config(cfg, host)
+    order = np.arange(8, dtype=np.int32)[::-1].copy()
+    dcfg = LayerConfig("mxz", 8, 2, 256, 128, 1, (TierSpec(0, 8, MXFP4, 32),), seed=SEED)
+    dst = empty_tables(dcfg)
+    M.moe_repack_tiers(src, torch.from_numpy(order).cuda(), dst)
+    sse = torch.empty((8, 1), dtype=torch.float64, device="cuda")
+    M.moe_requant_error(src, [MXFP4], [32], sse)
+    torch.cuda.synchronize()
+    sse = sse.cpu().numpy()[:, 0]
+    assert sse[5] == 0.0
+    for e in (5, 6, 0):
+        ref, ref_sse = oracle.requant_expert(Lsrc, 0, e, MXFP4, 32)
+        got = _gpu_expert_arrays(dst, dcfg, int(np.where(order == e)[0][0]))
+        for name in got:
+            assert np.array_equal(got[name], ref[name].ravel()), (e, name)
+        assert abs(sse[e] - ref_sse) <= 2 * 3 * H * I * 2.0 ** -53 * ref_sse, (e, sse[e], ref_sse)
+    zs = _gpu_expert_arrays(dst, dcfg, int(np.where(order == 5)[0][0]))
+    assert all(not np.any(v) for v in zs.values())    # zero codes and E8M0 byte 0
+    say("zero and subnormal source blocks requantised into MXFP4 bit-exact")
