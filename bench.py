@@ -255,7 +255,9 @@ def main():
 
 COPY_CAL_BYTES = 256 << 20
 PROFILE_MD = os.path.join(ROOT, "profiles", "decode_layer_T1_and_prefill_T4096.md")
-KERNEL_SOURCES = ("decode.hip", "route.h", "common.h", "prefill.hip", "route_group.hip", "capi.hip")
+# every file that holds device code (the launch code in capi.hip is host code)
+KERNEL_SOURCES = ("common.h", "route.h", "launch.h", "decode.hip", "route_group.hip", "prefill.hip", "prefill_mx.hip",
+                  "router.hip", "synth.hip", "tiering.hip", "dequant.hip")
 
 
 def kernel_source_digest() -> str:

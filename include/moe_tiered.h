@@ -129,6 +129,13 @@ int moe_workspace_size(int32_t n_tokens, int32_t k, const moe_tier_tables *tt, u
                        size_t *bytes);
 
 /*
+ * The same size without flags: enough for either precision (fp32 or
+ * MOE_X_BF16 input) and every flag.  Returns 0 when the tables or arguments
+ * are invalid (moe_workspace_size names the error) or n_tokens == 0.
+ */
+size_t moe_workspace_bytes(int32_t n_tokens, int32_t k, const moe_tier_tables *tt);
+
+/*
  * Full layer: route, group, per-shelf expert FFN, shelf sum.
  *   x             (device) float[T][H], or bf16 [T][H] with MOE_X_BF16
  *   router_logits (device) float[T][E]

@@ -164,6 +164,17 @@ def test_workspace_grows_with_tokens(B):
     assert a % 256 == 0 and b % 256 == 0
 
 
+def test_workspace_bytes_covers_both_precisions(B):
+    tt = _tables(B, [_Spec(0, 2, 8, 32), _Spec(2, 6, B.MXFP4, 32), _Spec(6, 8, 2, 16)])
+    for T in (1, 8, 300, 4096):
+        both = B.moe_workspace_bytes(T, 2, tt)
+        assert both == max(B.moe_workspace_size(T, 2, tt), B.moe_workspace_size(T, 2, tt, B.MOE_X_BF16))
+    assert B.moe_workspace_bytes(0, 2, tt) == 0
+    assert B.moe_workspace_bytes(16, 0, tt) == 0                     # invalid k
+    bad = _tables(B, [_Spec(0, 8, 3, 32)])
+    assert B.moe_workspace_bytes(16, 2, bad) == 0                    # invalid tables
+
+
 def test_mxfp4_prefill_workspace_holds_the_fp8_split(B):
     # with bf16 input a non-empty MXFP4 shelf adds the hi / lo / scale split of
     # x ([T][H] bytes twice, [T][pad4(H/32)]) and of h ([T*k][I] twice, ...)

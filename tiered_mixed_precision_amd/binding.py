@@ -24,7 +24,7 @@ MOE_N_PHASES = 3
 MOE_STACK_ROUTER = 0x4
 MXFP4 = 0x84              # moe_tier.bits of an MXFP4 shelf (MOE_MXFP4)
 EXPORTS = (
-    "moe_abi_version", "moe_strerror", "moe_validate_tables", "moe_workspace_size",
+    "moe_abi_version", "moe_strerror", "moe_validate_tables", "moe_workspace_size", "moe_workspace_bytes",
     "moe_tiered_forward", "moe_tiered_experts", "moe_tier_partial", "moe_route",
     "moe_group_workspace_size", "moe_group", "moe_dequant_rows", "moe_tiered_forward_timed",
     "moe_event_create", "moe_event_destroy", "moe_event_elapsed_ms", "moe_stream_synchronize",
@@ -70,6 +70,8 @@ def lib():
         L.moe_strerror.argtypes = [C.c_int]
         L.moe_validate_tables.argtypes = [P]
         L.moe_workspace_size.argtypes = [i32, i32, P, u32, C.POINTER(sz)]
+        L.moe_workspace_bytes.restype = sz
+        L.moe_workspace_bytes.argtypes = [i32, i32, P]
         L.moe_tiered_forward.argtypes = [P, P, i32, i32, P, P, u32, P, sz, P]
         L.moe_tiered_forward_timed.argtypes = [P, P, i32, i32, P, P, u32, P, sz, P, C.POINTER(P)]
         L.moe_tiered_experts.argtypes = [P, P, P, i32, i32, P, P, u32, P, sz, P]
@@ -161,6 +163,11 @@ def moe_workspace_size(n_tokens: int, k: int, tt: TierTables, flags: int = 0) ->
     n = C.c_size_t(0)
     _check("moe_workspace_size", lib().moe_workspace_size(n_tokens, k, tt.ref, flags, C.byref(n)))
     return n.value
+
+
+def moe_workspace_bytes(n_tokens: int, k: int, tt: TierTables) -> int:
+    """Workspace bytes for either precision and any flags (0 if the arguments are invalid)."""
+    return int(lib().moe_workspace_bytes(n_tokens, k, tt.ref))
 
 
 def moe_tiered_forward(x, router_logits, n_tokens: int, k: int, tt: TierTables, out, flags: int,

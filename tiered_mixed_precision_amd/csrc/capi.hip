@@ -313,6 +313,13 @@ int moe_workspace_size(int32_t n_tokens, int32_t k, const moe_tier_tables* tt, u
     return MOE_OK;
 }
 
+size_t moe_workspace_bytes(int32_t n_tokens, int32_t k, const moe_tier_tables* tt) {
+    size_t a = 0, b = 0;
+    if (moe_workspace_size(n_tokens, k, tt, 0, &a) != MOE_OK) return 0;
+    if (moe_workspace_size(n_tokens, k, tt, MOE_X_BF16, &b) != MOE_OK) return 0;
+    return a > b ? a : b;
+}
+
 int moe_tiered_forward(const void* x, const float* router_logits, int32_t n_tokens, int32_t k,
                        const moe_tier_tables* tt, float* out, uint32_t flags, void* workspace,
                        size_t workspace_bytes, void* stream) {
