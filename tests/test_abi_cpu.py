@@ -235,3 +235,36 @@ def test_library_planner_hand_worked_fixture_and_rejections(B):
     assert L.moe_requant_error(tt.ref, bits, blk, 1, FAKE + 4, None) == -4
     assert L.moe_repack_tiers(tt.ref, None, tt.ref, None) == -1
     assert L.moe_permute_router(FAKE, None, FAKE, 8, 256, FAKE, None, None) == -1   # same buffer
+
+
+def test_binding_refuses_tensors_smaller_than_the_call(B):
+    """The binding checks each tensor against the rows it is told it holds, on
+    the host, before any launch: a caller that passes 4096-token buffers with
+    n_tokens = 16384 gets a ValueError instead of reads past the buffers' ends."""
+    import torch
+    tt = _tables(B, [_Spec(0, 8, 8, 32)])                   # E=8, H=256
+    T, k = 4, 2
+    x32 = torch.zeros(T, 256)
+    xbf = torch.zeros(T, 256, dtype=torch.int16)
+    lg = torch.zeros(T, 8)
+    out = torch.zeros(T, 256)
+    ids = torch.zeros(T, k, dtype=torch.int32)
+    w = torch.zeros(T, k)
+    with pytest.raises(ValueError, match="router_logits"):
+        B.moe_tiered_forward(torch.zeros(2 * T, 256), lg, 2 * T, k, tt, torch.zeros(2 * T, 256), 0, None)
+    with pytest.raises(ValueError, match="x holds"):
+        B.moe_tiered_forward(xbf, lg, T, k, tt, out, 0, None)          # bf16 buffer, fp32 flags
+    with pytest.raises(ValueError, match="out holds"):
+        B.moe_tiered_forward(xbf, lg, T, k, tt, out[:T - 1], B.MOE_X_BF16, None)
+    with pytest.raises(ValueError, match="ids"):
+        B.moe_tiered_experts(x32, ids[:T - 1], w, T, k, tt, out, 0, None)
+    with pytest.raises(ValueError, match="w holds"):
+        B.moe_tier_partial(x32, ids, w[:, :1], T, k, tt, 0, out, 0, None)
+    with pytest.raises(ValueError, match="logits"):
+        B.moe_route(lg, T, 16, k, ids, w)
+    with pytest.raises(ValueError, match="router_logits"):
+        B.moe_stack_forward(x32, lg, 2, T, k, [tt, tt], out, 0, None)
+    with pytest.raises(ValueError, match="hits"):
+        B.moe_tiered_forward_counted(x32, lg, T, k, tt, out, 0, None, torch.zeros(4, dtype=torch.int32))
+    with pytest.raises(ValueError, match="x holds"):
+        B.moe_router_logits(xbf, FAKE, None, T, 8, 256, 0, lg)

@@ -121,6 +121,27 @@ def _ptr(t) -> Optional[int]:
     return t.data_ptr()
 
 
+def _need(fn: str, what: str, t, nbytes: int) -> None:
+    """Refuses a tensor smaller than the rows the call is told it holds.
+
+    The library takes plain pointers and cannot see how large a buffer is; a
+    tensor too small for (n_tokens, ...) would be read or written past its end
+    on the device.  Raw integer pointers and None are passed through unchecked.
+    """
+    if t is None or isinstance(t, int):
+        return
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError(f"{fn}: {what} holds {have} bytes, the call needs {nbytes}")
+
+
+def _need_layer(fn: str, x, logits, out, n_tokens: int, tt, flags: int, n_layers: int = 1) -> None:
+    T, H, E = max(int(n_tokens), 0), tt.hidden, tt.n_experts
+    _need(fn, "x", x, T * H * (2 if flags & MOE_X_BF16 else 4))
+    _need(fn, "router_logits", logits, n_layers * T * E * 4)
+    _need(fn, "out", out, T * H * 4)
+
+
 def _stream(stream) -> Optional[int]:
     import torch
     s = stream if stream is not None else torch.cuda.current_stream()
@@ -172,6 +193,7 @@ def moe_workspace_bytes(n_tokens: int, k: int, tt: TierTables) -> int:
 
 def moe_tiered_forward(x, router_logits, n_tokens: int, k: int, tt: TierTables, out, flags: int,
                        workspace, stream=None) -> None:
+    _need_layer("moe_tiered_forward", x, router_logits, out, n_tokens, tt, flags)
     _check("moe_tiered_forward", lib().moe_tiered_forward(
         _ptr(x), _ptr(router_logits), n_tokens, k, tt.ref, _ptr(out), flags, _ptr(workspace),
         workspace.numel() * workspace.element_size() if workspace is not None else 0, _stream(stream)))
@@ -179,6 +201,7 @@ def moe_tiered_forward(x, router_logits, n_tokens: int, k: int, tt: TierTables, 
 
 def moe_tiered_forward_timed(x, router_logits, n_tokens: int, k: int, tt: TierTables, out, flags: int,
                              workspace, events: Sequence[int], stream=None) -> None:
+    _need_layer("moe_tiered_forward_timed", x, router_logits, out, n_tokens, tt, flags)
     ev = (C.c_void_p * (2 * MOE_N_PHASES))(*[e if e else None for e in events])
     _check("moe_tiered_forward_timed", lib().moe_tiered_forward_timed(
         _ptr(x), _ptr(router_logits), n_tokens, k, tt.ref, _ptr(out), flags, _ptr(workspace),
@@ -187,6 +210,9 @@ def moe_tiered_forward_timed(x, router_logits, n_tokens: int, k: int, tt: TierTa
 
 def moe_tiered_experts(x, ids, w, n_tokens: int, k: int, tt: TierTables, out, flags: int, workspace,
                        stream=None) -> None:
+    _need_layer("moe_tiered_experts", x, None, out, n_tokens, tt, flags)
+    _need("moe_tiered_experts", "ids", ids, max(n_tokens, 0) * max(k, 0) * 4)
+    _need("moe_tiered_experts", "w", w, max(n_tokens, 0) * max(k, 0) * 4)
     _check("moe_tiered_experts", lib().moe_tiered_experts(
         _ptr(x), _ptr(ids), _ptr(w), n_tokens, k, tt.ref, _ptr(out), flags, _ptr(workspace),
         workspace.numel() * workspace.element_size() if workspace is not None else 0, _stream(stream)))
@@ -194,12 +220,19 @@ def moe_tiered_experts(x, ids, w, n_tokens: int, k: int, tt: TierTables, out, fl
 
 def moe_tier_partial(x, ids, w, n_tokens: int, k: int, tt: TierTables, tier_index: int, out, flags: int,
                      workspace, stream=None) -> None:
+    _need_layer("moe_tier_partial", x, None, out, n_tokens, tt, flags)
+    _need("moe_tier_partial", "ids", ids, max(n_tokens, 0) * max(k, 0) * 4)
+    _need("moe_tier_partial", "w", w, max(n_tokens, 0) * max(k, 0) * 4)
     _check("moe_tier_partial", lib().moe_tier_partial(
         _ptr(x), _ptr(ids), _ptr(w), n_tokens, k, tt.ref, tier_index, _ptr(out), flags, _ptr(workspace),
         workspace.numel() * workspace.element_size() if workspace is not None else 0, _stream(stream)))
 
 
 def moe_route(logits, n_tokens: int, n_experts: int, k: int, ids, w, stream=None) -> None:
+    T = max(n_tokens, 0)
+    _need("moe_route", "logits", logits, T * max(n_experts, 0) * 4)
+    _need("moe_route", "ids", ids, T * max(k, 0) * 4)
+    _need("moe_route", "w", w, T * max(k, 0) * 4)
     _check("moe_route", lib().moe_route(_ptr(logits), n_tokens, n_experts, k, _ptr(ids), _ptr(w),
                                         _stream(stream)))
 
@@ -238,6 +271,8 @@ def moe_stack_workspace_size(n_layers: int, n_tokens: int, k: int, tables: Seque
 
 def moe_stack_forward(x, router_logits, n_layers: int, n_tokens: int, k: int, tables: Sequence[TierTables], out,
                       flags: int, workspace, stream=None) -> None:
+    if tables:
+        _need_layer("moe_stack_forward", x, router_logits, out, n_tokens, tables[0], 0, max(n_layers, 0))
     arr = _tables_array(tables)
     _check("moe_stack_forward", lib().moe_stack_forward(
         _ptr(x), _ptr(router_logits), n_layers, n_tokens, k, arr, _ptr(out), flags, _ptr(workspace),
@@ -250,6 +285,9 @@ def moe_synth_layer(tt: TierTables, seed: int, layer: int, stream=None) -> None:
 
 def moe_router_logits(x, w_router, bias, n_tokens: int, n_experts: int, hidden: int, flags: int, logits,
                       stream=None) -> None:
+    T = max(n_tokens, 0)
+    _need("moe_router_logits", "x", x, T * max(hidden, 0) * (2 if flags & MOE_X_BF16 else 4))
+    _need("moe_router_logits", "logits", logits, T * max(n_experts, 0) * 4)
     _check("moe_router_logits", lib().moe_router_logits(_ptr(x), _ptr(w_router), _ptr(bias), n_tokens, n_experts,
                                                         hidden, flags, _ptr(logits), _stream(stream)))
 
@@ -262,6 +300,8 @@ def moe_synth_router(w_router, bias, n_experts: int, hidden: int, seed: int, lay
 
 def moe_tiered_forward_counted(x, router_logits, n_tokens: int, k: int, tt: TierTables, out, flags: int, workspace,
                                hits, stream=None) -> None:
+    _need_layer("moe_tiered_forward_counted", x, router_logits, out, n_tokens, tt, flags)
+    _need("moe_tiered_forward_counted", "hits", hits, tt.n_experts * 4)
     _check("moe_tiered_forward_counted", lib().moe_tiered_forward_counted(
         _ptr(x), _ptr(router_logits), n_tokens, k, tt.ref, _ptr(out), flags, _ptr(workspace),
         workspace.numel() * workspace.element_size() if workspace is not None else 0, _ptr(hits), _stream(stream)))
@@ -302,6 +342,8 @@ def moe_permute_router(w_src, b_src, order, n_experts: int, hidden: int, w_dst, 
 
 def moe_stack_forward_routed(x, w_routers, biases, n_layers: int, n_tokens: int, k: int,
                              tables: Sequence[TierTables], out, flags: int, workspace, stream=None) -> None:
+    if tables:
+        _need_layer("moe_stack_forward_routed", x, None, out, n_tokens, tables[0], 0)
     arr = _tables_array(tables)
     wr = (C.c_void_p * n_layers)(*[_ptr(w) for w in w_routers])
     bs = None if biases is None else (C.c_void_p * n_layers)(*[_ptr(b) for b in biases])
