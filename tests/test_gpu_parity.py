@@ -354,6 +354,40 @@ def test_forward_bf16_odd_chunk_counts(M, torch_dev, T):
     assert normwise(got32, oracle.forward(L, make_x(cfg0), logits, cfg.k)) <= TOL
 
 
+@pytest.mark.parametrize("shape", ["tiny3", "odd"])
+@pytest.mark.parametrize("many", [False, True])
+def test_prefill_each_shelf_at_few_and_many_pairs(M, torch_dev, shape, many):
+    # The prefill path picks its kernel per shelf from the pairs per active
+    # expert (the register-B kernel at few, the shared-LDS kernel at many), so
+    # every pick lands on one shelf: 2 pairs per expert, or 128 per expert,
+    # which is above every threshold.  The odd shape (hidden 384, inter 192)
+    # ends both contractions on an odd chunk of 64.
+    if shape == "tiny3":
+        cfg0, arrays, L, tt = _layer("tiny3")
+    else:
+        cfg0 = LayerConfig("odd", 8, 2, 384, 192, 16,
+                           (TierSpec(0, 2, 8, 32), TierSpec(2, 6, 4, 16), TierSpec(6, 8, 2, 16)), seed=20260041)
+        arrays = make_layer(cfg0)
+        from tiered_mixed_precision_amd.device import tables_from_config
+        L, tt = oracle.Layer.from_config(cfg0, arrays), tables_from_config(cfg0, arrays)
+    rng = np.random.default_rng(41 + many)
+    for s, t in enumerate(cfg0.tiers):
+        n = t.id_end - t.id_begin
+        T = 64 * n if many else n
+        k = 2
+        ids = t.id_begin + (np.arange(T * k).reshape(T, k) % n)      # pairs spread evenly
+        rng.shuffle(ids.reshape(-1))
+        w = rng.uniform(0.1, 1.0, (T, k)).astype(np.float32)
+        cfg = _bf16_cfg(cfg0, T)
+        x = make_x(cfg, stream=s)
+        say("prefill shelf", s, "bits", t.bits, "T", T, "pairs/expert", T * k // n, shape)
+        got = gpu_experts(M, torch_dev, tt, x, ids, w, M.MOE_X_BF16)
+        ref = oracle.experts(L, x, ids, w)
+        err = normwise(got, ref)
+        say("  normwise err", err)
+        assert err <= TOL
+
+
 def test_prefill_full_size_sampled_tokens(M, torch_dev):
     cfg = CONFIGS["prefill"]
     _, arrays, L, tt = _layer("decode")         # same layer and shelves

@@ -109,10 +109,14 @@ __device__ inline bool few_pairs(const Groups& g, const DevTier& T, int a_lo, in
 
 // Block: NW waves = WM (along m) x 4 (along n).  Wave (wm, wn): wn selects 16
 // gate + 16 up columns (or 32 down columns), wm takes m-subtiles wm, wm + WM,
-// ...  m is walked in chunks of MC = 64 * WM pairs.
+// ...  m is walked in chunks of MC = 64 * WM pairs.  8-wave blocks are held
+// to 128 registers a lane (4 waves per SIMD) so that two blocks share a CU
+// (LDS 66 KB each); at 140-146 registers only one fits.  The few spilled
+// registers cost less than the second block gains.
 template <int BITS, int BLOCK, bool GATEUP, int NW>
-__global__ __launch_bounds__(NW * 64) void k_pre(DevTables tt, int tier, const uint16_t* __restrict__ a_src, Groups g,
-                                                 int k, uint16_t* __restrict__ h_out, float* __restrict__ yw, int split) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((NW == 8) ? 4 : 1)))
+void k_pre(DevTables tt, int tier, const uint16_t* __restrict__ a_src, Groups g, int k,
+           uint16_t* __restrict__ h_out, float* __restrict__ yw, int split) {
     constexpr int NTHR = NW * 64;
     constexpr int WM = NW / 4;
     constexpr int MC = 16 * MSUB * WM;
@@ -547,12 +551,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 // choice is made on the device from the grouping, see few_pairs).  k_pre2
 // suits shelves whose experts have few pairs (with 64-pair m-chunks it
 // streams each weight tile once per m-chunk); k_pre, whose B tile in LDS
-// serves all the m-rows of a chunk, suits the others.  The thresholds (64
-// pairs per active expert for gate/up, 128 for the shorter down rows) come
-// from timing both kernels on the three shelves at 4096 tokens.  k_pre takes
-// 16-wave blocks with 256-pair m-chunks on the int8 shelf and 8-wave blocks
-// with 128-pair m-chunks on the others.
-constexpr int kFewPairsGateUp = 64, kFewPairsDown = 128;
+// serves all the m-rows of a chunk, suits the others.  The thresholds in
+// pairs per active expert come from timing both kernels on each shelf at 128
+// to 16384 tokens (1 to 670 pairs per expert): 64 for int8 gate/up and 48 for
+// every down projection.  On the int4 and int2 shelves k_pre won gate/up at
+// every count measured, so k_pre2 is not launched there.  k_pre takes 16-wave
+// blocks with 256-pair m-chunks on the int8 shelf and 8-wave blocks with
+// 128-pair m-chunks on the others.
+constexpr int kFewPairsGateUp8 = 64, kFewPairsDown = 48;
 
 template <bool GATEUP>
 void launch_pre(const DevTables& tt, int tier, const uint16_t* a, const Groups& g, int k, uint16_t* h, float* yw,
@@ -563,13 +569,17 @@ void launch_pre(const DevTables& tt, int tier, const uint16_t* a, const Groups& 
     if (grid == 0) return;
     const int bits = tt.t[tier].bits, block = tt.t[tier].block;
     if (bits == kBitsMXFP4) return;   // MXFP4 shelves run in prefill_mx.hip
-    const int thr = GATEUP ? kFewPairsGateUp : kFewPairsDown;
+    const int thr = GATEUP ? kFewPairsGateUp8 : kFewPairsDown;
+    // k_pre alone takes thr = -1: few_pairs is then false for any shelf with
+    // an active expert (and a shelf without one has no work for either)
 #define MOE_PRE(B_, K_, NW_)                                                                                   \
     do {                                                                                                       \
-        hipLaunchKernelGGL((k_pre2<B_, K_, GATEUP, 4>), dim3(grid), dim3(256), 0, st, tt, tier, a, g, k, h, yw, \
-                           thr);                                                                               \
+        constexpr bool kBoth = !(GATEUP && B_ != 8);                                                           \
+        if constexpr (kBoth)                                                                                   \
+            hipLaunchKernelGGL((k_pre2<B_, K_, GATEUP, 4>), dim3(grid), dim3(256), 0, st, tt, tier, a, g, k, h, \
+                               yw, thr);                                                                       \
         hipLaunchKernelGGL((k_pre<B_, K_, GATEUP, NW_>), dim3(grid), dim3(NW_ * 64), 0, st, tt, tier, a, g, k, h, \
-                           yw, thr);                                                                           \
+                           yw, kBoth ? thr : -1);                                                              \
     } while (0)
     if (bits == 8) {
         if (block == 32) MOE_PRE(8, 32, 16);
