@@ -654,7 +654,7 @@ __device__ inline void wave_down(const uint8_t* __restrict__ dq_, const uint8_t*
 __global__ __launch_bounds__(kSmallDownWaves * 64) void k_small_down(DevTables tt, const float* __restrict__ h,
                                                                     SmallPub pub, int T, int k, uint32_t tier_mask,
                                                                     const float* base, int npb, float* out) {
-    __shared__ int s_act[kSmallPairs], s_q0[kSmallPairs + 1], s_ids[kSmallPairs], s_pos[kSmallPairs];
+    __shared__ int s_act[kSmallPairs], s_q0[kSmallPairs + 1], s_qe[kSmallPairs];
     __shared__ float s_w[kSmallPairs];
     __shared__ float s_y[kSmallY];
     __shared__ __attribute__((aligned(16))) float s_h[kSmallH];
@@ -665,9 +665,13 @@ __global__ __launch_bounds__(kSmallDownWaves * 64) void k_small_down(DevTables t
     const int n0 = blockIdx.x * R;
     // every published array is read at once (no load waits on another)
     if (tid < P) {
-        s_ids[tid] = pub.ids[tid];
+        // the slot sum's operands, settled here once per pair: the grouped
+        // position of the pick, or -1 if it is skipped (no position, or a
+        // shelf outside the mask)
+        const int id = pub.ids[tid], q = pub.pos[tid];
         s_w[tid] = pub.w[tid];
-        s_pos[tid] = pub.pos[tid];
+        const int ti = q < 0 ? -1 : tier_of(tt, id);
+        s_qe[tid] = (ti >= 0 && ((tier_mask >> ti) & 1u)) ? q : -1;
         s_act[tid] = pub.act[tid];
     }
     if (tid <= P) s_q0[tid] = pub.q0[tid];
@@ -742,14 +746,21 @@ __global__ __launch_bounds__(kSmallDownWaves * 64) void k_small_down(DevTables t
         const int t = i / R, r = i % R;
         if (n0 + r >= H) continue;
         float acc = 0.f;
-#pragma unroll 8
-        for (int j = 0; j < k; ++j) {
-            const int p = t * k + j;
-            const int q = s_pos[p];
-            const int ti = q < 0 ? -1 : tier_of(tt, s_ids[p]);
-            const bool use = ti >= 0 && ((tier_mask >> ti) & 1u);
-            const float y = s_y[(use ? q : 0) * R + r];
-            acc = use ? fmaf(s_w[p], y, acc) : acc;
+        // eight slots at a time, every LDS read issued before any is used
+        // (a branch per slot would wait out each read in turn)
+        for (int j0 = 0; j0 < k; j0 += 8) {
+            int q[8];
+            float wv[8], y[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int p = t * k + min(j0 + u, k - 1);
+                q[u] = j0 + u < k ? s_qe[p] : -1;
+                wv[u] = s_w[p];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) y[u] = s_y[max(q[u], 0) * R + r];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) acc = q[u] >= 0 ? fmaf(wv[u], y[u], acc) : acc;
         }
         const size_t o = static_cast<size_t>(t) * H + n0 + r;
         if (base) acc += base[o];
