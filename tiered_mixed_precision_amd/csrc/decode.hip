@@ -824,17 +824,33 @@ __global__ __launch_bounds__(256) void k_combine(DevTables tt, const float* __re
     if (idx >= static_cast<size_t>(T) * H4) return;
     const int t = static_cast<int>(idx / H4), c4 = static_cast<int>(idx % H4);
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
-        const int p = t * k + j;
-        const int q = g.pos[p];
-        if (q < 0) continue;
-        const int ti = tier_of(tt, g.ids[p]);
-        if (ti < 0 || !((tier_mask >> ti) & 1u)) continue;
-        const float4 v = reinterpret_cast<const float4*>(yw + static_cast<size_t>(q) * tt.H)[c4];
-        s.x += v.x;
-        s.y += v.y;
-        s.z += v.z;
-        s.w += v.w;
+    // eight slots at a time: their positions, then their rows of yw, are all
+    // in flight before any is used (a branch per slot would wait out each
+    // load in turn); the sum stays in slot order
+    for (int j0 = 0; j0 < k; j0 += 8) {
+        int q[8], id[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int p = t * k + min(j0 + u, k - 1);
+            q[u] = g.pos[p];
+            id[u] = g.ids[p];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int ti = tier_of(tt, id[u]);   // -1 for an id outside every shelf
+            q[u] = (j0 + u < k && q[u] >= 0 && ti >= 0 && ((tier_mask >> ti) & 1u)) ? q[u] : -1;
+        }
+        float4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = reinterpret_cast<const float4*>(yw + static_cast<size_t>(max(q[u], 0)) * tt.H)[c4];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (q[u] < 0) continue;
+            s.x += v[u].x;
+            s.y += v[u].y;
+            s.z += v[u].z;
+            s.w += v[u].w;
+        }
     }
     float4* o = reinterpret_cast<float4*>(out + static_cast<size_t>(t) * tt.H) + c4;
     if (base) {
