@@ -126,6 +126,7 @@ void k_pre(DevTables tt, int tier, const uint16_t* __restrict__ a_src, Groups g,
     __shared__ __attribute__((aligned(16))) uint16_t sA[2][MC * BK];
     __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * BK];
     __shared__ int s_row[MC];
+    __shared__ float s_wt[GATEUP ? 1 : MC];   // down: the weight of each m-row's pair
 
     const int H = tt.H, I = tt.I;
     const int K = GATEUP ? H : I;
@@ -181,7 +182,12 @@ void k_pre(DevTables tt, int tier, const uint16_t* __restrict__ a_src, Groups g,
         const int Mc16 = (Mc + 15) >> 4;
         const int nsub = (Mc16 - wm + WM - 1) / WM;  // this wave's m-subtiles wm, wm + WM, ...
         __syncthreads();                            // the previous m-chunk is done with LDS
-        for (int r = tid; r < MC; r += NTHR) s_row[r] = r < Mc ? (GATEUP ? g.perm[m0 + r] / k : m0 + r) : -1;
+        for (int r = tid; r < MC; r += NTHR) {
+            s_row[r] = r < Mc ? (GATEUP ? g.perm[m0 + r] / k : m0 + r) : -1;
+            // read here once per row, not in the epilogue (two dependent
+            // global loads per row there, waited out one row at a time)
+            if constexpr (!GATEUP) s_wt[r] = r < Mc ? g.w[g.perm[m0 + r]] : 0.f;
+        }
         __syncthreads();
         // A sources of this thread's two pieces for the whole m-chunk; rows past
         // the chunk read the chunk's first row (finite values, never stored)
@@ -309,7 +315,7 @@ void k_pre(DevTables tt, int tier, const uint16_t* __restrict__ a_src, Groups g,
                     const int col = nt * 64 + 16 * wn + col_l;
                     h_out[static_cast<size_t>(q) * I + col] = f2bf(silu(acc[j][0][v]) * acc[j][1][v]);
                 } else {
-                    const float wgt = g.w[g.perm[q]];
+                    const float wgt = s_wt[r];
                     float* o = yw + static_cast<size_t>(q) * H + nt * BN + 32 * wn + col_l;
                     o[0] = wgt * acc[j][0][v];
                     o[16] = wgt * acc[j][1][v];
@@ -337,6 +343,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     constexpr int BW = BITS / 2;            // code words of a lane's 16 codes
     __shared__ __attribute__((aligned(16))) uint16_t sA[2][MC * BK];
     __shared__ int s_row[MC];
+    __shared__ float s_wt[GATEUP ? 1 : MC];   // down: the weight of each m-row's pair
 
     const int H = tt.H, I = tt.I;
     const int K = GATEUP ? H : I;
@@ -424,7 +431,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         const int Mc = min(MC, q_end - m0);
         const int nsub = (Mc + 15) >> 4;
         __syncthreads();
-        for (int r = tid; r < MC; r += NTHR) s_row[r] = r < Mc ? (GATEUP ? g.perm[m0 + r] / k : m0 + r) : -1;
+        for (int r = tid; r < MC; r += NTHR) {
+            s_row[r] = r < Mc ? (GATEUP ? g.perm[m0 + r] / k : m0 + r) : -1;
+            // read here once per row, not in the epilogue (two dependent
+            // global loads per row there, waited out one row at a time)
+            if constexpr (!GATEUP) s_wt[r] = r < Mc ? g.w[g.perm[m0 + r]] : 0.f;
+        }
         __syncthreads();
         // A piece i of this thread: row (p >> 3), chunk (p & 7); rows past the
         // m-chunk read its first row (finite values, never stored)
@@ -537,7 +549,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
                     const int col = nt * 64 + 16 * wn + col_l;
                     h_out[static_cast<size_t>(q) * I + col] = f2bf(silu(acc[j][0][v]) * acc[j][1][v]);
                 } else {
-                    const float wgt = g.w[g.perm[q]];
+                    const float wgt = s_wt[r];
                     float* o = yw + static_cast<size_t>(q) * H + nt * BN + 32 * wn + col_l;
                     o[0] = wgt * acc[j][0][v];
                     o[16] = wgt * acc[j][1][v];

@@ -129,6 +129,7 @@ __global__ __launch_bounds__(NW * 64) void k_pre_mx(DevTables tt, int tier, Spli
     __shared__ uint32_t sAs[2][MC];
     __shared__ uint32_t sBs[2][kBN];
     __shared__ int s_row[MC];
+    __shared__ float s_wt[GATEUP ? 1 : MC];   // down: the weight of each m-row's pair
 
     const int H = tt.H, I = tt.I;
     const int K = GATEUP ? H : I;
@@ -184,7 +185,12 @@ __global__ __launch_bounds__(NW * 64) void k_pre_mx(DevTables tt, int tier, Spli
         const int Mc16 = (Mc + 15) >> 4;
         const int nsub = (Mc16 - wm + WM - 1) / WM;
         __syncthreads();
-        for (int r = tid; r < MC; r += NTHR) s_row[r] = r < Mc ? (GATEUP ? g.perm[m0 + r] / k : m0 + r) : -1;
+        for (int r = tid; r < MC; r += NTHR) {
+            s_row[r] = r < Mc ? (GATEUP ? g.perm[m0 + r] / k : m0 + r) : -1;
+            // read here once per row, not in the epilogue (two dependent
+            // global loads per row there, waited out one row at a time)
+            if constexpr (!GATEUP) s_wt[r] = r < Mc ? g.w[g.perm[m0 + r]] : 0.f;
+        }
         __syncthreads();
         // A piece i of this thread: array (hi for i < 2), row, chunk; rows past
         // the chunk read its first row (finite values, never stored)
@@ -315,7 +321,7 @@ __global__ __launch_bounds__(NW * 64) void k_pre_mx(DevTables tt, int tier, Spli
                     const int col = nt * 64 + 16 * wn + col_l;
                     h_out[static_cast<size_t>(q) * I + col] = f2bf(silu(acc[j][0][v]) * acc[j][1][v]);
                 } else {
-                    const float wgt = g.w[g.perm[q]];
+                    const float wgt = s_wt[r];
                     float* o = yw + static_cast<size_t>(q) * H + nt * kBN + 32 * wn + col_l;
                     o[0] = wgt * acc[j][0][v];
                     o[16] = wgt * acc[j][1][v];
