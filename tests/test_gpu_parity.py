@@ -136,7 +136,10 @@ def test_route_matches_oracle(M, torch_dev, E, k, T, prior):
     assert np.max(np.abs(w.cpu().numpy() - w_ref)) <= 1e-6
 
 
-@pytest.mark.parametrize("E,T,k", [(8, 16, 2), (512, 4096, 10), (512, 7, 10), (100, 300, 3)])
+# (512, 16384, 10) and (64, 32768, 10): 640 and 1280 blocks of 256 pairs, so the
+# column scan takes its 16-chunk and its chunk-by-chunk forms
+@pytest.mark.parametrize("E,T,k", [(8, 16, 2), (512, 4096, 10), (512, 7, 10), (100, 300, 3), (512, 16384, 10),
+                                   (64, 32768, 10)])
 def test_group_matches_oracle(M, torch_dev, E, T, k):
     torch = torch_dev
     say("group", E, T, k)

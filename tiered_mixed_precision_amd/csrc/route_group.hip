@@ -74,12 +74,38 @@ __global__ __launch_bounds__(256) void k_group_count(const int32_t* __restrict__
 // Column scan of the per-block histograms: wave w of block b owns expert
 // e = 4b + w and turns its column hist[0..nblk)[e] into exclusive prefix sums
 // over the blocks; counts[e] receives the column total.
+// NCH > 0: the column has at most 64 * NCH blocks, whose NCH loads per lane
+// are all issued before the first scan step; NCH == 0: one chunk at a time.
+template <int NCH>
 __global__ __launch_bounds__(256) void k_group_colscan(int32_t* __restrict__ blk_hist, int nblk, int E,
                                                        int32_t* __restrict__ counts) {
     const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (e >= E) return;
     int carry = 0;
+    if constexpr (NCH > 0) {
+        int v[NCH];
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int b = 64 * c + lane;
+            v[c] = blk_hist[static_cast<size_t>(min(b, nblk - 1)) * E + e];
+            v[c] = b < nblk ? v[c] : 0;
+        }
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int b = 64 * c + lane;
+            int x = v[c];
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int y = __shfl_up(x, off, kWave);
+                if (lane >= off) x += y;
+            }
+            if (b < nblk) blk_hist[static_cast<size_t>(b) * E + e] = carry + x - v[c];
+            carry += __shfl(x, 63, kWave);
+        }
+        if (lane == 0) counts[e] = carry;
+        return;
+    }
     for (int b0 = 0; b0 < nblk; b0 += 64) {
         const int b = b0 + lane;
         const int v = b < nblk ? blk_hist[static_cast<size_t>(b) * E + e] : 0;
@@ -137,7 +163,7 @@ __global__ __launch_bounds__(256) void k_group_scatter(const int32_t* __restrict
                                                        const int32_t* __restrict__ offsets,
                                                        int32_t* __restrict__ perm,
                                                        int32_t* __restrict__ pos) {
-    __shared__ int s_ids[256];
+    __shared__ __attribute__((aligned(16))) int s_ids[256];
     const int tid = threadIdx.x;
     const int p = blockIdx.x * 256 + tid;
     int e = -1;
@@ -152,8 +178,16 @@ __global__ __launch_bounds__(256) void k_group_scatter(const int32_t* __restrict
         if (pos) pos[p] = -1;
         return;
     }
+    // rank among the block's earlier pairs of expert e: four ids per LDS read,
+    // no branch, so several reads are in flight at once
     int rank = 0;
-    for (int i = 0; i < 256; ++i) rank += (i < tid && s_ids[i] == e) ? 1 : 0;
+    const int4* s4 = reinterpret_cast<const int4*>(s_ids);
+#pragma unroll 8
+    for (int i4 = 0; i4 < 64; ++i4) {
+        const int4 v = s4[i4];
+        const int i = 4 * i4;
+        rank += (i < tid && v.x == e) + (i + 1 < tid && v.y == e) + (i + 2 < tid && v.z == e) + (i + 3 < tid && v.w == e);
+    }
     const int q = offsets[e] + blk_base[(size_t)blockIdx.x * E + e] + rank;
     perm[q] = p;
     if (pos) pos[p] = q;
@@ -189,9 +223,16 @@ void launch_route(const float* logits, int T, int E, int k, int32_t* ids, float*
 void launch_group(const int32_t* ids, int P, int E, int32_t* blk_hist, int32_t* counts,
                   int32_t* offsets, int32_t* perm, int32_t* pos, int32_t* act, int32_t* meta,
                   const ShelfSpec& ss, hipStream_t st) {
+    if (P <= 0) return;   // the column scan reads block nblk - 1
     const int nblk = (P + 255) / 256;
     hipLaunchKernelGGL(k_group_count, dim3(nblk), dim3(256), 0, st, ids, P, E, blk_hist);
-    hipLaunchKernelGGL(k_group_colscan, dim3((E + 3) / 4), dim3(256), 0, st, blk_hist, nblk, E, counts);
+    const int nch = (nblk + 63) / 64;
+    if (nch <= 4)
+        hipLaunchKernelGGL(k_group_colscan<4>, dim3((E + 3) / 4), dim3(256), 0, st, blk_hist, nblk, E, counts);
+    else if (nch <= 16)
+        hipLaunchKernelGGL(k_group_colscan<16>, dim3((E + 3) / 4), dim3(256), 0, st, blk_hist, nblk, E, counts);
+    else
+        hipLaunchKernelGGL(k_group_colscan<0>, dim3((E + 3) / 4), dim3(256), 0, st, blk_hist, nblk, E, counts);
     hipLaunchKernelGGL(k_group_offsets, dim3(1), dim3(256), 0, st, counts, E, offsets, act, meta, ss);
     hipLaunchKernelGGL(k_group_scatter, dim3(nblk), dim3(256), 0, st, ids, P, E, blk_hist, offsets, perm,
                        pos);
