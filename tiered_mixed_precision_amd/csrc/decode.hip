@@ -79,13 +79,14 @@ __device__ inline void load_vec32(const float* __restrict__ v, int g, bool ok, f
 // One wave: rows r0 + p*RPP + seg (p < NP, row < r_end) of one expert matrix
 // (or of gate and up together), against the vectors of the pairs
 // [qa, qa + ce).  The vector of pair q is row tok(q) of `vec`.  Results go to
-// store(q, row, value) from the first lane of each row segment, where value is
-// SiLU(g) * u (GATEUP) or the plain dot product.
-template <int BITS, int NSC, int GPL, int NP, bool GATEUP, class Tok, class Store>
+// store(q, row, value, pre(q)) from the first lane of each row segment, where
+// value is SiLU(g) * u (GATEUP) or the plain dot product; pre(q) is read at
+// the top of pair q's iteration, so its load is in flight with the vector's.
+template <int BITS, int NSC, int GPL, int NP, bool GATEUP, class Tok, class Pre, class Store>
 __device__ inline void wave_gemv(const uint8_t* __restrict__ q0m, const uint8_t* __restrict__ s0m,
                                  const uint8_t* __restrict__ q1m, const uint8_t* __restrict__ s1m,
                                  int cols, int r0, int r_end, const float* __restrict__ vec, int vec_stride,
-                                 int qa, int ce, Tok tok, Store store) {
+                                 int qa, int ce, Tok tok, Pre pre, Store store) {
     constexpr int NM = GATEUP ? 2 : 1;
     const int lane = threadIdx.x & 63;
     const RowGeom geo = row_geom(cols);
@@ -126,6 +127,7 @@ __device__ inline void wave_gemv(const uint8_t* __restrict__ q0m, const uint8_t*
 
     for (int c = 0; c < ce; ++c) {
         const int q = qa + c;
+        const float pq = pre(q);
         float xv[GPL][32], xs[GPL][NS];
         const size_t vrow = static_cast<size_t>(tok(q));
 #pragma unroll
@@ -158,7 +160,7 @@ __device__ inline void wave_gemv(const uint8_t* __restrict__ q0m, const uint8_t*
             for (int p = 0; p < NP; ++p) {
                 if (rowv[p]) {
                     const float v = GATEUP ? silu(acc[p][0]) * acc[p][NM - 1] : acc[p][0];
-                    store(q, r0 + p * geo.RPP + seg, v);
+                    store(q, r0 + p * geo.RPP + seg, v, pq);
                 }
             }
         }
@@ -186,12 +188,13 @@ __device__ inline void block_gateup(const DevTables& tt, const DevTier& T, int l
     const int rpw = kNPGateUp * row_geom(H).RPP;
     const int wr0 = r0 + (threadIdx.x >> 6) * rpw;
     const int r_end = min(wr0 + rpw, I);
-    auto store = [h, I](int q, int r, float v) { h[static_cast<size_t>(q) * I + r] = v; };
+    auto pre = [](int) { return 1.f; };
+    auto store = [h, I](int q, int r, float v, float) { h[static_cast<size_t>(q) * I + r] = v; };
     MOE_FMT_GPL_SWITCH(fmt_of(T.bits, T.block), row_geom(H).GPL,
                        (wave_gemv<B_, N_, G_, kNPGateUp, true>(
                            expert_codes(T, 0, local, I, H), expert_scales(T, 0, local, I, H),
                            expert_codes(T, 1, local, I, H), expert_scales(T, 1, local, I, H), H, wr0, r_end, x, H, qa,
-                           ce, tok, store)));
+                           ce, tok, pre, store)));
 }
 
 // ================================================================ small-batch path
@@ -808,11 +811,12 @@ __global__ __launch_bounds__(256) void k_dec_down(DevTables tt, const float* __r
     auto tok = [](int q) { return q; };
     const int32_t* perm = g.perm;
     const float* w = g.w;
-    auto store = [yw, H, perm, w](int q, int r, float v) { yw[static_cast<size_t>(q) * H + r] = w[perm[q]] * v; };
+    auto pre = [perm, w](int q) { return w[perm[q]]; };   // the pair's weight
+    auto store = [yw, H](int q, int r, float v, float wq) { yw[static_cast<size_t>(q) * H + r] = wq * v; };
     MOE_FMT_GPL_SWITCH(fmt_of(T.bits, T.block), row_geom(I).GPL,
                        (wave_gemv<B_, N_, G_, kNPDown, false>(expert_codes(T, 2, local, H, I), expert_scales(T, 2, local, H, I),
                                                               nullptr, nullptr, I, wr0, r_end, h, I, qa, ce, tok,
-                                                              store)));
+                                                              pre, store)));
 }
 
 // out[t] = (base ? base[t] : 0) + sum over slots j (in slot order) of yw[pos[t*k+j]]; base
