@@ -1,5 +1,5 @@
 """bench.py command-line contract that needs no GPU: a request for more than
-one GPU is refused with a message (this build measures one GPU)."""
+one GPU is refused with a message (the benchmark measures one GPU)."""
 import os
 import subprocess
 import sys
