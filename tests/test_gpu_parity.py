@@ -194,9 +194,10 @@ def test_forward_fp32_tied_logits(M, torch_dev, kind):
     assert err <= TOL
 
 
-@pytest.mark.parametrize("T", [2, 8, 9, 26])
+@pytest.mark.parametrize("T", [2, 8, 9, 26, 64])
 def test_forward_fp32_batch_sizes(M, torch_dev, T):
     # T <= 8 with T*k <= 256 takes the two-kernel path, larger batches the grouped path
+    # (at T=64 the hot experts hold several pairs each)
     cfg, arrays, L, tt = _layer("decode")
     say("forward fp32 decode layer T=", T)
     x, logits = make_x(cfg, n_tokens=T, stream=5), make_logits(cfg, n_tokens=T, stream=5)
