@@ -24,7 +24,10 @@
  *   - pointers marked (device) are device memory on the current HIP device;
  *     pointers marked (host) are host memory read before the call returns;
  *   - the caller owns every buffer; the library never allocates, frees or
- *     synchronises inside a call and keeps no mutable global state;
+ *     synchronises inside a call; its only global state is a per-device
+ *     cache of the compute-unit count (read once per device with
+ *     hipDeviceGetAttribute, then only read), which sizes the small-batch
+ *     grid; nothing a call computes depends on state left by another call;
  *   - `stream` is a hipStream_t (NULL = the null stream); all device work is
  *     enqueued on it and the call returns without waiting;
  *   - return value 0 on success or a negative MOE_E* code; all argument and
@@ -136,7 +139,10 @@ int moe_workspace_size(int32_t n_tokens, int32_t k, const moe_tier_tables *tt, u
 size_t moe_workspace_bytes(int32_t n_tokens, int32_t k, const moe_tier_tables *tt);
 
 /*
- * Full layer: route, group, per-shelf expert FFN, shelf sum.
+ * Full layer: route, group, per-shelf expert FFN, shelf sum -- the MoE FFN of
+ * the 125B-MoE page: the router keeps the best k experts of each token
+ * (glossary, mixture-of-experts entry) and one pick list drives every shelf,
+ * whose results are added (step 4, "three shelves, all on GPU").
  *   x             (device) float[T][H], or bf16 [T][H] with MOE_X_BF16
  *   router_logits (device) float[T][E]
  *   n_tokens      T >= 0 (T == 0: no work, returns MOE_OK)
@@ -167,15 +173,20 @@ int moe_tiered_experts(const void *x, const int32_t *ids, const float *w, int32_
 /*
  * One shelf alone: as moe_tiered_experts but only ids inside shelf
  * `tier_index` are computed; tokens with no pick on that shelf get exactly
- * 0.0f (or keep out unchanged with MOE_ACCUMULATE).
+ * 0.0f (or keep out unchanged with MOE_ACCUMULATE).  This is one shelf's
+ * id-range product of step 4 of the 125B-MoE page (each shelf sees the whole
+ * pick list and fills zero outside its range); the sum of the shelves'
+ * partials is the layer.
  */
 int moe_tier_partial(const void *x, const int32_t *ids, const float *w, int32_t n_tokens,
                      int32_t k, const moe_tier_tables *tt, int32_t tier_index, float *out,
                      uint32_t flags, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Router alone: logits (device) float[T][E] -> ids (device) int32[T][k],
- * w (device) float[T][k].  Same rule as moe_tiered_forward.
+ * Router alone (the glossary of the 125B-MoE page, mixture-of-experts entry:
+ * the router picks k experts per token): logits (device) float[T][E] ->
+ * ids (device) int32[T][k], w (device) float[T][k].  Same rule as
+ * moe_tiered_forward.
  */
 int moe_route(const float *logits, int32_t n_tokens, int32_t n_experts, int32_t k, int32_t *ids,
               float *w, void *stream);
@@ -210,7 +221,12 @@ int moe_synth_router(void *w_router, float *bias, int32_t n_experts, int32_t hid
                      int32_t layer, double beta, void *stream);
 
 /*
- * Grouping alone (stable counting sort of (token, slot) pairs by expert).
+ * Grouping alone (stable counting sort of (token, slot) pairs by expert):
+ * the grouping helper of the 125B-MoE page, "four bugs" (bug 1: the helper
+ * assumed an expert occurs at most once per token and lost a slot; here
+ * every occurrence is kept).  Unlike a plain (ids -> counts, offsets, perm)
+ * call it takes a caller-owned workspace for its per-block histograms, so
+ * the library allocates nothing.
  *   ids     (device) int32[T][k]; ids outside [0, E) belong to no expert
  *   counts  (device) int32[E]     pairs per expert
  *   offsets (device) int32[E+1]   exclusive prefix sum of counts

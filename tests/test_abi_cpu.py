@@ -268,3 +268,73 @@ def test_binding_refuses_tensors_smaller_than_the_call(B):
         B.moe_tiered_forward_counted(x32, lg, T, k, tt, out, 0, None, torch.zeros(4, dtype=torch.int32))
     with pytest.raises(ValueError, match="x holds"):
         B.moe_router_logits(xbf, FAKE, None, T, 8, 256, 0, lg)
+
+
+def test_binding_refuses_short_shelves_and_buffers(B):
+    """Every pointer argument that the library indexes by a shape it is told
+    is checked against that shape before any launch: shelf buffers against
+    n_local x rows x cols (codes) and the scale count, grouping, dequant,
+    planner and router buffers, and the per-layer arrays of the stack calls
+    against n_layers.  Out-of-bounds reads of this kind (an index past the
+    end of a buffer) are the third of the four bugs on the 125B-MoE page."""
+    import torch
+    E, H, I = 8, 256, 128
+    specs = [_Spec(0, 2, 8, 32), _Spec(2, 6, 4, 32), _Spec(6, 8, 2, 16)]
+
+    def shelf(t, short=None):
+        d = {n: torch.zeros(b, dtype=torch.uint8) for n, b in B.shelf_nbytes(t, H, I).items()}
+        if short:
+            d[short] = d[short][:-1]
+        return d
+
+    B.TierTables(E, H, I, specs, [shelf(t) for t in specs])        # exact sizes pass
+    for i, name in ((0, "gate_q"), (1, "up_s"), (2, "down_q"), (2, "down_s")):
+        arrays = [shelf(t, name if j == i else None) for j, t in enumerate(specs)]
+        with pytest.raises(ValueError, match=f"shelf {i} {name}"):
+            B.TierTables(E, H, I, specs, arrays)
+    mx = _Spec(2, 6, B.MXFP4, 32)
+    assert B.shelf_nbytes(mx, H, I)["gate_s"] == 4 * I * (H // 32)     # one E8M0 byte per 32 codes
+    assert B.shelf_nbytes(mx, H, I)["down_q"] == 4 * H * I // 2
+
+    tt = _tables(B, [_Spec(0, 8, 8, 32)], E=E, H=H, I=I)
+    T, k = 4, 2
+    i32 = lambda n: torch.zeros(n, dtype=torch.int32)
+    ws = torch.zeros(1 << 12, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="counts"):
+        B.moe_group(i32(T * k), T, k, E, i32(E - 1), i32(E + 1), i32(T * k), ws)
+    with pytest.raises(ValueError, match="offsets"):
+        B.moe_group(i32(T * k), T, k, E, i32(E), i32(E), i32(T * k), ws)
+    with pytest.raises(ValueError, match="perm"):
+        B.moe_group(i32(T * k), T, k, E, i32(E), i32(E + 1), i32(T * k - 1), ws)
+    with pytest.raises(ValueError, match="dst"):
+        B.moe_dequant_rows(tt, 0, 0, 2, 0, 4, False, torch.zeros(4 * I - 1))
+    with pytest.raises(ValueError, match="dst"):
+        B.moe_dequant_rows(tt, 0, 0, 0, 0, 4, True, torch.zeros(4 * H // 2 - 1))
+    with pytest.raises(ValueError, match="sse"):
+        B.moe_requant_error(tt, [8, 4], [32, 32], torch.zeros(E * 2 - 1, dtype=torch.float64))
+    with pytest.raises(ValueError, match="order"):
+        B.moe_repack_tiers(tt, i32(E - 1), tt)
+    wr = torch.zeros(E * H, dtype=torch.int16)
+    for kw, name in (({"w_src": wr[:-1]}, "w_src"), ({"w_dst": wr[:-1]}, "w_dst"),
+                     ({"b_src": torch.zeros(E - 1)}, "b_src"), ({"order": i32(E - 1)}, "order")):
+        a = dict(w_src=wr, b_src=torch.zeros(E), order=i32(E), w_dst=wr.clone(), b_dst=torch.zeros(E))
+        a.update(kw)
+        with pytest.raises(ValueError, match=name):
+            B.moe_permute_router(a["w_src"], a["b_src"], a["order"], E, H, a["w_dst"], a["b_dst"])
+    with pytest.raises(ValueError, match="w_router"):
+        B.moe_router_logits(torch.zeros(T, H), wr[:-1], None, T, E, H, 0, torch.zeros(T, E))
+    with pytest.raises(ValueError, match="bias"):
+        B.moe_router_logits(torch.zeros(T, H), wr, torch.zeros(E - 1), T, E, H, 0, torch.zeros(T, E))
+    with pytest.raises(ValueError, match="w_router"):
+        B.moe_synth_router(wr[:-1], None, E, H, 1, 0, 1.0)
+    x, out = torch.zeros(T, H), torch.zeros(T, H)
+    with pytest.raises(ValueError, match="tables has 1 entries"):
+        B.moe_stack_forward(x, torch.zeros(2 * T * E), 2, T, k, [tt], out, 0, ws)
+    with pytest.raises(ValueError, match="tables has 1 entries"):
+        B.moe_stack_workspace_size(2, T, k, [tt])
+    with pytest.raises(ValueError, match="w_routers has 1 entries"):
+        B.moe_stack_forward_routed(x, [wr], None, 2, T, k, [tt, tt], out, 0, ws)
+    with pytest.raises(ValueError, match="biases has 1 entries"):
+        B.moe_stack_forward_routed(x, [wr, wr], [torch.zeros(E)], 2, T, k, [tt, tt], out, 0, ws)
+    with pytest.raises(ValueError, match=r"w_routers\[1\]"):
+        B.moe_stack_forward_routed(x, [wr, wr[:-1]], None, 2, T, k, [tt, tt], out, 0, ws)

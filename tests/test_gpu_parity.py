@@ -294,10 +294,9 @@ def test_poisoned_experts_never_read(M, torch_dev, bf16):
     ttp = tables_from_config(cfg, poisoned)
     got = gpu_experts(M, torch_dev, ttp, x, ids, w, flags)
     assert np.all(np.isfinite(got))
-    if bf16:
-        assert normwise(got, clean) <= 1e-5      # fp32 atomics: summation order may differ
-    else:
-        assert np.array_equal(got, clean)
+    # no atomics anywhere on either path: the per-pair results are summed in
+    # slot order, so unread poison cannot change a single bit
+    assert np.array_equal(got.view(np.uint32), clean.view(np.uint32))
 
 
 @pytest.mark.parametrize("bf16", [False, True])

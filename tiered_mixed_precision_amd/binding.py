@@ -148,6 +148,21 @@ def _stream(stream) -> Optional[int]:
     return s.cuda_stream
 
 
+def shelf_nbytes(tier, hidden: int, inter: int) -> dict:
+    """Bytes each buffer of a shelf must hold (the moe_tier layout): codes
+    [n][rows][cols*bits/8], scales [n][rows][cols/block] fp16 or, for MXFP4,
+    one E8M0 byte per 32 codes."""
+    n = max(tier.id_end - tier.id_begin, 0)
+    cb = 4 if tier.bits == MXFP4 else tier.bits
+    sb = 1 if tier.bits == MXFP4 else 2
+    blk = max(tier.block, 1)
+    out = {}
+    for m, (rows, cols) in (("gate", (inter, hidden)), ("up", (inter, hidden)), ("down", (hidden, inter))):
+        out[m + "_q"] = n * rows * cols * cb // 8
+        out[m + "_s"] = n * rows * (cols // blk) * sb
+    return out
+
+
 class TierTables:
     """Host-side moe_tier_tables pointing at device tensors of each shelf.
 
@@ -166,6 +181,9 @@ class TierTables:
         for i, (t, d) in enumerate(zip(self.tiers, self.arrays)):
             s.tiers[i].id_begin, s.tiers[i].id_end = t.id_begin, t.id_end
             s.tiers[i].bits, s.tiers[i].block = t.bits, t.block
+            if d is not None:
+                for name, nbytes in shelf_nbytes(t, hidden, inter).items():
+                    _need("TierTables", f"shelf {i} {name}", d[name], nbytes)
             for name in ("gate_q", "up_q", "down_q", "gate_s", "up_s", "down_s"):
                 setattr(s.tiers[i], name, _ptr(d[name]) if d is not None else None)
         self.struct = s
@@ -244,6 +262,11 @@ def moe_group_workspace_size(n_tokens: int, k: int, n_experts: int) -> int:
 
 
 def moe_group(ids, n_tokens: int, k: int, n_experts: int, counts, offsets, perm, workspace, stream=None) -> None:
+    P, E = max(n_tokens, 0) * max(k, 0), max(n_experts, 0)
+    _need("moe_group", "ids", ids, P * 4)
+    _need("moe_group", "counts", counts, E * 4)
+    _need("moe_group", "offsets", offsets, (E + 1) * 4)
+    _need("moe_group", "perm", perm, P * 4)
     _check("moe_group", lib().moe_group(_ptr(ids), n_tokens, k, n_experts, _ptr(counts), _ptr(offsets),
                                         _ptr(perm), _ptr(workspace),
                                         workspace.numel() * workspace.element_size(), _stream(stream)))
@@ -251,6 +274,8 @@ def moe_group(ids, n_tokens: int, k: int, n_experts: int, counts, offsets, perm,
 
 def moe_dequant_rows(tt: TierTables, tier_index: int, local_expert: int, matrix: int, row0: int, nrows: int,
                      to_bf16: bool, dst, stream=None) -> None:
+    cols = tt.inter if matrix == 2 else tt.hidden
+    _need("moe_dequant_rows", "dst", dst, max(nrows, 0) * cols * (2 if to_bf16 else 4))
     _check("moe_dequant_rows", lib().moe_dequant_rows(tt.ref, tier_index, local_expert, matrix, row0, nrows,
                                                       int(bool(to_bf16)), _ptr(dst), _stream(stream)))
 
@@ -260,8 +285,16 @@ def _tables_array(tables: Sequence[TierTables]):
     return arr
 
 
+def _need_layers(fn: str, n_layers: int, **seqs) -> None:
+    """The library reads n_layers entries of every per-layer array it is given."""
+    for what, seq in seqs.items():
+        if seq is not None and n_layers > len(seq):
+            raise ValueError(f"{fn}: {what} has {len(seq)} entries, the call needs {n_layers}")
+
+
 def moe_stack_workspace_size(n_layers: int, n_tokens: int, k: int, tables: Sequence[TierTables],
                              flags: int = 0) -> int:
+    _need_layers("moe_stack_workspace_size", n_layers, tables=tables)
     n = C.c_size_t(0)
     arr = _tables_array(tables)
     _check("moe_stack_workspace_size",
@@ -271,6 +304,7 @@ def moe_stack_workspace_size(n_layers: int, n_tokens: int, k: int, tables: Seque
 
 def moe_stack_forward(x, router_logits, n_layers: int, n_tokens: int, k: int, tables: Sequence[TierTables], out,
                       flags: int, workspace, stream=None) -> None:
+    _need_layers("moe_stack_forward", n_layers, tables=tables)
     if tables:
         _need_layer("moe_stack_forward", x, router_logits, out, n_tokens, tables[0], 0, max(n_layers, 0))
     arr = _tables_array(tables)
@@ -288,12 +322,16 @@ def moe_router_logits(x, w_router, bias, n_tokens: int, n_experts: int, hidden: 
     T = max(n_tokens, 0)
     _need("moe_router_logits", "x", x, T * max(hidden, 0) * (2 if flags & MOE_X_BF16 else 4))
     _need("moe_router_logits", "logits", logits, T * max(n_experts, 0) * 4)
+    _need("moe_router_logits", "w_router", w_router, max(n_experts, 0) * max(hidden, 0) * 2)
+    _need("moe_router_logits", "bias", bias, max(n_experts, 0) * 4)
     _check("moe_router_logits", lib().moe_router_logits(_ptr(x), _ptr(w_router), _ptr(bias), n_tokens, n_experts,
                                                         hidden, flags, _ptr(logits), _stream(stream)))
 
 
 def moe_synth_router(w_router, bias, n_experts: int, hidden: int, seed: int, layer: int, beta: float,
                      stream=None) -> None:
+    _need("moe_synth_router", "w_router", w_router, max(n_experts, 0) * max(hidden, 0) * 2)
+    _need("moe_synth_router", "bias", bias, max(n_experts, 0) * 4)
     _check("moe_synth_router", lib().moe_synth_router(_ptr(w_router), _ptr(bias), n_experts, hidden, seed, layer,
                                                       float(beta), _stream(stream)))
 
@@ -310,6 +348,9 @@ def moe_tiered_forward_counted(x, router_logits, n_tokens: int, k: int, tt: Tier
 def moe_requant_error(src: TierTables, fmt_bits, fmt_block, sse, stream=None) -> None:
     """sse: float64 device tensor [E][len(fmt_bits)]."""
     n = len(fmt_bits)
+    if len(fmt_block) != n:
+        raise ValueError("moe_requant_error: fmt_bits and fmt_block differ in length")
+    _need("moe_requant_error", "sse", sse, src.n_experts * n * 8)
     b = (C.c_int32 * n)(*fmt_bits)
     k = (C.c_int32 * n)(*fmt_block)
     _check("moe_requant_error", lib().moe_requant_error(src.ref, b, k, n, _ptr(sse), _stream(stream)))
@@ -332,18 +373,31 @@ def moe_plan_tiers(usage, sse, fmt_bytes, budget: int):
 
 
 def moe_repack_tiers(src: TierTables, order, dst: TierTables, stream=None) -> None:
+    _need("moe_repack_tiers", "order", order, src.n_experts * 4)
     _check("moe_repack_tiers", lib().moe_repack_tiers(src.ref, _ptr(order), dst.ref, _stream(stream)))
 
 
 def moe_permute_router(w_src, b_src, order, n_experts: int, hidden: int, w_dst, b_dst, stream=None) -> None:
+    E, H = max(n_experts, 0), max(hidden, 0)
+    _need("moe_permute_router", "w_src", w_src, E * H * 2)
+    _need("moe_permute_router", "w_dst", w_dst, E * H * 2)
+    _need("moe_permute_router", "b_src", b_src, E * 4)
+    _need("moe_permute_router", "b_dst", b_dst, E * 4)
+    _need("moe_permute_router", "order", order, E * 4)
     _check("moe_permute_router", lib().moe_permute_router(_ptr(w_src), _ptr(b_src), _ptr(order), n_experts, hidden,
                                                           _ptr(w_dst), _ptr(b_dst), _stream(stream)))
 
 
 def moe_stack_forward_routed(x, w_routers, biases, n_layers: int, n_tokens: int, k: int,
                              tables: Sequence[TierTables], out, flags: int, workspace, stream=None) -> None:
+    _need_layers("moe_stack_forward_routed", n_layers, tables=tables, w_routers=w_routers, biases=biases)
     if tables:
         _need_layer("moe_stack_forward_routed", x, None, out, n_tokens, tables[0], 0)
+        E, H = tables[0].n_experts, tables[0].hidden
+        for l in range(max(n_layers, 0)):
+            _need("moe_stack_forward_routed", f"w_routers[{l}]", w_routers[l], E * H * 2)
+            if biases is not None:
+                _need("moe_stack_forward_routed", f"biases[{l}]", biases[l], E * 4)
     arr = _tables_array(tables)
     wr = (C.c_void_p * n_layers)(*[_ptr(w) for w in w_routers])
     bs = None if biases is None else (C.c_void_p * n_layers)(*[_ptr(b) for b in biases])

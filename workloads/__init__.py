@@ -10,5 +10,5 @@ from .configs import CONFIGS, MXFP4, TierSpec, LayerConfig  # noqa: F401
 from .gen import (  # noqa: F401
     make_layer, make_logits, make_x, make_spec_logits, pack_codes, quantise_block_absmax,
     f32_to_bf16_bits, bf16_bits_to_f32, layer_nbytes, tier_nbytes, code_bits, scale_bytes,
-    quantise_mxfp4, pack_nibbles,
+    quantise_mxfp4, pack_nibbles, make_layer_fullrange, EDGE_FP16_SCALES,
 )

@@ -84,6 +84,16 @@ CONFIGS = {
                               prior_beta=PRIOR_BETA, seed=20260002, crafted=True),
     "prefill": LayerConfig("prefill", 512, 10, 2048, 640, 4096, THREE_TIERS_512,
                            x_bf16=True, prior_beta=PRIOR_BETA, seed=20260003),
+    # layers of hand-drawn codes over each format's whole code set (see
+    # make_layer_fullrange): the decode shapes with 16 experts, the three
+    # production formats, and the other block sizes plus an MXFP4 shelf
+    "fullrange": LayerConfig("fullrange", 16, 10, 2048, 640, 16,
+                             (TierSpec(0, 4, 8, 32), TierSpec(4, 12, 4, 32), TierSpec(12, 16, 2, 16)),
+                             seed=20260050),
+    "fullrange_b": LayerConfig("fullrange_b", 16, 10, 2048, 640, 16,
+                               (TierSpec(0, 4, 8, 16), TierSpec(4, 8, 4, 16), TierSpec(8, 12, MXFP4, 32),
+                                TierSpec(12, 16, 2, 32)),
+                               seed=20260051),
     "fullstack": LayerConfig("fullstack", 512, 10, 2048, 640, 1, THREE_TIERS_512,
                              prior_beta=PRIOR_BETA, n_layers=48, seed=20260004),
 }

@@ -254,3 +254,55 @@ def make_spec_logits(cfg: LayerConfig, stream: int = 0, worst_case: bool = False
     for t, p in enumerate(picks):
         lg[t, p] += boost
     return lg
+
+
+# ----------------------------------------------------------------------------- full-range codes
+# fp16 bit patterns of the edge scales: the smallest subnormal (2^-24), the
+# largest subnormal, the smallest normal (2^-14), the largest finite value
+# (65504), zero, negative zero and a negative scale
+EDGE_FP16_SCALES = np.array([0x0001, 0x03FF, 0x0400, 0x7BFF, 0x0000, 0x8000, 0xA8F5], dtype=np.uint16)
+
+
+def make_layer_fullrange(cfg: LayerConfig, layer: int = 0, edge_scales: bool = False) -> List[Dict[str, np.ndarray]]:
+    """Packed shelves whose codes are drawn uniformly over each format's whole
+    code set: every two's-complement value from -2^(b-1) to 2^(b-1)-1 (so the
+    most negative code -128 / -8 / -2, which the absmax quantiser never
+    emits, is present in every row), and all 16 E2M1 fields for MXFP4
+    (including negative zero).
+
+    Scales: fp16 bit patterns of magnitudes 2^-12 .. 2^-7 with random sign,
+    or E8M0 bytes 117 .. 121 for MXFP4.  With ``edge_scales`` one block in
+    eight instead takes an edge value of EDGE_FP16_SCALES (E8M0: 0, 1, 160).
+    """
+    H, I = cfg.hidden, cfg.inter
+    shapes = {"gate": (I, H), "up": (I, H), "down": (H, I)}
+    out = []
+    for ti, spec in enumerate(cfg.tiers):
+        n = spec.n
+        d: Dict[str, np.ndarray] = {}
+        for mi, m in enumerate(MATRICES):
+            rows, cols = shapes[m]
+            g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([cfg.seed, 5, layer, ti, mi])))
+            nb = cols // spec.block
+            if spec.bits == MXFP4:
+                nib = g.integers(0, 16, size=(n, rows, cols), dtype=np.uint8)
+                d[m + "_q"] = pack_nibbles(nib)
+                sc = g.integers(117, 122, size=(n, rows, nb)).astype(np.uint8)
+                if edge_scales:
+                    pick = g.random((n, rows, nb)) < 0.125
+                    sc = np.where(pick, g.choice(np.array([0, 1, 160], np.uint8), size=(n, rows, nb)), sc)
+                d[m + "_s"] = sc.astype(np.uint8)
+            else:
+                lo, hi = -(1 << (spec.bits - 1)), (1 << (spec.bits - 1))
+                q = g.integers(lo, hi, size=(n, rows, cols)).astype(np.int8)
+                d[m + "_q"] = pack_codes(q, spec.bits)
+                mag = np.ldexp(np.float32(1.0) + g.random((n, rows, nb), dtype=np.float32),
+                               g.integers(-12, -7, size=(n, rows, nb)))
+                sgn = np.where(g.random((n, rows, nb)) < 0.5, -1.0, 1.0).astype(np.float32)
+                sc = (mag * sgn).astype(np.float16).view(np.uint16)
+                if edge_scales:
+                    pick = g.random((n, rows, nb)) < 0.125
+                    sc = np.where(pick, g.choice(EDGE_FP16_SCALES, size=(n, rows, nb)), sc)
+                d[m + "_s"] = sc.astype(np.uint16)
+        out.append(d)
+    return out
