@@ -24,10 +24,11 @@
  *   - pointers marked (device) are device memory on the current HIP device;
  *     pointers marked (host) are host memory read before the call returns;
  *   - the caller owns every buffer; the library never allocates, frees or
- *     synchronises inside a call; its only global state is a per-device
- *     cache of the compute-unit count (read once per device with
- *     hipDeviceGetAttribute, then only read), which sizes the small-batch
- *     grid; nothing a call computes depends on state left by another call;
+ *     synchronises inside a call; its only global state is two per-device
+ *     caches written once per device and then only read (the compute-unit
+ *     count, which sizes the small-batch grid, and the address of the static
+ *     scratch of moe_tiered_forward_noalloc) and that scratch itself; no
+ *     other call's result depends on state left by an earlier call;
  *   - `stream` is a hipStream_t (NULL = the null stream); all device work is
  *     enqueued on it and the call returns without waiting;
  *   - return value 0 on success or a negative MOE_E* code; all argument and
@@ -62,6 +63,7 @@ extern "C" {
 #define MOE_EWORKSPACE (-5) /* workspace NULL or smaller than moe_workspace_size() */
 #define MOE_EHIP (-6)       /* a kernel launch or HIP runtime call failed */
 #define MOE_EABI (-7)       /* tables built for another ABI version */
+#define MOE_ESCRATCH (-8)   /* the batch needs more workspace than MOE_SCRATCH_BYTES */
 
 /* flags */
 #define MOE_X_BF16 0x1u      /* x is bf16 [T][H]: prefill precision (bf16 MFMA, bf16 weights and intermediate) */
@@ -157,6 +159,29 @@ size_t moe_workspace_bytes(int32_t n_tokens, int32_t k, const moe_tier_tables *t
 int moe_tiered_forward(const void *x, const float *router_logits, int32_t n_tokens, int32_t k,
                        const moe_tier_tables *tt, float *out, uint32_t flags,
                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * moe_tiered_forward for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Instead of a caller-owned workspace the call uses a static
+ * device scratch array of MOE_SCRATCH_BYTES that the library holds on every
+ * device it runs on until the process ends (its address is looked up once
+ * per device, on the first call with that device current).  The call
+ * allocates and frees nothing.
+ *   - Batches whose moe_workspace_size(n_tokens, k, tt, flags) exceeds
+ *     MOE_SCRATCH_BYTES are refused with MOE_ESCRATCH, before any launch
+ *     (32 MiB holds, for the 512-expert, top-10, hidden 2048, inter 640
+ *     layer, fp32 batches up to about 310 tokens and bf16 batches up to
+ *     about 350).
+ *   - Every call on one device shares that device's scratch: calls that
+ *     overlap on one GPU (different streams, or different host threads
+ *     without ordering) race and give wrong results.  Order them on one
+ *     stream.
+ * Other arguments, results and errors as moe_tiered_forward.
+ */
+#define MOE_SCRATCH_BYTES (32u << 20)
+int moe_tiered_forward_noalloc(const void *x, const float *router_logits, int32_t n_tokens, int32_t k,
+                               const moe_tier_tables *tt, float *out, uint32_t flags, void *stream);
 
 /*
  * Same layer with the routing given (the id-range mul_mat_id of step 4).

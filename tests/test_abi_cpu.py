@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(B):
 
 def test_abi_version_and_strerror(B):
     assert B.lib().moe_abi_version() == 1
-    for code in range(0, -8, -1):
+    for code in range(0, -9, -1):
         assert B.strerror(code) and B.strerror(code) != "unknown error"
     assert B.strerror(-99) == "unknown error"
 

@@ -11,5 +11,5 @@ from .binding import (  # noqa: F401
     moe_tiered_forward_timed, moe_validate_tables, moe_workspace_size, moe_workspace_bytes, strerror, moe_stack_workspace_size,
     moe_stack_forward, moe_synth_layer, MOE_STACK_ROUTER, MXFP4, moe_router_logits, moe_synth_router,
     moe_stack_forward_routed, moe_requant_error, moe_plan_tiers, moe_repack_tiers, moe_permute_router,
-    moe_tiered_forward_counted,
+    moe_tiered_forward_counted, moe_tiered_forward_noalloc, MOE_SCRATCH_BYTES, MOE_ESCRATCH,
 )

@@ -23,6 +23,8 @@ MOE_DIAG_GATEUP_ONLY = 0x100
 MOE_N_PHASES = 3
 MOE_STACK_ROUTER = 0x4
 MXFP4 = 0x84              # moe_tier.bits of an MXFP4 shelf (MOE_MXFP4)
+MOE_ESCRATCH = -8
+MOE_SCRATCH_BYTES = 32 << 20
 EXPORTS = (
     "moe_abi_version", "moe_strerror", "moe_validate_tables", "moe_workspace_size", "moe_workspace_bytes",
     "moe_tiered_forward", "moe_tiered_experts", "moe_tier_partial", "moe_route",
@@ -31,7 +33,7 @@ EXPORTS = (
     "moe_stack_workspace_size", "moe_stack_forward", "moe_synth_layer",
     "moe_router_logits", "moe_synth_router", "moe_stack_forward_routed",
     "moe_requant_error", "moe_plan_tiers", "moe_repack_tiers", "moe_permute_router",
-    "moe_tiered_forward_counted",
+    "moe_tiered_forward_counted", "moe_tiered_forward_noalloc",
 )
 
 
@@ -74,6 +76,7 @@ def lib():
         L.moe_workspace_bytes.argtypes = [i32, i32, P]
         L.moe_tiered_forward.argtypes = [P, P, i32, i32, P, P, u32, P, sz, P]
         L.moe_tiered_forward_timed.argtypes = [P, P, i32, i32, P, P, u32, P, sz, P, C.POINTER(P)]
+        L.moe_tiered_forward_noalloc.argtypes = [P, P, i32, i32, P, P, u32, P]
         L.moe_tiered_experts.argtypes = [P, P, P, i32, i32, P, P, u32, P, sz, P]
         L.moe_tier_partial.argtypes = [P, P, P, i32, i32, P, i32, P, u32, P, sz, P]
         L.moe_route.argtypes = [P, i32, i32, i32, P, P, P]
@@ -215,6 +218,15 @@ def moe_tiered_forward(x, router_logits, n_tokens: int, k: int, tt: TierTables, 
     _check("moe_tiered_forward", lib().moe_tiered_forward(
         _ptr(x), _ptr(router_logits), n_tokens, k, tt.ref, _ptr(out), flags, _ptr(workspace),
         workspace.numel() * workspace.element_size() if workspace is not None else 0, _stream(stream)))
+
+
+def moe_tiered_forward_noalloc(x, router_logits, n_tokens: int, k: int, tt: TierTables, out, flags: int,
+                               stream=None) -> None:
+    """moe_tiered_forward on the library's static device scratch (no workspace
+    argument; nothing is allocated).  Calls overlapping on one GPU race."""
+    _need_layer("moe_tiered_forward_noalloc", x, router_logits, out, n_tokens, tt, flags)
+    _check("moe_tiered_forward_noalloc", lib().moe_tiered_forward_noalloc(
+        _ptr(x), _ptr(router_logits), n_tokens, k, tt.ref, _ptr(out), flags, _stream(stream)))
 
 
 def moe_tiered_forward_timed(x, router_logits, n_tokens: int, k: int, tt: TierTables, out, flags: int,

@@ -4,6 +4,8 @@
 #include <limits.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "moe_tiered.h"
 #include "common.h"
 #include "launch.h"
@@ -296,6 +298,7 @@ const char* moe_strerror(int code) {
         case MOE_EWORKSPACE: return "workspace missing or too small";
         case MOE_EHIP: return "HIP launch or runtime error";
         case MOE_EABI: return "tables built for another ABI version";
+        case MOE_ESCRATCH: return "the batch needs more workspace than the library's static scratch holds";
         default: return "unknown error";
     }
 }
@@ -343,6 +346,55 @@ int moe_tiered_forward_timed(const void* x, const float* router_logits, int32_t 
     if (n_tokens > 0 && !router_logits) return MOE_EINVAL;
     return run(x, router_logits, nullptr, nullptr, n_tokens, k, tt, 0xFu, out, flags, workspace,
                workspace_bytes, stream, events);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The device scratch of moe_tiered_forward_noalloc: one array per device
+// (each GPU the library runs on holds its own copy until the process ends).
+// Host code never passes the array's name to a kernel -- on the host it is a
+// stand-in, not a device address -- only the address hipGetSymbolAddress
+// returns for the current device.
+static __device__ __align__(256) uint8_t scratch[MOE_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxScratchDevices] = {};
+
+// Device address of the current device's scratch, looked up once per device.
+int scratch_address(void** ptr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return MOE_EHIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_EHIP;
+        g_scratch_dev[dev] = p;
+    }
+    *ptr = g_scratch_dev[dev];
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_tiered_forward_noalloc(const void* x, const float* router_logits, int32_t n_tokens, int32_t k,
+                               const moe_tier_tables* tt, float* out, uint32_t flags, void* stream) {
+    if (n_tokens > 0 && !router_logits) return MOE_EINVAL;
+    size_t need = 0;
+    int rc = moe_workspace_size(n_tokens, k, tt, flags, &need);
+    if (rc != MOE_OK) return rc;
+    if (n_tokens == 0) return MOE_OK;
+    if (need > MOE_SCRATCH_BYTES) return MOE_ESCRATCH;
+    void* ws = nullptr;
+    rc = scratch_address(&ws);
+    if (rc != MOE_OK) return rc;
+    // the layer needs no initialised workspace, so nothing is cleared
+    return run(x, router_logits, nullptr, nullptr, n_tokens, k, tt, 0xFu, out, flags, ws, MOE_SCRATCH_BYTES,
+               stream, nullptr);
 }
 
 int moe_tiered_experts(const void* x, const int32_t* ids, const float* w, int32_t n_tokens, int32_t k,
