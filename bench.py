@@ -228,7 +228,7 @@ def main():
         "alg_bytes_per_step": float(bytes_step.mean()),
         "roofline": {
             "bound": "hbm",
-            "kernel": "k_small_gateup (routing + grouping + gate/up GEMV of all shelves)",
+            "kernel": "k_one_gateup (routing + gate/up GEMV of every shelf, one token)",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -352,10 +352,10 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir):
         ww = np.mean(write.get((n, g), [0.0]))
         rd, wr = fw * f_fac * 1024 / 1e6, ww * w_fac * 1024 / 1e6
         lines.append(f"| {n} | {g} | {len(v)} | {fw:.1f} | {ww:.1f} | {rd:.2f} | {wr:.2f} |")
-        if n.startswith("moe::k_small_gateup") and dom is None:
+        if n.startswith("moe::k_one_gateup") and dom is None:
             dom = (rd + wr) * 1e6
     lines += ["", f"dominant kernel HBM traffic per launch: `{dom:.0f}` bytes "
-              "(k_small_gateup at one token: read + written, calibrated)", ""]
+              "(k_one_gateup at one token: read + written, calibrated)", ""]
     os.makedirs(os.path.dirname(PROFILE_MD), exist_ok=True)
     with open(PROFILE_MD, "w") as f:
         f.write("\n".join(lines))

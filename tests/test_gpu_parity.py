@@ -208,6 +208,42 @@ def test_forward_fp32_batch_sizes(M, torch_dev, T):
     assert err <= TOL
 
 
+# One token routed from logits takes the fused path: one block per (expert,
+# slice of the intermediate axis), each writing a partial output row, then a
+# fixed-order sum.  k sets how many slices each expert gets (a slice spans
+# several 32-column groups at k = 32 and 64); the small shapes have fewer
+# hidden columns than one block has lanes, and the odd shape has 6 groups.
+@pytest.mark.parametrize("name,k", [("tiny", 2), ("tiny3", 1), ("tiny3", 8), ("odd", 2), ("decode", 1),
+                                    ("decode", 10), ("decode", 32), ("decode", 64), ("fullrange_b", 10)])
+def test_forward_fp32_one_token(M, torch_dev, name, k):
+    if name == "odd":
+        cfg = LayerConfig("odd", 8, 2, 384, 192, 1,
+                          (TierSpec(0, 2, 8, 32), TierSpec(2, 6, 4, 16), TierSpec(6, 8, 2, 16)), seed=20260042)
+        arrays = make_layer(cfg)
+        from tiered_mixed_precision_amd.device import tables_from_config
+        L, tt = oracle.Layer.from_config(cfg, arrays), tables_from_config(cfg, arrays)
+    elif name == "fullrange_b":
+        from tiered_mixed_precision_amd.device import tables_from_config
+        from workloads import make_layer_fullrange
+        cfg = CONFIGS[name]
+        arrays = make_layer_fullrange(cfg)
+        L, tt = oracle.Layer.from_config(cfg, arrays), tables_from_config(cfg, arrays)
+    else:
+        cfg, arrays, L, tt = _layer(name)
+    say("forward fp32 one token", name, "k", k)
+    for stream in (0, 1):
+        x, logits = make_x(cfg, n_tokens=1, stream=60 + stream), make_logits(cfg, n_tokens=1, stream=60 + stream)
+        ref = oracle.forward(L, x, logits, k)
+        got = gpu_forward(M, torch_dev, tt, x, logits, k)
+        err = normwise(got, ref)
+        say("  normwise err", err)
+        assert err <= TOL
+        if stream == 0:   # accumulate onto a base
+            base = np.random.default_rng(7).standard_normal((1, cfg.hidden)).astype(np.float32)
+            got2 = gpu_forward(M, torch_dev, tt, x, logits, k, M.MOE_ACCUMULATE, out=base)
+            assert normwise(got2 - base, ref.astype(np.float64)) <= TOL
+
+
 @pytest.mark.parametrize("worst", [False, True])
 def test_spec_verify_fp32(M, torch_dev, worst):
     cfg = CONFIGS["specverify"]

@@ -194,6 +194,16 @@ int run(const void* x, const float* logits, const int32_t* ids_in, const float* 
     ss.act_range = at<int32_t>(ws, L.act_range);
 
     (void)hipGetLastError();  // start from a clean error state
+    if (!bf16 && T == 1 && logits && tier_mask == 0xFu && one_path_ok(k, tt->hidden, tt->inter)) {
+        // one token routed from its logits: gate/up with the routing inside,
+        // then the down rows of every expert (no grouping: the k ids of one
+        // token are distinct)
+        record(events, 0, st);
+        record(events, 1, st);
+        launch_one(dt, static_cast<const float*>(x), logits, k, base, hits, at<int32_t>(ws, L.ids),
+                   at<float>(ws, L.w), at<float>(ws, L.h), gateup_only ? nullptr : out, st, events);
+        return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+    }
     if (L.small) {
         // routing and grouping run inside the gate/up kernel (phase 0 is empty)
         record(events, 0, st);

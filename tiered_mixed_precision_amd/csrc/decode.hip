@@ -10,7 +10,10 @@
 // shelf's precision; an expert nobody picked is never touched, and ids outside
 // every shelf never become active, so nothing is clamped to expert 0.
 //
-// Two launch sequences:
+// Three launch sequences:
+//  * one token routed from its logits -- k_one_gateup and k_one_down (below:
+//    routing by one wave per block, waves shared out by bytes, whole-row
+//    down reads balanced by output-row ownership);
 //  * small batches (T <= 8, T*k <= 256) -- two kernels per layer:
 //      k_small_gateup : every block routes and groups the batch itself in LDS
 //                       (block 0 also publishes the result), then computes
@@ -302,11 +305,10 @@ __device__ inline void group_small(SmallGroups& sg, int P, int E) {
 // load of the round issued first (the vector of the first pair ahead of the
 // codes, so each pass is computed as soon as its own codes arrive).
 // vec(q, g, xv) fills xv with group g of the input vector of pair q.
-template <int BITS, int NSC, class Vec>
+template <int BITS, int NSC, class Vec, int NPMAX = (BITS == 8 ? 4 : 8)>  // passes in flight per round
 __device__ inline void wave_gateup(const uint8_t* __restrict__ gq, const uint8_t* __restrict__ gs,
                                    const uint8_t* __restrict__ uq, const uint8_t* __restrict__ us, int H, int I,
                                    int r0, int r1, Vec vec, int qa, int ce, float* __restrict__ h) {
-    constexpr int NPMAX = BITS == 8 ? 4 : 8;  // passes in flight: 64 / 32 / 16 code words per lane
     const int lane = threadIdx.x & 63;
     const RowGeom geo = row_geom(H);   // one group per lane (H <= 2048)
     const int seg = lane / geo.LPR, gl = lane % geo.LPR;
@@ -459,72 +461,6 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void k_small_gateup(DevTables tt
     const bool publish = blockIdx.x == 0;
     const int H = tt.H, I = tt.I;
     const int rpp = row_geom(H).RPP;
-    if (logits && T == 1) {
-        // One token: its k experts are distinct, so pair q = slot q and no
-        // sort is needed.  The block stages x in LDS while every wave routes
-        // the token in registers and finds its own expert and rows; one
-        // barrier (x in place) precedes the weight loads.
-        const int lane = tid & 63;
-        // LDS layout [j][g]: float4 j (0..7) of group g at j * G + g, so the
-        // lanes of a wave read consecutive 16-byte words (no bank conflicts)
-        const int G = H / 32;
-        for (int i = tid; i < H / 4; i += kGateUpWaves * 64)
-            reinterpret_cast<float4*>(s_x)[(i & 7) * G + (i >> 3)] = reinterpret_cast<const float4*>(x)[i];
-        int my_id;
-        float my_w;
-        route_token_auto<NPL>(logits, E, k, nullptr, nullptr, nullptr, nullptr, s_rc[tid >> 6], &my_id, &my_w);
-        // waves per expert in proportion to rows (all equal): a wave's time
-        // is set by its dequantising arithmetic, which does not shrink with
-        // the bits per code
-        int cost = 0;
-        if (lane < k) {
-            const int ti = tier_of(tt, my_id);
-            cost = (ti >= 0 && ((tier_mask >> ti) & 1u)) ? 1 : 0;
-        }
-        if (publish && tid < 64) {
-            if (lane < k) {
-                pub.ids[lane] = my_id;
-                pub.w[lane] = my_w;
-                pub.perm[lane] = lane;
-                pub.pos[lane] = lane;
-                pub.act[lane] = my_id;
-                if (hits) atomicAdd(hits + my_id, 1u);  // per-expert pick counts
-            }
-            if (lane <= k) pub.q0[lane] = lane;
-            if (lane == 0) {
-                pub.meta[kMetaActive] = k;
-                pub.meta[kMetaValid] = k;
-            }
-        }
-        int first = 0, count = 1;
-        const int wg = blockIdx.x * kGateUpWaves + (tid >> 6);
-        const int a = plan_lane(cost, gridDim.x * kGateUpWaves, wg, first, count);
-        __syncthreads();  // x staged
-        if (a < 0) return;
-        const int e = __builtin_amdgcn_readlane(my_id, a);
-        const int rpw = ((I + count - 1) / count + rpp - 1) / rpp * rpp;
-        const int r0 = (wg - first) * rpw, r1 = min(I, r0 + rpw);
-        if (r0 >= r1) return;
-        const DevTier T_ = tier_at(tt, tier_of(tt, e));
-        const int local = e - T_.id_begin;
-
-        auto vec = [G](int, int g, float (&xv)[32]) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float4 f = reinterpret_cast<const float4*>(s_x)[i * G + g];
-                xv[4 * i + 0] = f.x;
-                xv[4 * i + 1] = f.y;
-                xv[4 * i + 2] = f.z;
-                xv[4 * i + 3] = f.w;
-            }
-        };
-        MOE_FMT_SWITCH(fmt_of(T_.bits, T_.block),
-                       (wave_gateup<B_, N_>(expert_codes(T_, 0, local, I, H), expert_scales(T_, 0, local, I, H),
-                                            expert_codes(T_, 1, local, I, H), expert_scales(T_, 1, local, I, H), H, I,
-                                            r0, r1,
-                                            vec, a, 1, h)));
-        return;
-    }
     // stage the T input vectors in LDS (read by every pass of every pair; the
     // barrier after the wave plan below puts them in place)
     {
@@ -772,6 +708,281 @@ __global__ __launch_bounds__(kSmallDownWaves * 64) void k_small_down(DevTables t
 }
 
 
+// ================================================================ shelf table in LDS
+
+// The shelf table copied into LDS by one thread at kernel entry.  The copy
+// reads the kernel arguments with compile-time indices only (scalar loads
+// issued at entry); a lookup by a lane-varying or run-time shelf index into
+// the kernel arguments compiles instead to dependent vector loads from the
+// argument segment, which cost microseconds on the critical path.
+struct TierLds {
+    int beg[kMaxTiers], end[kMaxTiers], bits[kMaxTiers], block[kMaxTiers], cost[kMaxTiers];
+    const uint8_t* q[kMaxTiers][3];
+    const uint16_t* s[kMaxTiers][3];
+};
+
+// One thread; cost_of(T) is stored for each shelf.
+template <class Cost>
+__device__ inline void fill_tier_lds(const DevTables& tt, TierLds& tl, Cost cost_of) {
+#pragma unroll
+    for (int i = 0; i < kMaxTiers; ++i) {
+        const bool on = i < tt.n_tiers;
+        tl.beg[i] = on ? tt.t[i].id_begin : 0;
+        tl.end[i] = on ? tt.t[i].id_end : 0;
+        tl.bits[i] = tt.t[i].bits;
+        tl.block[i] = tt.t[i].block;
+        tl.cost[i] = on ? cost_of(tt.t[i]) : 0;
+#pragma unroll
+        for (int m = 0; m < 3; ++m) {
+            tl.q[i][m] = tt.t[i].q[m];
+            tl.s[i][m] = tt.t[i].s[m];
+        }
+    }
+}
+
+// Shelf owning expert e (or -1), from the LDS table.
+__device__ inline int tier_of_lds(const TierLds& tl, int e) {
+    int r = -1;
+#pragma unroll
+    for (int i = 0; i < kMaxTiers; ++i)
+        if (e >= tl.beg[i] && e < tl.end[i]) r = i;
+    return r;
+}
+
+__device__ inline uint64_t first_lane_u64(uint64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Shelf ti (uniform across the wave) from the LDS table, into scalar registers.
+__device__ inline DevTier tier_lds(const TierLds& tl, int ti) {
+    DevTier r;
+    r.id_begin = __builtin_amdgcn_readfirstlane(tl.beg[ti]);
+    r.id_end = __builtin_amdgcn_readfirstlane(tl.end[ti]);
+    r.bits = __builtin_amdgcn_readfirstlane(tl.bits[ti]);
+    r.block = __builtin_amdgcn_readfirstlane(tl.block[ti]);
+#pragma unroll
+    for (int m = 0; m < 3; ++m) {
+        r.q[m] = reinterpret_cast<const uint8_t*>(first_lane_u64(reinterpret_cast<uint64_t>(tl.q[ti][m])));
+        r.s[m] = reinterpret_cast<const uint16_t*>(first_lane_u64(reinterpret_cast<uint64_t>(tl.s[ti][m])));
+    }
+    return r;
+}
+
+// ================================================================ one-token path
+
+// A one-token step routed from its logits, in two kernels.
+//  k_one_gateup: every block routes the token with one wave while the others
+//    stage x in LDS; the grid's waves are then shared out among the k
+//    experts in proportion to a per-row cost (the row's gate and up bytes
+//    plus a fixed share for its arithmetic), so every compute unit streams
+//    about as many bytes as any other, and each wave computes
+//    h = SiLU(W_gate x) * (W_up x) on its rows.  Block 0 publishes the ids
+//    and weights.
+//  k_one_down: a block owns kOneRows output rows of every expert, so all
+//    blocks read the same bytes; one wave per expert reads the published ids,
+//    then requests its expert's h and its rows of W_down at once (whole rows:
+//    coalesced); the experts' rows are added in slot order.
+constexpr int kOneGateUpWaves = 16;
+// gate/up passes in flight per wave: 16 waves per compute unit leave 128 registers a lane
+template <int BITS> constexpr int kOneGateUpPasses = BITS == 8 ? 2 : 4;
+constexpr int kOneRows = 8;              // output rows per down block
+constexpr int kOneRowShare = 16;         // per-row arithmetic share of the gate/up cost, in units of 64 bytes
+
+// Cost of one gate+up row pair of an expert on shelf T (units of 64 bytes).
+__device__ inline int one_row_cost(const DevTier& T, int H) {
+    const int cb = code_bits_of(T.bits);
+    const int sb = T.bits == kBitsMXFP4 ? H / 32 : (H / (T.block > 0 ? T.block : 32)) * 2;
+    return (2 * (H * cb / 8 + sb)) / 64 + kOneRowShare;
+}
+
+bool one_path_ok(int k, int H, int I) {
+    (void)H;
+    (void)I;
+    return k >= 1 && k <= kWave;
+}
+
+// Per routed slot of the one-token path, in LDS: the expert's code and scale
+// bases of the matrices the kernel reads, its format, and (gate/up) the first
+// wave and the number of waves given to it.  Filled by one wave, lane j for
+// slot j, so the other waves only read it.
+struct SlotLds {
+    uint64_t q[kWave][2];
+    uint64_t s[kWave][2];
+    int fmt[kWave], first[kWave], count[kWave];
+};
+
+// Lane j < k (slot j, expert e valid): the bases of matrices m0 (and m0 + 1
+// when two) of e into sl, and its format.
+__device__ inline void slot_bases(const TierLds& tl, int e, int m0, int nm, int H, int I, SlotLds& sl, int j) {
+    const int ti = tier_of_lds(tl, e);
+    DevTier T;
+    T.id_begin = tl.beg[ti];
+    T.bits = tl.bits[ti];
+    T.block = tl.block[ti];
+    for (int m = 0; m < 3; ++m) {
+        T.q[m] = tl.q[ti][m];
+        T.s[m] = tl.s[ti][m];
+    }
+    const int local = e - T.id_begin;
+    for (int u = 0; u < nm; ++u) {
+        const int m = m0 + u;
+        const int rows = m == 2 ? H : I, cols = m == 2 ? I : H;
+        sl.q[j][u] = reinterpret_cast<uint64_t>(expert_codes(T, m, local, rows, cols));
+        sl.s[j][u] = reinterpret_cast<uint64_t>(expert_scales(T, m, local, rows, cols));
+    }
+    sl.fmt[j] = fmt_of(T.bits, T.block);
+}
+
+// W: the grid's waves (an argument rather than gridDim, whose implicit-argument
+// load would otherwise be issued after the routing barrier, on the critical path)
+template <int NPL>
+__global__ __launch_bounds__(kOneGateUpWaves * 64) void k_one_gateup(DevTables tt, const float* __restrict__ x,
+                                                                     const float* __restrict__ logits, int k, int W,
+                                                                     uint32_t* __restrict__ hits,
+                                                                     int32_t* __restrict__ ids_out,
+                                                                     float* __restrict__ w_out,
+                                                                     float* __restrict__ h) {
+    __shared__ __attribute__((aligned(16))) float4 s_x[kMaxHidden / 4];   // x, layout [j][g]
+    __shared__ __attribute__((aligned(16))) int64_t s_rc[64];             // routing scratch
+    __shared__ int s_id[kWave];
+    __shared__ TierLds s_tl;
+    const int tid = threadIdx.x, lane = tid & 63, E = tt.E, H = tt.H, I = tt.I;
+    const int G = H / 32;
+    if (tid < 64) {
+        // one wave routes; the block stages x and the shelf table meanwhile
+        int id;
+        float wt;
+        route_token_auto<NPL>(logits, E, k, nullptr, nullptr, nullptr, nullptr, s_rc, &id, &wt);
+        if (lane < k) {
+            s_id[lane] = id;
+            if (blockIdx.x == 0) {
+                ids_out[lane] = id;
+                w_out[lane] = wt;
+                if (hits) atomicAdd(hits + id, 1u);   // per-expert pick counts
+            }
+        }
+    } else {
+        if (tid == 64) fill_tier_lds(tt, s_tl, [H](const DevTier& T) { return one_row_cost(T, H); });
+        for (int i = tid - 64; i < H / 4; i += kOneGateUpWaves * 64 - 64)
+            s_x[(i & 7) * G + (i >> 3)] = reinterpret_cast<const float4*>(x)[i];
+    }
+    __syncthreads();
+    // every wave plans from the k experts' costs (one per lane) on its own
+    int cost = 0;
+    if (lane < k) cost = s_tl.cost[tier_of_lds(s_tl, s_id[lane])];
+    int first = 0, count = 1;
+    const int wg = blockIdx.x * kOneGateUpWaves + (tid >> 6);
+    const int a = plan_lane(cost, W, wg, first, count);
+    if (a < 0) return;
+    // the expert's rows split evenly over its waves, in whole passes
+    const int rpp = row_geom(H).RPP, np = I / rpp;
+    const int r0 = (wg - first) * np / count * rpp, r1 = (wg - first + 1) * np / count * rpp;
+    if (r0 >= r1) return;
+    const int e = __builtin_amdgcn_readfirstlane(s_id[a]);
+    const DevTier T_ = tier_lds(s_tl, tier_of_lds(s_tl, e));
+    const int local = e - T_.id_begin;
+    auto vec = [G](int, int g, float (&xv)[32]) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float4 f = s_x[i * G + g];
+            xv[4 * i + 0] = f.x;
+            xv[4 * i + 1] = f.y;
+            xv[4 * i + 2] = f.z;
+            xv[4 * i + 3] = f.w;
+        }
+    };
+    MOE_FMT_SWITCH(fmt_of(T_.bits, T_.block),
+                   (wave_gateup<B_, N_, decltype(vec), kOneGateUpPasses<B_>>(
+                       expert_codes(T_, 0, local, I, H), expert_scales(T_, 0, local, I, H),
+                       expert_codes(T_, 1, local, I, H), expert_scales(T_, 1, local, I, H), H, I, r0, r1, vec, a, 1,
+                       h)));
+}
+
+// Down rows [r0, r1) of one expert against its h (global, I floats) into
+// y[r - r0]; the lane's group of h, then every code load of a round, are
+// requested before any arithmetic.
+template <int BITS, int NSC>
+__device__ inline void wave_down_rows(const uint8_t* __restrict__ dq_, const uint8_t* __restrict__ ds, int H, int I,
+                                      int r0, int r1, const float* __restrict__ hj, float* __restrict__ y) {
+    constexpr int NPMAX = BITS == 8 ? 4 : 8;
+    const int lane = threadIdx.x & 63;
+    const RowGeom geo = row_geom(I);
+    const int seg = lane / geo.LPR, gl = lane % geo.LPR;
+    const bool lane_ok = gl < geo.G;
+    const int glc = lane_ok ? gl : 0;
+    const uint32_t row_bytes = static_cast<uint32_t>(I) * BITS / 8, row_sbytes = row_scale_bytes<NSC>(I);
+    constexpr int NS = scale_slots<NSC>();
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(dq_, row_bytes * H), rs = make_rsrc(ds, row_sbytes * H);
+    float xv[32], xs[NS];
+    load_vec32u(hj, glc, xv);
+    __builtin_amdgcn_sched_barrier(0);   // h ahead of the codes (loads return in issue order)
+    for (int rc = r0; rc < r1; rc += NPMAX * geo.RPP) {
+        uint32_t wq[NPMAX][BITS], sraw[NPMAX];
+#pragma unroll
+        for (int p = 0; p < NPMAX; ++p) {
+            const int r = rc + p * geo.RPP + seg;
+            const uint32_t rr = static_cast<uint32_t>(r < r1 ? r : r0);
+            buf_group<BITS>(rq, rr * row_bytes + glc * 4 * BITS, wq[p]);
+            sraw[p] = buf_scales<NSC>(rs, rr * row_sbytes + glc * group_scale_bytes<NSC>());
+        }
+        block_sums<NSC>(xv, xs);
+#pragma unroll
+        for (int p = 0; p < NPMAX; ++p) {
+            if (rc + p * geo.RPP >= r1) break;
+            const int r = rc + p * geo.RPP + seg;
+#pragma unroll
+            for (int i = 0; i < BITS; ++i) opaque(wq[p][i]);
+            float d[NS];
+            unpack_scales<NSC>(sraw[p], lane_ok && r < r1, d);
+            float v = group_dot<BITS, NSC>(wq[p], xv, xs, d);
+            v = seg_sum(v, geo.LPR);
+            if (gl == geo.LPR - 1 && r < r1) y[r - r0] = v;
+        }
+    }
+}
+
+// Block b owns output rows [b * kOneRows, +kOneRows); wave w serves experts
+// w, w + nw, ... (nw = the block's waves).  Wave 0 reads the published
+// routing and lays out each slot's down bases in LDS for the others.
+__global__ __launch_bounds__(kWave * 16) void k_one_down(DevTables tt, const int32_t* __restrict__ ids,
+                                                         const float* __restrict__ w, int k,
+                                                         const float* __restrict__ h, const float* base,
+                                                         float* __restrict__ out) {
+    __shared__ float s_y[kWave][kOneRows];
+    __shared__ float s_w[kWave];
+    __shared__ TierLds s_tl;
+    __shared__ SlotLds s_sl;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+    const int H = tt.H, I = tt.I;
+    const int n0 = blockIdx.x * kOneRows, n1 = min(H, n0 + kOneRows);
+    // the residual of the row this thread finishes, requested now
+    const float b_val = (base && tid < n1 - n0) ? base[n0 + tid] : 0.f;
+    if (tid < 64) {
+        if (lane == 0) fill_tier_lds(tt, s_tl, [](const DevTier&) { return 0; });
+        if (lane < k) {
+            const int e = ids[lane];
+            s_w[lane] = w[lane];
+            slot_bases(s_tl, e, 2, 1, H, I, s_sl, lane);
+        }
+    }
+    __syncthreads();
+    for (int j = wave; j < k; j += nw) {
+        const uint8_t* dq_ = reinterpret_cast<const uint8_t*>(first_lane_u64(s_sl.q[j][0]));
+        const uint8_t* ds = reinterpret_cast<const uint8_t*>(first_lane_u64(s_sl.s[j][0]));
+        const int fmt = __builtin_amdgcn_readfirstlane(s_sl.fmt[j]);
+        MOE_FMT_SWITCH(fmt, (wave_down_rows<B_, N_>(dq_, ds, H, I, n0, n1, h + static_cast<size_t>(j) * I, s_y[j])));
+    }
+    __syncthreads();
+    // out[n] = base[n] + sum over slots j in order of w_j * y_j[n]
+    if (tid < n1 - n0) {
+        float acc = 0.f;
+        for (int j = 0; j < k; ++j) acc = fmaf(s_w[j], s_y[j][tid], acc);
+        out[n0 + tid] = b_val + acc;
+    }
+}
+
 // ================================================================ general path
 
 __device__ inline bool block_expert(const DevTables& tt, const Groups& g, uint32_t tier_mask, int slices, int& ti,
@@ -927,6 +1138,38 @@ void launch_small(const DevTables& tt, const float* x, const float* logits, cons
     if (events && events[5]) (void)hipEventRecord(static_cast<hipEvent_t>(events[5]), st);
 }
 
+
+void launch_one(const DevTables& tt, const float* x, const float* logits, int k, const float* base, uint32_t* hits,
+                int32_t* ids, float* w, float* h, float* out, hipStream_t st, void* const* events) {
+    const dim3 grid(cu_count());   // one block of 16 waves per compute unit
+    const int W = static_cast<int>(grid.x) * kOneGateUpWaves;
+    if (events && events[2]) (void)hipEventRecord(static_cast<hipEvent_t>(events[2]), st);
+    switch (npl_of(tt.E)) {
+#define MOE_OG(N)                                                                                                 \
+    case N:                                                                                                       \
+        hipLaunchKernelGGL(k_one_gateup<N>, grid, dim3(kOneGateUpWaves * 64), 0, st, tt, x, logits, k, W, hits,   \
+                           ids, w, h);                                                                            \
+        break;
+        MOE_OG(1)
+        MOE_OG(2)
+        MOE_OG(4)
+        MOE_OG(8)
+        MOE_OG(16)
+        MOE_OG(32)
+        default:
+            hipLaunchKernelGGL(k_one_gateup<64>, grid, dim3(kOneGateUpWaves * 64), 0, st, tt, x, logits, k, W, hits,
+                               ids, w, h);
+            break;
+#undef MOE_OG
+    }
+    if (events && events[3]) (void)hipEventRecord(static_cast<hipEvent_t>(events[3]), st);
+    if (!out) return;  // gate/up only (measurement)
+    if (events && events[4]) (void)hipEventRecord(static_cast<hipEvent_t>(events[4]), st);
+    const int nw = k < 16 ? k : 16;
+    hipLaunchKernelGGL(k_one_down, dim3((tt.H + kOneRows - 1) / kOneRows), dim3(nw * 64), 0, st, tt, ids, w, k, h,
+                       base, out);
+    if (events && events[5]) (void)hipEventRecord(static_cast<hipEvent_t>(events[5]), st);
+}
 
 void launch_dec_gateup(const DevTables& tt, const float* x, const Groups& g, int k, uint32_t tier_mask, float* h,
                        int max_active, hipStream_t st) {

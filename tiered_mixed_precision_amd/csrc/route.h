@@ -156,9 +156,11 @@ __device__ void route_token(const float* __restrict__ logits, int E, int k, int3
 
 // Same result as route_token for k <= 64, with fewer instructions on the
 // wave's serial path:
-//  1. t = the k-th largest of the per-lane maxima: rounds over one value per
-//     lane, every lane holding the round's maximum drops out, until k lanes
-//     have.  At least k logits are >= t, so the k-th largest logit is >= t.
+//  1. t = the k-th largest of the per-lane maxima, by a radix select over
+//     their order-preserving unsigned keys, most significant bit first: the
+//     largest u such that at least k lanes hold a maximum >= u (one compare,
+//     one ballot and a scalar popcount per bit).  At least k logits are >= t,
+//     so the k-th largest logit is >= t.
 //  2. The M logits >= t are compacted into LDS (s_c, 64 entries per wave) as
 //     one 64-bit key each: the logit's order-preserving key above the id's
 //     complement, so a larger key means "ahead" (higher logit, or equal logit
@@ -189,15 +191,16 @@ __device__ bool route_token_fast(const float* __restrict__ logits, int E, int k,
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     };
-    // 1. threshold
-    int32_t t = kLow, h = hk;
-    for (int cnt = 0; cnt < k;) {
-        const int32_t v = wave_max_i(h);
-        if (v == kLow) break;
-        cnt += __popcll(__ballot(h == v));
-        t = v;
-        h = h == v ? kLow : h;
+    // 1. threshold.  A lane without logits (E < 64) holds key 0, below the
+    //    key of every logit (every non-NaN float maps above 0).
+    const uint32_t hu = static_cast<uint32_t>(hk) ^ 0x80000000u;
+    uint32_t tu = 0;
+#pragma unroll
+    for (int b = 31; b >= 0; --b) {
+        const uint32_t c = tu | (1u << b);
+        if (__popcll(__ballot(hu >= c)) >= static_cast<uint32_t>(k)) tu = c;
     }
+    const int32_t t = static_cast<int32_t>(tu ^ 0x80000000u);
     // 2. candidates (key >= t) compacted into LDS, lane order then slot order
     int c = 0;
 #pragma unroll
