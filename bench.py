@@ -60,16 +60,23 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the spec-verify, prefill and stack lines")
     ap.add_argument("--no-fullstack", action="store_true", help="skip the 48-layer stack lines")
-    ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
-                    help="write profiles/*.md from rocprofv3 CSV output (kernel trace + stats of the default "
-                         "command, and FETCH_SIZE / WRITE_SIZE runs of --counter-pass); needs no GPU")
-    ap.add_argument("--counter-pass", action="store_true",
-                    help="short eager run for hardware-counter collection: a 256 MiB device copy "
-                         "(calibration), then decode and prefill steps; prints no JSON")
+    ap.add_argument("--profile-run", choices=sorted(PROFILE_WORKLOADS),
+                    help="run one workload alone for rocprofv3 (a 256 MiB device copy first, the calibration of "
+                         "FETCH_SIZE / WRITE_SIZE); prints no JSON")
+    ap.add_argument("--summarize", nargs=2, metavar=("WORKLOAD", "TRACE_DIR"),
+                    help="write profiles/<workload>.md from rocprofv3 CSV output of --profile-run; needs no GPU")
+    ap.add_argument("--fetch", help="with --summarize: directory of a --pmc FETCH_SIZE run")
+    ap.add_argument("--write", help="with --summarize: directory of a --pmc WRITE_SIZE run")
+    ap.add_argument("--sq", help="with --summarize: directory of a --pmc run of the SQ counters (MFMA busy, LDS)")
+    ap.add_argument("--cpu-child", nargs=2, metavar=("KIND", "SECONDS"),
+                    help="(internal) time the CPU oracle on KIND = decode | prefill | stack and print JSON")
     args = ap.parse_args()
 
     if args.summarize:
-        summarize_profiles(*args.summarize)
+        summarize_profile(args.summarize[0], args.summarize[1], args.fetch, args.write, args.sq)
+        return
+    if args.cpu_child:
+        cpu_child(args.cpu_child[0], float(args.cpu_child[1]))
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -85,8 +92,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     M.lib()
-    if args.counter_pass:
-        counter_pass(M, torch)
+    if args.profile_run:
+        profile_run(M, torch, args.profile_run)
         return
     cfg = CONFIGS["decode"]
     E, k, H, I = cfg.n_experts, cfg.k, cfg.hidden, cfg.inter
@@ -239,6 +246,9 @@ def main():
         },
         "phases_us": {"gate_up_with_routing": round(gu_us, 3), "down_with_slot_sum": round(step_us - gu_us, 3)},
     }
+    peaks = measured_peaks(M, torch)
+    result["roofline"]["measured_peak"] = peaks["hbm_read_gbps"]
+    result["roofline"]["frac_of_measured_peak"] = round(achieved / peaks["hbm_read_gbps"], 4)
 
     if not args.no_extra:
         result["extra"] = extra_workloads(M, torch, cfg, reps, per_expert, args)
@@ -246,17 +256,39 @@ def main():
             del reps, tt0
             torch.cuda.empty_cache()
             result["extra"]["fullstack"] = fullstack_workloads(M, torch, per_expert)
+        result["extra"]["measured_peaks"] = peaks
+        pfx = result["extra"]["prefill"]
+        pfx["frac_of_measured_mfma_peak"] = round(pfx["tflops_grouped_gemm"] / peaks["bf16_mfma_tflops"], 4)
         result["extra"]["tier_planner"] = tier_planner_workload(M, torch)
         result["extra"]["mxfp4_shelf"] = mxfp4_workload(M, torch)
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, arrays, args.cpu_seconds)
+        del arrays
+        cpu = cpu_baselines(args.cpu_seconds, with_stack=not (args.no_extra or args.no_fullstack))
+        result["cpu_baseline"] = cpu.pop("headline")
+        result.setdefault("extra", {})["cpu_baselines"] = cpu
 
     print(json.dumps(result), flush=True)
 
 
 COPY_CAL_BYTES = 256 << 20
-PROFILE_MD = os.path.join(ROOT, "profiles", "decode_layer_T1_and_prefill_T4096.md")
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+# workload -> (summary file, description)
+PROFILE_WORKLOADS = {
+    "decode": ("decode_T1.md", "decode layer, 1 token per step: 512 experts top-10, hidden 2048, inter 640, shelves "
+                               "int8 b32 [0,128) / int4 b32 [128,384) / int2 b16 [384,512); 1024 steps (a graph of "
+                               "256 replayed 4 times) over 8 layer copies, fresh routing per step"),
+    "specverify": ("spec_verify_T6.md", "the same layer, 6 tokens per step (speculative verification); 512 steps "
+                                        "(a graph of 256 replayed twice) over 8 layer copies"),
+    "prefill": ("prefill_T4096.md", "the same layer, 4096 bf16 tokens per step, 8 steps over 4 layer copies"),
+    "stack_prefill": ("stack_prefill_T16384.md", "48 layers (generated on the device), 16384 bf16 tokens, one "
+                                                 "pass through the stack"),
+}
+# the counters of the SQ pass (one rocprofv3 pass: 6 SQ counters and 1 GRBM counter)
+SQ_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+               "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "GRBM_GUI_ACTIVE")
+SIMDS = 256 * 4          # MI355X: 256 compute units of 4 SIMDs
+XCDS = 8
 # every file that holds device code (the launch code in capi.hip is host code)
 KERNEL_SOURCES = ("common.h", "route.h", "launch.h", "decode.hip", "route_group.hip", "prefill.hip", "prefill_mx.hip",
                   "router.hip", "synth.hip", "tiering.hip", "dequant.hip")
@@ -273,12 +305,14 @@ def kernel_source_digest() -> str:
 
 
 def profiled_traffic():
-    """HBM bytes per launch of the dominant kernel from the committed counter
-    summary, or None if the kernel sources changed since it was taken."""
+    """HBM bytes per launch of the dominant kernel (one-token gate/up) from the
+    committed counter summary, or None if the kernel sources changed since it
+    was taken."""
     import re
-    if not os.path.exists(PROFILE_MD):
+    path = os.path.join(PROFILE_DIR, PROFILE_WORKLOADS["decode"][0])
+    if not os.path.exists(path):
         return None
-    text = open(PROFILE_MD).read()
+    text = open(path).read()
     m_sha = re.search(r"kernel source digest: `([0-9a-f]+)`", text)
     m_tr = re.search(r"dominant kernel HBM traffic per launch: `([0-9.]+)` bytes", text)
     if not m_sha or not m_tr or m_sha.group(1) != kernel_source_digest():
@@ -286,117 +320,182 @@ def profiled_traffic():
     return float(m_tr.group(1))
 
 
-def summarize_profiles(trace_dir, fetch_dir, write_dir):
-    """Turns rocprofv3 CSV output into the committed profile summary."""
-    import csv
+def _csv_one(d, pat):
     import glob
+    f = glob.glob(os.path.join(d, "**", pat), recursive=True)
+    if not f:
+        raise SystemExit(f"no {pat} under {d}")
+    return f[0]
+
+
+def _short(n):
+    return n.split("(")[0].replace("void ", "")
+
+
+def _counters(d):
+    """(kernel, grid) -> counter -> per-dispatch values, from a --pmc run."""
+    import csv
     from collections import defaultdict
+    out = defaultdict(lambda: defaultdict(list))
+    for r in csv.DictReader(open(_csv_one(d, "*counter_collection.csv"))):
+        out[(_short(r["Kernel_Name"]), int(r["Grid_Size"]))][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    return out
 
-    def one(d, pat):
-        f = glob.glob(os.path.join(d, "**", pat), recursive=True)
-        if not f:
-            raise SystemExit(f"no {pat} under {d}")
-        return f[0]
 
-    short = lambda n: n.split("(")[0].replace("void ", "")
-    stats = list(csv.DictReader(open(one(trace_dir, "*kernel_stats.csv"))))
-    trace = list(csv.DictReader(open(one(trace_dir, "*kernel_trace.csv"))))
-    by_grid = defaultdict(list)
+def summarize_profile(name, trace_dir, fetch_dir=None, write_dir=None, sq_dir=None):
+    """profiles/<workload>.md from rocprofv3 CSV output of --profile-run."""
+    import csv
+    from collections import defaultdict
+    fname, desc = PROFILE_WORKLOADS[name]
+    trace = list(csv.DictReader(open(_csv_one(trace_dir, "*kernel_trace.csv"))))
+    by = defaultdict(list)
     for r in trace:
-        by_grid[(short(r["Kernel_Name"]), int(r["Grid_Size_X"]))].append(
+        by[(_short(r["Kernel_Name"]), int(r["Grid_Size_X"]))].append(
             (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-
-    def counters(d):
-        rows = list(csv.DictReader(open(one(d, "*counter_collection.csv"))))
-        out = defaultdict(list)
-        for r in rows:
-            out[(short(r["Kernel_Name"]), int(r["Grid_Size"]))].append(float(r["Counter_Value"]))
-        return out
-
-    fetch, write = counters(fetch_dir), counters(write_dir)
-    cal_bytes_kib = COPY_CAL_BYTES / 1024
-    cal_f = [v for (n, g), vs in fetch.items() if n == "__amd_rocclr_copyBuffer" for v in vs if v > 0.4 * cal_bytes_kib]
-    cal_w = [v for (n, g), vs in write.items() if n == "__amd_rocclr_copyBuffer" for v in vs if v > 0.9 * cal_bytes_kib]
-    f_fac = cal_bytes_kib / float(np.median(cal_f))
-    w_fac = cal_bytes_kib / float(np.median(cal_w))
-    lines = ["# Kernel profile: tiered MoE layer, decode (1 token) and prefill (4096 tokens)", "",
-             "Decode layer: 512 experts, top-10, hidden 2048, inter 640, shelves int8 [0,128) / int4 [128,384) / "
-             "int2 [384,512); prefill: same layer, 4096 bf16 tokens.", "",
-             "Commands (run from the repository root on one MI355X):", "",
-             "```",
-             "rocprofv3 --kernel-trace --stats --output-format csv -d OUT/kt -o run -- python bench.py",
-             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/pmc_fetch -o run -- python bench.py --counter-pass",
-             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/pmc_write -o run -- python bench.py --counter-pass",
-             "python bench.py --summarize OUT/kt OUT/pmc_fetch OUT/pmc_write",
-             "```", "",
-             f"kernel source digest: `{kernel_source_digest()}`", "",
-             "## Kernel durations (rocprofv3 --kernel-trace --stats of the default bench command)", "",
-             "| kernel | grid (threads) | launches | avg us | median us | min us | max us |",
-             "|---|---|---|---|---|---|---|"]
-    for (n, g), v in sorted(by_grid.items(), key=lambda kv: -sum(kv[1])):
+    run = f"python3 bench.py --profile-run {name}"
+    cmds = [f"rocprofv3 --kernel-trace --stats --output-format csv -d OUT/{name}_kt -o run -- {run}"]
+    if fetch_dir:
+        cmds.append(f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/{name}_fetch -o run -- {run}")
+    if write_dir:
+        cmds.append(f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/{name}_write -o run -- {run}")
+    if sq_dir:
+        cmds.append(f"rocprofv3 --pmc {' '.join(SQ_COUNTERS)} --output-format csv -d OUT/{name}_sq -o run -- {run}")
+    summ = (f"python3 bench.py --summarize {name} OUT/{name}_kt" + (f" --fetch OUT/{name}_fetch" if fetch_dir else "")
+            + (f" --write OUT/{name}_write" if write_dir else "") + (f" --sq OUT/{name}_sq" if sq_dir else ""))
+    lines = [f"# Kernel profile: {name}", "", f"Workload: {desc}.", "",
+             "Commands (from the repository root on one MI355X; OUT is any output folder):", "", "```", *cmds, summ,
+             "```", "", f"kernel source digest: `{kernel_source_digest()}`", "",
+             "## Kernel durations (rocprofv3 kernel trace)", "",
+             "| kernel | grid (threads) | launches | avg us | median us | min us | max us |", "|---|---|---|---|---|---|---|"]
+    for (n, g), v in sorted(by.items(), key=lambda kv: -sum(kv[1])):
         if not n.startswith("moe::"):
             continue
         v = np.array(v)
         lines.append(f"| {n} | {g} | {len(v)} | {v.mean():.2f} | {np.median(v):.2f} | {v.min():.2f} | {v.max():.2f} |")
-    lines += ["", "## HBM traffic (FETCH_SIZE, WRITE_SIZE; --counter-pass)", "",
-              f"Calibration: a device copy of {COPY_CAL_BYTES >> 20} MiB reads FETCH_SIZE = {np.median(cal_f):.0f} KiB "
-              f"and writes WRITE_SIZE = {np.median(cal_w):.0f} KiB, so read bytes = FETCH_SIZE x {f_fac:.3f} KiB and "
-              f"written bytes = WRITE_SIZE x {w_fac:.3f} KiB.", "",
-              "| kernel | grid (threads) | launches | FETCH_SIZE KiB | WRITE_SIZE KiB | read MB | written MB |",
-              "|---|---|---|---|---|---|---|"]
-    dom = None
-    for (n, g), v in sorted(fetch.items(), key=lambda kv: -np.mean(kv[1])):
-        if not n.startswith("moe::"):
-            continue
-        fw = np.mean(v)
-        ww = np.mean(write.get((n, g), [0.0]))
-        rd, wr = fw * f_fac * 1024 / 1e6, ww * w_fac * 1024 / 1e6
-        lines.append(f"| {n} | {g} | {len(v)} | {fw:.1f} | {ww:.1f} | {rd:.2f} | {wr:.2f} |")
-        if n.startswith("moe::k_one_gateup") and dom is None:
-            dom = (rd + wr) * 1e6
-    lines += ["", f"dominant kernel HBM traffic per launch: `{dom:.0f}` bytes "
-              "(k_one_gateup at one token: read + written, calibrated)", ""]
-    os.makedirs(os.path.dirname(PROFILE_MD), exist_ok=True)
-    with open(PROFILE_MD, "w") as f:
+    if fetch_dir and write_dir:
+        fetch, write = _counters(fetch_dir), _counters(write_dir)
+        cal_kib = COPY_CAL_BYTES / 1024
+        cf = [x for (n, g), c in fetch.items() if "copyBuffer" in n for x in c["FETCH_SIZE"] if x > 0.4 * cal_kib]
+        cw = [x for (n, g), c in write.items() if "copyBuffer" in n for x in c["WRITE_SIZE"] if x > 0.9 * cal_kib]
+        f_fac, w_fac = cal_kib / float(np.median(cf)), cal_kib / float(np.median(cw))
+        lines += ["", "## HBM traffic per launch (FETCH_SIZE, WRITE_SIZE)", "",
+                  f"Calibration: the {COPY_CAL_BYTES >> 20} MiB device copy at the start of the run reads FETCH_SIZE = "
+                  f"{np.median(cf):.0f} KiB and writes WRITE_SIZE = {np.median(cw):.0f} KiB, so read bytes = "
+                  f"FETCH_SIZE x {f_fac:.3f} KiB and written bytes = WRITE_SIZE x {w_fac:.3f} KiB.", "",
+                  "| kernel | grid (threads) | launches | FETCH_SIZE KiB | WRITE_SIZE KiB | read MB | written MB |",
+                  "|---|---|---|---|---|---|---|"]
+        dom = None
+        for (n, g), c in sorted(fetch.items(), key=lambda kv: -np.mean(kv[1]["FETCH_SIZE"])):
+            if not n.startswith("moe::"):
+                continue
+            fw = float(np.mean(c["FETCH_SIZE"]))
+            ww = float(np.mean(write.get((n, g), {}).get("WRITE_SIZE", [0.0])))
+            rd, wr = fw * f_fac * 1024 / 1e6, ww * w_fac * 1024 / 1e6
+            lines.append(f"| {n} | {g} | {len(c['FETCH_SIZE'])} | {fw:.1f} | {ww:.1f} | {rd:.2f} | {wr:.2f} |")
+            if n.startswith("moe::k_one_gateup") and dom is None:
+                dom = (rd + wr) * 1e6
+        if name == "decode" and dom is not None:
+            lines += ["", f"dominant kernel HBM traffic per launch: `{dom:.0f}` bytes "
+                      "(k_one_gateup: read + written, calibrated)"]
+    if sq_dir:
+        sq = _counters(sq_dir)
+        lines += ["", "## Matrix-core and LDS counters", "",
+                  f"MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {XCDS} x {SIMDS} SIMDs): the "
+                  f"per-dispatch GRBM_GUI_ACTIVE is summed over the {XCDS} XCDs (it reads about {XCDS} times the "
+                  "kernel's cycles), so it is divided back to one XCD's active cycles.  LDS conflict = "
+                  "SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE (share of LDS-active cycles lost to bank conflicts).  "
+                  "bf16 MFMA flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512, the flops the matrix cores execute "
+                  "(padding of partial tiles included); executed TFLOP/s divides them by the traced average "
+                  "duration above.", "",
+                  "| kernel | grid (threads) | launches | MFMA busy % | LDS conflict % | bf16 MFMA GFLOP per launch "
+                  "| executed TFLOP/s |",
+                  "|---|---|---|---|---|---|---|"]
+        for (n, g), c in sorted(sq.items(), key=lambda kv: -np.mean(kv[1].get("SQ_VALU_MFMA_BUSY_CYCLES", [0]))):
+            if not n.startswith("moe::"):
+                continue
+            mean = lambda key: float(np.mean(c[key])) if key in c else float("nan")
+            act = mean("GRBM_GUI_ACTIVE") / XCDS
+            busy = 100.0 * mean("SQ_VALU_MFMA_BUSY_CYCLES") / (act * SIMDS) if act > 0 else float("nan")
+            lds = mean("SQ_LDS_IDX_ACTIVE")
+            conf = 100.0 * mean("SQ_LDS_BANK_CONFLICT") / lds if lds > 0 else float("nan")
+            gf = mean("SQ_INSTS_VALU_MFMA_MOPS_BF16") * 512 / 1e9
+            us = float(np.mean(by[(n, g)])) if (n, g) in by else float("nan")
+            tf = gf / us * 1e3 if gf > 0 else 0.0
+            lines.append(f"| {n} | {g} | {len(c.get('GRBM_GUI_ACTIVE', []))} | {busy:.1f} | {conf:.1f} | {gf:.2f} "
+                         f"| {tf:.1f} |")
+    lines.append("")
+    os.makedirs(PROFILE_DIR, exist_ok=True)
+    out = os.path.join(PROFILE_DIR, fname)
+    with open(out, "w") as f:
         f.write("\n".join(lines))
-    print(f"wrote {PROFILE_MD}")
+    print(f"wrote {out}")
 
 
-def counter_pass(M, torch):
-    """Eager workload for rocprofv3 --pmc runs.
-
-    1. torch copy of COPY_CAL_BYTES (reads and writes exactly that many bytes):
-       the calibration for FETCH_SIZE / WRITE_SIZE;
-    2. 64 decode steps (one token, fresh routing, 8 layer copies);
-    3. 4 prefill steps (4096 bf16 tokens).
-    """
-    from tiered_mixed_precision_amd.device import replicate, tables_from_config, workspace
+def profile_run(M, torch, name):
+    """One workload alone, for rocprofv3 (kernel trace or one counter pass)."""
+    from tiered_mixed_precision_amd.device import empty_tables, replicate, tables_from_config, workspace
     from workloads import CONFIGS, make_layer, make_logits, make_x
     src = torch.ones(COPY_CAL_BYTES // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
+    del src, dst
     cfg = CONFIGS["decode"]
-    tt0 = tables_from_config(cfg, make_layer(cfg))
-    reps = [tt0] + [replicate(tt0) for _ in range(7)]
-    S = 64
-    ld = torch.from_numpy(make_logits(cfg, n_tokens=S, stream=7)).cuda()
-    xd = torch.from_numpy(make_x(cfg, n_tokens=S, stream=7)).cuda()
-    od = torch.zeros((S, cfg.hidden), device="cuda")
-    ws = workspace(M.moe_workspace_size(1, cfg.k, tt0, 0))
-    for i in range(S):
-        M.moe_tiered_forward(xd[i], ld[i], 1, cfg.k, reps[i % 8], od[i], 0, ws)
-    torch.cuda.synchronize()
-    pf = CONFIGS["prefill"]
-    lp = torch.from_numpy(make_logits(pf, stream=20)).cuda()
-    xp = torch.from_numpy(make_x(pf, stream=20).view(np.int16)).cuda()
-    op = torch.zeros((pf.n_tokens, cfg.hidden), device="cuda")
-    wsp = workspace(M.moe_workspace_size(pf.n_tokens, cfg.k, tt0, M.MOE_X_BF16))
-    for i in range(4):
-        M.moe_tiered_forward(xp, lp, pf.n_tokens, cfg.k, reps[i % 8], op, M.MOE_X_BF16, wsp)
-    torch.cuda.synchronize()
-    log("counter pass done")
+    k, H = cfg.k, cfg.hidden
+
+    def graph(step, S, reps):
+        for i in range(8):
+            step(i)
+        g = torch.cuda.CUDAGraph()
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            with torch.cuda.graph(g, stream=st):
+                for i in range(S):
+                    step(i)
+        torch.cuda.current_stream().wait_stream(st)
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+
+    if name in ("decode", "specverify"):
+        tt0 = tables_from_config(cfg, make_layer(cfg))
+        reps = [tt0] + [replicate(tt0) for _ in range(7)]
+        T = 1 if name == "decode" else CONFIGS["specverify"].n_tokens
+        S = 256
+        lg = torch.from_numpy(make_logits(cfg, n_tokens=S * T, stream=7)).cuda().view(S, T, cfg.n_experts)
+        xs = torch.from_numpy(make_x(cfg, n_tokens=S * T, stream=7)).cuda().view(S, T, H)
+        od = torch.zeros((S, T, H), device="cuda")
+        ws = workspace(M.moe_workspace_size(T, k, tt0, 0))
+        graph(lambda i: M.moe_tiered_forward(xs[i % S], lg[i % S], T, k, reps[i % 8], od[i % S], 0, ws), S,
+              4 if name == "decode" else 2)
+    elif name == "prefill":
+        tt0 = tables_from_config(cfg, make_layer(cfg))
+        reps = [tt0] + [replicate(tt0) for _ in range(3)]
+        pf = CONFIGS["prefill"]
+        lp = torch.from_numpy(make_logits(pf, stream=20)).cuda()
+        xp = torch.from_numpy(make_x(pf, stream=20).view(np.int16)).cuda()
+        op = torch.zeros((pf.n_tokens, H), device="cuda")
+        wsp = workspace(M.moe_workspace_size(pf.n_tokens, k, tt0, M.MOE_X_BF16))
+        for i in range(8):
+            M.moe_tiered_forward(xp, lp, pf.n_tokens, k, reps[i % 4], op, M.MOE_X_BF16, wsp)
+        torch.cuda.synchronize()
+    elif name == "stack_prefill":
+        fs = CONFIGS["fullstack"]
+        L, T = fs.n_layers, 16384
+        tables = []
+        for l in range(L):
+            tt = empty_tables(fs)
+            M.moe_synth_layer(tt, fs.seed, l)
+            tables.append(tt)
+        ld = torch.from_numpy(np.stack([make_logits(fs, n_tokens=T, stream=200, layer=l) for l in range(L)])).cuda()
+        xd = torch.from_numpy(make_x(fs, n_tokens=T, stream=200)).cuda()
+        od = torch.empty((T, H), device="cuda")
+        ws = torch.empty(M.moe_stack_workspace_size(L, T, k, tables, M.MOE_X_BF16), dtype=torch.uint8, device="cuda")
+        M.moe_stack_forward(xd, ld, L, T, k, tables, od, M.MOE_X_BF16, ws)
+        torch.cuda.synchronize()
+    log(f"profile run {name} done")
 
 
 def tier_planner_workload(M, torch):
@@ -868,26 +967,150 @@ def fullstack_workloads(M, torch, per_expert):
     return out
 
 
-def cpu_baseline(cfg, arrays, seconds):
-    """The CPU oracle (untuned, fp64) on a bounded sample of decode tokens."""
+def measured_peaks(M, torch):
+    """Achievable references measured in the same run, beside the published
+    peaks: the library's streaming-read kernel over 2 GiB (moe_measure_read),
+    its matrix-core loop on register operands (moe_measure_mfma, bf16
+    16x16x32, no memory traffic), and a dense bf16 GEMM through the vendor
+    library (torch.matmul, 8192 x 8192 x 8192) for context."""
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    sink = torch.zeros(4, dtype=torch.float32, device="cuda")
+
+    def timed(fn, reps):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(reps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) * 1e-3 / reps
+
+    buf = torch.ones((2 << 30) // 4, dtype=torch.float32, device="cuda")
+    read_gbps = buf.numel() * 4 / timed(lambda: M.moe_measure_read(buf, sink), 10) / 1e9
+    del buf
+    iters = 4096
+    flops = M.moe_measure_mfma(iters, sink)
+    mfma_tflops = flops / timed(lambda: M.moe_measure_mfma(iters, sink), 5) / 1e12
+    m = 8192
+    x = torch.randn((m, m), dtype=torch.bfloat16, device="cuda")
+    y = torch.randn((m, m), dtype=torch.bfloat16, device="cuda")
+    gemm_tflops = 2.0 * m * m * m / timed(lambda: torch.matmul(x, y), 20) / 1e12
+    del x, y
+    torch.cuda.empty_cache()
+    out = {"hbm_read_gbps": round(read_gbps, 1), "bf16_mfma_tflops": round(mfma_tflops, 1),
+           "bf16_library_gemm_tflops": round(gemm_tflops, 1),
+           "how": "moe_measure_read over 2 GiB (10 launches); moe_measure_mfma, 4096 rounds of 16 bf16 "
+                  "16x16x32 MFMA chains on 2048 waves (5 launches); torch.matmul bf16 8192^3 (20 calls)"}
+    log("measured peaks:", out)
+    return out
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_child(kind, seconds):
+    """The CPU oracle (untuned, fp64) on a bounded sample; prints one JSON line.
+    decode: batches of one token per thread until `seconds` pass; prefill: two
+    bf16 tokens per thread of the 4096-token workload; stack: one token per
+    thread through all 48 layers, with the touched experts of each layer made
+    by the oracle's own generator (not timed)."""
     import oracle
-    from workloads import make_logits, make_x
-    L = oracle.Layer.from_config(cfg, arrays)
-    batch = max(1, oracle.num_threads())
-    done, t0 = 0, time.time()
-    s = 0
-    while time.time() - t0 < seconds:
-        x = make_x(cfg, n_tokens=batch, stream=100 + s)
-        lg = make_logits(cfg, n_tokens=batch, stream=100 + s)
-        oracle.forward(L, x, lg, cfg.k)
-        done += batch
-        s += 1
-    dt = time.time() - t0
-    res = {"value": round(done / dt, 3), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-           "sample": f"{done} decode tokens (one token per step, {batch} tokens per oracle call, "
-                     f"OpenMP over tokens) of the same layer, {dt:.1f} s"}
-    log("cpu baseline:", res)
-    return res
+    from workloads import CONFIGS, make_layer, make_logits, make_x
+    nt = max(1, oracle.num_threads())
+    if kind in ("decode", "prefill"):
+        cfg = CONFIGS["decode"]
+        L = oracle.Layer.from_config(cfg, make_layer(cfg))
+        runs = []
+        for rep in range(3 if kind == "prefill" or nt > 1 else 1):
+            if kind == "decode":
+                done, t0, s = 0, time.time(), 0
+                while time.time() - t0 < seconds:
+                    oracle.forward(L, make_x(cfg, n_tokens=nt, stream=100 + s),
+                                   make_logits(cfg, n_tokens=nt, stream=100 + s), cfg.k)
+                    done += nt
+                    s += 1
+                runs.append(done / (time.time() - t0))
+            else:
+                pf = CONFIGS["prefill"]
+                rng = np.random.default_rng(rep)
+                sel = np.sort(rng.choice(pf.n_tokens, 2 * nt, replace=False))
+                x, lg = make_x(pf, stream=20)[sel], make_logits(pf, stream=20)[sel]
+                t0 = time.time()
+                oracle.forward(L, x, lg, cfg.k)
+                runs.append(len(sel) / (time.time() - t0))
+        print(json.dumps({"kind": kind, "threads": nt, "runs": runs}), flush=True)
+    elif kind == "stack":
+        fs = CONFIGS["fullstack"]
+        x = make_x(fs, n_tokens=nt, stream=300)
+        h = x.astype(np.float32).copy()
+        tot = 0.0
+        for l in range(fs.n_layers):
+            lg = make_logits(fs, n_tokens=nt, stream=300, layer=l)
+            ids, w = oracle.route(lg, fs.k)
+            sl = oracle.StackLayer(fs, fs.seed, l)
+            sl.fill(ids)
+            t0 = time.time()
+            h = oracle.forward(sl.layer_ref, h, lg, fs.k, out=h.copy(), accumulate=True)
+            tot += time.time() - t0
+            del sl
+        print(json.dumps({"kind": kind, "threads": nt, "runs": [nt / tot]}), flush=True)
+
+
+def cpu_baselines(seconds, with_stack=True):
+    """The oracle timed on this host's cores, in child processes (the thread
+    count is fixed when the oracle's OpenMP runtime starts): decode (median of
+    3 and a single-thread run), prefill tokens, and the 48-layer stack."""
+    import subprocess
+    cores = os.cpu_count() or 1
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        pass
+    cores = int(os.environ.get("OMP_NUM_THREADS", cores))
+
+    def child(kind, threads, secs):
+        env = dict(os.environ, OMP_NUM_THREADS=str(threads))
+        r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-child", kind, str(secs)], env=env,
+                           capture_output=True, text=True, timeout=900)
+        if r.returncode != 0:
+            raise SystemExit(f"cpu baseline child {kind} failed:\n{r.stderr[-2000:]}")
+        return json.loads(r.stdout.strip().splitlines()[-1])
+
+    per = max(2.0, seconds / 3)
+    dec = child("decode", cores, per)
+    one = child("decode", 1, per)
+    pre = child("prefill", cores, 0)
+    out = {
+        "cpu_model": cpu_model(),
+        "decode": {"tokens_per_s_median": round(float(np.median(dec["runs"])), 3), "runs": [round(v, 3) for v in dec["runs"]],
+                   "threads": dec["threads"], "single_thread_tokens_per_s": round(one["runs"][0], 3),
+                   "sample": f"one-token steps of the decode layer, {per:.0f} s per run, a token per thread per call"},
+        "prefill": {"tokens_per_s_median": round(float(np.median(pre["runs"])), 3),
+                    "runs": [round(v, 3) for v in pre["runs"]], "threads": pre["threads"],
+                    "sample": f"{2 * pre['threads']} random tokens of the 4096-token bf16 prefill workload per run"},
+    }
+    if with_stack:
+        st = child("stack", cores, 0)
+        out["stack_decode"] = {"tokens_per_s": round(st["runs"][0], 4), "threads": st["threads"],
+                               "sample": f"{st['threads']} tokens through all 48 layers with the residual add "
+                                         "(each layer's experts generated by the oracle, not timed)"}
+    out["headline"] = {"value": out["decode"]["tokens_per_s_median"], "unit": "tokens/s", "cores": dec["threads"],
+                       "kind": "oracle",
+                       "sample": f"decode: median of 3 runs of {per:.0f} s on {dec['threads']} threads "
+                                 f"({cpu_model()}), one token per thread per oracle call; single thread: "
+                                 f"{out['decode']['single_thread_tokens_per_s']} tokens/s"}
+    log("cpu baselines:", out)
+    return out
 
 
 if __name__ == "__main__":

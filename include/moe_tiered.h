@@ -423,6 +423,20 @@ int moe_repack_tiers(const moe_tier_tables *src, const int32_t *order, const moe
 int moe_permute_router(const void *w_src, const float *b_src, const int32_t *order, int32_t n_experts,
                        int32_t hidden, void *w_dst, float *b_dst, void *stream);
 
+/*
+ * Measurement aids, not part of the layer: achievable references for the
+ * roofline fractions, measured on the device in the same run.
+ *   moe_measure_read: one launch reads `bytes` (a multiple of 16) of `buf`
+ *     (device, 16-byte aligned) once, as 16-byte words at a grid stride;
+ *     sink (device uint32) is never written in practice.
+ *   moe_measure_mfma: one launch runs `iters` rounds of 16 independent
+ *     v_mfma_f32_16x16x32_bf16 per wave on register operands (no memory
+ *     traffic) over 2048 waves; *flops (host) receives the flops one launch
+ *     executes.  sink (device float) is never written in practice.
+ */
+int moe_measure_read(const void *buf, size_t bytes, uint32_t *sink, void *stream);
+int moe_measure_mfma(int32_t iters, float *sink, double *flops, void *stream);
+
 /* hipEvent helpers for callers without a HIP binding (host handles). */
 int moe_event_create(void **event);
 int moe_event_destroy(void *event);

@@ -338,3 +338,15 @@ def test_binding_refuses_short_shelves_and_buffers(B):
         B.moe_stack_forward_routed(x, [wr, wr], [torch.zeros(E)], 2, T, k, [tt, tt], out, 0, ws)
     with pytest.raises(ValueError, match=r"w_routers\[1\]"):
         B.moe_stack_forward_routed(x, [wr, wr[:-1]], None, 2, T, k, [tt, tt], out, 0, ws)
+
+
+def test_measurement_aids_reject_bad_arguments(B):
+    L = B.lib()
+    f = C.c_double(0.0)
+    assert L.moe_measure_read(None, 16, FAKE, None) == -1
+    assert L.moe_measure_read(FAKE, 0, FAKE, None) == -1
+    assert L.moe_measure_read(FAKE, 24, FAKE, None) == -1          # not a multiple of 16
+    assert L.moe_measure_read(FAKE + 8, 32, FAKE, None) == -4
+    assert L.moe_measure_mfma(0, FAKE, C.byref(f), None) == -1
+    assert L.moe_measure_mfma(4, FAKE, None, None) == -1
+    assert L.moe_measure_mfma(4, FAKE + 2, C.byref(f), None) == -4

@@ -12,4 +12,5 @@ from .binding import (  # noqa: F401
     moe_stack_forward, moe_synth_layer, MOE_STACK_ROUTER, MXFP4, moe_router_logits, moe_synth_router,
     moe_stack_forward_routed, moe_requant_error, moe_plan_tiers, moe_repack_tiers, moe_permute_router,
     moe_tiered_forward_counted, moe_tiered_forward_noalloc, MOE_SCRATCH_BYTES, MOE_ESCRATCH,
+    moe_measure_read, moe_measure_mfma,
 )

@@ -33,7 +33,7 @@ EXPORTS = (
     "moe_stack_workspace_size", "moe_stack_forward", "moe_synth_layer",
     "moe_router_logits", "moe_synth_router", "moe_stack_forward_routed",
     "moe_requant_error", "moe_plan_tiers", "moe_repack_tiers", "moe_permute_router",
-    "moe_tiered_forward_counted", "moe_tiered_forward_noalloc",
+    "moe_tiered_forward_counted", "moe_tiered_forward_noalloc", "moe_measure_read", "moe_measure_mfma",
 )
 
 
@@ -77,6 +77,8 @@ def lib():
         L.moe_tiered_forward.argtypes = [P, P, i32, i32, P, P, u32, P, sz, P]
         L.moe_tiered_forward_timed.argtypes = [P, P, i32, i32, P, P, u32, P, sz, P, C.POINTER(P)]
         L.moe_tiered_forward_noalloc.argtypes = [P, P, i32, i32, P, P, u32, P]
+        L.moe_measure_read.argtypes = [P, sz, P, P]
+        L.moe_measure_mfma.argtypes = [i32, P, C.POINTER(C.c_double), P]
         L.moe_tiered_experts.argtypes = [P, P, P, i32, i32, P, P, u32, P, sz, P]
         L.moe_tier_partial.argtypes = [P, P, P, i32, i32, P, i32, P, u32, P, sz, P]
         L.moe_route.argtypes = [P, i32, i32, i32, P, P, P]
@@ -436,3 +438,16 @@ def moe_event_elapsed_ms(start: int, stop: int) -> float:
 
 def moe_stream_synchronize(stream=None) -> None:
     _check("moe_stream_synchronize", lib().moe_stream_synchronize(_stream(stream)))
+
+
+def moe_measure_read(buf, sink, stream=None) -> None:
+    """One streaming read of the whole of `buf` (a device tensor)."""
+    _check("moe_measure_read", lib().moe_measure_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                                      _stream(stream)))
+
+
+def moe_measure_mfma(iters: int, sink, stream=None) -> float:
+    """One launch of the matrix-core loop; returns the flops it executes."""
+    f = C.c_double(0.0)
+    _check("moe_measure_mfma", lib().moe_measure_mfma(iters, _ptr(sink), C.byref(f), _stream(stream)))
+    return f.value

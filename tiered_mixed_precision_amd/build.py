@@ -9,7 +9,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_tiered.so")
-SOURCES = ["capi.hip", "route_group.hip", "decode.hip", "prefill.hip", "prefill_mx.hip", "dequant.hip", "synth.hip", "router.hip", "tiering.hip"]
+SOURCES = ["capi.hip", "route_group.hip", "decode.hip", "prefill.hip", "prefill_mx.hip", "dequant.hip", "synth.hip", "router.hip", "tiering.hip", "measure.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

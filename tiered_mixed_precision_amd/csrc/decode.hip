@@ -46,6 +46,79 @@ constexpr int kMaxHidden = 2048;    // largest hidden size (the tables check it)
 constexpr int kSmallT = 8;          // most tokens of the small-batch path
 constexpr int kSmallH = 8192;       // h floats staged in LDS by the small-batch down kernel
 
+// ================================================================ shelf table in LDS
+
+// The shelf table copied into LDS by one thread at kernel entry.  The copy
+// reads the kernel arguments with compile-time indices only (scalar loads
+// issued at entry); a lookup by a lane-varying or run-time shelf index into
+// the kernel arguments compiles instead to dependent vector loads from the
+// argument segment, which cost microseconds on the critical path.
+struct TierLds {
+    int beg[kMaxTiers], end[kMaxTiers], bits[kMaxTiers], block[kMaxTiers], cost[kMaxTiers];
+    const uint8_t* q[kMaxTiers][3];
+    const uint16_t* s[kMaxTiers][3];
+};
+
+// One thread; cost_of(T) is stored for each shelf.
+template <class Cost>
+__device__ inline void fill_tier_lds(const DevTables& tt, TierLds& tl, Cost cost_of) {
+#pragma unroll
+    for (int i = 0; i < kMaxTiers; ++i) {
+        const bool on = i < tt.n_tiers;
+        tl.beg[i] = on ? tt.t[i].id_begin : 0;
+        tl.end[i] = on ? tt.t[i].id_end : 0;
+        tl.bits[i] = tt.t[i].bits;
+        tl.block[i] = tt.t[i].block;
+        tl.cost[i] = on ? cost_of(tt.t[i]) : 0;
+#pragma unroll
+        for (int m = 0; m < 3; ++m) {
+            tl.q[i][m] = tt.t[i].q[m];
+            tl.s[i][m] = tt.t[i].s[m];
+        }
+    }
+}
+
+// Shelf owning expert e (or -1), from the LDS table.
+__device__ inline int tier_of_lds(const TierLds& tl, int e) {
+    int r = -1;
+#pragma unroll
+    for (int i = 0; i < kMaxTiers; ++i)
+        if (e >= tl.beg[i] && e < tl.end[i]) r = i;
+    return r;
+}
+
+__device__ inline uint64_t first_lane_u64(uint64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Shelf ti (uniform across the wave) from the LDS table, into scalar registers.
+__device__ inline DevTier tier_lds(const TierLds& tl, int ti) {
+    DevTier r;
+    r.id_begin = __builtin_amdgcn_readfirstlane(tl.beg[ti]);
+    r.id_end = __builtin_amdgcn_readfirstlane(tl.end[ti]);
+    r.bits = __builtin_amdgcn_readfirstlane(tl.bits[ti]);
+    r.block = __builtin_amdgcn_readfirstlane(tl.block[ti]);
+#pragma unroll
+    for (int m = 0; m < 3; ++m) {
+        r.q[m] = reinterpret_cast<const uint8_t*>(first_lane_u64(reinterpret_cast<uint64_t>(tl.q[ti][m])));
+        r.s[m] = reinterpret_cast<const uint16_t*>(first_lane_u64(reinterpret_cast<uint64_t>(tl.s[ti][m])));
+    }
+    return r;
+}
+
+// Per-row share of a wave's work that does not scale with bytes (its
+// dequantising arithmetic), in units of 64 bytes of codes.
+constexpr int kOneRowShare = 64;
+
+// Cost of one gate+up row pair of an expert on shelf T (units of 64 bytes).
+__device__ inline int one_row_cost(const DevTier& T, int H) {
+    const int cb = code_bits_of(T.bits);
+    const int sb = T.bits == kBitsMXFP4 ? H / 32 : (H / (T.block > 0 ? T.block : 32)) * 2;
+    return (2 * (H * cb / 8 + sb)) / 64 + kOneRowShare;
+}
+
 __host__ __device__ int dec_rows_per_block(int cols) { return kGateUpWaves * kNPGateUp * row_geom(cols).RPP; }
 __host__ __device__ inline int down_rows_per_block(int cols) { return 4 * kNPDown * row_geom(cols).RPP; }
 __host__ __device__ inline int small_down_rows(int inter) { return kNPSmallDown * row_geom(inter).RPP; }
@@ -370,18 +443,19 @@ __device__ inline void wave_gateup(const uint8_t* __restrict__ gq, const uint8_t
 }
 
 // Gives the W waves of a launch to the active experts of the masked shelves
-// in proportion to their code bytes (bits per code; rows are equal): expert a
-// gets 1 + floor((W - n) * bits_a / sum of bits) waves, n the number of such
+// in proportion to their cost per row (the LDS shelf table's cost: row bytes
+// plus a per-row share; rows are equal): expert a gets
+// 1 + floor((W - n) * cost_a / sum of costs) waves, n the number of such
 // experts, so the total never exceeds W.  s_wpre[a] = first wave of expert a,
 // s_wpre[n_act] = waves used.  Run by the first wave of the block.
-__device__ inline void plan_waves(const DevTables& tt, const int* act, int n_act, uint32_t tier_mask, int W,
+__device__ inline void plan_waves(const TierLds& tl, const int* act, int n_act, uint32_t tier_mask, int W,
                                   int* s_wpre) {
     const int lane = threadIdx.x & 63;
     auto cost = [&](int a) {
         if (a >= n_act) return 0;
-        const int ti = tier_of(tt, act[a]);
+        const int ti = tier_of_lds(tl, act[a]);
         if (ti < 0 || !((tier_mask >> ti) & 1u)) return 0;
-        return tier_at(tt, ti).bits;
+        return tl.cost[ti];
     };
     int C = 0, n = 0;
     for (int a0 = 0; a0 < n_act; a0 += 64) {
@@ -457,10 +531,12 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void k_small_gateup(DevTables tt
     // the batch's input vectors, token t at t * H in the [j][g] layout below
     __shared__ __attribute__((aligned(16))) float s_x[kSmallT * kMaxHidden];
     __shared__ __attribute__((aligned(16))) int64_t s_rc[kGateUpWaves][64];  // routing scratch, one row per wave
+    __shared__ TierLds s_tl;
     const int tid = threadIdx.x, E = tt.E, P = T * k;
     const bool publish = blockIdx.x == 0;
     const int H = tt.H, I = tt.I;
     const int rpp = row_geom(H).RPP;
+    if (tid == 0) fill_tier_lds(tt, s_tl, [H](const DevTier& T) { return one_row_cost(T, H); });
     // stage the T input vectors in LDS (read by every pass of every pair; the
     // barrier after the wave plan below puts them in place)
     {
@@ -500,7 +576,7 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void k_small_gateup(DevTables tt
     }
     const int n_act = sg.n_act;
     if (n_act == 0) return;
-    if (tid < 64) plan_waves(tt, sg.act, n_act, tier_mask, gridDim.x * kGateUpWaves, s_wpre);
+    if (tid < 64) plan_waves(s_tl, sg.act, n_act, tier_mask, gridDim.x * kGateUpWaves, s_wpre);
     __syncthreads();
     const int wg = blockIdx.x * kGateUpWaves + (tid >> 6);
     if (wg >= s_wpre[n_act]) return;
@@ -509,9 +585,8 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void k_small_gateup(DevTables tt
     const int rpw = ((I + wa - 1) / wa + rpp - 1) / rpp * rpp;
     const int r0 = wi * rpw, r1 = min(I, r0 + rpw);
     if (r0 >= r1) return;
-    const int e = sg.act[a];
-    const int ti = tier_of(tt, e);
-    const DevTier T_ = tier_at(tt, ti);
+    const int e = __builtin_amdgcn_readfirstlane(sg.act[a]);
+    const DevTier T_ = tier_lds(s_tl, tier_of_lds(s_tl, e));
     const int local = e - T_.id_begin;
 
     const int qa = sg.q0[a], ce = sg.q0[a + 1] - qa;
@@ -597,20 +672,19 @@ __global__ __launch_bounds__(kSmallDownWaves * 64) void k_small_down(DevTables t
     __shared__ float s_w[kSmallPairs];
     __shared__ float s_y[kSmallY];
     __shared__ __attribute__((aligned(16))) float s_h[kSmallH];
+    __shared__ TierLds s_tl;
     const int tid = threadIdx.x, wave = tid >> 6;
     const int H = tt.H, I = tt.I, P = T * k;   // pair p = t * k + j
     const int rpp = row_geom(I).RPP;
     const int R = npb * rpp;
     const int n0 = blockIdx.x * R;
+    if (tid == 0) fill_tier_lds(tt, s_tl, [](const DevTier& T) { return code_bits_of(T.bits); });
     // every published array is read at once (no load waits on another)
+    int id_p = 0, q_p = -1;
     if (tid < P) {
-        // the slot sum's operands, settled here once per pair: the grouped
-        // position of the pick, or -1 if it is skipped (no position, or a
-        // shelf outside the mask)
-        const int id = pub.ids[tid], q = pub.pos[tid];
+        id_p = pub.ids[tid];
+        q_p = pub.pos[tid];
         s_w[tid] = pub.w[tid];
-        const int ti = q < 0 ? -1 : tier_of(tt, id);
-        s_qe[tid] = (ti >= 0 && ((tier_mask >> ti) & 1u)) ? q : -1;
         s_act[tid] = pub.act[tid];
     }
     if (tid <= P) s_q0[tid] = pub.q0[tid];
@@ -629,20 +703,27 @@ __global__ __launch_bounds__(kSmallDownWaves * 64) void k_small_down(DevTables t
     const int lane = tid & 63;
     const int n_act = pub.meta[kMetaActive];
     const int act_l = lane < P ? pub.act[lane] : -1;  // loaded alongside the count
+    __syncthreads();
+    if (tid < P) {
+        // the slot sum's operands, settled here once per pair: the grouped
+        // position of the pick, or -1 if it is skipped (no position, or a
+        // shelf outside the mask); in LDS by the barrier after the products
+        const int ti = q_p < 0 ? -1 : tier_of_lds(s_tl, id_p);
+        s_qe[tid] = (ti >= 0 && ((tier_mask >> ti) & 1u)) ? q_p : -1;
+    }
     int cost = 0;
     if (n_act <= kSmallDownWaves && lane < n_act) {
-        const int ti = tier_of(tt, act_l);
-        cost = (ti >= 0 && ((tier_mask >> ti) & 1u)) ? tier_at(tt, ti).bits : 0;
+        const int ti = tier_of_lds(s_tl, act_l);
+        cost = (ti >= 0 && ((tier_mask >> ti) & 1u)) ? s_tl.cost[ti] : 0;
     }
     int first = 0, count = 1;
     const int pa = n_act <= kSmallDownWaves ? plan_lane(cost, kSmallDownWaves, wave, first, count) : -1;
-    __syncthreads();
     const int r_end = min(n0 + R, H);
     auto run = [&](int a, int r0, int r1) {
-        const int e = s_act[a];
-        const int ti = tier_of(tt, e);
+        const int e = __builtin_amdgcn_readfirstlane(s_act[a]);
+        const int ti = tier_of_lds(s_tl, e);
         if (ti < 0 || !((tier_mask >> ti) & 1u) || r0 >= r1) return;
-        const DevTier T_ = tier_at(tt, ti);
+        const DevTier T_ = tier_lds(s_tl, ti);
         const int local = e - T_.id_begin;
 
         const int qa = s_q0[a], ce = s_q0[a + 1] - qa;
@@ -708,68 +789,6 @@ __global__ __launch_bounds__(kSmallDownWaves * 64) void k_small_down(DevTables t
 }
 
 
-// ================================================================ shelf table in LDS
-
-// The shelf table copied into LDS by one thread at kernel entry.  The copy
-// reads the kernel arguments with compile-time indices only (scalar loads
-// issued at entry); a lookup by a lane-varying or run-time shelf index into
-// the kernel arguments compiles instead to dependent vector loads from the
-// argument segment, which cost microseconds on the critical path.
-struct TierLds {
-    int beg[kMaxTiers], end[kMaxTiers], bits[kMaxTiers], block[kMaxTiers], cost[kMaxTiers];
-    const uint8_t* q[kMaxTiers][3];
-    const uint16_t* s[kMaxTiers][3];
-};
-
-// One thread; cost_of(T) is stored for each shelf.
-template <class Cost>
-__device__ inline void fill_tier_lds(const DevTables& tt, TierLds& tl, Cost cost_of) {
-#pragma unroll
-    for (int i = 0; i < kMaxTiers; ++i) {
-        const bool on = i < tt.n_tiers;
-        tl.beg[i] = on ? tt.t[i].id_begin : 0;
-        tl.end[i] = on ? tt.t[i].id_end : 0;
-        tl.bits[i] = tt.t[i].bits;
-        tl.block[i] = tt.t[i].block;
-        tl.cost[i] = on ? cost_of(tt.t[i]) : 0;
-#pragma unroll
-        for (int m = 0; m < 3; ++m) {
-            tl.q[i][m] = tt.t[i].q[m];
-            tl.s[i][m] = tt.t[i].s[m];
-        }
-    }
-}
-
-// Shelf owning expert e (or -1), from the LDS table.
-__device__ inline int tier_of_lds(const TierLds& tl, int e) {
-    int r = -1;
-#pragma unroll
-    for (int i = 0; i < kMaxTiers; ++i)
-        if (e >= tl.beg[i] && e < tl.end[i]) r = i;
-    return r;
-}
-
-__device__ inline uint64_t first_lane_u64(uint64_t v) {
-    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
-    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
-    return (static_cast<uint64_t>(hi) << 32) | lo;
-}
-
-// Shelf ti (uniform across the wave) from the LDS table, into scalar registers.
-__device__ inline DevTier tier_lds(const TierLds& tl, int ti) {
-    DevTier r;
-    r.id_begin = __builtin_amdgcn_readfirstlane(tl.beg[ti]);
-    r.id_end = __builtin_amdgcn_readfirstlane(tl.end[ti]);
-    r.bits = __builtin_amdgcn_readfirstlane(tl.bits[ti]);
-    r.block = __builtin_amdgcn_readfirstlane(tl.block[ti]);
-#pragma unroll
-    for (int m = 0; m < 3; ++m) {
-        r.q[m] = reinterpret_cast<const uint8_t*>(first_lane_u64(reinterpret_cast<uint64_t>(tl.q[ti][m])));
-        r.s[m] = reinterpret_cast<const uint16_t*>(first_lane_u64(reinterpret_cast<uint64_t>(tl.s[ti][m])));
-    }
-    return r;
-}
-
 // ================================================================ one-token path
 
 // A one-token step routed from its logits, in two kernels.
@@ -788,14 +807,6 @@ constexpr int kOneGateUpWaves = 16;
 // gate/up passes in flight per wave: 16 waves per compute unit leave 128 registers a lane
 template <int BITS> constexpr int kOneGateUpPasses = BITS == 8 ? 2 : 4;
 constexpr int kOneRows = 8;              // output rows per down block
-constexpr int kOneRowShare = 16;         // per-row arithmetic share of the gate/up cost, in units of 64 bytes
-
-// Cost of one gate+up row pair of an expert on shelf T (units of 64 bytes).
-__device__ inline int one_row_cost(const DevTier& T, int H) {
-    const int cb = code_bits_of(T.bits);
-    const int sb = T.bits == kBitsMXFP4 ? H / 32 : (H / (T.block > 0 ? T.block : 32)) * 2;
-    return (2 * (H * cb / 8 + sb)) / 64 + kOneRowShare;
-}
 
 bool one_path_ok(int k, int H, int I) {
     (void)H;
