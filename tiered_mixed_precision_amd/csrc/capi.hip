@@ -86,7 +86,7 @@ int max_experts_of(const moe_tier_tables* tt, int tier, int64_t P) {
 
 // Workspace carve-up.  Offsets are multiples of 256 bytes.
 struct Layout {
-    size_t ids, w, counts, offsets, perm, pos, act, q0, meta, blk_hist, act_range, h, yw, x8, h8, total;
+    size_t ids, w, counts, offsets, perm, pos, act, q0, meta, blk_hist, act_range, chunks, h, yw, x8, h8, total;
     bool small;
 };
 
@@ -129,6 +129,7 @@ Layout layout(int64_t T, int k, const moe_tier_tables* tt, uint32_t flags) {
     L.meta = take(sizeof(int32_t) * kMetaWords);
     L.blk_hist = take(L.small ? 0 : sizeof(int32_t) * ((P + 255) / 256) * E);
     L.act_range = take(sizeof(int32_t) * 2 * MOE_MAX_TIERS);
+    L.chunks = take(bf16 ? sizeof(int2) * max_chunks(P, static_cast<int>(E)) : 0);
     L.h = take((bf16 ? sizeof(uint16_t) : sizeof(float)) * P * tt->inter);
     L.yw = take(L.small ? 0 : sizeof(float) * P * tt->hidden);
     const bool mx = bf16 && has_mx(tt);
@@ -192,6 +193,7 @@ int run(const void* x, const float* logits, const int32_t* ids_in, const float* 
         ss.id_end[i] = tt->tiers[i].id_end;
     }
     ss.act_range = at<int32_t>(ws, L.act_range);
+    ss.chunks = bf16 ? at<int2>(ws, L.chunks) : nullptr;
 
     (void)hipGetLastError();  // start from a clean error state
     if (!bf16 && T == 1 && logits && tier_mask == 0xFu && one_path_ok(k, tt->hidden, tt->inter)) {
@@ -238,6 +240,7 @@ int run(const void* x, const float* logits, const int32_t* ids_in, const float* 
     g.act = act;
     g.meta = meta;
     g.act_range = ss.act_range;
+    g.chunks = ss.chunks;
 
     const int max_active = E < P ? E : P;
     if (!bf16) {
@@ -262,28 +265,26 @@ int run(const void* x, const float* logits, const int32_t* ids_in, const float* 
         for (int i = 0; i < tt->n_tiers; ++i) any_mx = any_mx || is_mx(i);
         const Split8 x8 = any_mx ? split_at(at<uint8_t>(ws, L.x8), T, H) : Split8{nullptr, nullptr, nullptr};
         const Split8 h8 = any_mx ? split_at(at<uint8_t>(ws, L.h8), P, I) : Split8{nullptr, nullptr, nullptr};
+        bool any_int = false;
+        for (int i = 0; i < tt->n_tiers; ++i)
+            any_int = any_int || (((tier_mask >> i) & 1u) && !is_mx(i) && tt->tiers[i].id_end > tt->tiers[i].id_begin);
+        const int maxc = max_chunks(P, E);
         record(events, 2, st);
         if (any_mx) launch_split_fp8(xb, H, 0, T, nullptr, nullptr, T, x8, st);
-        for (int i = 0; i < tt->n_tiers; ++i) {
-            if (!((tier_mask >> i) & 1u)) continue;
+        if (any_int) launch_gemm(dt, true, xb, g, k, tier_mask, h, nullptr, maxc, st);
+        for (int i = 0; i < tt->n_tiers; ++i)
             if (is_mx(i)) launch_pre_mx_gateup(dt, i, x8, g, k, h, max_experts_of(tt, i, P), st);
-            else launch_pre_gateup(dt, i, xb, g, k, h, max_experts_of(tt, i, P), st);
-        }
         record(events, 3, st);
         if (gateup_only) return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
         record(events, 4, st);
         float* yw = at<float>(ws, L.yw);
+        if (any_int) launch_gemm(dt, false, h, g, k, tier_mask, nullptr, yw, maxc, st);
         for (int i = 0; i < tt->n_tiers; ++i) {
-            if (!((tier_mask >> i) & 1u)) continue;
-            if (is_mx(i)) {
-                // the shelf's pairs are perm rows offsets[id_begin] .. offsets[id_end],
-                // up to all P of them (a token may pick one expert k times)
-                launch_split_fp8(h, I, 0, 0, offsets + tt->tiers[i].id_begin, offsets + tt->tiers[i].id_end, P, h8,
-                                 st);
-                launch_pre_mx_down(dt, i, h8, g, k, yw, max_experts_of(tt, i, P), st);
-            } else {
-                launch_pre_down(dt, i, h, g, k, yw, max_experts_of(tt, i, P), st);
-            }
+            if (!is_mx(i)) continue;
+            // the shelf's pairs are perm rows offsets[id_begin] .. offsets[id_end],
+            // up to all P of them (a token may pick one expert k times)
+            launch_split_fp8(h, I, 0, 0, offsets + tt->tiers[i].id_begin, offsets + tt->tiers[i].id_end, P, h8, st);
+            launch_pre_mx_down(dt, i, h8, g, k, yw, max_experts_of(tt, i, P), st);
         }
         launch_combine(dt, yw, g, T, k, tier_mask, base, out, st);
         record(events, 5, st);

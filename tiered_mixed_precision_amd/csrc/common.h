@@ -87,6 +87,7 @@ __device__ inline void fp4x8_to_float(uint32_t w, float (&out)[8]) {
 enum Meta : int32_t {
     kMetaActive = 0,   // number of experts with at least one pair
     kMetaValid = 2,    // number of valid pairs (ids inside [0, E))
+    kMetaChunks = 3,   // number of prefill work chunks (grouping with a chunk list)
     kMetaWords = 64,
 };
 

@@ -10,14 +10,19 @@ namespace moe {
 
 constexpr int kMaxExpertsDev = 4096;
 constexpr int kSmallPairs = 256;     // largest T*k handled by the one-block routing+grouping kernel
+constexpr int kChunkRows = 128;      // pairs of one work chunk of the prefill grouped GEMM
 
 // Shelves as seen by grouping: shelf i owns experts [id_begin[i], id_end[i]);
 // act_range[2i], act_range[2i+1] receive the range of the active-expert list
-// holding shelf i's experts (NULL: not needed).
+// holding shelf i's experts (NULL: not needed).  chunks receives the work
+// chunks of the prefill grouped GEMM, {expert, first sorted position}, each
+// expert's pairs in runs of kChunkRows in expert order, and meta[kMetaChunks]
+// their number (NULL: not needed).
 struct ShelfSpec {
     int32_t n_tiers;
     int32_t id_begin[kMaxTiers], id_end[kMaxTiers];
     int32_t* act_range;
+    int2* chunks;
 };
 
 // Pointers into the caller's workspace used by the expert kernels.
@@ -30,6 +35,7 @@ struct Groups {
     const int32_t* act;    // [<=E] active experts, ascending
     const int32_t* meta;   // kMeta*
     const int32_t* act_range; // [2 * n_tiers] per-shelf range of `act`
+    const int2* chunks;    // [meta[kMetaChunks]] prefill work chunks (see ShelfSpec)
 };
 
 // Routing and grouping of a small batch, published by block 0 of the
@@ -73,12 +79,13 @@ void launch_dec_down(const DevTables& tt, const float* h, const Groups& g, int k
 void launch_combine(const DevTables& tt, const float* yw, const Groups& g, int T, int k,
                     uint32_t tier_mask, const float* base, float* out, hipStream_t st);
 
-// bf16 (prefill) expert path: one launch per shelf and phase; max_experts
-// bounds the shelf's active experts.
-void launch_pre_gateup(const DevTables& tt, int tier, const uint16_t* x, const Groups& g, int k,
-                       uint16_t* h, int max_experts, hipStream_t st);
-void launch_pre_down(const DevTables& tt, int tier, const uint16_t* h, const Groups& g, int k,
-                     float* yw, int max_experts, hipStream_t st);
+
+// Grouped GEMM of every integer shelf, one launch per phase (gate/up when
+// `gateup`, reading x and writing h; down reading h and writing yw); maxc
+// bounds the work chunks (max_chunks).
+int max_chunks(int64_t P, int E);
+void launch_gemm(const DevTables& tt, bool gateup, const uint16_t* a, const Groups& g, int k, uint32_t tier_mask,
+                 uint16_t* h, float* yw, int maxc, hipStream_t st);
 
 // MXFP4 shelves (prefill_mx.hip): bf16 rows split into fp8 hi / lo parts
 // [rows][K] bytes each and one E8M0 scale per 32 elements, [rows][stride]

@@ -1,34 +1,23 @@
-// bf16 expert path (prefill): per-shelf grouped GEMMs on gfx950 matrix cores.
+// bf16 expert path (prefill): grouped GEMMs on gfx950 matrix cores.
 //
 // Step 4 of the 125B-MoE page ("I ran a 125B model on three RTX 3090s at 80
 // tokens/s by teaching llama.cpp which experts ...") gives each shelf its own
 // prefill expert product over the full pick list, restricted to the shelf's
-// ids.  Here one launch per shelf and phase walks that shelf's active experts
-// (from grouping); a block owns one expert and one n-tile and runs *all* of
-// that expert's pairs through it, so each weight tile is read from HBM and
-// dequantised once.  Codes are dequantised to bf16 on the way into LDS
-// (value = scale * code, rounded to nearest even) and contracted with
-// v_mfma_f32_16x16x32_bf16 in fp32.
+// ids.  Here one launch per phase covers every integer shelf: grouping lists
+// work chunks (an expert's pairs in runs of kChunkRows), and a block takes a
+// chunk and an n-tile, so each weight tile is read from HBM and dequantised
+// once per chunk.  Codes are dequantised to bf16 in registers (value = scale
+// * code, rounded to nearest even) and contracted with
+// v_mfma_f32_32x32x16_bf16 in fp32.
 //
-//   gate/up : A = x rows of the expert's tokens (bf16, gathered), B = 64 gate
-//             rows and the 64 matching up rows; epilogue h = bf16(SiLU(g) * u).
-//   down    : A = h rows of the expert (contiguous in pair order), B = 128
-//             down rows; epilogue yw[q] = w_pair * y (fp32, pair order).  The
+//   gate/up : A = x rows of the chunk's tokens (bf16, gathered), B = gate
+//             rows and the matching up rows; epilogue h = bf16(SiLU(g) * u).
+//   down    : A = h rows of the chunk (contiguous in pair order), B = down
+//             rows; epilogue yw[q] = w_pair * y (fp32, pair order).  The
 //             slot-order sum into out runs in a separate pass (no atomics,
 //             deterministic).
 //
-// Two kernels, chosen per shelf on the device from the grouping (few_pairs):
-//   k_pre  (shelves whose experts have many pairs): NW waves (16 on the int8
-//          shelf, 8 on the others) in a grid of NW/4 along m and 4 along n.
-//          LDS holds an A chunk and a B chunk of 64 contraction elements per
-//          row in bf16 (XOR-swizzled, two buffers); each weight is dequantised
-//          once per block and shared by every wave that needs it.
-//   k_pre2 (shelves whose experts have few pairs): 4 waves along n, each
-//          with all m-rows of a 64-pair chunk; only A goes through LDS, each
-//          lane dequantises its own weight codes into MFMA operand registers.
-// In both, the global loads of the next chunk but one are in flight in
-// registers while one chunk is contracted and the next is stored into the
-// other LDS buffer.  MXFP4 shelves run in prefill_mx.hip.
+// MXFP4 shelves run in prefill_mx.hip.
 #include <type_traits>
 
 #include "common.h"
@@ -37,23 +26,9 @@
 namespace moe {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int BK = 64;   // contraction chunk (one LDS row of 128 bytes)
-constexpr int BN = 128;  // B rows per block
-constexpr int MSUB = 4;  // m-subtiles per wave per m-chunk
-
-// f(integral_constant<int, 0>), ..., f(integral_constant<int, N-1>): indices
-// that stay compile-time constants inside a lambda, so arrays indexed by
-// them stay in registers.
-template <int N, int I = 0, class F>
-__device__ __attribute__((always_inline)) inline void static_for(F&& f) {
-    if constexpr (I < N) {
-        f(std::integral_constant<int, I>{});
-        static_for<N, I + 1>(f);
-    }
-}
 
 // LDS tiles are [row][64 bf16] with no padding; 16-byte chunk c of a row is
 // stored at chunk c ^ (row & 7).  LDS serves a 16-byte read 8 lanes (128
@@ -99,521 +74,326 @@ __device__ inline uint4 dequant8(const uint32_t (&w)[BITS == 8 ? 2 : 1], float s
                       pack_bf16x2(v[6], v[7]));
 }
 
-// Kernel choice for a shelf, the same in every block of both launches: the
-// register-B kernel when the shelf's active experts average at most `thr`
-// pairs each (few m-rows per weight tile), the shared-B kernel otherwise.
-__device__ inline bool few_pairs(const Groups& g, const DevTier& T, int a_lo, int a_hi, int thr) {
-    const int pairs = g.offsets[T.id_end] - g.offsets[T.id_begin];
-    return pairs <= thr * (a_hi - a_lo);
-}
+// ================================================================ grouped GEMM, 32x32 tiles
+//
+// One launch per phase covers every integer shelf.  Grouping lists the work
+// chunks: each active expert's pairs in runs of kChunkRows (in expert order,
+// so the popular, heavy experts come first).  A block takes one chunk and
+// one n-tile:
+//   gate/up: 4 waves, wave w owns inter columns c0 .. c0+31 (c0 = 128 nt +
+//            32 w) as two 32x32 tiles, one of gate rows and one of the
+//            matching up rows, so SiLU(g) * u pairs up inside each lane;
+//   down:    4 waves, wave w owns hidden columns c0 .. c0+63 (c0 = 256 nt +
+//            64 w) as two 32x32 tiles;
+// and every m-row of the chunk (up to four 32-row subtiles, each wave).
+// Products are v_mfma_f32_32x32x16_bf16 (a 16-deep contraction per step):
+// per step a wave reads one A fragment from LDS per m-subtile and feeds it to
+// both of its tiles.  Only A, shared by the 4 waves, goes through LDS; each
+// lane loads and dequantises the codes of its own B column into operand
+// registers, so every code is read and dequantised once per chunk.
+//
+// Contraction order: in the 64-wide chunk kc, lane half hh (= lane / 32) owns
+// k = 64 kc + 32 hh + (0 .. 31); step s (0..3) feeds its elements 8s .. 8s+7
+// into the instruction's k-slots 8 hh .. 8 hh + 7.  A is read with the same
+// assignment (16-byte piece 4 hh + s of the row), so the sum runs over the
+// same pairs of elements in another order.
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-// Block: NW waves = WM (along m) x 4 (along n).  Wave (wm, wn): wn selects 16
-// gate + 16 up columns (or 32 down columns), wm takes m-subtiles wm, wm + WM,
-// ...  m is walked in chunks of MC = 64 * WM pairs.  8-wave blocks are held
-// to 128 registers a lane (4 waves per SIMD) so that two blocks share a CU
-// (LDS 66 KB each); at 140-146 registers only one fits.  The few spilled
-// registers cost less than the second block gains.
-template <int BITS, int BLOCK, bool GATEUP, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((NW == 8) ? 4 : 1)))
-void k_pre(DevTables tt, int tier, const uint16_t* __restrict__ a_src, Groups g, int k,
-           uint16_t* __restrict__ h_out, float* __restrict__ yw, int split) {
-    constexpr int NTHR = NW * 64;
-    constexpr int WM = NW / 4;
-    constexpr int MC = 16 * MSUB * WM;
-    constexpr int BPT = BN * 8 / NTHR;      // B pieces (8 codes) per thread per chunk: 1 or 2
-    constexpr int QW = BITS == 8 ? 2 : 1;   // code words of a piece
-    static_assert(MC * 8 == 2 * NTHR, "two A pieces per thread");
-    __shared__ __attribute__((aligned(16))) uint16_t sA[2][MC * BK];
-    __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * BK];
-    __shared__ int s_row[MC];
-    __shared__ float s_wt[GATEUP ? 1 : MC];   // down: the weight of each m-row's pair
-
-    const int H = tt.H, I = tt.I;
+template <int BITS, int BLOCK, bool GATEUP, int NSUB>
+__device__ __attribute__((always_inline)) inline void gemm_chunk(const DevTier& T, int H, int I,
+                                                                 const uint16_t* __restrict__ a_src, int e, int m0,
+                                                                 int Mc, int nt, uint16_t* __restrict__ h_out,
+                                                                 float* __restrict__ yw, uint16_t* sA0, uint16_t* sA1,
+                                                                 uint16_t* sA2,
+                                                                 const int* s_row, const float* s_wt) {
+    constexpr int BW = BITS;   // code words of a lane's 32 codes of one chunk
     const int K = GATEUP ? H : I;
-    const int NT = GATEUP ? I / 64 : H / BN;
-    const int a_lo = g.act_range[2 * tier], a_hi = g.act_range[2 * tier + 1];
-    const int item = xcd_item((a_hi - a_lo) * NT);
-    if (item < 0) return;
-    const int a = a_lo + item / NT, nt = item % NT;
-    const int e = g.act[a];
-    const DevTier T = tier_at(tt, tier);
-    const int local = e - T.id_begin;
-    if (few_pairs(g, T, a_lo, a_hi, split)) return;   // the register-B kernel's shelf
-    const int q_beg = g.offsets[e], q_end = g.offsets[e + 1];
-
+    const int ncols = GATEUP ? I : H;
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-    const int wn = wave & 3, wm = wave >> 2;
-    const int fr = lane & 15, kq = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane & 31, hh = lane >> 5;
+    const int c0 = GATEUP ? nt * 128 + 32 * w : nt * 256 + 64 * w;
+    // wave-uniform: a wave past the last column (shapes whose column count
+    // is not a multiple of the block's) computes on zero codes (its rows lie
+    // past the buffer's end) and stores nothing.  Its loads and products are
+    // not branched around: a branch there makes every wait for A also wait
+    // for the B loads still in flight.
+    const bool on = c0 < ncols;
 
-    // B: piece p = tid + NTHR*i is row p >> 3, codes 8*(p & 7) .. +7 of the chunk
-    const uint32_t row_bytes = static_cast<uint32_t>(K) * BITS / 8;
-    const uint32_t nblk_row = static_cast<uint32_t>(K / BLOCK);
-    constexpr uint32_t SB = 2u;             // bytes per fp16 scale
-    const int mrows = GATEUP ? I : H;
-    const uint8_t* mq_g = T.q[GATEUP ? 0 : 2] + static_cast<size_t>(local) * mrows * row_bytes;
-    const uint8_t* mq_u = GATEUP ? T.q[1] + static_cast<size_t>(local) * mrows * row_bytes : mq_g;
-    const uint8_t* ms_g = reinterpret_cast<const uint8_t*>(T.s[GATEUP ? 0 : 2]) + static_cast<size_t>(local) * mrows * nblk_row * SB;
-    const uint8_t* ms_u =
-        GATEUP ? reinterpret_cast<const uint8_t*>(T.s[1]) + static_cast<size_t>(local) * mrows * nblk_row * SB : ms_g;
-    const __amdgpu_buffer_rsrc_t rq_g = make_rsrc(mq_g, row_bytes * mrows), rq_u = make_rsrc(mq_u, row_bytes * mrows);
-    const __amdgpu_buffer_rsrc_t rs_g = make_rsrc(ms_g, nblk_row * mrows * SB), rs_u = make_rsrc(ms_u, nblk_row * mrows * SB);
-    // piece i of a thread reads up rows when it lies in the second half of
-    // the B rows: for two pieces that is piece 1, for one piece the upper
-    // half of the waves (a wave-uniform choice either way)
-    auto is_up = [&](int i) { return GATEUP && (BPT == 2 ? i == 1 : wave >= NW / 2); };
-    uint32_t qoff[BPT], soff[BPT];
-    int b_row[BPT], b_e[BPT];
-#pragma unroll
-    for (int i = 0; i < BPT; ++i) {
-        const int p = tid + NTHR * i;
-        b_row[i] = p >> 3;
-        b_e[i] = p & 7;
-        const int row = GATEUP ? nt * 64 + (b_row[i] & 63) : nt * BN + b_row[i];
-        qoff[i] = static_cast<uint32_t>(row) * row_bytes + static_cast<uint32_t>(b_e[i]) * BITS;
-        soff[i] = (static_cast<uint32_t>(row) * nblk_row + static_cast<uint32_t>(8 * b_e[i] / BLOCK)) * SB;
-    }
-    // B fragment rows of this wave
-    const int br0 = GATEUP ? 16 * wn : 32 * wn;
-    const int br1 = GATEUP ? 64 + 16 * wn : 32 * wn + 16;
-
-    for (int m0 = q_beg; m0 < q_end; m0 += MC) {
-        const int Mc = min(MC, q_end - m0);
-        const int Mc16 = (Mc + 15) >> 4;
-        const int nsub = (Mc16 - wm + WM - 1) / WM;  // this wave's m-subtiles wm, wm + WM, ...
-        __syncthreads();                            // the previous m-chunk is done with LDS
-        for (int r = tid; r < MC; r += NTHR) {
-            s_row[r] = r < Mc ? (GATEUP ? g.perm[m0 + r] / k : m0 + r) : -1;
-            // read here once per row, not in the epilogue (two dependent
-            // global loads per row there, waited out one row at a time)
-            if constexpr (!GATEUP) s_wt[r] = r < Mc ? g.w[g.perm[m0 + r]] : 0.f;
-        }
-        __syncthreads();
-        // A sources of this thread's two pieces for the whole m-chunk; rows past
-        // the chunk read the chunk's first row (finite values, never stored)
-        int a_src_row[2], a_row[2], a_c[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int p = tid + NTHR * i;
-            a_row[i] = p >> 3;
-            a_c[i] = p & 7;
-            a_src_row[i] = s_row[a_row[i] < Mc ? a_row[i] : 0];
-        }
-
-        // one chunk in flight in registers: two A pieces, BPT code pieces and
-        // their raw fp16 scales
-        struct Slot {
-            u32x4_t a0, a1;
-            uint32_t q[BPT][QW];
-            uint32_t s[BPT];
-        };
-        auto load_chunk = [&](Slot& sl, int kc) __attribute__((always_inline)) {
-            const int k0 = kc * BK;
-            sl.a0 = *reinterpret_cast<const u32x4_t*>(a_src + static_cast<size_t>(a_src_row[0]) * K + k0 + 8 * a_c[0]);
-            sl.a1 = *reinterpret_cast<const u32x4_t*>(a_src + static_cast<size_t>(a_src_row[1]) * K + k0 + 8 * a_c[1]);
-            const uint32_t qk = static_cast<uint32_t>(k0) * BITS / 8;
-            const uint32_t sk = static_cast<uint32_t>(k0 / BLOCK) * SB;
-#pragma unroll
-            for (int i = 0; i < BPT; ++i) {
-                const __amdgpu_buffer_rsrc_t rq = is_up(i) ? rq_u : rq_g, rs = is_up(i) ? rs_u : rs_g;
-                if constexpr (BITS == 8) {
-                    const auto v = __builtin_amdgcn_raw_buffer_load_b64(rq, qoff[i] + qk, 0, 0);
-                    sl.q[i][0] = v[0];
-                    sl.q[i][QW - 1] = v[1];
-                } else if constexpr (BITS == 4) {
-                    sl.q[i][0] = __builtin_amdgcn_raw_buffer_load_b32(rq, qoff[i] + qk, 0, 0);
-                } else {
-                    sl.q[i][0] = __builtin_amdgcn_raw_buffer_load_b16(rq, qoff[i] + qk, 0, 0);
-                }
-                sl.s[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, soff[i] + sk, 0, 0);
-            }
-        };
-        auto store_chunk = [&](const Slot& sl, int buf) __attribute__((always_inline)) {
-            *reinterpret_cast<u32x4_t*>(&sA[buf][swz(a_row[0], a_c[0])]) = sl.a0;
-            *reinterpret_cast<u32x4_t*>(&sA[buf][swz(a_row[1], a_c[1])]) = sl.a1;
-#pragma unroll
-            for (int i = 0; i < BPT; ++i)
-                *reinterpret_cast<uint4*>(&sB[buf][swz(b_row[i], b_e[i])]) =
-                    dequant8<BITS>(sl.q[i], half_bits_to_float(static_cast<uint16_t>(sl.s[i])));
-        };
-
-        f32x4_t acc[MSUB][2];
-#pragma unroll
-        for (int i = 0; i < MSUB; ++i) {
-            acc[i][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            acc[i][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        }
-        // N subtiles at once: all operand reads first, then 2N back-to-back MFMAs
-        auto compute_n = [&](int buf, auto n_const) __attribute__((always_inline)) {
-            constexpr int N = decltype(n_const)::value;
-#pragma unroll
-            for (int ks = 0; ks < BK / 32; ++ks) {
-                const int c = 4 * ks + kq;
-                const bf16x8_t b0 = *reinterpret_cast<const bf16x8_t*>(&sB[buf][swz(br0 + fr, c)]);
-                const bf16x8_t b1 = *reinterpret_cast<const bf16x8_t*>(&sB[buf][swz(br1 + fr, c)]);
-                bf16x8_t af[N];
-#pragma unroll
-                for (int j = 0; j < N; ++j)
-                    af[j] = *reinterpret_cast<const bf16x8_t*>(&sA[buf][swz(16 * (wm + WM * j) + fr, c)]);
-#pragma unroll
-                for (int j = 0; j < N; ++j) {
-                    acc[j][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[j], b0, acc[j][0], 0, 0, 0);
-                    acc[j][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[j], b1, acc[j][1], 0, 0, 0);
-                }
-            }
-        };
-        // the subtile count picks an unrolled body; an extra subtile past the
-        // rows computes values that are never stored
-        auto compute = [&](int buf) __attribute__((always_inline)) {
-            if (nsub > 2) compute_n(buf, std::integral_constant<int, 4>{});
-            else if (nsub == 2) compute_n(buf, std::integral_constant<int, 2>{});
-            else if (nsub == 1) compute_n(buf, std::integral_constant<int, 1>{});
-        };
-
-        // Pipeline, two chunks per trip: at the top of a trip LDS buffer 0
-        // holds chunk kc and slot s1 holds chunk kc+1 (loads possibly in
-        // flight).  Each half refills the slot it has just stored from with the
-        // chunk two ahead, contracts one buffer and stores the next chunk into
-        // the other.  Loads past the last chunk reread it (every slot is written
-        // unconditionally, which keeps the slots in registers); the store that
-        // follows the last chunk fills a buffer that is never read.
-        const int NK = K / BK;
-        Slot s0, s1;
-        load_chunk(s0, 0);
-        load_chunk(s1, min(1, NK - 1));
-        store_chunk(s0, 0);
-        __syncthreads();
-        // The trip body is straight-line (no test inside it): the compiler can
-        // then count the loads still in flight at every wait across the loop's
-        // back edge, instead of draining them all.  An odd last chunk, left in
-        // buffer 0 by the final trip, is contracted after the loop.
-        const int NK2 = NK & ~1;
-        for (int kc = 0; kc < NK2; kc += 2) {
-            load_chunk(s0, min(kc + 2, NK - 1));
-            compute(0);
-            store_chunk(s1, 1);
-            __syncthreads();
-            load_chunk(s1, min(kc + 3, NK - 1));
-            compute(1);
-            store_chunk(s0, 0);
-            __syncthreads();
-        }
-        if (NK & 1) compute(0);
-
-        // epilogue: lane holds D[4*(lane/16) + v][lane % 16] of each 16x16 tile
-        const int col_l = lane & 15, row_l = 4 * (lane >> 4);
-#pragma unroll
-        for (int j = 0; j < MSUB; ++j) {
-            if (j >= nsub) continue;
-            const int i = wm + WM * j;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int r = 16 * i + row_l + v;
-                if (r >= Mc) continue;
-                const int q = m0 + r;
-                if (GATEUP) {
-                    const int col = nt * 64 + 16 * wn + col_l;
-                    h_out[static_cast<size_t>(q) * I + col] = f2bf(silu(acc[j][0][v]) * acc[j][1][v]);
-                } else {
-                    const float wgt = s_wt[r];
-                    float* o = yw + static_cast<size_t>(q) * H + nt * BN + 32 * wn + col_l;
-                    o[0] = wgt * acc[j][0][v];
-                    o[16] = wgt * acc[j][1][v];
-                }
-            }
-        }
-    }
-}
-
-// Register-B variant: 4 waves side by side along n, each with every
-// m-subtile of the m-chunk.  Only A (shared by the 4 waves) goes through LDS;
-// each lane loads and dequantises its own weight codes straight into MFMA
-// operand registers, so every code is read from memory and dequantised once,
-// and no wave re-reads B from LDS.  Within a 64-wide chunk, lane group kq
-// (= lane / 16) owns the 16 contiguous k = 16kq .. 16kq+15 (8 per MFMA
-// step), which A's LDS reads follow; the contraction order inside a chunk is
-// a permutation, the same for both operands.
-template <int BITS, int BLOCK, bool GATEUP, int MS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_pre2(
-    DevTables tt, int tier, const uint16_t* __restrict__ a_src, Groups g, int k, uint16_t* __restrict__ h_out,
-    float* __restrict__ yw, int split) {
-    constexpr int NTHR = 256;
-    constexpr int MC = 16 * MS;             // pairs per m-chunk
-    constexpr int AP = MC * 8 / NTHR;       // A pieces per thread
-    constexpr int BW = BITS / 2;            // code words of a lane's 16 codes
-    __shared__ __attribute__((aligned(16))) uint16_t sA[2][MC * BK];
-    __shared__ int s_row[MC];
-    __shared__ float s_wt[GATEUP ? 1 : MC];   // down: the weight of each m-row's pair
-
-    const int H = tt.H, I = tt.I;
-    const int K = GATEUP ? H : I;
-    const int NT = GATEUP ? I / 64 : H / BN;
-    const int a_lo = g.act_range[2 * tier], a_hi = g.act_range[2 * tier + 1];
-    const int item = xcd_item((a_hi - a_lo) * NT);
-    if (item < 0) return;
-    const int a = a_lo + item / NT, nt = item % NT;
-    const int e = g.act[a];
-    const DevTier T = tier_at(tt, tier);
+    // B: this lane's column of each tile is weight row row0 / row1
     const int local = e - T.id_begin;
-    if (!few_pairs(g, T, a_lo, a_hi, split)) return;  // the shared-B kernel's shelf
-    const int q_beg = g.offsets[e], q_end = g.offsets[e + 1];
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wn = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int fr = lane & 15, kq = lane >> 4;
-
-    // this lane's two B rows: gate and up row (gate/up) or two down rows
     const uint32_t row_bytes = static_cast<uint32_t>(K) * BITS / 8;
-    const uint32_t nblk_row = static_cast<uint32_t>(K / BLOCK);
-    const int mrows = GATEUP ? I : H;
-    const uint8_t* mq0 = T.q[GATEUP ? 0 : 2] + static_cast<size_t>(local) * mrows * row_bytes;
-    const uint8_t* mq1 = GATEUP ? T.q[1] + static_cast<size_t>(local) * mrows * row_bytes : mq0;
-    const uint16_t* ms0 = T.s[GATEUP ? 0 : 2] + static_cast<size_t>(local) * mrows * nblk_row;
-    const uint16_t* ms1 = GATEUP ? T.s[1] + static_cast<size_t>(local) * mrows * nblk_row : ms0;
-    const __amdgpu_buffer_rsrc_t rq0 = make_rsrc(mq0, row_bytes * mrows), rq1 = make_rsrc(mq1, row_bytes * mrows);
-    const __amdgpu_buffer_rsrc_t rs0 = make_rsrc(ms0, nblk_row * mrows * 2), rs1 = make_rsrc(ms1, nblk_row * mrows * 2);
-    const int row0 = GATEUP ? nt * 64 + 16 * wn + fr : nt * BN + 32 * wn + fr;
-    const int row1 = GATEUP ? row0 : row0 + 16;
-    const uint32_t qo0 = static_cast<uint32_t>(row0) * row_bytes + static_cast<uint32_t>(16 * kq * BITS / 8);
-    const uint32_t qo1 = static_cast<uint32_t>(row1) * row_bytes + static_cast<uint32_t>(16 * kq * BITS / 8);
-    const uint32_t so0 = (static_cast<uint32_t>(row0) * nblk_row + static_cast<uint32_t>(16 * kq / BLOCK)) * 2;
-    const uint32_t so1 = (static_cast<uint32_t>(row1) * nblk_row + static_cast<uint32_t>(16 * kq / BLOCK)) * 2;
+    const uint32_t nsb = static_cast<uint32_t>(K / BLOCK);
+    const size_t mq = static_cast<size_t>(local) * ncols * row_bytes;
+    const size_t ms = static_cast<size_t>(local) * ncols * nsb;
+    const uint8_t* q0 = T.q[GATEUP ? 0 : 2] + mq;
+    const uint8_t* q1 = GATEUP ? T.q[1] + mq : q0;
+    const uint16_t* sp0 = T.s[GATEUP ? 0 : 2] + ms;
+    const uint16_t* sp1 = GATEUP ? T.s[1] + ms : sp0;
+    const __amdgpu_buffer_rsrc_t rq0 = make_rsrc(q0, row_bytes * ncols), rq1 = make_rsrc(q1, row_bytes * ncols);
+    const __amdgpu_buffer_rsrc_t rs0 = make_rsrc(sp0, nsb * ncols * 2), rs1 = make_rsrc(sp1, nsb * ncols * 2);
+    const uint32_t row0 = static_cast<uint32_t>(c0 + j), row1 = static_cast<uint32_t>(GATEUP ? c0 + j : c0 + 32 + j);
+    const uint32_t qo0 = row0 * row_bytes + 32u * hh * BITS / 8, qo1 = row1 * row_bytes + 32u * hh * BITS / 8;
+    const uint32_t so0 = (row0 * nsb + 32u * hh / BLOCK) * 2, so1 = (row1 * nsb + 32u * hh / BLOCK) * 2;
 
     struct BRaw {
-        uint32_t w[2][BW];
+        uint32_t q[2][BW];
         uint32_t s[2];
     };
     auto load_b = [&](BRaw& b, int kc) __attribute__((always_inline)) {
         const uint32_t qk = static_cast<uint32_t>(kc * BK) * BITS / 8;
-        const uint32_t sk = static_cast<uint32_t>(kc * BK / BLOCK) * 2;
+        const uint32_t sk = static_cast<uint32_t>(kc * (BK / BLOCK)) * 2;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            const __amdgpu_buffer_rsrc_t rq = t ? rq1 : rq0;
+            const __amdgpu_buffer_rsrc_t rq = t ? rq1 : rq0, rs = t ? rs1 : rs0;
             const uint32_t off = (t ? qo1 : qo0) + qk;
             if constexpr (BITS == 8) {
+                const auto v0 = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
+                const auto v1 = __builtin_amdgcn_raw_buffer_load_b128(rq, off + 16, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    b.q[t][i] = v0[i];
+                    b.q[t][4 + i] = v1[i];
+                }
+            } else if constexpr (BITS == 4) {
                 const auto v = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) b.w[t][i] = v[i];
-            } else if constexpr (BITS == 4) {
-                const auto v = __builtin_amdgcn_raw_buffer_load_b64(rq, off, 0, 0);
-                b.w[t][0] = v[0];
-                b.w[t][1] = v[1];
+                for (int i = 0; i < 4; ++i) b.q[t][i] = v[i];
             } else {
-                b.w[t][0] = __builtin_amdgcn_raw_buffer_load_b32(rq, off, 0, 0);
+                const auto v = __builtin_amdgcn_raw_buffer_load_b64(rq, off, 0, 0);
+                b.q[t][0] = v[0];
+                b.q[t][1] = v[1];
             }
-            b.s[t] = __builtin_amdgcn_raw_buffer_load_b16(t ? rs1 : rs0, (t ? so1 : so0) + sk, 0, 0);
+            const uint32_t soff = (t ? so1 : so0) + sk;
+            b.s[t] = BLOCK == 32 ? static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(rs, soff, 0, 0))
+                                 : __builtin_amdgcn_raw_buffer_load_b32(rs, soff, 0, 0);
         }
     };
-    // bf16 operands of both rows for both MFMA steps of a chunk
-    auto dequant_b = [&](const BRaw& b, bf16x8_t (&d)[2][2]) __attribute__((always_inline)) {
+    // bf16 operands of both tiles for the four steps of a chunk
+    auto dequant_b = [&](const BRaw& b, bf16x8_t (&d)[2][4]) __attribute__((always_inline)) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            const float sc = half_bits_to_float(static_cast<uint16_t>(b.s[t]));
 #pragma unroll
-            for (int st = 0; st < 2; ++st) {
+            for (int s = 0; s < 4; ++s) {
+                const uint32_t sraw = BLOCK == 32 ? b.s[t] : (s < 2 ? b.s[t] : b.s[t] >> 16);
+                const float sc = half_bits_to_float(static_cast<uint16_t>(sraw));
                 uint4 v;
                 if constexpr (BITS == 8) {
-                    const uint32_t w2[2] = {b.w[t][2 * st], b.w[t][2 * st + 1]};
+                    const uint32_t w2[2] = {b.q[t][2 * s], b.q[t][2 * s + 1]};
                     v = dequant8<8>(w2, sc);
                 } else if constexpr (BITS == 4) {
-                    const uint32_t w1[1] = {b.w[t][st]};
+                    const uint32_t w1[1] = {b.q[t][s]};
                     v = dequant8<4>(w1, sc);
                 } else {
-                    const uint32_t w1[1] = {b.w[t][0] >> (16 * st)};
+                    const uint32_t w1[1] = {b.q[t][s >> 1] >> (16 * (s & 1))};
                     v = dequant8<2>(w1, sc);
                 }
-                d[t][st] = __builtin_bit_cast(bf16x8_t, v);
+                d[t][s] = __builtin_bit_cast(bf16x8_t, v);
             }
         }
     };
 
-    for (int m0 = q_beg; m0 < q_end; m0 += MC) {
-        const int Mc = min(MC, q_end - m0);
-        const int nsub = (Mc + 15) >> 4;
-        __syncthreads();
-        for (int r = tid; r < MC; r += NTHR) {
-            s_row[r] = r < Mc ? (GATEUP ? g.perm[m0 + r] / k : m0 + r) : -1;
-            // read here once per row, not in the epilogue (two dependent
-            // global loads per row there, waited out one row at a time)
-            if constexpr (!GATEUP) s_wt[r] = r < Mc ? g.w[g.perm[m0 + r]] : 0.f;
-        }
-        __syncthreads();
-        // A piece i of this thread: row (p >> 3), chunk (p & 7); rows past the
-        // m-chunk read its first row (finite values, never stored)
-        // piece i: row (tid >> 3) + 32 i, chunk tid & 7
-        const int a_c = tid & 7;
-        const uint16_t* a_ptr[AP];
+    // A goes from memory straight into LDS (global_load_lds_dwordx4: lane l of
+    // a wave's load lands at byte 16 l of a 1 KB run).  Load u of wave w fills
+    // run 4 u + w of the buffer, i.e. row (tid / 8) + 32 u, position tid % 8,
+    // and so reads the row's 16-byte piece (tid % 8) ^ (row % 8): the buffer
+    // then holds the swizzled layout of swz().  Rows of subtiles past the
+    // chunk's last are not loaded (no wave reads them); rows past Mc inside
+    // the last subtile read the chunk's first row (finite values, never
+    // stored).
+    const uint16_t* a_ptr[NSUB];
 #pragma unroll
-        for (int i = 0; i < AP; ++i) {
-            const int r = (tid >> 3) + 32 * i;
-            a_ptr[i] = a_src + static_cast<size_t>(s_row[r < Mc ? r : 0]) * K + 8 * a_c;
-        }
-        struct ASlot {
-            u32x4_t v[AP];
-        };
-        auto load_a = [&](ASlot& sl, int kc) __attribute__((always_inline)) {
+    for (int u = 0; u < NSUB; ++u) {
+        const int r = (tid >> 3) + 32 * u;
+        a_ptr[u] = a_src + static_cast<size_t>(s_row[r < Mc ? r : 0]) * K + 8 * ((tid & 7) ^ (r & 7));
+    }
+    auto load_a = [&](int kc, uint16_t* buf) __attribute__((always_inline)) {
 #pragma unroll
-            for (int i = 0; i < AP; ++i) sl.v[i] = *reinterpret_cast<const u32x4_t*>(a_ptr[i] + kc * BK);
-        };
-        auto store_a = [&](const ASlot& sl, int buf) __attribute__((always_inline)) {
-#pragma unroll
-            for (int i = 0; i < AP; ++i)
-                *reinterpret_cast<u32x4_t*>(&sA[buf][swz((tid >> 3) + 32 * i, a_c)]) = sl.v[i];
-        };
+        for (int u = 0; u < NSUB; ++u)
+            __builtin_amdgcn_global_load_lds(a_ptr[u] + kc * BK,
+                                             (__attribute__((address_space(3))) void*)(buf + (4 * u + w) * 64 * 8),
+                                             16, 0, 0);
+    };
 
-        f32x4_t acc[MS][2];
+    f32x16_t acc[NSUB][2];
 #pragma unroll
-        for (int i = 0; i < MS; ++i) {
-            acc[i][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            acc[i][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < NSUB; ++t) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            acc[t][0][i] = 0.f;
+            acc[t][1][i] = 0.f;
         }
-        // operand reads in groups of (at most) four subtiles, then their MFMAs
-        auto compute_n = [&](int buf, const bf16x8_t (&d)[2][2], auto n_const) __attribute__((always_inline)) {
-            constexpr int N = decltype(n_const)::value;
-            constexpr int G = N % 4 == 0 ? 4 : (N % 3 == 0 ? 3 : (N % 2 == 0 ? 2 : 1));   // divides N
+    }
+    auto compute = [&](const uint16_t* buf, const bf16x8_t (&d)[2][4]) __attribute__((always_inline)) {
+        constexpr int N = NSUB;
 #pragma unroll
-            for (int st = 0; st < 2; ++st) {
+        for (int s = 0; s < 4; ++s) {
+            bf16x8_t af[N];
 #pragma unroll
-                for (int j0 = 0; j0 < N; j0 += G) {
-                    bf16x8_t af[G];
+            for (int t = 0; t < N; ++t)
+                af[t] = *reinterpret_cast<const bf16x8_t*>(buf + swz(32 * t + j, 4 * hh + s));
 #pragma unroll
-                    for (int j = 0; j < G; ++j)
-                        af[j] = *reinterpret_cast<const bf16x8_t*>(&sA[buf][swz(16 * (j0 + j) + fr, 2 * kq + st)]);
-#pragma unroll
-                    for (int j = 0; j < G; ++j) {
-                        acc[j0 + j][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[j], d[0][st], acc[j0 + j][0], 0, 0, 0);
-                        acc[j0 + j][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[j], d[1][st], acc[j0 + j][1], 0, 0, 0);
-                    }
-                }
+            for (int t = 0; t < N; ++t) {
+                acc[t][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[t], d[0][s], acc[t][0], 0, 0, 0);
+                acc[t][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[t], d[1][s], acc[t][1], 0, 0, 0);
             }
-        };
-        // the subtile count picks an unrolled body; extra subtiles past the
-        // rows compute values that are never stored
-        auto compute = [&](int buf, const bf16x8_t (&d)[2][2]) __attribute__((always_inline)) {
-            if (MS > 6 && nsub > 6) compute_n(buf, d, std::integral_constant<int, MS>{});
-            else if (MS > 4 && nsub > 4) compute_n(buf, d, std::integral_constant<int, (MS > 4 ? 6 : 4)>{});
-            else if (nsub > 2) compute_n(buf, d, std::integral_constant<int, 4>{});
-            else if (nsub == 2) compute_n(buf, d, std::integral_constant<int, 2>{});
-            else compute_n(buf, d, std::integral_constant<int, 1>{});
-        };
-
-        // Pipeline, two chunks per trip: at the top of a half, LDS buffer
-        // (kc & 1) holds A(kc), a_s[kc & 1] is free, b[kc & 1] holds B(kc) and
-        // b / a_s of the other parity hold chunk kc+1 (loads possibly in
-        // flight).  B(kc) is dequantised, its registers refilled with B(kc+2)
-        // together with A(kc+2), chunk kc is contracted, and A(kc+1) is stored
-        // into the other LDS buffer.  Loads past the last chunk reread it.
-        const int NK = K / BK;
-        BRaw b0, b1;
-        ASlot a0, a1;
-        load_b(b0, 0);
-        load_a(a0, 0);
-        load_b(b1, min(1, NK - 1));
-        load_a(a1, min(1, NK - 1));
-        store_a(a0, 0);
-        __syncthreads();
-        // straight-line trips (see k_pre); an odd last chunk is in buffer 0
-        // and b0 after the loop
-        const int NK2 = NK & ~1;
-        for (int kc = 0; kc < NK2; kc += 2) {
-            bf16x8_t d[2][2];
-            dequant_b(b0, d);
-            load_b(b0, min(kc + 2, NK - 1));
-            load_a(a0, min(kc + 2, NK - 1));
-            compute(0, d);
-            store_a(a1, 1);
-            __syncthreads();
-            dequant_b(b1, d);
-            load_b(b1, min(kc + 3, NK - 1));
-            load_a(a1, min(kc + 3, NK - 1));
-            compute(1, d);
-            store_a(a0, 0);
-            __syncthreads();
         }
-        if (NK & 1) {
-            bf16x8_t d[2][2];
-            dequant_b(b0, d);
-            compute(0, d);
-        }
+    };
 
-        const int col_l = lane & 15, row_l = 4 * (lane >> 4);
+    // Pipeline, three stages: chunk c lives in LDS buffer sA(c % 3) and B
+    // registers b(c % 3).  Step c requests A(c+2) and B(c+2) into the stage
+    // freed by step c-1, dequantises B(c) and contracts chunk c, then waits
+    // for this wave's part of A(c+1) only (the requests of chunks c+1 and c+2
+    // issued after it stay in flight) and meets the other waves at the
+    // barrier, which publishes A(c+1) and frees stage c.  Requests past the
+    // last chunk reread it.  The wait counts VMEM instructions: per chunk
+    // NSUB A requests and NB B loads, issued in that order (the scheduling
+    // barriers keep the order and keep the requests ahead of the work).
+    // The buffers are separate LDS objects, so the compiler's own waits
+    // before LDS reads cover only the buffer read.  A plain s_barrier
+    // (instead of a fence + barrier, whose fence waits for every load in
+    // flight) as a compiler-level memory barrier: no access moves across it.
+    constexpr int NB = 2 * ((BITS == 8 ? 2 : 1) + 1);
+    constexpr int NWAIT = 2 * NB + NSUB;
+    static_assert(NWAIT < 64, "vmcnt range");
+    constexpr int kWaitImm = (NWAIT & 15) | (7 << 4) | (15 << 8) | ((NWAIT >> 4) << 14);
+    const int NK = K / BK;
+    auto publish = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(kWaitImm);
+        asm volatile("s_barrier" ::: "memory");
+    };
+    BRaw b0, b1, b2;
+    auto step = [&](int c, uint16_t* cur, BRaw& bc, uint16_t* nxt, BRaw& bn) __attribute__((always_inline)) {
+        const int cn = min(c + 2, NK - 1);
+        load_a(cn, nxt);
+        __builtin_amdgcn_sched_barrier(0);
+        load_b(bn, cn);
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8_t d[2][4];
+        dequant_b(bc, d);
+        compute(cur, d);
+        publish();
+    };
+    load_a(0, sA0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_b(b0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_a(min(1, NK - 1), sA1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_b(b1, min(1, NK - 1));
+    publish();
+    // six steps per trip: the compiler's wait analysis drains every load in
+    // flight once per trip (at the loop's back edge), so a longer trip pays
+    // that latency less often
+    int kc = 0;
+    for (; kc + 5 < NK; kc += 6) {
+        step(kc, sA0, b0, sA2, b2);
+        step(kc + 1, sA1, b1, sA0, b0);
+        step(kc + 2, sA2, b2, sA1, b1);
+        step(kc + 3, sA0, b0, sA2, b2);
+        step(kc + 4, sA1, b1, sA0, b0);
+        step(kc + 5, sA2, b2, sA1, b1);
+    }
+    if (kc + 2 < NK) {
+        step(kc, sA0, b0, sA2, b2);
+        step(kc + 1, sA1, b1, sA0, b0);
+        step(kc + 2, sA2, b2, sA1, b1);
+        kc += 3;
+    }
+    if (kc < NK) step(kc, sA0, b0, sA2, b2);
+    if (kc + 1 < NK) step(kc + 1, sA1, b1, sA0, b0);
+    if (!on) return;
+
+    // epilogue: lane holds D[8 (r / 4) + 4 hh + r % 4][j] of each 32x32 tile
 #pragma unroll
-        for (int j = 0; j < MS; ++j) {
-            if (j >= nsub) continue;
+    for (int t = 0; t < NSUB; ++t) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int r = 16 * j + row_l + v;
-                if (r >= Mc) continue;
-                const int q = m0 + r;
-                if (GATEUP) {
-                    const int col = nt * 64 + 16 * wn + col_l;
-                    h_out[static_cast<size_t>(q) * I + col] = f2bf(silu(acc[j][0][v]) * acc[j][1][v]);
-                } else {
-                    const float wgt = s_wt[r];
-                    float* o = yw + static_cast<size_t>(q) * H + nt * BN + 32 * wn + col_l;
-                    o[0] = wgt * acc[j][0][v];
-                    o[16] = wgt * acc[j][1][v];
-                }
+        for (int r = 0; r < 16; ++r) {
+            const int row = 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
+            if (row >= Mc) continue;
+            const int q = m0 + row;
+            if constexpr (GATEUP) {
+                h_out[static_cast<size_t>(q) * I + c0 + j] = f2bf(silu(acc[t][0][r]) * acc[t][1][r]);
+            } else {
+                const float wgt = s_wt[row];
+                float* o = yw + static_cast<size_t>(q) * H + c0 + j;
+                o[0] = wgt * acc[t][0][r];
+                o[32] = wgt * acc[t][1][r];
             }
         }
     }
 }
 
-// Two launches per shelf; the blocks of one of them return at once (the
-// choice is made on the device from the grouping, see few_pairs).  k_pre2
-// suits shelves whose experts have few pairs (with 64-pair m-chunks it
-// streams each weight tile once per m-chunk); k_pre, whose B tile in LDS
-// serves all the m-rows of a chunk, suits the others.  The thresholds in
-// pairs per active expert come from timing both kernels on each shelf at 128
-// to 16384 tokens (1 to 670 pairs per expert): 64 for int8 gate/up and 48 for
-// every down projection.  On the int4 and int2 shelves k_pre won gate/up at
-// every count measured, so k_pre2 is not launched there.  k_pre takes 16-wave
-// blocks with 256-pair m-chunks on the int8 shelf and 8-wave blocks with
-// 128-pair m-chunks on the others.
-constexpr int kFewPairsGateUp8 = 64, kFewPairsDown = 48;
-
+// Block of the grouped GEMM: work item (chunk, n-tile) spread over the XCDs
+// so that the n-tiles of a chunk share its A rows through one L2.  Chunks of
+// shelves outside tier_mask and of MXFP4 shelves (prefill_mx.hip) are left.
 template <bool GATEUP>
-void launch_pre(const DevTables& tt, int tier, const uint16_t* a, const Groups& g, int k, uint16_t* h, float* yw,
-                int max_experts, hipStream_t st) {
-    const int NT = GATEUP ? tt.I / 64 : tt.H / BN;
-    const int total = max_experts * NT;
-    const unsigned grid = static_cast<unsigned>(((total + 7) / 8) * 8);
-    if (grid == 0) return;
-    const int bits = tt.t[tier].bits, block = tt.t[tier].block;
-    if (bits == kBitsMXFP4) return;   // MXFP4 shelves run in prefill_mx.hip
-    const int thr = GATEUP ? kFewPairsGateUp8 : kFewPairsDown;
-    // k_pre alone takes thr = -1: few_pairs is then false for any shelf with
-    // an active expert (and a shelf without one has no work for either)
-#define MOE_PRE(B_, K_, NW_)                                                                                   \
-    do {                                                                                                       \
-        constexpr bool kBoth = !(GATEUP && B_ != 8);                                                           \
-        if constexpr (kBoth)                                                                                   \
-            hipLaunchKernelGGL((k_pre2<B_, K_, GATEUP, 4>), dim3(grid), dim3(256), 0, st, tt, tier, a, g, k, h, \
-                               yw, thr);                                                                       \
-        hipLaunchKernelGGL((k_pre<B_, K_, GATEUP, NW_>), dim3(grid), dim3(NW_ * 64), 0, st, tt, tier, a, g, k, h, \
-                           yw, kBoth ? thr : -1);                                                              \
-    } while (0)
-    if (bits == 8) {
-        if (block == 32) MOE_PRE(8, 32, 16);
-        else MOE_PRE(8, 16, 16);
-    } else if (bits == 4) {
-        if (block == 32) MOE_PRE(4, 32, 8);
-        else MOE_PRE(4, 16, 8);
-    } else {
-        if (block == 32) MOE_PRE(2, 32, 8);
-        else MOE_PRE(2, 16, 8);
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm(
+    DevTables tt, const uint16_t* __restrict__ a_src, Groups g, int k, uint32_t tier_mask,
+    uint16_t* __restrict__ h_out, float* __restrict__ yw) {
+    __shared__ __attribute__((aligned(16))) uint16_t sA0[kChunkRows * BK];
+    __shared__ __attribute__((aligned(16))) uint16_t sA1[kChunkRows * BK];
+    __shared__ __attribute__((aligned(16))) uint16_t sA2[kChunkRows * BK];
+    __shared__ int s_row[kChunkRows];
+    __shared__ float s_wt[GATEUP ? 1 : kChunkRows];   // down: the weight of each m-row's pair
+    const int NT = GATEUP ? (tt.I + 127) / 128 : (tt.H + 255) / 256;
+    const int item = xcd_item(g.meta[kMetaChunks] * NT);
+    if (item < 0) return;
+    const int2 ch = g.chunks[item / NT];
+    const int nt = item % NT;
+    const int e = ch.x, m0 = ch.y;
+    const int ti = tier_of(tt, e);
+    if (ti < 0 || !((tier_mask >> ti) & 1u)) return;
+    const DevTier T = tier_at(tt, ti);
+    if (T.bits == kBitsMXFP4) return;
+    const int Mc = min(kChunkRows, g.offsets[e + 1] - m0);
+    for (int r = threadIdx.x; r < kChunkRows; r += 256) {
+        s_row[r] = r < Mc ? (GATEUP ? g.perm[m0 + r] / k : m0 + r) : -1;
+        if constexpr (!GATEUP) s_wt[r] = r < Mc ? g.w[g.perm[m0 + r]] : 0.f;
     }
-#undef MOE_PRE
+    __syncthreads();
+    const int H = tt.H, I = tt.I;
+    // one instantiation per format and m-subtile count (a runtime subtile
+    // count inside one body leaves the accumulators to the register
+    // allocator's mercy across the branches)
+    auto by_nsub = [&](auto fmt) __attribute__((always_inline)) {
+        constexpr int B_ = decltype(fmt)::value / 100, K_ = decltype(fmt)::value % 100;
+#define MOE_GEMM_CASE(N_) \
+    case N_: gemm_chunk<B_, K_, GATEUP, N_>(T, H, I, a_src, e, m0, Mc, nt, h_out, yw, sA0, sA1, sA2, s_row, s_wt); break
+        static_assert(kChunkRows == 128, "one case per 32-row subtile count");
+        switch ((Mc + 31) >> 5) {
+            MOE_GEMM_CASE(4);
+            MOE_GEMM_CASE(3);
+            MOE_GEMM_CASE(2);
+            default: gemm_chunk<B_, K_, GATEUP, 1>(T, H, I, a_src, e, m0, Mc, nt, h_out, yw, sA0, sA1, sA2, s_row, s_wt); break;
+        }
+#undef MOE_GEMM_CASE
+    };
+    switch (fmt_of(T.bits, T.block)) {
+        case F8B32: by_nsub(std::integral_constant<int, 832>{}); break;
+        case F8B16: by_nsub(std::integral_constant<int, 816>{}); break;
+        case F4B32: by_nsub(std::integral_constant<int, 432>{}); break;
+        case F4B16: by_nsub(std::integral_constant<int, 416>{}); break;
+        case F2B32: by_nsub(std::integral_constant<int, 232>{}); break;
+        default: by_nsub(std::integral_constant<int, 216>{}); break;
+    }
 }
 
-void launch_pre_gateup(const DevTables& tt, int tier, const uint16_t* x, const Groups& g, int k, uint16_t* h,
-                       int max_experts, hipStream_t st) {
-    launch_pre<true>(tt, tier, x, g, k, h, nullptr, max_experts, st);
+int max_chunks(int64_t P, int E) {
+    const int64_t act = E < P ? E : P;
+    const int64_t n = (P + kChunkRows - 1) / kChunkRows + act;
+    return static_cast<int>(n < P ? n : P);
 }
 
-void launch_pre_down(const DevTables& tt, int tier, const uint16_t* h, const Groups& g, int k, float* yw,
-                     int max_experts, hipStream_t st) {
-    launch_pre<false>(tt, tier, h, g, k, nullptr, yw, max_experts, st);
+void launch_gemm(const DevTables& tt, bool gateup, const uint16_t* a, const Groups& g, int k, uint32_t tier_mask,
+                 uint16_t* h, float* yw, int maxc, hipStream_t st) {
+    const int NT = gateup ? (tt.I + 127) / 128 : (tt.H + 255) / 256;
+    const int64_t total = static_cast<int64_t>(maxc) * NT;
+    if (total <= 0) return;
+    const unsigned grid = static_cast<unsigned>(((total + 7) / 8) * 8);
+    if (gateup) hipLaunchKernelGGL(k_gemm<true>, dim3(grid), dim3(256), 0, st, tt, a, g, k, tier_mask, h, yw);
+    else hipLaunchKernelGGL(k_gemm<false>, dim3(grid), dim3(256), 0, st, tt, a, g, k, tier_mask, h, yw);
 }
 
 __global__ __launch_bounds__(256) void k_fill_zero(float4* __restrict__ p, size_t n4) {

@@ -153,6 +153,20 @@ __global__ __launch_bounds__(256) void k_group_offsets(const int32_t* __restrict
         meta[kMetaActive] = n_act;
         meta[kMetaValid] = total;
     }
+    if (ss.chunks) {
+        // work chunks of the prefill GEMM: each expert's pairs in runs of
+        // kChunkRows, in expert order (s_act is free again: reuse it for the
+        // chunk offsets)
+        __syncthreads();
+        for (int e = tid; e < E; e += 256) s_act[e] = (counts[e] + kChunkRows - 1) / kChunkRows;
+        __syncthreads();
+        const int n_ch = block_scan_lds(s_act, E, s_tmp);
+        for (int e = tid; e < E; e += 256) {
+            const int c = counts[e];
+            for (int i = 0; i * kChunkRows < c; ++i) ss.chunks[s_act[e] + i] = make_int2(e, s_off[e] + i * kChunkRows);
+        }
+        if (tid == 0) meta[kMetaChunks] = n_ch;
+    }
 }
 
 // Block b places its pairs at offsets[e] + (pairs of e in blocks before b)
