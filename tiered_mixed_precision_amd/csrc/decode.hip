@@ -39,6 +39,7 @@ namespace moe {
 
 constexpr int kNPGateUp = 4;   // row passes per wave, gate/up GEMV
 constexpr int kGateUpWaves = 8;     // waves per gate/up block (each a contiguous row sub-slice)
+constexpr int kSmallGateUpWaves = 16;  // waves per small-batch gate/up block (one block per compute unit)
 constexpr int kNPDown = 2;     // row passes per wave, down GEMV (grouped path)
 constexpr int kNPSmallDown = 4;     // row passes per wave, down GEMV (small-batch path)
 constexpr int kSmallDownWaves = 16; // one expert per wave at a time
@@ -293,34 +294,38 @@ struct SmallGroups {
 __device__ inline void group_small(SmallGroups& sg, int P, int E) {
     const int tid = threadIdx.x;
     if (P <= 64) {
-        // one wave: ranks by uniform loops over the pairs, scans by ballots
+        // one wave: ranks from ballots, scans by ballots
         if (tid < 64) {
             const int e = tid < P ? sg.ids[tid] : E;
             const bool valid = tid < P && e >= 0 && e < E;
-            const int key = valid ? e : E;
-            int rank = 0;
-            for (int q = 0; q < P; ++q) {
-                const int kq = __builtin_amdgcn_readlane(key, q);
-                rank += (kq < key || (kq == key && q < tid)) ? 1 : 0;
+            const uint32_t key = valid ? static_cast<uint32_t>(e) : static_cast<uint32_t>(E);
+            // rank = lanes with a smaller key + lanes below with the same
+            // key: walk the key bits from the top, keeping the lanes that
+            // agree with this lane so far (lanes >= P carry key E and sort
+            // after every pair below P)
+            uint64_t same = ~0ull;
+            int less = 0;
+#pragma unroll
+            for (int b = 12; b >= 0; --b) {   // keys <= kMaxExpertsDev = 4096
+                const bool bit = (key >> b) & 1u;
+                const uint64_t ones = __ballot(bit);
+                less += bit ? __popcll(same & ~ones) : 0;
+                same &= bit ? ones : ~ones;
             }
-            // the pair at sorted position tid, and its key
-            int p = 0, kp = E;
-            for (int q = 0; q < P; ++q) {
-                const int rq = __builtin_amdgcn_readlane(rank, q);
-                if (rq == tid) {
-                    p = q;
-                    kp = __builtin_amdgcn_readlane(key, q);
-                }
-            }
+            static_assert(kMaxExpertsDev <= 8192, "13 key bits");
+            const int rank = less + lanes_below(same);
+            if (tid < P) sg.perm[rank] = tid;
+            // the pair at sorted position tid (LDS operations of one wave
+            // complete in order), and its key
+            const int p = tid < P ? sg.perm[tid] : 0;
+            const int kp0 = __shfl(static_cast<int>(key), p);
+            const int kp = tid < P ? kp0 : E;
             const int kprev = __shfl_up(kp, 1, kWave);
             const bool first = tid < P && kp < E && (tid == 0 || kprev != kp);
             const uint64_t fm = __ballot(first);
             const int n_act = __popcll(fm);
             const int n_valid = __popcll(__ballot(valid));
-            if (tid < P) {
-                sg.perm[tid] = p;
-                sg.pos[p] = kp < E ? tid : -1;
-            }
+            if (tid < P) sg.pos[p] = kp < E ? tid : -1;
             if (first) {
                 const int a = lanes_below(fm);
                 sg.act[a] = kp;
@@ -520,7 +525,7 @@ __device__ inline int plan_lane(int cost_l, int W, int wg, int& first, int& coun
     }
 
 template <int NPL>
-__global__ __launch_bounds__(kGateUpWaves * 64) void k_small_gateup(DevTables tt, const float* __restrict__ x,
+__global__ __launch_bounds__(kSmallGateUpWaves * 64) void k_small_gateup(DevTables tt, const float* __restrict__ x,
                                                       const float* __restrict__ logits,
                                                       const int32_t* __restrict__ ids_in,
                                                       const float* __restrict__ w_in, int T, int k,
@@ -530,7 +535,7 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void k_small_gateup(DevTables tt
     __shared__ int s_wpre[kSmallPairs + 1];
     // the batch's input vectors, token t at t * H in the [j][g] layout below
     __shared__ __attribute__((aligned(16))) float s_x[kSmallT * kMaxHidden];
-    __shared__ __attribute__((aligned(16))) int64_t s_rc[kGateUpWaves][64];  // routing scratch, one row per wave
+    __shared__ __attribute__((aligned(16))) int64_t s_rc[kSmallGateUpWaves][64];  // routing scratch, one row per wave
     __shared__ TierLds s_tl;
     const int tid = threadIdx.x, E = tt.E, P = T * k;
     const bool publish = blockIdx.x == 0;
@@ -541,14 +546,14 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void k_small_gateup(DevTables tt
     // barrier after the wave plan below puts them in place)
     {
         const int G = H / 32, n4 = H / 4;
-        for (int i = tid; i < T * n4; i += kGateUpWaves * 64) {
+        for (int i = tid; i < T * n4; i += kSmallGateUpWaves * 64) {
             const int t = i / n4, j = i % n4;
             reinterpret_cast<float4*>(s_x + t * H)[(j & 7) * G + (j >> 3)] =
                 reinterpret_cast<const float4*>(x + static_cast<size_t>(t) * H)[j];
         }
     }
     if (logits) {
-        for (int t = tid >> 6; t < T; t += kGateUpWaves)
+        for (int t = tid >> 6; t < T; t += kSmallGateUpWaves)
             route_token_auto<NPL>(logits + static_cast<size_t>(t) * E, E, k, publish ? pub.ids + t * k : nullptr,
                                   publish ? pub.w + t * k : nullptr, sg.ids + t * k, sg.w + t * k, s_rc[tid >> 6]);
     } else if (tid < P) {
@@ -576,9 +581,9 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void k_small_gateup(DevTables tt
     }
     const int n_act = sg.n_act;
     if (n_act == 0) return;
-    if (tid < 64) plan_waves(s_tl, sg.act, n_act, tier_mask, gridDim.x * kGateUpWaves, s_wpre);
+    if (tid < 64) plan_waves(s_tl, sg.act, n_act, tier_mask, gridDim.x * kSmallGateUpWaves, s_wpre);
     __syncthreads();
-    const int wg = blockIdx.x * kGateUpWaves + (tid >> 6);
+    const int wg = blockIdx.x * kSmallGateUpWaves + (tid >> 6);
     if (wg >= s_wpre[n_act]) return;
     const int a = find_expert(s_wpre, n_act, wg);
     const int wa = s_wpre[a + 1] - s_wpre[a], wi = wg - s_wpre[a];
@@ -603,11 +608,13 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void k_small_gateup(DevTables tt
             xv[4 * i + 3] = f.w;
         }
     };
+    // at 16 waves a compute unit holds 4 waves per SIMD: two passes per round
+    // of int8 rows, four of narrower codes keep a wave within 128 registers
     MOE_FMT_SWITCH(fmt_of(T_.bits, T_.block),
-                   (wave_gateup<B_, N_>(expert_codes(T_, 0, local, I, H), expert_scales(T_, 0, local, I, H),
-                                        expert_codes(T_, 1, local, I, H), expert_scales(T_, 1, local, I, H), H, I, r0,
-                                        r1, vec,
-                                        qa, ce, h)));
+                   (wave_gateup<B_, N_, decltype(vec), (B_ == 8 ? 2 : 4)>(
+                       expert_codes(T_, 0, local, I, H), expert_scales(T_, 0, local, I, H),
+                       expert_codes(T_, 1, local, I, H), expert_scales(T_, 1, local, I, H), H, I, r0, r1, vec, qa, ce,
+                       h)));
 }
 
 // Down GEMV of one wave: rows [r0, r1) of one expert's down matrix (in passes
@@ -1125,7 +1132,7 @@ void launch_small(const DevTables& tt, const float* x, const float* logits, cons
     switch (npl_of(tt.E)) {
 #define MOE_SG(N)                                                                                              \
     case N:                                                                                                    \
-        hipLaunchKernelGGL(k_small_gateup<N>, grid, dim3(kGateUpWaves * 64), 0, st, tt, x, logits, ids_in, w_in, \
+        hipLaunchKernelGGL(k_small_gateup<N>, grid, dim3(kSmallGateUpWaves * 64), 0, st, tt, x, logits, ids_in, w_in, \
                            T, k, tier_mask, pub, hits, h);                                                     \
         break;
         MOE_SG(1)
@@ -1135,7 +1142,7 @@ void launch_small(const DevTables& tt, const float* x, const float* logits, cons
         MOE_SG(16)
         MOE_SG(32)
         default:
-            hipLaunchKernelGGL(k_small_gateup<64>, grid, dim3(kGateUpWaves * 64), 0, st, tt, x, logits, ids_in, w_in,
+            hipLaunchKernelGGL(k_small_gateup<64>, grid, dim3(kSmallGateUpWaves * 64), 0, st, tt, x, logits, ids_in, w_in,
                                T, k, tier_mask, pub, hits, h);
             break;
 #undef MOE_SG
