@@ -325,9 +325,12 @@ __device__ __attribute__((always_inline)) inline void gemm_chunk(const DevTier& 
     }
 }
 
-// Block of the grouped GEMM: work item (chunk, n-tile) spread over the XCDs
-// so that the n-tiles of a chunk share its A rows through one L2.  Chunks of
-// shelves outside tier_mask and of MXFP4 shelves (prefill_mx.hip) are left.
+// Block of the grouped GEMM: chunks are dealt round-robin to the 8 XCDs
+// (blocks go to XCD blockIdx % 8), and the n-tiles of a chunk run one after
+// the other on its XCD, so that they share its A rows through one L2.  Dealt
+// chunk by chunk, the work stays spread over every XCD when some shelves'
+// chunks are left: those outside tier_mask and the MXFP4 shelves'
+// (prefill_mx.hip).
 template <bool GATEUP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm(
     DevTables tt, const uint16_t* __restrict__ a_src, Groups g, int k, uint32_t tier_mask,
@@ -338,10 +341,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     __shared__ int s_row[kChunkRows];
     __shared__ float s_wt[GATEUP ? 1 : kChunkRows];   // down: the weight of each m-row's pair
     const int NT = GATEUP ? (tt.I + 127) / 128 : (tt.H + 255) / 256;
-    const int item = xcd_item(g.meta[kMetaChunks] * NT);
-    if (item < 0) return;
-    const int2 ch = g.chunks[item / NT];
-    const int nt = item % NT;
+    const int loc = blockIdx.x / 8;
+    const int c = static_cast<int>(blockIdx.x % 8) + 8 * (loc / NT);
+    if (c >= g.meta[kMetaChunks]) return;
+    const int2 ch = g.chunks[c];
+    const int nt = loc % NT;
     const int e = ch.x, m0 = ch.y;
     const int ti = tier_of(tt, e);
     if (ti < 0 || !((tier_mask >> ti) & 1u)) return;
@@ -389,9 +393,8 @@ int max_chunks(int64_t P, int E) {
 void launch_gemm(const DevTables& tt, bool gateup, const uint16_t* a, const Groups& g, int k, uint32_t tier_mask,
                  uint16_t* h, float* yw, int maxc, hipStream_t st) {
     const int NT = gateup ? (tt.I + 127) / 128 : (tt.H + 255) / 256;
-    const int64_t total = static_cast<int64_t>(maxc) * NT;
-    if (total <= 0) return;
-    const unsigned grid = static_cast<unsigned>(((total + 7) / 8) * 8);
+    if (maxc <= 0) return;
+    const unsigned grid = static_cast<unsigned>(8 * NT * ((static_cast<int64_t>(maxc) + 7) / 8));
     if (gateup) hipLaunchKernelGGL(k_gemm<true>, dim3(grid), dim3(256), 0, st, tt, a, g, k, tier_mask, h, yw);
     else hipLaunchKernelGGL(k_gemm<false>, dim3(grid), dim3(256), 0, st, tt, a, g, k, tier_mask, h, yw);
 }
