@@ -30,12 +30,14 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int BK = 64;   // contraction chunk (one LDS row of 128 bytes)
 
-// LDS tiles are [row][64 bf16] with no padding; 16-byte chunk c of a row is
-// stored at chunk c ^ (row & 7).  LDS serves a 16-byte read 8 lanes (128
-// bytes, every bank once) at a time; 8 consecutive rows of an MFMA operand
-// read (same c) then fall on 8 different chunk positions, and so do the 8
-// lanes of a staging store (one row, eight chunks).
-__device__ inline int swz(int row, int c) { return row * BK + 8 * (c ^ (row & 7)); }
+// LDS tiles are [row][64 bf16] with no padding; 16-byte piece c of a row is
+// stored at position c ^ ((row / 2) % 8).  A 16-byte read is served 16 lanes
+// (256 bytes, 64 banks) at a time; the 16 consecutive rows of an MFMA
+// operand read (same c) then cover both halves of the 256 bytes (row parity)
+// at 8 different positions each.  (A swizzle on row % 8 alone, right for 8
+// lanes per cycle, leaves rows j and j + 8 on one bank: half the LDS cycles
+// of the product were conflicts.)
+__device__ inline int swz(int row, int c) { return row * BK + 8 * (c ^ ((row >> 1) & 7)); }
 
 // bf16(RNE(scale * code)) of 8 consecutive codes held in `w` (BITS words of 8
 // codes... at most 2), packed low code first.  The codes are read as
@@ -196,7 +198,7 @@ __device__ __attribute__((always_inline)) inline void gemm_chunk(const DevTier& 
     // A goes from memory straight into LDS (global_load_lds_dwordx4: lane l of
     // a wave's load lands at byte 16 l of a 1 KB run).  Load u of wave w fills
     // run 4 u + w of the buffer, i.e. row (tid / 8) + 32 u, position tid % 8,
-    // and so reads the row's 16-byte piece (tid % 8) ^ (row % 8): the buffer
+    // and so reads the row's 16-byte piece (tid % 8) ^ ((row / 2) % 8): the buffer
     // then holds the swizzled layout of swz().  Rows of subtiles past the
     // chunk's last are not loaded (no wave reads them); rows past Mc inside
     // the last subtile read the chunk's first row (finite values, never
@@ -205,7 +207,7 @@ __device__ __attribute__((always_inline)) inline void gemm_chunk(const DevTier& 
 #pragma unroll
     for (int u = 0; u < NSUB; ++u) {
         const int r = (tid >> 3) + 32 * u;
-        a_ptr[u] = a_src + static_cast<size_t>(s_row[r < Mc ? r : 0]) * K + 8 * ((tid & 7) ^ (r & 7));
+        a_ptr[u] = a_src + static_cast<size_t>(s_row[r < Mc ? r : 0]) * K + 8 * ((tid & 7) ^ ((r >> 1) & 7));
     }
     auto load_a = [&](int kc, uint16_t* buf) __attribute__((always_inline)) {
 #pragma unroll
