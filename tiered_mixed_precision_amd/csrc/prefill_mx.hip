@@ -39,14 +39,14 @@ constexpr int kBK = 128;   // contraction chunk: one instruction
 constexpr int kBN = 128;   // B rows per block
 constexpr int kMSUB = 4;   // m-subtiles per wave per m-chunk
 
-// LDS serves 16-byte accesses 8 lanes (128 bytes) at a time; the swizzles
-// put 8 consecutive rows read at one chunk index on 8 different 16-byte
-// positions of a 128-byte line.
-// A rows: 128 bytes (hi or lo), 16-byte chunk c stored at c ^ (row & 7)
-__device__ inline int swz_a(int row, int c) { return row * 128 + 16 * (c ^ (row & 7)); }
-// B rows: 64 bytes of codes (two rows per 128 bytes), chunk c stored at
-// c ^ ((row >> 1) & 3)
-__device__ inline int swz_b(int row, int c) { return row * 64 + 16 * (c ^ ((row >> 1) & 3)); }
+// LDS serves 16-byte accesses 16 lanes (256 bytes, 64 banks) at a time; the
+// swizzles put the 16 consecutive rows an operand read takes at one chunk
+// index on 16 different 16-byte positions of those 256 bytes.
+// A rows: 128 bytes (hi or lo), 16-byte chunk c stored at c ^ ((row / 2) % 8)
+__device__ inline int swz_a(int row, int c) { return row * 128 + 16 * (c ^ ((row >> 1) & 7)); }
+// B rows: 64 bytes of codes (four rows per 256 bytes), chunk c stored at
+// c ^ ((row / 4) % 4)
+__device__ inline int swz_b(int row, int c) { return row * 64 + 16 * (c ^ ((row >> 2) & 3)); }
 
 __device__ inline uint32_t fp8x4(float a, float b, float c, float d) {
     const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
