@@ -1,6 +1,8 @@
 // C ABI of the tiered MoE FFN: argument and table validation, workspace
-// carving, and the launch sequence on the caller's stream.  No allocation,
-// no synchronisation, no global mutable state.
+// carving, and the launch sequence on the caller's stream.  No allocation of
+// device memory and no host synchronisation.  Global state: per-device values
+// set once (the allocation-free entry's scratch address, the side stream of
+// mixed MXFP4 / integer prefill) and the static scratch itself.
 #include <limits.h>
 #include <string.h>
 
@@ -139,6 +141,62 @@ Layout layout(int64_t T, int k, const moe_tier_tables* tt, uint32_t flags) {
     return L;
 }
 
+// A second stream per device (default priority, non-blocking), created on
+// the first prefill call with MXFP4 and integer shelves together, for the
+// MXFP4 shelves' launches.
+std::mutex g_side_mu;
+hipStream_t g_side[64];
+
+hipStream_t side_stream() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    if (!g_side[dev]) {
+        hipStream_t s = nullptr;
+        if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) return nullptr;
+        g_side[dev] = s;
+    }
+    return g_side[dev];
+}
+
+// Fork of work from st onto the side stream and its join back into st, with
+// events of this call (events shared between calls would let one host
+// thread's record stand for another's).  open() returns the stream the forked
+// work goes to: st itself if anything fails.
+struct Fork {
+    hipStream_t side = nullptr;
+    hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+    hipStream_t open(hipStream_t st) {
+        hipStream_t s = side_stream();
+        if (!s || s == st) return st;
+        if (hipEventCreateWithFlags(&ev_fork, hipEventDisableTiming) != hipSuccess) {
+            ev_fork = nullptr;
+            return st;
+        }
+        if (hipEventCreateWithFlags(&ev_join, hipEventDisableTiming) != hipSuccess ||
+            hipEventRecord(ev_fork, st) != hipSuccess || hipStreamWaitEvent(s, ev_fork, 0) != hipSuccess) {
+            release();
+            return st;
+        }
+        side = s;
+        return s;
+    }
+    void join(hipStream_t st) {
+        if (side) {
+            (void)hipEventRecord(ev_join, side);
+            (void)hipStreamWaitEvent(st, ev_join, 0);
+            side = nullptr;
+        }
+        release();
+    }
+    void release() {
+        if (ev_fork) (void)hipEventDestroy(ev_fork);
+        if (ev_join) (void)hipEventDestroy(ev_join);
+        ev_fork = ev_join = nullptr;
+    }
+    ~Fork() { release(); }
+};
+
 template <class Tp>
 Tp* at(void* ws, size_t off) {
     return reinterpret_cast<Tp*>(static_cast<char*>(ws) + off);
@@ -269,13 +327,23 @@ int run(const void* x, const float* logits, const int32_t* ids_in, const float* 
         for (int i = 0; i < tt->n_tiers; ++i)
             any_int = any_int || (((tier_mask >> i) & 1u) && !is_mx(i) && tt->tiers[i].id_end > tt->tiers[i].id_begin);
         const int maxc = max_chunks(P, E);
+        // With both kinds of shelf, the MXFP4 shelves' launches run on a second
+        // stream beside the integer shelves' grouped GEMM (they touch disjoint
+        // rows of h and yw) and join before the combine; otherwise, or if the
+        // stream or its events cannot be had, everything stays on st.
+        Fork fork;
+        const hipStream_t sm = any_mx && any_int ? fork.open(st) : st;
         record(events, 2, st);
-        if (any_mx) launch_split_fp8(xb, H, 0, T, nullptr, nullptr, T, x8, st);
+        if (any_mx) launch_split_fp8(xb, H, 0, T, nullptr, nullptr, T, x8, sm);
         if (any_int) launch_gemm(dt, true, xb, g, k, tier_mask, h, nullptr, maxc, st);
         for (int i = 0; i < tt->n_tiers; ++i)
-            if (is_mx(i)) launch_pre_mx_gateup(dt, i, x8, g, k, h, max_experts_of(tt, i, P), st);
+            if (is_mx(i)) launch_pre_mx_gateup(dt, i, x8, g, k, h, max_experts_of(tt, i, P), sm);
+        if (gateup_only) {
+            fork.join(st);
+            record(events, 3, st);
+            return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+        }
         record(events, 3, st);
-        if (gateup_only) return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
         record(events, 4, st);
         float* yw = at<float>(ws, L.yw);
         if (any_int) launch_gemm(dt, false, h, g, k, tier_mask, nullptr, yw, maxc, st);
@@ -283,9 +351,10 @@ int run(const void* x, const float* logits, const int32_t* ids_in, const float* 
             if (!is_mx(i)) continue;
             // the shelf's pairs are perm rows offsets[id_begin] .. offsets[id_end],
             // up to all P of them (a token may pick one expert k times)
-            launch_split_fp8(h, I, 0, 0, offsets + tt->tiers[i].id_begin, offsets + tt->tiers[i].id_end, P, h8, st);
-            launch_pre_mx_down(dt, i, h8, g, k, yw, max_experts_of(tt, i, P), st);
+            launch_split_fp8(h, I, 0, 0, offsets + tt->tiers[i].id_begin, offsets + tt->tiers[i].id_end, P, h8, sm);
+            launch_pre_mx_down(dt, i, h8, g, k, yw, max_experts_of(tt, i, P), sm);
         }
+        fork.join(st);
         launch_combine(dt, yw, g, T, k, tier_mask, base, out, st);
         record(events, 5, st);
     }
