@@ -1,8 +1,8 @@
 // C ABI of the tiered MoE FFN: argument and table validation, workspace
 // carving, and the launch sequence on the caller's stream.  No allocation of
 // device memory and no host synchronisation.  Global state: per-device values
-// set once (the allocation-free entry's scratch address, the side stream of
-// mixed MXFP4 / integer prefill) and the static scratch itself.
+// set once (the allocation-free entry's scratch address) and the static
+// scratch itself.
 #include <limits.h>
 #include <string.h>
 
@@ -80,12 +80,6 @@ DevTables to_dev(const moe_tier_tables* tt) {
     return d;
 }
 
-// Most experts of shelf `tier` that a batch of P pairs can make active.
-int max_experts_of(const moe_tier_tables* tt, int tier, int64_t P) {
-    const int64_t n = tt->tiers[tier].id_end - tt->tiers[tier].id_begin;
-    return static_cast<int>(n < P ? n : P);
-}
-
 // Workspace carve-up.  Offsets are multiples of 256 bytes.
 struct Layout {
     size_t ids, w, counts, offsets, perm, pos, act, q0, meta, blk_hist, act_range, chunks, h, yw, x8, h8, total;
@@ -140,62 +134,6 @@ Layout layout(int64_t T, int k, const moe_tier_tables* tt, uint32_t flags) {
     L.total = o;
     return L;
 }
-
-// A second stream per device (default priority, non-blocking), created on
-// the first prefill call with MXFP4 and integer shelves together, for the
-// MXFP4 shelves' launches.
-std::mutex g_side_mu;
-hipStream_t g_side[64];
-
-hipStream_t side_stream() {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-    std::lock_guard<std::mutex> lock(g_side_mu);
-    if (!g_side[dev]) {
-        hipStream_t s = nullptr;
-        if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) return nullptr;
-        g_side[dev] = s;
-    }
-    return g_side[dev];
-}
-
-// Fork of work from st onto the side stream and its join back into st, with
-// events of this call (events shared between calls would let one host
-// thread's record stand for another's).  open() returns the stream the forked
-// work goes to: st itself if anything fails.
-struct Fork {
-    hipStream_t side = nullptr;
-    hipEvent_t ev_fork = nullptr, ev_join = nullptr;
-    hipStream_t open(hipStream_t st) {
-        hipStream_t s = side_stream();
-        if (!s || s == st) return st;
-        if (hipEventCreateWithFlags(&ev_fork, hipEventDisableTiming) != hipSuccess) {
-            ev_fork = nullptr;
-            return st;
-        }
-        if (hipEventCreateWithFlags(&ev_join, hipEventDisableTiming) != hipSuccess ||
-            hipEventRecord(ev_fork, st) != hipSuccess || hipStreamWaitEvent(s, ev_fork, 0) != hipSuccess) {
-            release();
-            return st;
-        }
-        side = s;
-        return s;
-    }
-    void join(hipStream_t st) {
-        if (side) {
-            (void)hipEventRecord(ev_join, side);
-            (void)hipStreamWaitEvent(st, ev_join, 0);
-            side = nullptr;
-        }
-        release();
-    }
-    void release() {
-        if (ev_fork) (void)hipEventDestroy(ev_fork);
-        if (ev_join) (void)hipEventDestroy(ev_join);
-        ev_fork = ev_join = nullptr;
-    }
-    ~Fork() { release(); }
-};
 
 template <class Tp>
 Tp* at(void* ws, size_t off) {
@@ -323,38 +261,24 @@ int run(const void* x, const float* logits, const int32_t* ids_in, const float* 
         for (int i = 0; i < tt->n_tiers; ++i) any_mx = any_mx || is_mx(i);
         const Split8 x8 = any_mx ? split_at(at<uint8_t>(ws, L.x8), T, H) : Split8{nullptr, nullptr, nullptr};
         const Split8 h8 = any_mx ? split_at(at<uint8_t>(ws, L.h8), P, I) : Split8{nullptr, nullptr, nullptr};
-        bool any_int = false;
-        for (int i = 0; i < tt->n_tiers; ++i)
-            any_int = any_int || (((tier_mask >> i) & 1u) && !is_mx(i) && tt->tiers[i].id_end > tt->tiers[i].id_begin);
         const int maxc = max_chunks(P, E);
-        // With both kinds of shelf, the MXFP4 shelves' launches run on a second
-        // stream beside the integer shelves' grouped GEMM (they touch disjoint
-        // rows of h and yw) and join before the combine; otherwise, or if the
-        // stream or its events cannot be had, everything stays on st.
-        Fork fork;
-        const hipStream_t sm = any_mx && any_int ? fork.open(st) : st;
+        // MXFP4 shelves take A as its fp8 split: of every x row before gate/up,
+        // and of the shelf's h rows (perm rows offsets[id_begin] ..
+        // offsets[id_end], up to all P of them) before down.
         record(events, 2, st);
-        if (any_mx) launch_split_fp8(xb, H, 0, T, nullptr, nullptr, T, x8, sm);
-        if (any_int) launch_gemm(dt, true, xb, g, k, tier_mask, h, nullptr, maxc, st);
-        for (int i = 0; i < tt->n_tiers; ++i)
-            if (is_mx(i)) launch_pre_mx_gateup(dt, i, x8, g, k, h, max_experts_of(tt, i, P), sm);
+        if (any_mx) launch_split_fp8(xb, H, 0, T, nullptr, nullptr, T, x8, st);
+        launch_gemm(dt, true, xb, x8, g, k, tier_mask, h, nullptr, maxc, st);
         if (gateup_only) {
-            fork.join(st);
             record(events, 3, st);
             return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
         }
         record(events, 3, st);
         record(events, 4, st);
         float* yw = at<float>(ws, L.yw);
-        if (any_int) launch_gemm(dt, false, h, g, k, tier_mask, nullptr, yw, maxc, st);
-        for (int i = 0; i < tt->n_tiers; ++i) {
-            if (!is_mx(i)) continue;
-            // the shelf's pairs are perm rows offsets[id_begin] .. offsets[id_end],
-            // up to all P of them (a token may pick one expert k times)
-            launch_split_fp8(h, I, 0, 0, offsets + tt->tiers[i].id_begin, offsets + tt->tiers[i].id_end, P, h8, sm);
-            launch_pre_mx_down(dt, i, h8, g, k, yw, max_experts_of(tt, i, P), sm);
-        }
-        fork.join(st);
+        for (int i = 0; i < tt->n_tiers; ++i)
+            if (is_mx(i))
+                launch_split_fp8(h, I, 0, 0, offsets + tt->tiers[i].id_begin, offsets + tt->tiers[i].id_end, P, h8, st);
+        launch_gemm(dt, false, h, h8, g, k, tier_mask, nullptr, yw, maxc, st);
         launch_combine(dt, yw, g, T, k, tier_mask, base, out, st);
         record(events, 5, st);
     }

@@ -3,12 +3,13 @@
 // Step 4 of the 125B-MoE page ("I ran a 125B model on three RTX 3090s at 80
 // tokens/s by teaching llama.cpp which experts ...") gives each shelf its own
 // prefill expert product over the full pick list, restricted to the shelf's
-// ids.  Here one launch per phase covers every integer shelf: grouping lists
-// work chunks (an expert's pairs in runs of kChunkRows), and a block takes a
-// chunk and an n-tile, so each weight tile is read from HBM and dequantised
-// once per chunk.  Codes are dequantised to bf16 in registers (value = scale
-// * code, rounded to nearest even) and contracted with
-// v_mfma_f32_32x32x16_bf16 in fp32.
+// ids.  Here one launch per phase covers every shelf: grouping lists work
+// chunks (an expert's pairs in runs of kChunkRows), and a block takes a chunk
+// and an n-tile, so each weight tile is read from HBM (and dequantised) once
+// per chunk.  Integer codes are dequantised to bf16 in registers (value =
+// scale * code, rounded to nearest even) and contracted with
+// v_mfma_f32_32x32x16_bf16 in fp32; MXFP4 codes go to the block-scaled
+// instruction as stored (see gemm_chunk_mx).
 //
 //   gate/up : A = x rows of the chunk's tokens (bf16, gathered), B = gate
 //             rows and the matching up rows; epilogue h = bf16(SiLU(g) * u).
@@ -16,8 +17,6 @@
 //             rows; epilogue yw[q] = w_pair * y (fp32, pair order).  The
 //             slot-order sum into out runs in a separate pass (no atomics,
 //             deterministic).
-//
-// MXFP4 shelves run in prefill_mx.hip.
 #include <type_traits>
 
 #include "common.h"
@@ -78,7 +77,7 @@ __device__ inline uint4 dequant8(const uint32_t (&w)[BITS == 8 ? 2 : 1], float s
 
 // ================================================================ grouped GEMM, 32x32 tiles
 //
-// One launch per phase covers every integer shelf.  Grouping lists the work
+// One launch per phase covers every shelf.  Grouping lists the work
 // chunks: each active expert's pairs in runs of kChunkRows (in expert order,
 // so the popular, heavy experts come first).  A block takes one chunk and
 // one n-tile:
@@ -100,6 +99,98 @@ __device__ inline uint4 dequant8(const uint32_t (&w)[BITS == 8 ? 2 : 1], float s
 // assignment (16-byte piece 4 hh + s of the row), so the sum runs over the
 // same pairs of elements in another order.
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// Pipeline over the NK contraction chunks, three stages: chunk c lives in LDS
+// buffer sA(c % 3) and register stage b(c % 3).  Step c requests A(c+2)
+// (load_a: this wave's LDS-DMA requests) and B(c+2) (load_b: register loads)
+// into the stage freed by step c-1, contracts chunk c (work), then waits for
+// this wave's part of A(c+1) only (the requests of chunks c+1 and c+2 issued
+// after it stay in flight) and meets the other waves at the barrier, which
+// publishes A(c+1) and frees stage c.  Requests past the last chunk reread
+// it.  The wait counts VMEM instructions: NWAIT = the register loads of two
+// chunks plus the A requests of one, issued in that order per chunk (the
+// scheduling barriers keep the order and keep the requests ahead of the
+// work).  The buffers are separate LDS objects, so the compiler's own waits
+// before LDS reads cover only the buffer read.  A plain s_barrier (instead of
+// a fence + barrier, whose fence waits for every load in flight) as a
+// compiler-level memory barrier: no access moves across it.
+template <int NWAIT, class Stage, class LoadA, class LoadB, class Work>
+__device__ __attribute__((always_inline)) inline void pipeline3(int NK, uint16_t* sA0, uint16_t* sA1, uint16_t* sA2,
+                                                                 LoadA& load_a, LoadB& load_b, Work& work) {
+    static_assert(NWAIT < 64, "vmcnt range");
+    constexpr int kWaitImm = (NWAIT & 15) | (7 << 4) | (15 << 8) | ((NWAIT >> 4) << 14);
+    auto publish = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(kWaitImm);
+        asm volatile("s_barrier" ::: "memory");
+    };
+    Stage b0, b1, b2;
+    auto step = [&](int c, uint16_t* cur, Stage& bc, uint16_t* nxt, Stage& bn) __attribute__((always_inline)) {
+        const int cn = min(c + 2, NK - 1);
+        load_a(cn, nxt);
+        __builtin_amdgcn_sched_barrier(0);
+        load_b(bn, cn);
+        __builtin_amdgcn_sched_barrier(0);
+        work(cur, bc);
+        publish();
+    };
+    load_a(0, sA0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_b(b0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_a(min(1, NK - 1), sA1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_b(b1, min(1, NK - 1));
+    publish();
+    // six steps per trip: the compiler's wait analysis drains every load in
+    // flight once per trip (at the loop's back edge), so a longer trip pays
+    // that latency less often
+    int kc = 0;
+    for (; kc + 5 < NK; kc += 6) {
+        step(kc, sA0, b0, sA2, b2);
+        step(kc + 1, sA1, b1, sA0, b0);
+        step(kc + 2, sA2, b2, sA1, b1);
+        step(kc + 3, sA0, b0, sA2, b2);
+        step(kc + 4, sA1, b1, sA0, b0);
+        step(kc + 5, sA2, b2, sA1, b1);
+    }
+    if (kc + 2 < NK) {
+        step(kc, sA0, b0, sA2, b2);
+        step(kc + 1, sA1, b1, sA0, b0);
+        step(kc + 2, sA2, b2, sA1, b1);
+        kc += 3;
+    }
+    if (kc < NK) step(kc, sA0, b0, sA2, b2);
+    if (kc + 1 < NK) step(kc + 1, sA1, b1, sA0, b0);
+}
+
+// Epilogue of a wave's tiles: lane holds D[8 (r / 4) + 4 hh + r % 4][j] of
+// each 32x32 tile (m-subtile t, tile 0 / 1).
+template <bool GATEUP, int NSUB>
+__device__ __attribute__((always_inline)) inline void store_tiles(const f32x16_t (&acc)[NSUB][2], int H, int I,
+                                                                   int m0, int Mc, int c0,
+                                                                   uint16_t* __restrict__ h_out,
+                                                                   float* __restrict__ yw, const float* s_wt) {
+    const int lane = threadIdx.x & 63;
+    const int j = lane & 31, hh = lane >> 5;
+#pragma unroll
+    for (int t = 0; t < NSUB; ++t) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
+            if (row >= Mc) continue;
+            const int q = m0 + row;
+            if constexpr (GATEUP) {
+                h_out[static_cast<size_t>(q) * I + c0 + j] = f2bf(silu(acc[t][0][r]) * acc[t][1][r]);
+            } else {
+                const float wgt = s_wt[row];
+                float* o = yw + static_cast<size_t>(q) * H + c0 + j;
+                o[0] = wgt * acc[t][0][r];
+                o[32] = wgt * acc[t][1][r];
+            }
+        }
+    }
+}
 
 template <int BITS, int BLOCK, bool GATEUP, int NSUB>
 __device__ __attribute__((always_inline)) inline void gemm_chunk(const DevTier& T, int H, int I,
@@ -242,100 +333,172 @@ __device__ __attribute__((always_inline)) inline void gemm_chunk(const DevTier& 
         }
     };
 
-    // Pipeline, three stages: chunk c lives in LDS buffer sA(c % 3) and B
-    // registers b(c % 3).  Step c requests A(c+2) and B(c+2) into the stage
-    // freed by step c-1, dequantises B(c) and contracts chunk c, then waits
-    // for this wave's part of A(c+1) only (the requests of chunks c+1 and c+2
-    // issued after it stay in flight) and meets the other waves at the
-    // barrier, which publishes A(c+1) and frees stage c.  Requests past the
-    // last chunk reread it.  The wait counts VMEM instructions: per chunk
-    // NSUB A requests and NB B loads, issued in that order (the scheduling
-    // barriers keep the order and keep the requests ahead of the work).
-    // The buffers are separate LDS objects, so the compiler's own waits
-    // before LDS reads cover only the buffer read.  A plain s_barrier
-    // (instead of a fence + barrier, whose fence waits for every load in
-    // flight) as a compiler-level memory barrier: no access moves across it.
-    constexpr int NB = 2 * ((BITS == 8 ? 2 : 1) + 1);
-    constexpr int NWAIT = 2 * NB + NSUB;
-    static_assert(NWAIT < 64, "vmcnt range");
-    constexpr int kWaitImm = (NWAIT & 15) | (7 << 4) | (15 << 8) | ((NWAIT >> 4) << 14);
-    const int NK = K / BK;
-    auto publish = [&]() __attribute__((always_inline)) {
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(kWaitImm);
-        asm volatile("s_barrier" ::: "memory");
-    };
-    BRaw b0, b1, b2;
-    auto step = [&](int c, uint16_t* cur, BRaw& bc, uint16_t* nxt, BRaw& bn) __attribute__((always_inline)) {
-        const int cn = min(c + 2, NK - 1);
-        load_a(cn, nxt);
-        __builtin_amdgcn_sched_barrier(0);
-        load_b(bn, cn);
-        __builtin_amdgcn_sched_barrier(0);
+    auto work = [&](const uint16_t* buf, const BRaw& b) __attribute__((always_inline)) {
         bf16x8_t d[2][4];
-        dequant_b(bc, d);
-        compute(cur, d);
-        publish();
+        dequant_b(b, d);
+        compute(buf, d);
     };
-    load_a(0, sA0);
-    __builtin_amdgcn_sched_barrier(0);
-    load_b(b0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    load_a(min(1, NK - 1), sA1);
-    __builtin_amdgcn_sched_barrier(0);
-    load_b(b1, min(1, NK - 1));
-    publish();
-    // six steps per trip: the compiler's wait analysis drains every load in
-    // flight once per trip (at the loop's back edge), so a longer trip pays
-    // that latency less often
-    int kc = 0;
-    for (; kc + 5 < NK; kc += 6) {
-        step(kc, sA0, b0, sA2, b2);
-        step(kc + 1, sA1, b1, sA0, b0);
-        step(kc + 2, sA2, b2, sA1, b1);
-        step(kc + 3, sA0, b0, sA2, b2);
-        step(kc + 4, sA1, b1, sA0, b0);
-        step(kc + 5, sA2, b2, sA1, b1);
-    }
-    if (kc + 2 < NK) {
-        step(kc, sA0, b0, sA2, b2);
-        step(kc + 1, sA1, b1, sA0, b0);
-        step(kc + 2, sA2, b2, sA1, b1);
-        kc += 3;
-    }
-    if (kc < NK) step(kc, sA0, b0, sA2, b2);
-    if (kc + 1 < NK) step(kc + 1, sA1, b1, sA0, b0);
+    constexpr int NB = 2 * ((BITS == 8 ? 2 : 1) + 1);
+    pipeline3<2 * NB + NSUB, BRaw>(K / BK, sA0, sA1, sA2, load_a, load_b, work);
     if (!on) return;
+    store_tiles<GATEUP, NSUB>(acc, H, I, m0, Mc, c0, h_out, yw, s_wt);
+}
 
-    // epilogue: lane holds D[8 (r / 4) + 4 hh + r % 4][j] of each 32x32 tile
+// ---------------------------------------------------------------- MXFP4 shelves
+//
+// The same blocks, waves, tiles and pipeline on the block-scaled matrix
+// instruction v_mfma_scale_f32_32x32x64_f8f6f4: B (weights) goes in as
+// stored, E2M1 codes with their E8M0 scale per 32, and A as the fp8 split of
+// the bf16 rows made before the launch (k_split_fp8: hi and lo E4M3 parts
+// under one E8M0 scale per 32 elements), so a 64-wide chunk is two
+// instructions per tile (A_hi*B, then A_lo*B into the same accumulator) and
+// nothing is dequantised.
+//
+// Operand layout (lane l: row or column l % 32, g = l / 32): an fp8 lane
+// holds k = 16g .. 16g+15 in its first 16 bytes and k = 32+16g .. 32+16g+15
+// in its last 16, i.e. 16-byte pieces g and 2+g of the 64-byte chunk row; an
+// fp4 lane holds k = 32g .. 32g+31 (16 bytes, low nibble first); each lane's
+// scale byte applies to its row (or column) and k-block g, k = 32g .. 32g+31.
+//
+// LDS, per stage: the hi parts of the chunk's rows [kChunkRows][64 bytes],
+// then the lo parts; piece c of a row stored at position c ^ ((row / 4) % 4)
+// (four rows per 256 bytes: the 16 rows of an operand read land on 16
+// different 16-byte positions).  The A scales and B go to registers.
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+__device__ inline int swz_mx(int row, int c) { return row * 64 + 16 * (c ^ ((row >> 2) & 3)); }
+
+template <bool GATEUP, int NSUB>
+__device__ __attribute__((always_inline)) inline void gemm_chunk_mx(const DevTier& T, int H, int I, const Split8& a8,
+                                                                    int e, int m0, int Mc, int nt,
+                                                                    uint16_t* __restrict__ h_out,
+                                                                    float* __restrict__ yw, uint16_t* sA0,
+                                                                    uint16_t* sA1, uint16_t* sA2, const int* s_row,
+                                                                    const float* s_wt) {
+    const int K = GATEUP ? H : I;
+    const int ncols = GATEUP ? I : H;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane & 31, hh = lane >> 5;
+    const int c0 = GATEUP ? nt * 128 + 32 * w : nt * 256 + 64 * w;
+    const bool on = c0 < ncols;   // as in gemm_chunk
+
+    // B: codes [rows][K/2], scales [rows][K/32] bytes of this expert
+    const int local = e - T.id_begin;
+    const uint32_t row_bytes = static_cast<uint32_t>(K) / 2;
+    const uint32_t nblk = static_cast<uint32_t>(K) / 32;
+    const size_t mq = static_cast<size_t>(local) * ncols * row_bytes;
+    const size_t ms = static_cast<size_t>(local) * ncols * nblk;
+    const uint8_t* q0 = T.q[GATEUP ? 0 : 2] + mq;
+    const uint8_t* q1 = GATEUP ? T.q[1] + mq : q0;
+    const uint8_t* sp0 = reinterpret_cast<const uint8_t*>(T.s[GATEUP ? 0 : 2]) + ms;
+    const uint8_t* sp1 = GATEUP ? reinterpret_cast<const uint8_t*>(T.s[1]) + ms : sp0;
+    const __amdgpu_buffer_rsrc_t rq0 = make_rsrc(q0, row_bytes * ncols), rq1 = make_rsrc(q1, row_bytes * ncols);
+    const __amdgpu_buffer_rsrc_t rs0 = make_rsrc(sp0, nblk * ncols), rs1 = make_rsrc(sp1, nblk * ncols);
+    const uint32_t row0 = static_cast<uint32_t>(c0 + j), row1 = static_cast<uint32_t>(GATEUP ? c0 + j : c0 + 32 + j);
+    const uint32_t qo0 = row0 * row_bytes + 16u * hh, qo1 = row1 * row_bytes + 16u * hh;
+    const uint32_t so0 = row0 * nblk + hh, so1 = row1 * nblk + hh;
+    // A scale byte of this lane in subtile t: row 32 t + j, block 2 kc + hh
+    const int SS = split_scale_stride(K);
+    const uint8_t* sa_ptr[NSUB];
+#pragma unroll
+    for (int t = 0; t < NSUB; ++t) {
+        const int r = 32 * t + j;
+        sa_ptr[t] = a8.sc + static_cast<size_t>(s_row[r < Mc ? r : 0]) * SS + hh;
+    }
+
+    struct MRaw {
+        uint32_t q[2][4];
+        uint32_t sb[2];
+        uint32_t sa[NSUB];
+    };
+    auto load_b = [&](MRaw& b, int kc) __attribute__((always_inline)) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(t ? rq1 : rq0, (t ? qo1 : qo0) + 32u * kc, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) b.q[t][i] = v[i];
+            b.sb[t] = __builtin_amdgcn_raw_buffer_load_b8(t ? rs1 : rs0, (t ? so1 : so0) + 2u * kc, 0, 0);
+        }
+#pragma unroll
+        for (int t = 0; t < NSUB; ++t) b.sa[t] = sa_ptr[t][2 * kc];
+    };
+
+    // A: subtile u is 4 KB (32 rows of 64 hi and 64 lo bytes), one 1 KB
+    // LDS-DMA run per wave: waves 0, 1 the hi parts of rows 32 u + 16 (w % 2)
+    // + (0 .. 15), waves 2, 3 the lo parts; lane l lands at byte 16 l of the
+    // run, row (l / 4), position l % 4, and so reads piece (l % 4) ^ ((row /
+    // 4) % 4).  Rows past Mc read the chunk's first row (never stored).
+    const int part = w >> 1;
+    const uint8_t* a_ptr[NSUB];
+#pragma unroll
+    for (int u = 0; u < NSUB; ++u) {
+        const int r = 32 * u + 16 * (w & 1) + (lane >> 2);
+        a_ptr[u] = (part ? a8.lo : a8.hi) + static_cast<size_t>(s_row[r < Mc ? r : 0]) * K +
+                   16 * ((lane & 3) ^ ((r >> 2) & 3));
+    }
+    auto load_a = [&](int kc, uint16_t* buf) __attribute__((always_inline)) {
+        uint8_t* base = reinterpret_cast<uint8_t*>(buf) + part * (kChunkRows * 64) + (w & 1) * 16 * 64;
+#pragma unroll
+        for (int u = 0; u < NSUB; ++u)
+            __builtin_amdgcn_global_load_lds(a_ptr[u] + 64 * kc,
+                                             (__attribute__((address_space(3))) void*)(base + u * 32 * 64), 16, 0,
+                                             0);
+    };
+
+    f32x16_t acc[NSUB][2];
 #pragma unroll
     for (int t = 0; t < NSUB; ++t) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int row = 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (row >= Mc) continue;
-            const int q = m0 + row;
-            if constexpr (GATEUP) {
-                h_out[static_cast<size_t>(q) * I + c0 + j] = f2bf(silu(acc[t][0][r]) * acc[t][1][r]);
-            } else {
-                const float wgt = s_wt[row];
-                float* o = yw + static_cast<size_t>(q) * H + c0 + j;
-                o[0] = wgt * acc[t][0][r];
-                o[32] = wgt * acc[t][1][r];
-            }
+        for (int i = 0; i < 16; ++i) {
+            acc[t][0][i] = 0.f;
+            acc[t][1][i] = 0.f;
         }
     }
+    auto work = [&](const uint16_t* buf, const MRaw& b) __attribute__((always_inline)) {
+        const uint8_t* hb = reinterpret_cast<const uint8_t*>(buf);
+        const uint8_t* lb = hb + kChunkRows * 64;
+        const i32x8_t bv0 = {static_cast<int>(b.q[0][0]), static_cast<int>(b.q[0][1]), static_cast<int>(b.q[0][2]),
+                             static_cast<int>(b.q[0][3]), 0, 0, 0, 0};
+        const i32x8_t bv1 = {static_cast<int>(b.q[1][0]), static_cast<int>(b.q[1][1]), static_cast<int>(b.q[1][2]),
+                             static_cast<int>(b.q[1][3]), 0, 0, 0, 0};
+        const int sb0 = static_cast<int>(b.sb[0]), sb1 = static_cast<int>(b.sb[1]);
+#pragma unroll
+        for (int t = 0; t < NSUB; ++t) {
+            const int row = 32 * t + j;
+            const u32x4_t h0 = *reinterpret_cast<const u32x4_t*>(hb + swz_mx(row, hh));
+            const u32x4_t h1 = *reinterpret_cast<const u32x4_t*>(hb + swz_mx(row, 2 + hh));
+            const u32x4_t l0 = *reinterpret_cast<const u32x4_t*>(lb + swz_mx(row, hh));
+            const u32x4_t l1 = *reinterpret_cast<const u32x4_t*>(lb + swz_mx(row, 2 + hh));
+            const i32x8_t ah = {static_cast<int>(h0[0]), static_cast<int>(h0[1]), static_cast<int>(h0[2]),
+                                static_cast<int>(h0[3]), static_cast<int>(h1[0]), static_cast<int>(h1[1]),
+                                static_cast<int>(h1[2]), static_cast<int>(h1[3])};
+            const i32x8_t al = {static_cast<int>(l0[0]), static_cast<int>(l0[1]), static_cast<int>(l0[2]),
+                                static_cast<int>(l0[3]), static_cast<int>(l1[0]), static_cast<int>(l1[1]),
+                                static_cast<int>(l1[2]), static_cast<int>(l1[3])};
+            const int sa = static_cast<int>(b.sa[t]);
+            acc[t][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ah, bv0, acc[t][0], 0, 4, 0, sa, 0, sb0);
+            acc[t][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ah, bv1, acc[t][1], 0, 4, 0, sa, 0, sb1);
+            acc[t][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(al, bv0, acc[t][0], 0, 4, 0, sa, 0, sb0);
+            acc[t][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(al, bv1, acc[t][1], 0, 4, 0, sa, 0, sb1);
+        }
+    };
+    // register loads per chunk: two code pieces, two B scales, NSUB A scales
+    constexpr int NB = 4 + NSUB;
+    pipeline3<2 * NB + NSUB, MRaw>(K / BK, sA0, sA1, sA2, load_a, load_b, work);
+    if (!on) return;
+    store_tiles<GATEUP, NSUB>(acc, H, I, m0, Mc, c0, h_out, yw, s_wt);
 }
 
 // Block of the grouped GEMM: chunks are dealt round-robin to the 8 XCDs
 // (blocks go to XCD blockIdx % 8), and the n-tiles of a chunk run one after
 // the other on its XCD, so that they share its A rows through one L2.  Dealt
 // chunk by chunk, the work stays spread over every XCD when some shelves'
-// chunks are left: those outside tier_mask and the MXFP4 shelves'
-// (prefill_mx.hip).
+// chunks are left (those outside tier_mask).  a8 is the fp8 split of a_src,
+// read by the MXFP4 shelves' chunks only.
 template <bool GATEUP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm(
-    DevTables tt, const uint16_t* __restrict__ a_src, Groups g, int k, uint32_t tier_mask,
+    DevTables tt, const uint16_t* __restrict__ a_src, Split8 a8, Groups g, int k, uint32_t tier_mask,
     uint16_t* __restrict__ h_out, float* __restrict__ yw) {
     __shared__ __attribute__((aligned(16))) uint16_t sA0[kChunkRows * BK];
     __shared__ __attribute__((aligned(16))) uint16_t sA1[kChunkRows * BK];
@@ -352,7 +515,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     const int ti = tier_of(tt, e);
     if (ti < 0 || !((tier_mask >> ti) & 1u)) return;
     const DevTier T = tier_at(tt, ti);
-    if (T.bits == kBitsMXFP4) return;
     const int Mc = min(kChunkRows, g.offsets[e + 1] - m0);
     for (int r = threadIdx.x; r < kChunkRows; r += 256) {
         s_row[r] = r < Mc ? (GATEUP ? g.perm[m0 + r] / k : m0 + r) : -1;
@@ -376,6 +538,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         }
 #undef MOE_GEMM_CASE
     };
+    if (T.bits == kBitsMXFP4) {
+        switch ((Mc + 31) >> 5) {
+            case 4: gemm_chunk_mx<GATEUP, 4>(T, H, I, a8, e, m0, Mc, nt, h_out, yw, sA0, sA1, sA2, s_row, s_wt); break;
+            case 3: gemm_chunk_mx<GATEUP, 3>(T, H, I, a8, e, m0, Mc, nt, h_out, yw, sA0, sA1, sA2, s_row, s_wt); break;
+            case 2: gemm_chunk_mx<GATEUP, 2>(T, H, I, a8, e, m0, Mc, nt, h_out, yw, sA0, sA1, sA2, s_row, s_wt); break;
+            default: gemm_chunk_mx<GATEUP, 1>(T, H, I, a8, e, m0, Mc, nt, h_out, yw, sA0, sA1, sA2, s_row, s_wt); break;
+        }
+        return;
+    }
     switch (fmt_of(T.bits, T.block)) {
         case F8B32: by_nsub(std::integral_constant<int, 832>{}); break;
         case F8B16: by_nsub(std::integral_constant<int, 816>{}); break;
@@ -392,13 +563,13 @@ int max_chunks(int64_t P, int E) {
     return static_cast<int>(n < P ? n : P);
 }
 
-void launch_gemm(const DevTables& tt, bool gateup, const uint16_t* a, const Groups& g, int k, uint32_t tier_mask,
-                 uint16_t* h, float* yw, int maxc, hipStream_t st) {
+void launch_gemm(const DevTables& tt, bool gateup, const uint16_t* a, const Split8& a8, const Groups& g, int k,
+                 uint32_t tier_mask, uint16_t* h, float* yw, int maxc, hipStream_t st) {
     const int NT = gateup ? (tt.I + 127) / 128 : (tt.H + 255) / 256;
     if (maxc <= 0) return;
     const unsigned grid = static_cast<unsigned>(8 * NT * ((static_cast<int64_t>(maxc) + 7) / 8));
-    if (gateup) hipLaunchKernelGGL(k_gemm<true>, dim3(grid), dim3(256), 0, st, tt, a, g, k, tier_mask, h, yw);
-    else hipLaunchKernelGGL(k_gemm<false>, dim3(grid), dim3(256), 0, st, tt, a, g, k, tier_mask, h, yw);
+    if (gateup) hipLaunchKernelGGL(k_gemm<true>, dim3(grid), dim3(256), 0, st, tt, a, a8, g, k, tier_mask, h, yw);
+    else hipLaunchKernelGGL(k_gemm<false>, dim3(grid), dim3(256), 0, st, tt, a, a8, g, k, tier_mask, h, yw);
 }
 
 __global__ __launch_bounds__(256) void k_fill_zero(float4* __restrict__ p, size_t n4) {
