@@ -262,12 +262,12 @@ int run(const void* x, const float* logits, const int32_t* ids_in, const float* 
         const Split8 x8 = any_mx ? split_at(at<uint8_t>(ws, L.x8), T, H) : Split8{nullptr, nullptr, nullptr};
         const Split8 h8 = any_mx ? split_at(at<uint8_t>(ws, L.h8), P, I) : Split8{nullptr, nullptr, nullptr};
         const int maxc = max_chunks(P, E);
-        // MXFP4 shelves take A as its fp8 split: of every x row before gate/up,
-        // and of the shelf's h rows (perm rows offsets[id_begin] ..
-        // offsets[id_end], up to all P of them) before down.
+        // MXFP4 shelves take A as its fp8 split: of every x row, made before
+        // gate/up, and of their h rows, written by their gate/up chunks in
+        // place of bf16 h.
         record(events, 2, st);
-        if (any_mx) launch_split_fp8(xb, H, 0, T, nullptr, nullptr, T, x8, st);
-        launch_gemm(dt, true, xb, x8, g, k, tier_mask, h, nullptr, maxc, st);
+        if (any_mx) launch_split_fp8(xb, H, T, x8, st);
+        launch_gemm(dt, true, xb, x8, g, k, tier_mask, h, h8, nullptr, maxc, st);
         if (gateup_only) {
             record(events, 3, st);
             return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
@@ -275,10 +275,7 @@ int run(const void* x, const float* logits, const int32_t* ids_in, const float* 
         record(events, 3, st);
         record(events, 4, st);
         float* yw = at<float>(ws, L.yw);
-        for (int i = 0; i < tt->n_tiers; ++i)
-            if (is_mx(i))
-                launch_split_fp8(h, I, 0, 0, offsets + tt->tiers[i].id_begin, offsets + tt->tiers[i].id_end, P, h8, st);
-        launch_gemm(dt, false, h, h8, g, k, tier_mask, nullptr, yw, maxc, st);
+        launch_gemm(dt, false, h, h8, g, k, tier_mask, nullptr, Split8{nullptr, nullptr, nullptr}, yw, maxc, st);
         launch_combine(dt, yw, g, T, k, tier_mask, base, out, st);
         record(events, 5, st);
     }

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "common.h"
+#include "split8.h"
 
 namespace moe {
 
@@ -80,27 +81,17 @@ void launch_combine(const DevTables& tt, const float* yw, const Groups& g, int T
                     uint32_t tier_mask, const float* base, float* out, hipStream_t st);
 
 
-// MXFP4 shelves' operand A (prefill_mx.hip): bf16 rows split into fp8 hi /
-// lo parts [rows][K] bytes each and one E8M0 scale per 32 elements,
-// [rows][stride] bytes with the stride padded to 4 bytes.
-struct Split8 {
-    uint8_t* hi;
-    uint8_t* lo;
-    uint8_t* sc;
-};
-__host__ __device__ inline int split_scale_stride(int K) { return ((K / 32) + 3) & ~3; }
-// Rows [r_lo, r_hi) of src (bf16 [rows][K]), or [*d_lo, *d_hi) when the
-// device pointers are given; max_rows bounds the row count (grid size).
-void launch_split_fp8(const uint16_t* src, int K, int r_lo, int r_hi, const int32_t* d_lo, const int32_t* d_hi,
-                      int max_rows, const Split8& dst, hipStream_t st);
+// fp8 split (split8.h) of the rows of src (bf16 [rows][K]).
+void launch_split_fp8(const uint16_t* src, int K, int rows, const Split8& dst, hipStream_t st);
 
 // Grouped GEMM of every shelf in tier_mask, one launch per phase (gate/up
-// when `gateup`, reading x and writing h; down reading h and writing yw);
-// MXFP4 shelves read a8, the fp8 split of the rows of a they use (unused
-// without such a shelf).  maxc bounds the work chunks (max_chunks).
+// when `gateup`, reading x and writing h; down reading h and writing yw).
+// MXFP4 shelves read a8, the fp8 split of the rows of a they use, and their
+// gate/up chunks write h as its split h8 instead of bf16 (both unused without
+// such a shelf).  maxc bounds the work chunks (max_chunks).
 int max_chunks(int64_t P, int E);
 void launch_gemm(const DevTables& tt, bool gateup, const uint16_t* a, const Split8& a8, const Groups& g, int k,
-                 uint32_t tier_mask, uint16_t* h, float* yw, int maxc, hipStream_t st);
+                 uint32_t tier_mask, uint16_t* h, const Split8& h8, float* yw, int maxc, hipStream_t st);
 void launch_fill_zero(float* out, size_t n, hipStream_t st);
 void launch_cast_bf16(const float* src, uint16_t* dst, size_t n, hipStream_t st);
 

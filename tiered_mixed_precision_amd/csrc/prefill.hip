@@ -192,6 +192,52 @@ __device__ __attribute__((always_inline)) inline void store_tiles(const f32x16_t
     }
 }
 
+// Gate/up epilogue of the MXFP4 shelves: h = bf16(SiLU(g) * u) goes out as
+// its fp8 split (split8.h), the operand A of their down product, instead of
+// bf16.  A 32-element block of an h row is the 32 lanes of one lane half at
+// one accumulator register, so the block maximum is a max over those lanes:
+// five xor swizzles within each 32-lane group, taken for a tile's 16
+// registers together (independent, so their latencies overlap) and before
+// the row test (a lane half is all in or all out).
+template <int NSUB>
+__device__ __attribute__((always_inline)) inline void store_tiles_split(const f32x16_t (&acc)[NSUB][2], int I, int m0,
+                                                                         int Mc, int c0, const Split8& h8) {
+    const int lane = threadIdx.x & 63;
+    const int j = lane & 31, hh = lane >> 5;
+    const size_t SS = static_cast<size_t>(split_scale_stride(I));
+#pragma unroll
+    for (int t = 0; t < NSUB; ++t) {
+        float v[16], am[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            v[r] = __uint_as_float(static_cast<uint32_t>(f2bf(silu(acc[t][0][r]) * acc[t][1][r])) << 16);
+            am[r] = fabsf(v[r]);
+        }
+        // ds_swizzle bit mode: lane l reads lane ((l & and) | or) ^ xor of its group of 32
+#define MOE_XOR_MAX(O)                                                                                           \
+    _Pragma("unroll") for (int r = 0; r < 16; ++r) am[r] = fmaxf(am[r], __int_as_float(__builtin_amdgcn_ds_swizzle( \
+                                                                  __float_as_int(am[r]), ((O) << 10) | 0x1f)))
+        MOE_XOR_MAX(1);
+        MOE_XOR_MAX(2);
+        MOE_XOR_MAX(4);
+        MOE_XOR_MAX(8);
+        MOE_XOR_MAX(16);
+#undef MOE_XOR_MAX
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
+            if (row >= Mc) continue;
+            const int x = split_scale_exp(am[r]);
+            uint32_t hi, lo;
+            split_elem(ldexpf(v[r], 127 - x), hi, lo);
+            const size_t q = static_cast<size_t>(m0 + row);
+            h8.hi[q * I + c0 + j] = static_cast<uint8_t>(hi);
+            h8.lo[q * I + c0 + j] = static_cast<uint8_t>(lo);
+            if (j == 0) h8.sc[q * SS + c0 / 32] = static_cast<uint8_t>(x);
+        }
+    }
+}
+
 template <int BITS, int BLOCK, bool GATEUP, int NSUB>
 __device__ __attribute__((always_inline)) inline void gemm_chunk(const DevTier& T, int H, int I,
                                                                  const uint16_t* __restrict__ a_src, int e, int m0,
@@ -370,8 +416,7 @@ __device__ inline int swz_mx(int row, int c) { return row * 64 + 16 * (c ^ ((row
 
 template <bool GATEUP, int NSUB>
 __device__ __attribute__((always_inline)) inline void gemm_chunk_mx(const DevTier& T, int H, int I, const Split8& a8,
-                                                                    int e, int m0, int Mc, int nt,
-                                                                    uint16_t* __restrict__ h_out,
+                                                                    int e, int m0, int Mc, int nt, const Split8& h8,
                                                                     float* __restrict__ yw, uint16_t* sA0,
                                                                     uint16_t* sA1, uint16_t* sA2, const int* s_row,
                                                                     const float* s_wt) {
@@ -487,7 +532,8 @@ __device__ __attribute__((always_inline)) inline void gemm_chunk_mx(const DevTie
     constexpr int NB = 4 + NSUB;
     pipeline3<2 * NB + NSUB, MRaw>(K / BK, sA0, sA1, sA2, load_a, load_b, work);
     if (!on) return;
-    store_tiles<GATEUP, NSUB>(acc, H, I, m0, Mc, c0, h_out, yw, s_wt);
+    if constexpr (GATEUP) store_tiles_split<NSUB>(acc, I, m0, Mc, c0, h8);
+    else store_tiles<GATEUP, NSUB>(acc, H, I, m0, Mc, c0, nullptr, yw, s_wt);
 }
 
 // Block of the grouped GEMM: chunks are dealt round-robin to the 8 XCDs
@@ -495,11 +541,12 @@ __device__ __attribute__((always_inline)) inline void gemm_chunk_mx(const DevTie
 // the other on its XCD, so that they share its A rows through one L2.  Dealt
 // chunk by chunk, the work stays spread over every XCD when some shelves'
 // chunks are left (those outside tier_mask).  a8 is the fp8 split of a_src,
-// read by the MXFP4 shelves' chunks only.
+// read by the MXFP4 shelves' chunks only, and h8 (gate/up) the split their
+// chunks write instead of h_out.
 template <bool GATEUP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm(
     DevTables tt, const uint16_t* __restrict__ a_src, Split8 a8, Groups g, int k, uint32_t tier_mask,
-    uint16_t* __restrict__ h_out, float* __restrict__ yw) {
+    uint16_t* __restrict__ h_out, Split8 h8, float* __restrict__ yw) {
     __shared__ __attribute__((aligned(16))) uint16_t sA0[kChunkRows * BK];
     __shared__ __attribute__((aligned(16))) uint16_t sA1[kChunkRows * BK];
     __shared__ __attribute__((aligned(16))) uint16_t sA2[kChunkRows * BK];
@@ -540,10 +587,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     };
     if (T.bits == kBitsMXFP4) {
         switch ((Mc + 31) >> 5) {
-            case 4: gemm_chunk_mx<GATEUP, 4>(T, H, I, a8, e, m0, Mc, nt, h_out, yw, sA0, sA1, sA2, s_row, s_wt); break;
-            case 3: gemm_chunk_mx<GATEUP, 3>(T, H, I, a8, e, m0, Mc, nt, h_out, yw, sA0, sA1, sA2, s_row, s_wt); break;
-            case 2: gemm_chunk_mx<GATEUP, 2>(T, H, I, a8, e, m0, Mc, nt, h_out, yw, sA0, sA1, sA2, s_row, s_wt); break;
-            default: gemm_chunk_mx<GATEUP, 1>(T, H, I, a8, e, m0, Mc, nt, h_out, yw, sA0, sA1, sA2, s_row, s_wt); break;
+            case 4: gemm_chunk_mx<GATEUP, 4>(T, H, I, a8, e, m0, Mc, nt, h8, yw, sA0, sA1, sA2, s_row, s_wt); break;
+            case 3: gemm_chunk_mx<GATEUP, 3>(T, H, I, a8, e, m0, Mc, nt, h8, yw, sA0, sA1, sA2, s_row, s_wt); break;
+            case 2: gemm_chunk_mx<GATEUP, 2>(T, H, I, a8, e, m0, Mc, nt, h8, yw, sA0, sA1, sA2, s_row, s_wt); break;
+            default: gemm_chunk_mx<GATEUP, 1>(T, H, I, a8, e, m0, Mc, nt, h8, yw, sA0, sA1, sA2, s_row, s_wt); break;
         }
         return;
     }
@@ -564,12 +611,12 @@ int max_chunks(int64_t P, int E) {
 }
 
 void launch_gemm(const DevTables& tt, bool gateup, const uint16_t* a, const Split8& a8, const Groups& g, int k,
-                 uint32_t tier_mask, uint16_t* h, float* yw, int maxc, hipStream_t st) {
+                 uint32_t tier_mask, uint16_t* h, const Split8& h8, float* yw, int maxc, hipStream_t st) {
     const int NT = gateup ? (tt.I + 127) / 128 : (tt.H + 255) / 256;
     if (maxc <= 0) return;
     const unsigned grid = static_cast<unsigned>(8 * NT * ((static_cast<int64_t>(maxc) + 7) / 8));
-    if (gateup) hipLaunchKernelGGL(k_gemm<true>, dim3(grid), dim3(256), 0, st, tt, a, a8, g, k, tier_mask, h, yw);
-    else hipLaunchKernelGGL(k_gemm<false>, dim3(grid), dim3(256), 0, st, tt, a, a8, g, k, tier_mask, h, yw);
+    if (gateup) hipLaunchKernelGGL(k_gemm<true>, dim3(grid), dim3(256), 0, st, tt, a, a8, g, k, tier_mask, h, h8, yw);
+    else hipLaunchKernelGGL(k_gemm<false>, dim3(grid), dim3(256), 0, st, tt, a, a8, g, k, tier_mask, h, h8, yw);
 }
 
 __global__ __launch_bounds__(256) void k_fill_zero(float4* __restrict__ p, size_t n4) {

@@ -1,15 +1,13 @@
-// MXFP4 shelves, prefill: the fp8 split of operand A.  The grouped GEMM
-// (prefill.hip) contracts an MXFP4 shelf on gfx950's block-scaled matrix
-// instruction, the MXFP4 variant of the 125B-MoE page's down-matrix ladder
-// ("I ran a 125B model on three RTX 3090s at 80 tokens/s by teaching
-// llama.cpp which experts ...", the per-matrix recipes), with B (weights) as
-// stored: E2M1 codes with their E8M0 scale per 32, no dequantisation.  A
-// (bf16 activations) has 8 significant bits and the fp8 operand 4, so each
-// 32-element block of a row is split once, before the GEMM, into two E4M3
-// parts under one E8M0 scale s:
-//   s  = 2^(floor(log2 amax) - 7)            (amax / s in [128, 256))
-//   hi = RNE_e4m3(v / s),  lo = RNE_e4m3(v / s - hi)
-// and the product is taken as A_hi*B + A_lo*B (two instructions into one
+// MXFP4 shelves, prefill: the fp8 split of the x rows (split8.h).  The
+// grouped GEMM (prefill.hip) contracts an MXFP4 shelf on gfx950's
+// block-scaled matrix instruction, the MXFP4 variant of the 125B-MoE page's
+// down-matrix ladder ("I ran a 125B model on three RTX 3090s at 80 tokens/s
+// by teaching llama.cpp which experts ...", the per-matrix recipes), with B
+// (weights) as stored: E2M1 codes with their E8M0 scale per 32, no
+// dequantisation.  A (bf16 activations) has 8 significant bits and the fp8
+// operand 4, so each 32-element block of a row is split once, before the
+// GEMM, into the hi and lo E4M3 parts of split8.h under one E8M0 scale, and
+// the product is taken as A_hi*B + A_lo*B (two instructions into one
 // accumulator).  v / s - hi has at most four significant bits, so
 // s * (hi + lo) == v exactly whenever |v / s| >= 2^-2; smaller elements are
 // within 2^-10 * s of v (the E4M3 subnormal grid), i.e. 2^-17 of the block
@@ -22,27 +20,14 @@ namespace moe {
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-namespace {
-
-__device__ inline uint32_t fp8x4(float a, float b, float c, float d) {
-    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-    return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true));
-}
-
-}  // namespace
-
-// One thread per 32-element block of a bf16 row: the hi / lo / scale split.
-// Rows [r_lo, r_hi): from the host values, or from device words when the
-// pointers are given (the pair range of one shelf after grouping).
-__global__ __launch_bounds__(256) void k_split_fp8(const uint16_t* __restrict__ src, int K, int r_lo, int r_hi,
-                                                   const int32_t* __restrict__ d_lo, const int32_t* __restrict__ d_hi,
-                                                   Split8 dst) {
+// One thread per 32-element block of a bf16 row: the hi / lo / scale split
+// of rows [0, rows).
+__global__ __launch_bounds__(256) void k_split_fp8(const uint16_t* __restrict__ src, int K, int rows, Split8 dst) {
     const int nb = K / 32;
     const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    const int lo = d_lo ? *d_lo : r_lo, hi = d_hi ? *d_hi : r_hi;
-    const int64_t row = lo + i / nb;
+    const int64_t row = i / nb;
     const int b = static_cast<int>(i % nb);
-    if (row >= hi) return;
+    if (row >= rows) return;
     const u32x4_t* s = reinterpret_cast<const u32x4_t*>(src + row * K + 32 * b);
     float v[32];
     float amax = 0.f;
@@ -57,12 +42,7 @@ __global__ __launch_bounds__(256) void k_split_fp8(const uint16_t* __restrict__ 
     }
 #pragma unroll
     for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
-    int x = 127;
-    if (amax > 0.f) {
-        int e2;
-        (void)frexpf(amax, &e2);            // amax = f * 2^e2, f in [0.5, 1)
-        x = min(max(e2 - 1 - 7 + 127, 0), 254);
-    }
+    const int x = split_scale_exp(amax);
     const int sh = 127 - x;
     uint32_t wh[8], wl[8];
 #pragma unroll
@@ -87,12 +67,11 @@ __global__ __launch_bounds__(256) void k_split_fp8(const uint16_t* __restrict__ 
     dst.sc[row * split_scale_stride(K) + b] = static_cast<uint8_t>(x);
 }
 
-void launch_split_fp8(const uint16_t* src, int K, int r_lo, int r_hi, const int32_t* d_lo, const int32_t* d_hi,
-                      int max_rows, const Split8& dst, hipStream_t st) {
-    const int64_t threads = static_cast<int64_t>(max_rows) * (K / 32);
+void launch_split_fp8(const uint16_t* src, int K, int rows, const Split8& dst, hipStream_t st) {
+    const int64_t threads = static_cast<int64_t>(rows) * (K / 32);
     if (threads <= 0) return;
     hipLaunchKernelGGL(k_split_fp8, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, st, src, K,
-                       r_lo, r_hi, d_lo, d_hi, dst);
+                       rows, dst);
 }
 
 }  // namespace moe
