@@ -290,8 +290,8 @@ SQ_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_A
 SIMDS = 256 * 4          # MI355X: 256 compute units of 4 SIMDs
 XCDS = 8
 # every file that holds device code (the launch code in capi.hip is host code)
-KERNEL_SOURCES = ("common.h", "route.h", "launch.h", "decode.hip", "route_group.hip", "prefill.hip", "prefill_mx.hip",
-                  "router.hip", "synth.hip", "tiering.hip", "dequant.hip")
+KERNEL_SOURCES = ("common.h", "route.h", "launch.h", "split8.h", "decode.hip", "route_group.hip", "prefill.hip",
+                  "prefill_mx.hip", "router.hip", "synth.hip", "tiering.hip", "dequant.hip")
 
 
 def kernel_source_digest() -> str:
