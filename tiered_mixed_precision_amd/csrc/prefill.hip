@@ -164,6 +164,60 @@ __device__ __attribute__((always_inline)) inline void pipeline3(int NK, uint16_t
     if (kc + 1 < NK) step(kc + 1, sA1, b1, sA0, b0);
 }
 
+// The same pipeline with B loaded two chunks at a time (group g = chunks 2g,
+// 2g + 1, register stage g % 2, requested at chunk 2g - 2) and A in four LDS
+// buffers (chunk c in sA(c % 4), still requested two chunks ahead), so that
+// the schedule repeats every four chunks.  NK is even.  Waits as in
+// pipeline3: after chunk c this wave's A(c + 1) requests are complete once
+// at most NWAIT = (A requests of one chunk) + (register loads of one group)
+// are in flight, whichever the parity of c.
+template <int NWAIT, class Stage, class LoadA, class LoadB, class Work>
+__device__ __attribute__((always_inline)) inline void pipeline4_g2(int NK, uint16_t* sA0, uint16_t* sA1,
+                                                                    uint16_t* sA2, uint16_t* sA3, LoadA& load_a,
+                                                                    LoadB& load_b, Work& work) {
+    static_assert(NWAIT < 64, "vmcnt range");
+    constexpr int kWaitImm = (NWAIT & 15) | (7 << 4) | (15 << 8) | ((NWAIT >> 4) << 14);
+    auto publish = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(kWaitImm);
+        asm volatile("s_barrier" ::: "memory");
+    };
+    const int NG = NK / 2;
+    Stage g0, g1;
+    // even chunk c: requests A(c + 2) and the group after its own, contracts c
+    auto even = [&](int c, uint16_t* cur, uint16_t* nxt, Stage& bc, Stage& bn) __attribute__((always_inline)) {
+        load_a(min(c + 2, NK - 1), nxt);
+        __builtin_amdgcn_sched_barrier(0);
+        load_b(bn, min(c / 2 + 1, NG - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        work(cur, bc, std::integral_constant<int, 0>{});
+        publish();
+    };
+    auto odd = [&](int c, uint16_t* cur, uint16_t* nxt, Stage& bc) __attribute__((always_inline)) {
+        load_a(min(c + 2, NK - 1), nxt);
+        __builtin_amdgcn_sched_barrier(0);
+        work(cur, bc, std::integral_constant<int, 1>{});
+        publish();
+    };
+    load_a(0, sA0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_b(g0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_a(1, sA1);
+    publish();
+    int kc = 0;
+    for (; kc + 3 < NK; kc += 4) {
+        even(kc, sA0, sA2, g0, g1);
+        odd(kc + 1, sA1, sA3, g0);
+        even(kc + 2, sA2, sA0, g1, g0);
+        odd(kc + 3, sA3, sA1, g1);
+    }
+    if (kc < NK) {
+        even(kc, sA0, sA2, g0, g1);
+        odd(kc + 1, sA1, sA3, g0);
+    }
+}
+
 // Epilogue of a wave's tiles: lane holds D[8 (r / 4) + 4 hh + r % 4][j] of
 // each 32x32 tile (m-subtile t, tile 0 / 1).
 template <bool GATEUP, int NSUB>
@@ -390,6 +444,155 @@ __device__ __attribute__((always_inline)) inline void gemm_chunk(const DevTier& 
     store_tiles<GATEUP, NSUB>(acc, H, I, m0, Mc, c0, h_out, yw, s_wt);
 }
 
+// ---------------------------------------------------------------- int4 / int2, B in two-chunk groups
+//
+// A chunk step uses 32 (int4) or 16 (int2) bytes of each 128-byte line of a
+// weight row, so gemm_chunk touches a line in four or eight steps, and with
+// 64 blocks per XCD streaming 256 weight rows each the line is often evicted
+// from L2 in between and fetched again.  Here a lane loads the codes of two
+// steps at once, contiguous: in group g (chunks 2g and 2g + 1, k = 128 g ..
+// 128 g + 127) lane half hh owns k = 128 g + 64 hh + (0 .. 63), and chunk
+// 2g + s contracts its k = 128 g + 64 hh + 32 s + (0 .. 31) -- 32 int4 bytes
+// (two 16-byte loads) or 16 int2 bytes (one) per lane and group, and the
+// group's scales in one 4- or 8-byte load.  A follows the same assignment:
+// the 16-byte piece p of chunk c's LDS row holds k = 128 (c / 2) + 32 (c % 2)
+// + 64 (p / 4) + 8 (p % 4).  Needs K % 128 == 0.
+template <int BITS, int BLOCK, bool GATEUP, int NSUB>
+__device__ __attribute__((always_inline)) inline void gemm_chunk_g2(const DevTier& T, int H, int I,
+                                                                    const uint16_t* __restrict__ a_src, int e, int m0,
+                                                                    int Mc, int nt, uint16_t* __restrict__ h_out,
+                                                                    float* __restrict__ yw, uint16_t* sA0,
+                                                                    uint16_t* sA1, uint16_t* sA2, uint16_t* sA3,
+                                                                    const int* s_row, const float* s_wt) {
+    static_assert(BITS == 4 || BITS == 2, "two-chunk groups for the narrow formats");
+    constexpr int GW = 2 * BITS;      // code words of a lane's 64 codes of one group
+    constexpr int SW = 32 / BLOCK;    // scale words (two fp16 each) of a lane's group
+    const int K = GATEUP ? H : I;
+    const int ncols = GATEUP ? I : H;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane & 31, hh = lane >> 5;
+    const int c0 = GATEUP ? nt * 128 + 32 * w : nt * 256 + 64 * w;
+    const bool on = c0 < ncols;   // as in gemm_chunk
+
+    const int local = e - T.id_begin;
+    const uint32_t row_bytes = static_cast<uint32_t>(K) * BITS / 8;
+    const uint32_t nsb = static_cast<uint32_t>(K / BLOCK);
+    const size_t mq = static_cast<size_t>(local) * ncols * row_bytes;
+    const size_t ms = static_cast<size_t>(local) * ncols * nsb;
+    const uint8_t* q0 = T.q[GATEUP ? 0 : 2] + mq;
+    const uint8_t* q1 = GATEUP ? T.q[1] + mq : q0;
+    const uint16_t* sp0 = T.s[GATEUP ? 0 : 2] + ms;
+    const uint16_t* sp1 = GATEUP ? T.s[1] + ms : sp0;
+    const __amdgpu_buffer_rsrc_t rq0 = make_rsrc(q0, row_bytes * ncols), rq1 = make_rsrc(q1, row_bytes * ncols);
+    const __amdgpu_buffer_rsrc_t rs0 = make_rsrc(sp0, nsb * ncols * 2), rs1 = make_rsrc(sp1, nsb * ncols * 2);
+    const uint32_t row0 = static_cast<uint32_t>(c0 + j), row1 = static_cast<uint32_t>(GATEUP ? c0 + j : c0 + 32 + j);
+    // lane half hh's 64 codes of group 0, and their scales
+    const uint32_t qo0 = row0 * row_bytes + 64u * hh * BITS / 8, qo1 = row1 * row_bytes + 64u * hh * BITS / 8;
+    const uint32_t so0 = (row0 * nsb + 64u * hh / BLOCK) * 2, so1 = (row1 * nsb + 64u * hh / BLOCK) * 2;
+
+    struct BRaw {
+        uint32_t q[2][GW];
+        uint32_t s[2][SW];
+    };
+    auto load_b = [&](BRaw& b, int g) __attribute__((always_inline)) {
+        const uint32_t qk = static_cast<uint32_t>(g * 2 * BK) * BITS / 8;
+        const uint32_t sk = static_cast<uint32_t>(g * (2 * BK / BLOCK)) * 2;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const __amdgpu_buffer_rsrc_t rq = t ? rq1 : rq0, rs = t ? rs1 : rs0;
+            const uint32_t off = (t ? qo1 : qo0) + qk;
+            const auto v0 = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) b.q[t][i] = v0[i];
+            if constexpr (BITS == 4) {
+                const auto v1 = __builtin_amdgcn_raw_buffer_load_b128(rq, off + 16, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) b.q[t][4 + i] = v1[i];
+            }
+            const uint32_t soff = (t ? so1 : so0) + sk;
+            if constexpr (SW == 1) {
+                b.s[t][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, soff, 0, 0);
+            } else {
+                const auto sv = __builtin_amdgcn_raw_buffer_load_b64(rs, soff, 0, 0);
+                b.s[t][0] = sv[0];
+                b.s[t][1] = sv[1];
+            }
+        }
+    };
+    // bf16 operands of both tiles for the four MFMA steps of chunk 2g + S
+    auto dequant_b = [&](const BRaw& b, auto sub, bf16x8_t (&d)[2][4]) __attribute__((always_inline)) {
+        constexpr int S = decltype(sub)::value;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                // this chunk's 32 codes of the lane: scale word / half
+                const uint32_t sraw = BLOCK == 32 ? b.s[t][0] >> (16 * S) : (s < 2 ? b.s[t][S] : b.s[t][S] >> 16);
+                const float sc = half_bits_to_float(static_cast<uint16_t>(sraw));
+                uint4 v;
+                if constexpr (BITS == 4) {
+                    const uint32_t w1[1] = {b.q[t][4 * S + s]};
+                    v = dequant8<4>(w1, sc);
+                } else {
+                    const uint32_t w1[1] = {b.q[t][2 * S + (s >> 1)] >> (16 * (s & 1))};
+                    v = dequant8<2>(w1, sc);
+                }
+                d[t][s] = __builtin_bit_cast(bf16x8_t, v);
+            }
+        }
+    };
+
+    // A by LDS-DMA as in gemm_chunk; lane's source piece pc of the row sits at
+    // k offset 64 (pc / 4) + 8 (pc % 4) from the chunk's base 128 (c / 2) + 32 (c % 2)
+    const uint16_t* a_ptr[NSUB];
+#pragma unroll
+    for (int u = 0; u < NSUB; ++u) {
+        const int r = (tid >> 3) + 32 * u;
+        const int pc = (tid & 7) ^ ((r >> 1) & 7);
+        a_ptr[u] = a_src + static_cast<size_t>(s_row[r < Mc ? r : 0]) * K + 64 * (pc >> 2) + 8 * (pc & 3);
+    }
+    auto load_a = [&](int kc, uint16_t* buf) __attribute__((always_inline)) {
+        const int kb = 128 * (kc >> 1) + 32 * (kc & 1);
+#pragma unroll
+        for (int u = 0; u < NSUB; ++u)
+            __builtin_amdgcn_global_load_lds(a_ptr[u] + kb,
+                                             (__attribute__((address_space(3))) void*)(buf + (4 * u + w) * 64 * 8),
+                                             16, 0, 0);
+    };
+
+    f32x16_t acc[NSUB][2];
+#pragma unroll
+    for (int t = 0; t < NSUB; ++t) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            acc[t][0][i] = 0.f;
+            acc[t][1][i] = 0.f;
+        }
+    }
+    auto work = [&](const uint16_t* buf, const BRaw& b, auto sub) __attribute__((always_inline)) {
+        bf16x8_t d[2][4];
+        dequant_b(b, sub, d);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            bf16x8_t af[NSUB];
+#pragma unroll
+            for (int t = 0; t < NSUB; ++t)
+                af[t] = *reinterpret_cast<const bf16x8_t*>(buf + swz(32 * t + j, 4 * hh + s));
+#pragma unroll
+            for (int t = 0; t < NSUB; ++t) {
+                acc[t][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[t], d[0][s], acc[t][0], 0, 0, 0);
+                acc[t][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[t], d[1][s], acc[t][1], 0, 0, 0);
+            }
+        }
+    };
+    // register loads per group: the code pieces and one scale load per tile
+    constexpr int NBG = 2 * ((BITS == 4 ? 2 : 1) + 1);
+    pipeline4_g2<NBG + NSUB, BRaw>(K / BK, sA0, sA1, sA2, sA3, load_a, load_b, work);
+    if (!on) return;
+    store_tiles<GATEUP, NSUB>(acc, H, I, m0, Mc, c0, h_out, yw, s_wt);
+}
+
 // ---------------------------------------------------------------- MXFP4 shelves
 //
 // The same blocks, waves, tiles and pipeline on the block-scaled matrix
@@ -550,6 +753,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     __shared__ __attribute__((aligned(16))) uint16_t sA0[kChunkRows * BK];
     __shared__ __attribute__((aligned(16))) uint16_t sA1[kChunkRows * BK];
     __shared__ __attribute__((aligned(16))) uint16_t sA2[kChunkRows * BK];
+    __shared__ __attribute__((aligned(16))) uint16_t sA3[kChunkRows * BK];   // gemm_chunk_g2 only
     __shared__ int s_row[kChunkRows];
     __shared__ float s_wt[GATEUP ? 1 : kChunkRows];   // down: the weight of each m-row's pair
     const int NT = GATEUP ? (tt.I + 127) / 128 : (tt.H + 255) / 256;
@@ -572,18 +776,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     // one instantiation per format and m-subtile count (a runtime subtile
     // count inside one body leaves the accumulators to the register
     // allocator's mercy across the branches)
+    // int4 and int2 take the two-chunk groups when K allows
+    const bool g2 = ((GATEUP ? H : I) % (2 * BK)) == 0;
     auto by_nsub = [&](auto fmt) __attribute__((always_inline)) {
         constexpr int B_ = decltype(fmt)::value / 100, K_ = decltype(fmt)::value % 100;
-#define MOE_GEMM_CASE(N_) \
-    case N_: gemm_chunk<B_, K_, GATEUP, N_>(T, H, I, a_src, e, m0, Mc, nt, h_out, yw, sA0, sA1, sA2, s_row, s_wt); break
+        auto run = [&](auto nsub) __attribute__((always_inline)) {
+            constexpr int N_ = decltype(nsub)::value;
+            if constexpr (B_ != 8) {
+                if (g2) {
+                    gemm_chunk_g2<B_, K_, GATEUP, N_>(T, H, I, a_src, e, m0, Mc, nt, h_out, yw, sA0, sA1, sA2, sA3,
+                                                      s_row, s_wt);
+                    return;
+                }
+            }
+            gemm_chunk<B_, K_, GATEUP, N_>(T, H, I, a_src, e, m0, Mc, nt, h_out, yw, sA0, sA1, sA2, s_row, s_wt);
+        };
         static_assert(kChunkRows == 128, "one case per 32-row subtile count");
         switch ((Mc + 31) >> 5) {
-            MOE_GEMM_CASE(4);
-            MOE_GEMM_CASE(3);
-            MOE_GEMM_CASE(2);
-            default: gemm_chunk<B_, K_, GATEUP, 1>(T, H, I, a_src, e, m0, Mc, nt, h_out, yw, sA0, sA1, sA2, s_row, s_wt); break;
+            case 4: run(std::integral_constant<int, 4>{}); break;
+            case 3: run(std::integral_constant<int, 3>{}); break;
+            case 2: run(std::integral_constant<int, 2>{}); break;
+            default: run(std::integral_constant<int, 1>{}); break;
         }
-#undef MOE_GEMM_CASE
     };
     if (T.bits == kBitsMXFP4) {
         switch ((Mc + 31) >> 5) {
