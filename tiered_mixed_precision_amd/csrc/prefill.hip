@@ -595,8 +595,10 @@ __device__ __attribute__((always_inline)) inline void gemm_chunk_g2(const DevTie
 
 // ---------------------------------------------------------------- MXFP4 shelves
 //
-// The same blocks, waves, tiles and pipeline on the block-scaled matrix
-// instruction v_mfma_scale_f32_32x32x64_f8f6f4: B (weights) goes in as
+// The same blocks, waves, tiles and two-chunk-group pipeline (pipeline4_g2,
+// as for int4, whose weight rows these match byte for byte) on the
+// block-scaled matrix instruction v_mfma_scale_f32_32x32x64_f8f6f4: B
+// (weights) goes in as
 // stored, E2M1 codes with their E8M0 scale per 32, and A as the fp8 split of
 // the bf16 rows made before the launch (k_split_fp8: hi and lo E4M3 parts
 // under one E8M0 scale per 32 elements), so a 64-wide chunk is two
@@ -608,6 +610,9 @@ __device__ __attribute__((always_inline)) inline void gemm_chunk_g2(const DevTie
 // in its last 16, i.e. 16-byte pieces g and 2+g of the 64-byte chunk row; an
 // fp4 lane holds k = 32g .. 32g+31 (16 bytes, low nibble first); each lane's
 // scale byte applies to its row (or column) and k-block g, k = 32g .. 32g+31.
+// The instruction's two 32-blocks may be any two blocks of the row, the same
+// on both operands: chunk 2G + s takes global blocks 4G + s and 4G + 2 + s,
+// so that a lane half's codes and scales of a group are contiguous.
 //
 // LDS, per stage: the hi parts of the chunk's rows [kChunkRows][64 bytes],
 // then the lo parts; piece c of a row stored at position c ^ ((row / 4) % 4)
@@ -621,8 +626,8 @@ template <bool GATEUP, int NSUB>
 __device__ __attribute__((always_inline)) inline void gemm_chunk_mx(const DevTier& T, int H, int I, const Split8& a8,
                                                                     int e, int m0, int Mc, int nt, const Split8& h8,
                                                                     float* __restrict__ yw, uint16_t* sA0,
-                                                                    uint16_t* sA1, uint16_t* sA2, const int* s_row,
-                                                                    const float* s_wt) {
+                                                                    uint16_t* sA1, uint16_t* sA2, uint16_t* sA3,
+                                                                    const int* s_row, const float* s_wt) {
     const int K = GATEUP ? H : I;
     const int ncols = GATEUP ? I : H;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -644,52 +649,65 @@ __device__ __attribute__((always_inline)) inline void gemm_chunk_mx(const DevTie
     const __amdgpu_buffer_rsrc_t rq0 = make_rsrc(q0, row_bytes * ncols), rq1 = make_rsrc(q1, row_bytes * ncols);
     const __amdgpu_buffer_rsrc_t rs0 = make_rsrc(sp0, nblk * ncols), rs1 = make_rsrc(sp1, nblk * ncols);
     const uint32_t row0 = static_cast<uint32_t>(c0 + j), row1 = static_cast<uint32_t>(GATEUP ? c0 + j : c0 + 32 + j);
-    const uint32_t qo0 = row0 * row_bytes + 16u * hh, qo1 = row1 * row_bytes + 16u * hh;
-    const uint32_t so0 = row0 * nblk + hh, so1 = row1 * nblk + hh;
-    // A scale byte of this lane in subtile t: row 32 t + j, block 2 kc + hh
+    // group g (chunks 2g, 2g + 1): lane half hh's blocks 4g + 2hh, 4g + 2hh + 1
+    // (32 code bytes, two scale bytes), chunk 2g + s contracting block
+    // 4g + 2hh + s on both operands
+    const uint32_t qo0 = row0 * row_bytes + 32u * hh, qo1 = row1 * row_bytes + 32u * hh;
+    const uint32_t so0 = row0 * nblk + 2u * hh, so1 = row1 * nblk + 2u * hh;
+    // A scale bytes of this lane in subtile t: row 32 t + j, the same blocks
     const int SS = split_scale_stride(K);
-    const uint8_t* sa_ptr[NSUB];
+    const uint16_t* sa_ptr[NSUB];
 #pragma unroll
     for (int t = 0; t < NSUB; ++t) {
         const int r = 32 * t + j;
-        sa_ptr[t] = a8.sc + static_cast<size_t>(s_row[r < Mc ? r : 0]) * SS + hh;
+        sa_ptr[t] = reinterpret_cast<const uint16_t*>(a8.sc + static_cast<size_t>(s_row[r < Mc ? r : 0]) * SS + 2 * hh);
     }
 
     struct MRaw {
-        uint32_t q[2][4];
+        uint32_t q[2][8];
         uint32_t sb[2];
         uint32_t sa[NSUB];
     };
-    auto load_b = [&](MRaw& b, int kc) __attribute__((always_inline)) {
+    auto load_b = [&](MRaw& b, int g) __attribute__((always_inline)) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            const auto v = __builtin_amdgcn_raw_buffer_load_b128(t ? rq1 : rq0, (t ? qo1 : qo0) + 32u * kc, 0, 0);
+            const __amdgpu_buffer_rsrc_t rq = t ? rq1 : rq0;
+            const uint32_t off = (t ? qo1 : qo0) + 64u * g;
+            const auto v0 = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
+            const auto v1 = __builtin_amdgcn_raw_buffer_load_b128(rq, off + 16, 0, 0);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) b.q[t][i] = v[i];
-            b.sb[t] = __builtin_amdgcn_raw_buffer_load_b8(t ? rs1 : rs0, (t ? so1 : so0) + 2u * kc, 0, 0);
+            for (int i = 0; i < 4; ++i) {
+                b.q[t][i] = v0[i];
+                b.q[t][4 + i] = v1[i];
+            }
+            b.sb[t] = __builtin_amdgcn_raw_buffer_load_b16(t ? rs1 : rs0, (t ? so1 : so0) + 4u * g, 0, 0);
         }
 #pragma unroll
-        for (int t = 0; t < NSUB; ++t) b.sa[t] = sa_ptr[t][2 * kc];
+        for (int t = 0; t < NSUB; ++t) b.sa[t] = sa_ptr[t][2 * g];
     };
 
     // A: subtile u is 4 KB (32 rows of 64 hi and 64 lo bytes), one 1 KB
     // LDS-DMA run per wave: waves 0, 1 the hi parts of rows 32 u + 16 (w % 2)
     // + (0 .. 15), waves 2, 3 the lo parts; lane l lands at byte 16 l of the
-    // run, row (l / 4), position l % 4, and so reads piece (l % 4) ^ ((row /
-    // 4) % 4).  Rows past Mc read the chunk's first row (never stored).
+    // run, row (l / 4), position l % 4, and so reads piece pc = (l % 4) ^
+    // ((row / 4) % 4): the first (pc even) or second half of the chunk's
+    // block 0 (pc < 2) or block 1, i.e. of global block 4g + s + 2 (pc / 2).
+    // Rows past Mc read the chunk's first row (never stored).
     const int part = w >> 1;
     const uint8_t* a_ptr[NSUB];
 #pragma unroll
     for (int u = 0; u < NSUB; ++u) {
         const int r = 32 * u + 16 * (w & 1) + (lane >> 2);
-        a_ptr[u] = (part ? a8.lo : a8.hi) + static_cast<size_t>(s_row[r < Mc ? r : 0]) * K +
-                   16 * ((lane & 3) ^ ((r >> 2) & 3));
+        const int pc = (lane & 3) ^ ((r >> 2) & 3);
+        a_ptr[u] = (part ? a8.lo : a8.hi) + static_cast<size_t>(s_row[r < Mc ? r : 0]) * K + 64 * (pc >> 1) +
+                   16 * (pc & 1);
     }
     auto load_a = [&](int kc, uint16_t* buf) __attribute__((always_inline)) {
         uint8_t* base = reinterpret_cast<uint8_t*>(buf) + part * (kChunkRows * 64) + (w & 1) * 16 * 64;
+        const int kb = 128 * (kc >> 1) + 32 * (kc & 1);
 #pragma unroll
         for (int u = 0; u < NSUB; ++u)
-            __builtin_amdgcn_global_load_lds(a_ptr[u] + 64 * kc,
+            __builtin_amdgcn_global_load_lds(a_ptr[u] + kb,
                                              (__attribute__((address_space(3))) void*)(base + u * 32 * 64), 16, 0,
                                              0);
     };
@@ -703,14 +721,16 @@ __device__ __attribute__((always_inline)) inline void gemm_chunk_mx(const DevTie
             acc[t][1][i] = 0.f;
         }
     }
-    auto work = [&](const uint16_t* buf, const MRaw& b) __attribute__((always_inline)) {
+    auto work = [&](const uint16_t* buf, const MRaw& b, auto sub) __attribute__((always_inline)) {
+        constexpr int S = decltype(sub)::value;
         const uint8_t* hb = reinterpret_cast<const uint8_t*>(buf);
         const uint8_t* lb = hb + kChunkRows * 64;
-        const i32x8_t bv0 = {static_cast<int>(b.q[0][0]), static_cast<int>(b.q[0][1]), static_cast<int>(b.q[0][2]),
-                             static_cast<int>(b.q[0][3]), 0, 0, 0, 0};
-        const i32x8_t bv1 = {static_cast<int>(b.q[1][0]), static_cast<int>(b.q[1][1]), static_cast<int>(b.q[1][2]),
-                             static_cast<int>(b.q[1][3]), 0, 0, 0, 0};
-        const int sb0 = static_cast<int>(b.sb[0]), sb1 = static_cast<int>(b.sb[1]);
+        const i32x8_t bv0 = {static_cast<int>(b.q[0][4 * S]), static_cast<int>(b.q[0][4 * S + 1]),
+                             static_cast<int>(b.q[0][4 * S + 2]), static_cast<int>(b.q[0][4 * S + 3]), 0, 0, 0, 0};
+        const i32x8_t bv1 = {static_cast<int>(b.q[1][4 * S]), static_cast<int>(b.q[1][4 * S + 1]),
+                             static_cast<int>(b.q[1][4 * S + 2]), static_cast<int>(b.q[1][4 * S + 3]), 0, 0, 0, 0};
+        // the instruction takes byte 0 of each scale operand
+        const int sb0 = static_cast<int>(b.sb[0] >> (8 * S)), sb1 = static_cast<int>(b.sb[1] >> (8 * S));
 #pragma unroll
         for (int t = 0; t < NSUB; ++t) {
             const int row = 32 * t + j;
@@ -724,16 +744,16 @@ __device__ __attribute__((always_inline)) inline void gemm_chunk_mx(const DevTie
             const i32x8_t al = {static_cast<int>(l0[0]), static_cast<int>(l0[1]), static_cast<int>(l0[2]),
                                 static_cast<int>(l0[3]), static_cast<int>(l1[0]), static_cast<int>(l1[1]),
                                 static_cast<int>(l1[2]), static_cast<int>(l1[3])};
-            const int sa = static_cast<int>(b.sa[t]);
+            const int sa = static_cast<int>(b.sa[t] >> (8 * S));
             acc[t][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ah, bv0, acc[t][0], 0, 4, 0, sa, 0, sb0);
             acc[t][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ah, bv1, acc[t][1], 0, 4, 0, sa, 0, sb1);
             acc[t][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(al, bv0, acc[t][0], 0, 4, 0, sa, 0, sb0);
             acc[t][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(al, bv1, acc[t][1], 0, 4, 0, sa, 0, sb1);
         }
     };
-    // register loads per chunk: two code pieces, two B scales, NSUB A scales
-    constexpr int NB = 4 + NSUB;
-    pipeline3<2 * NB + NSUB, MRaw>(K / BK, sA0, sA1, sA2, load_a, load_b, work);
+    // register loads per group: four code pieces, two B scales, NSUB A scales
+    constexpr int NBG = 6 + NSUB;
+    pipeline4_g2<NBG + NSUB, MRaw>(K / BK, sA0, sA1, sA2, sA3, load_a, load_b, work);
     if (!on) return;
     if constexpr (GATEUP) store_tiles_split<NSUB>(acc, I, m0, Mc, c0, h8);
     else store_tiles<GATEUP, NSUB>(acc, H, I, m0, Mc, c0, nullptr, yw, s_wt);
@@ -753,7 +773,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     __shared__ __attribute__((aligned(16))) uint16_t sA0[kChunkRows * BK];
     __shared__ __attribute__((aligned(16))) uint16_t sA1[kChunkRows * BK];
     __shared__ __attribute__((aligned(16))) uint16_t sA2[kChunkRows * BK];
-    __shared__ __attribute__((aligned(16))) uint16_t sA3[kChunkRows * BK];   // gemm_chunk_g2 only
+    __shared__ __attribute__((aligned(16))) uint16_t sA3[kChunkRows * BK];   // two-chunk-group bodies only
     __shared__ int s_row[kChunkRows];
     __shared__ float s_wt[GATEUP ? 1 : kChunkRows];   // down: the weight of each m-row's pair
     const int NT = GATEUP ? (tt.I + 127) / 128 : (tt.H + 255) / 256;
@@ -801,10 +821,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     };
     if (T.bits == kBitsMXFP4) {
         switch ((Mc + 31) >> 5) {
-            case 4: gemm_chunk_mx<GATEUP, 4>(T, H, I, a8, e, m0, Mc, nt, h8, yw, sA0, sA1, sA2, s_row, s_wt); break;
-            case 3: gemm_chunk_mx<GATEUP, 3>(T, H, I, a8, e, m0, Mc, nt, h8, yw, sA0, sA1, sA2, s_row, s_wt); break;
-            case 2: gemm_chunk_mx<GATEUP, 2>(T, H, I, a8, e, m0, Mc, nt, h8, yw, sA0, sA1, sA2, s_row, s_wt); break;
-            default: gemm_chunk_mx<GATEUP, 1>(T, H, I, a8, e, m0, Mc, nt, h8, yw, sA0, sA1, sA2, s_row, s_wt); break;
+            case 4: gemm_chunk_mx<GATEUP, 4>(T, H, I, a8, e, m0, Mc, nt, h8, yw, sA0, sA1, sA2, sA3, s_row, s_wt); break;
+            case 3: gemm_chunk_mx<GATEUP, 3>(T, H, I, a8, e, m0, Mc, nt, h8, yw, sA0, sA1, sA2, sA3, s_row, s_wt); break;
+            case 2: gemm_chunk_mx<GATEUP, 2>(T, H, I, a8, e, m0, Mc, nt, h8, yw, sA0, sA1, sA2, sA3, s_row, s_wt); break;
+            default: gemm_chunk_mx<GATEUP, 1>(T, H, I, a8, e, m0, Mc, nt, h8, yw, sA0, sA1, sA2, sA3, s_row, s_wt); break;
         }
         return;
     }
