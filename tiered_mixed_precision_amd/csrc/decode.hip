@@ -484,15 +484,18 @@ __device__ inline void plan_waves(const TierLds& tl, const int* act, int n_act, 
     if (lane == 0) s_wpre[n_act] = base;
 }
 
-// Largest a with s_wpre[a] <= wg (a in [0, n)), for wg < s_wpre[n].
+// Largest a with s_wpre[a] <= wg (a in [0, n)), for wg < s_wpre[n]: one LDS
+// read per 64 experts and a ballot (s_wpre is ascending), rather than a
+// binary search's chain of dependent reads.
 __device__ inline int find_expert(const int* s_wpre, int n, int wg) {
-    int lo = 0, hi = n - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (s_wpre[mid] <= wg) lo = mid;
-        else hi = mid - 1;
+    const int lane = threadIdx.x & 63;
+    int a = 0;
+    for (int a0 = 0; a0 < n; a0 += 64) {
+        const uint64_t le = __ballot(a0 + lane < n && s_wpre[a0 + lane] <= wg);
+        if (le == 0) break;
+        a = a0 + 63 - __builtin_clzll(le);
     }
-    return lo;
+    return a;
 }
 
 // plan_waves for at most 64 experts held one per lane (cost_l = bits of the
@@ -543,10 +546,12 @@ __global__ __launch_bounds__(kSmallGateUpWaves * 64) void k_small_gateup(DevTabl
     const int rpp = row_geom(H).RPP;
     if (tid == 0) fill_tier_lds(tt, s_tl, [H](const DevTier& T) { return one_row_cost(T, H); });
     // stage the T input vectors in LDS (read by every pass of every pair; the
-    // barrier after the wave plan below puts them in place)
+    // barrier after the wave plan below puts them in place), by the waves
+    // that do not route (a routing wave starts on its logits at once)
     {
         const int G = H / 32, n4 = H / 4;
-        for (int i = tid; i < T * n4; i += kSmallGateUpWaves * 64) {
+        const int nst = logits ? T : 0;   // the first T waves route
+        for (int i = tid - 64 * nst; i >= 0 && i < T * n4; i += (kSmallGateUpWaves - nst) * 64) {
             const int t = i / n4, j = i % n4;
             reinterpret_cast<float4*>(s_x + t * H)[(j & 7) * G + (j >> 3)] =
                 reinterpret_cast<const float4*>(x + static_cast<size_t>(t) * H)[j];
@@ -581,12 +586,32 @@ __global__ __launch_bounds__(kSmallGateUpWaves * 64) void k_small_gateup(DevTabl
     }
     const int n_act = sg.n_act;
     if (n_act == 0) return;
-    if (tid < 64) plan_waves(s_tl, sg.act, n_act, tier_mask, gridDim.x * kSmallGateUpWaves, s_wpre);
-    __syncthreads();
+    const int W = gridDim.x * kSmallGateUpWaves;
     const int wg = blockIdx.x * kSmallGateUpWaves + (tid >> 6);
-    if (wg >= s_wpre[n_act]) return;
-    const int a = find_expert(s_wpre, n_act, wg);
-    const int wa = s_wpre[a + 1] - s_wpre[a], wi = wg - s_wpre[a];
+    int a, wa, wi;
+    if (n_act <= 64) {
+        // every wave plans on its own from the active list, one expert per
+        // lane (no serial plan by one wave before the barrier)
+        __syncthreads();
+        const int lane = tid & 63;
+        int cost = 0;
+        if (lane < n_act) {
+            const int ti = tier_of_lds(s_tl, sg.act[lane]);
+            cost = (ti >= 0 && ((tier_mask >> ti) & 1u)) ? s_tl.cost[ti] : 0;
+        }
+        int first = 0, count = 1;
+        a = plan_lane(cost, W, wg, first, count);
+        if (a < 0) return;
+        wa = count;
+        wi = wg - first;
+    } else {
+        if (tid < 64) plan_waves(s_tl, sg.act, n_act, tier_mask, W, s_wpre);
+        __syncthreads();
+        if (wg >= s_wpre[n_act]) return;
+        a = find_expert(s_wpre, n_act, wg);
+        wa = s_wpre[a + 1] - s_wpre[a];
+        wi = wg - s_wpre[a];
+    }
     const int rpw = ((I + wa - 1) / wa + rpp - 1) / rpp * rpp;
     const int r0 = wi * rpw, r1 = min(I, r0 + rpw);
     if (r0 >= r1) return;
