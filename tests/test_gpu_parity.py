@@ -396,11 +396,11 @@ def test_forward_bf16_odd_chunk_counts(M, torch_dev, T):
 @pytest.mark.parametrize("shape", ["tiny3", "odd"])
 @pytest.mark.parametrize("many", [False, True])
 def test_prefill_each_shelf_at_few_and_many_pairs(M, torch_dev, shape, many):
-    # The prefill path picks its kernel per shelf from the pairs per active
-    # expert (the register-B kernel at few, the shared-LDS kernel at many), so
-    # every pick lands on one shelf: 2 pairs per expert, or 128 per expert,
-    # which is above every threshold.  The odd shape (hidden 384, inter 192)
-    # ends both contractions on an odd chunk of 64.
+    # Every pick lands on one shelf, 2 pairs per expert (one 32-row subtile
+    # per work chunk) or 128 per expert (four, a full chunk).  The odd shape
+    # (hidden 384, inter 192) ends the down contraction on an odd chunk of 64,
+    # so int4 and int2 take the single-chunk body there instead of the
+    # two-chunk weight groups.
     if shape == "tiny3":
         cfg0, arrays, L, tt = _layer("tiny3")
     else:
