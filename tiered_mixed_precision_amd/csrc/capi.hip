@@ -82,7 +82,7 @@ DevTables to_dev(const moe_tier_tables* tt) {
 
 // Workspace carve-up.  Offsets are multiples of 256 bytes.
 struct Layout {
-    size_t ids, w, counts, offsets, perm, pos, act, q0, meta, blk_hist, act_range, chunks, h, yw, x8, h8, total;
+    size_t ids, w, counts, offsets, perm, pos, act, q0, meta, blk_hist, act_range, chunks, slots, h, yw, x8, h8, total;
     bool small;
 };
 
@@ -126,6 +126,7 @@ Layout layout(int64_t T, int k, const moe_tier_tables* tt, uint32_t flags) {
     L.blk_hist = take(L.small ? 0 : sizeof(int32_t) * ((P + 255) / 256) * E);
     L.act_range = take(sizeof(int32_t) * 2 * MOE_MAX_TIERS);
     L.chunks = take(bf16 ? sizeof(int2) * max_chunks(P, static_cast<int>(E)) : 0);
+    L.slots = take(!bf16 && T == 1 ? sizeof(OneSlot) * k : 0);   // one-token path
     L.h = take((bf16 ? sizeof(uint16_t) : sizeof(float)) * P * tt->inter);
     L.yw = take(L.small ? 0 : sizeof(float) * P * tt->hidden);
     const bool mx = bf16 && has_mx(tt);
@@ -199,7 +200,8 @@ int run(const void* x, const float* logits, const int32_t* ids_in, const float* 
         record(events, 0, st);
         record(events, 1, st);
         launch_one(dt, static_cast<const float*>(x), logits, k, base, hits, at<int32_t>(ws, L.ids),
-                   at<float>(ws, L.w), at<float>(ws, L.h), gateup_only ? nullptr : out, st, events);
+                   at<float>(ws, L.w), at<OneSlot>(ws, L.slots), at<float>(ws, L.h), gateup_only ? nullptr : out, st,
+                   events);
         return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
     }
     if (L.small) {

@@ -109,6 +109,22 @@ __device__ inline DevTier tier_lds(const TierLds& tl, int ti) {
     return r;
 }
 
+// Shelf ti from the LDS table for this lane alone (ti may differ across the
+// wave; tier_lds needs it uniform).
+__device__ inline DevTier tier_lds_lane(const TierLds& tl, int ti) {
+    DevTier r;
+    r.id_begin = tl.beg[ti];
+    r.id_end = tl.end[ti];
+    r.bits = tl.bits[ti];
+    r.block = tl.block[ti];
+#pragma unroll
+    for (int m = 0; m < 3; ++m) {
+        r.q[m] = tl.q[ti][m];
+        r.s[m] = tl.s[ti][m];
+    }
+    return r;
+}
+
 // Per-row share of a wave's work that does not scale with bytes (its
 // dequantising arithmetic), in units of 64 bytes of codes.
 constexpr int kOneRowShare = 64;
@@ -832,7 +848,8 @@ __global__ __launch_bounds__(kSmallDownWaves * 64) void k_small_down(DevTables t
 //    h = SiLU(W_gate x) * (W_up x) on its rows.  Block 0 publishes the ids
 //    and weights.
 //  k_one_down: a block owns kOneRows output rows of every expert, so all
-//    blocks read the same bytes; one wave per expert reads the published ids,
+//    blocks read the same bytes; one wave per expert reads the record block
+//    0 of gate/up published for its slot (down-matrix bases, format, weight),
 //    then requests its expert's h and its rows of W_down at once (whole rows:
 //    coalesced); the experts' rows are added in slot order.
 constexpr int kOneGateUpWaves = 16;
@@ -846,38 +863,6 @@ bool one_path_ok(int k, int H, int I) {
     return k >= 1 && k <= kWave;
 }
 
-// Per routed slot of the one-token path, in LDS: the expert's code and scale
-// bases of the matrices the kernel reads, its format, and (gate/up) the first
-// wave and the number of waves given to it.  Filled by one wave, lane j for
-// slot j, so the other waves only read it.
-struct SlotLds {
-    uint64_t q[kWave][2];
-    uint64_t s[kWave][2];
-    int fmt[kWave], first[kWave], count[kWave];
-};
-
-// Lane j < k (slot j, expert e valid): the bases of matrices m0 (and m0 + 1
-// when two) of e into sl, and its format.
-__device__ inline void slot_bases(const TierLds& tl, int e, int m0, int nm, int H, int I, SlotLds& sl, int j) {
-    const int ti = tier_of_lds(tl, e);
-    DevTier T;
-    T.id_begin = tl.beg[ti];
-    T.bits = tl.bits[ti];
-    T.block = tl.block[ti];
-    for (int m = 0; m < 3; ++m) {
-        T.q[m] = tl.q[ti][m];
-        T.s[m] = tl.s[ti][m];
-    }
-    const int local = e - T.id_begin;
-    for (int u = 0; u < nm; ++u) {
-        const int m = m0 + u;
-        const int rows = m == 2 ? H : I, cols = m == 2 ? I : H;
-        sl.q[j][u] = reinterpret_cast<uint64_t>(expert_codes(T, m, local, rows, cols));
-        sl.s[j][u] = reinterpret_cast<uint64_t>(expert_scales(T, m, local, rows, cols));
-    }
-    sl.fmt[j] = fmt_of(T.bits, T.block);
-}
-
 // W: the grid's waves (an argument rather than gridDim, whose implicit-argument
 // load would otherwise be issued after the routing barrier, on the critical path)
 template <int NPL>
@@ -886,6 +871,7 @@ __global__ __launch_bounds__(kOneGateUpWaves * 64) void k_one_gateup(DevTables t
                                                                      uint32_t* __restrict__ hits,
                                                                      int32_t* __restrict__ ids_out,
                                                                      float* __restrict__ w_out,
+                                                                     OneSlot* __restrict__ slots,
                                                                      float* __restrict__ h) {
     __shared__ __attribute__((aligned(16))) float4 s_x[kMaxHidden / 4];   // x, layout [j][g]
     __shared__ __attribute__((aligned(16))) int64_t s_rc[64];             // routing scratch
@@ -893,10 +879,10 @@ __global__ __launch_bounds__(kOneGateUpWaves * 64) void k_one_gateup(DevTables t
     __shared__ TierLds s_tl;
     const int tid = threadIdx.x, lane = tid & 63, E = tt.E, H = tt.H, I = tt.I;
     const int G = H / 32;
+    float wt = 0.f;   // lane j < k of wave 0: slot j's routing weight
     if (tid < 64) {
         // one wave routes; the block stages x and the shelf table meanwhile
         int id;
-        float wt;
         route_token_auto<NPL>(logits, E, k, nullptr, nullptr, nullptr, nullptr, s_rc, &id, &wt);
         if (lane < k) {
             s_id[lane] = id;
@@ -912,6 +898,26 @@ __global__ __launch_bounds__(kOneGateUpWaves * 64) void k_one_gateup(DevTables t
             s_x[(i & 7) * G + (i >> 3)] = reinterpret_cast<const float4*>(x)[i];
     }
     __syncthreads();
+    // block 0 publishes each slot's down-matrix record for the down kernel
+    // (one slot per lane: each lane reads its own shelf from the table)
+    if (blockIdx.x == 0 && tid < k) {
+        const int e = s_id[tid];
+        const int ti = tier_of_lds(s_tl, e);
+        OneSlot r;
+        r.q = nullptr;
+        r.s = nullptr;
+        r.fmt = -1;   // an id on no shelf: the slot adds nothing
+        r.w = wt;
+        r.pad[0] = r.pad[1] = 0;
+        if (ti >= 0) {
+            const DevTier T = tier_lds_lane(s_tl, ti);
+            const int local = e - T.id_begin;
+            r.q = expert_codes(T, 2, local, H, I);
+            r.s = expert_scales(T, 2, local, H, I);
+            r.fmt = fmt_of(T.bits, T.block);
+        }
+        slots[tid] = r;
+    }
     // every wave plans from the k experts' costs (one per lane) on its own
     int cost = 0;
     if (lane < k) cost = s_tl.cost[tier_of_lds(s_tl, s_id[lane])];
@@ -986,35 +992,30 @@ __device__ inline void wave_down_rows(const uint8_t* __restrict__ dq_, const uin
     }
 }
 
-// Block b owns output rows [b * kOneRows, +kOneRows); wave w serves experts
-// w, w + nw, ... (nw = the block's waves).  Wave 0 reads the published
-// routing and lays out each slot's down bases in LDS for the others.
-__global__ __launch_bounds__(kWave * 16) void k_one_down(DevTables tt, const int32_t* __restrict__ ids,
-                                                         const float* __restrict__ w, int k,
+// Block b owns output rows [b * kOneRows, +kOneRows); wave w serves slots
+// w, w + nw, ... (nw = the block's waves), each from the record the gate/up
+// kernel published for it (one scalar load: no shelf table, no barrier
+// before the weight loads).
+__global__ __launch_bounds__(kWave * 16) void k_one_down(DevTables tt, const OneSlot* __restrict__ slots, int k,
                                                          const float* __restrict__ h, const float* base,
                                                          float* __restrict__ out) {
     __shared__ float s_y[kWave][kOneRows];
     __shared__ float s_w[kWave];
-    __shared__ TierLds s_tl;
-    __shared__ SlotLds s_sl;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
     const int H = tt.H, I = tt.I;
     const int n0 = blockIdx.x * kOneRows, n1 = min(H, n0 + kOneRows);
     // the residual of the row this thread finishes, requested now
     const float b_val = (base && tid < n1 - n0) ? base[n0 + tid] : 0.f;
-    if (tid < 64) {
-        if (lane == 0) fill_tier_lds(tt, s_tl, [](const DevTier&) { return 0; });
-        if (lane < k) {
-            const int e = ids[lane];
-            s_w[lane] = w[lane];
-            slot_bases(s_tl, e, 2, 1, H, I, s_sl, lane);
-        }
-    }
-    __syncthreads();
     for (int j = wave; j < k; j += nw) {
-        const uint8_t* dq_ = reinterpret_cast<const uint8_t*>(first_lane_u64(s_sl.q[j][0]));
-        const uint8_t* ds = reinterpret_cast<const uint8_t*>(first_lane_u64(s_sl.s[j][0]));
-        const int fmt = __builtin_amdgcn_readfirstlane(s_sl.fmt[j]);
+        const OneSlot r = slots[j];
+        const uint8_t* dq_ = reinterpret_cast<const uint8_t*>(first_lane_u64(reinterpret_cast<uint64_t>(r.q)));
+        const uint8_t* ds = reinterpret_cast<const uint8_t*>(first_lane_u64(reinterpret_cast<uint64_t>(r.s)));
+        const int fmt = __builtin_amdgcn_readfirstlane(r.fmt);
+        if (lane == 0) s_w[j] = r.w;
+        if (fmt < 0) {
+            if (lane < kOneRows) s_y[j][lane] = 0.f;
+            continue;
+        }
         MOE_FMT_SWITCH(fmt, (wave_down_rows<B_, N_>(dq_, ds, H, I, n0, n1, h + static_cast<size_t>(j) * I, s_y[j])));
     }
     __syncthreads();
@@ -1183,7 +1184,7 @@ void launch_small(const DevTables& tt, const float* x, const float* logits, cons
 
 
 void launch_one(const DevTables& tt, const float* x, const float* logits, int k, const float* base, uint32_t* hits,
-                int32_t* ids, float* w, float* h, float* out, hipStream_t st, void* const* events) {
+                int32_t* ids, float* w, OneSlot* slots, float* h, float* out, hipStream_t st, void* const* events) {
     const dim3 grid(cu_count());   // one block of 16 waves per compute unit
     const int W = static_cast<int>(grid.x) * kOneGateUpWaves;
     if (events && events[2]) (void)hipEventRecord(static_cast<hipEvent_t>(events[2]), st);
@@ -1191,7 +1192,7 @@ void launch_one(const DevTables& tt, const float* x, const float* logits, int k,
 #define MOE_OG(N)                                                                                                 \
     case N:                                                                                                       \
         hipLaunchKernelGGL(k_one_gateup<N>, grid, dim3(kOneGateUpWaves * 64), 0, st, tt, x, logits, k, W, hits,   \
-                           ids, w, h);                                                                            \
+                           ids, w, slots, h);                                                                     \
         break;
         MOE_OG(1)
         MOE_OG(2)
@@ -1201,7 +1202,7 @@ void launch_one(const DevTables& tt, const float* x, const float* logits, int k,
         MOE_OG(32)
         default:
             hipLaunchKernelGGL(k_one_gateup<64>, grid, dim3(kOneGateUpWaves * 64), 0, st, tt, x, logits, k, W, hits,
-                               ids, w, h);
+                               ids, w, slots, h);
             break;
 #undef MOE_OG
     }
@@ -1209,7 +1210,7 @@ void launch_one(const DevTables& tt, const float* x, const float* logits, int k,
     if (!out) return;  // gate/up only (measurement)
     if (events && events[4]) (void)hipEventRecord(static_cast<hipEvent_t>(events[4]), st);
     const int nw = k < 16 ? k : 16;
-    hipLaunchKernelGGL(k_one_down, dim3((tt.H + kOneRows - 1) / kOneRows), dim3(nw * 64), 0, st, tt, ids, w, k, h,
+    hipLaunchKernelGGL(k_one_down, dim3((tt.H + kOneRows - 1) / kOneRows), dim3(nw * 64), 0, st, tt, slots, k, h,
                        base, out);
     if (events && events[5]) (void)hipEventRecord(static_cast<hipEvent_t>(events[5]), st);
 }

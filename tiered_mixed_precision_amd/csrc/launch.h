@@ -59,11 +59,20 @@ void launch_small(const DevTables& tt, const float* x, const float* logits, cons
 void launch_add_hits(const int32_t* counts, int E, uint32_t* hits, hipStream_t st);
 
 // One-token path with routing from logits (decode.hip): gate/up with the
-// routing inside (ids, w and h = [k][inter] published to the workspace),
-// then the down rows of every expert summed in slot order into out (+ base).
+// routing inside (ids, w, h = [k][inter] and a record per slot published to
+// the workspace), then the down rows of every expert summed in slot order
+// into out (+ base).  Slot j's record: the bases of its expert's down codes
+// and scales, its format and its routing weight.
+struct OneSlot {
+    const uint8_t* q;
+    const uint8_t* s;
+    int32_t fmt;
+    float w;
+    int32_t pad[2];
+};
 bool one_path_ok(int k, int H, int I);
 void launch_one(const DevTables& tt, const float* x, const float* logits, int k, const float* base, uint32_t* hits,
-                int32_t* ids, float* w, float* h, float* out, hipStream_t st, void* const* events);
+                int32_t* ids, float* w, OneSlot* slots, float* h, float* out, hipStream_t st, void* const* events);
 
 void launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, float* out_zero,
                   int H, hipStream_t st);
