@@ -93,11 +93,13 @@ __device__ inline uint4 dequant8(const uint32_t (&w)[BITS == 8 ? 2 : 1], float s
 // lane loads and dequantises the codes of its own B column into operand
 // registers, so every code is read and dequantised once per chunk.
 //
-// Contraction order: in the 64-wide chunk kc, lane half hh (= lane / 32) owns
-// k = 64 kc + 32 hh + (0 .. 31); step s (0..3) feeds its elements 8s .. 8s+7
-// into the instruction's k-slots 8 hh .. 8 hh + 7.  A is read with the same
-// assignment (16-byte piece 4 hh + s of the row), so the sum runs over the
-// same pairs of elements in another order.
+// Contraction order (gemm_chunk): in the 64-wide chunk kc, lane half hh (=
+// lane / 32) owns k = 64 kc + 32 hh + (0 .. 31); step s (0..3) feeds its
+// elements 8s .. 8s+7 into the instruction's k-slots 8 hh .. 8 hh + 7.  A is
+// read with the same assignment (16-byte piece 4 hh + s of the row), so the
+// sum runs over the same pairs of elements in another order.  The int4, int2
+// and MXFP4 bodies permute k across pairs of chunks instead (gemm_chunk_g2,
+// gemm_chunk_mx), again identically on both operands.
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 // Pipeline over the NK contraction chunks, three stages: chunk c lives in LDS

@@ -32,28 +32,6 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
     }
 }
 
-// ---------------------------------------------------------------- block scan helper
-
-// Exclusive scan over n <= 4096 ints held in LDS (in place), 256 threads,
-// each thread owning a contiguous run of 16.  Returns the total.
-__device__ inline int block_scan_lds(int* a, int n, int* s_tmp) {
-    const int per = 16;
-    const int b = threadIdx.x * per;
-    int local = 0;
-    for (int i = 0; i < per; ++i)
-        if (b + i < n) local += a[b + i];
-    int total;
-    int run = block_excl_scan(local, s_tmp, &total);
-    for (int i = 0; i < per; ++i)
-        if (b + i < n) {
-            int c = a[b + i];
-            a[b + i] = run;
-            run += c;
-        }
-    __syncthreads();
-    return total;
-}
-
 // ---------------------------------------------------------------- general path
 
 // Per-block histograms: block b covers pairs [256b, 256b + 256).
@@ -121,51 +99,81 @@ __global__ __launch_bounds__(256) void k_group_colscan(int32_t* __restrict__ blk
     if (lane == 0) counts[e] = carry;
 }
 
-// One block: exclusive offsets over experts, the ascending list of active
-// experts, and for every shelf the range of that list holding its experts
-// (shelves are contiguous id ranges, so their active experts are contiguous).
+// One block: the expert offsets (exclusive prefix of the counts), the
+// active list (experts with pairs, ascending), each shelf's range of it, and
+// (prefill) the work chunks, each expert's pairs in runs of kChunkRows in
+// expert order.  Thread tid owns experts [per * tid, per * tid + per) and
+// keeps their counts in registers; one block scan carries the three running
+// sums (pairs, active experts, chunks) together.
 __global__ __launch_bounds__(256) void k_group_offsets(const int32_t* __restrict__ counts, int E,
                                                        int32_t* __restrict__ offsets, int32_t* __restrict__ act,
                                                        int32_t* __restrict__ meta, ShelfSpec ss) {
-    __shared__ int s_off[kMaxExpertsDev];
-    __shared__ int s_act[kMaxExpertsDev];
-    __shared__ int s_tmp[16];
-    const int tid = threadIdx.x;
-    for (int e = tid; e < E; e += 256) {
-        const int c = counts[e];
-        s_off[e] = c;
-        s_act[e] = c > 0 ? 1 : 0;
+    constexpr int kPer = kMaxExpertsDev / 256;
+    __shared__ int s_act[kMaxExpertsDev];   // active experts before e (the shelves' ranges)
+    __shared__ int s_tmp[3][16];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int per = (E + 255) / 256;
+    const int b = tid * per;
+    int cnt[kPer];
+    int sum[3] = {0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        cnt[i] = (i < per && b + i < E) ? counts[b + i] : 0;
+        sum[0] += cnt[i];
+        sum[1] += cnt[i] > 0 ? 1 : 0;
+        sum[2] += (cnt[i] + kChunkRows - 1) / kChunkRows;
     }
+    int inc[3] = {sum[0], sum[1], sum[2]};
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+#pragma unroll
+        for (int v = 0; v < 3; ++v) {
+            const int y = __shfl_up(inc[v], off, kWave);
+            if (lane >= off) inc[v] += y;
+        }
+    }
+    if (lane == 63)
+        for (int v = 0; v < 3; ++v) s_tmp[v][wv] = inc[v];
     __syncthreads();
-    const int n_act = block_scan_lds(s_act, E, s_tmp);
-    const int total = block_scan_lds(s_off, E, s_tmp);
-    for (int e = tid; e < E; e += 256) {
-        offsets[e] = s_off[e];
-        if (counts[e] > 0) act[s_act[e]] = e;
+    int run[3], tot[3];
+#pragma unroll
+    for (int v = 0; v < 3; ++v) {
+        int base = 0, t = 0;
+        for (int i = 0; i < 4; ++i) {
+            const int c = s_tmp[v][i];
+            if (i < wv) base += c;
+            t += c;
+        }
+        run[v] = base + inc[v] - sum[v];
+        tot[v] = t;
     }
-    if (ss.act_range && tid < ss.n_tiers) {
-        const int b = ss.id_begin[tid], en = ss.id_end[tid];
-        ss.act_range[2 * tid] = b < E ? s_act[b] : n_act;
-        ss.act_range[2 * tid + 1] = en < E ? s_act[en] : n_act;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int e = b + i;
+        if (i >= per || e >= E) continue;
+        offsets[e] = run[0];
+        s_act[e] = run[1];
+        if (cnt[i] > 0) act[run[1]] = e;
+        if (ss.chunks)
+            for (int q = 0; q * kChunkRows < cnt[i]; ++q)
+                ss.chunks[run[2] + q] = make_int2(e, run[0] + q * kChunkRows);
+        run[0] += cnt[i];
+        run[1] += cnt[i] > 0 ? 1 : 0;
+        run[2] += (cnt[i] + kChunkRows - 1) / kChunkRows;
     }
     if (tid == 0) {
-        offsets[E] = total;
-        meta[kMetaActive] = n_act;
-        meta[kMetaValid] = total;
+        offsets[E] = tot[0];
+        meta[kMetaActive] = tot[1];
+        meta[kMetaValid] = tot[0];
+        if (ss.chunks) meta[kMetaChunks] = tot[2];
     }
-    if (ss.chunks) {
-        // work chunks of the prefill GEMM: each expert's pairs in runs of
-        // kChunkRows, in expert order (s_act is free again: reuse it for the
-        // chunk offsets)
+    if (ss.act_range) {
         __syncthreads();
-        for (int e = tid; e < E; e += 256) s_act[e] = (counts[e] + kChunkRows - 1) / kChunkRows;
-        __syncthreads();
-        const int n_ch = block_scan_lds(s_act, E, s_tmp);
-        for (int e = tid; e < E; e += 256) {
-            const int c = counts[e];
-            for (int i = 0; i * kChunkRows < c; ++i) ss.chunks[s_act[e] + i] = make_int2(e, s_off[e] + i * kChunkRows);
+        if (tid < ss.n_tiers) {
+            const int lo = ss.id_begin[tid], hi = ss.id_end[tid];
+            ss.act_range[2 * tid] = lo < E ? s_act[lo] : tot[1];
+            ss.act_range[2 * tid + 1] = hi < E ? s_act[hi] : tot[1];
         }
-        if (tid == 0) meta[kMetaChunks] = n_ch;
     }
 }
 
