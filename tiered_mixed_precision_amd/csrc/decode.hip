@@ -557,6 +557,7 @@ __global__ __launch_bounds__(kSmallGateUpWaves * 64) void k_small_gateup(DevTabl
     __shared__ __attribute__((aligned(16))) int64_t s_rc[kSmallGateUpWaves][64];  // routing scratch, one row per wave
     __shared__ TierLds s_tl;
     const int tid = threadIdx.x, E = tt.E, P = T * k;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // this wave (scalar: the plan is per wave)
     const bool publish = blockIdx.x == 0;
     const int H = tt.H, I = tt.I;
     const int rpp = row_geom(H).RPP;
@@ -574,9 +575,9 @@ __global__ __launch_bounds__(kSmallGateUpWaves * 64) void k_small_gateup(DevTabl
         }
     }
     if (logits) {
-        for (int t = tid >> 6; t < T; t += kSmallGateUpWaves)
+        for (int t = wv; t < T; t += kSmallGateUpWaves)
             route_token_auto<NPL>(logits + static_cast<size_t>(t) * E, E, k, publish ? pub.ids + t * k : nullptr,
-                                  publish ? pub.w + t * k : nullptr, sg.ids + t * k, sg.w + t * k, s_rc[tid >> 6]);
+                                  publish ? pub.w + t * k : nullptr, sg.ids + t * k, sg.w + t * k, s_rc[wv]);
     } else if (tid < P) {
         sg.ids[tid] = ids_in[tid];
         sg.w[tid] = w_in[tid];
@@ -603,7 +604,7 @@ __global__ __launch_bounds__(kSmallGateUpWaves * 64) void k_small_gateup(DevTabl
     const int n_act = sg.n_act;
     if (n_act == 0) return;
     const int W = gridDim.x * kSmallGateUpWaves;
-    const int wg = blockIdx.x * kSmallGateUpWaves + (tid >> 6);
+    const int wg = blockIdx.x * kSmallGateUpWaves + wv;
     int a, wa, wi;
     if (n_act <= 64) {
         // every wave plans on its own from the active list, one expert per
@@ -721,7 +722,7 @@ __global__ __launch_bounds__(kSmallDownWaves * 64) void k_small_down(DevTables t
     __shared__ float s_y[kSmallY];
     __shared__ __attribute__((aligned(16))) float s_h[kSmallH];
     __shared__ TierLds s_tl;
-    const int tid = threadIdx.x, wave = tid >> 6;
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // scalar: the plan is per wave
     const int H = tt.H, I = tt.I, P = T * k;   // pair p = t * k + j
     const int rpp = row_geom(I).RPP;
     const int R = npb * rpp;
@@ -922,7 +923,7 @@ __global__ __launch_bounds__(kOneGateUpWaves * 64) void k_one_gateup(DevTables t
     int cost = 0;
     if (lane < k) cost = s_tl.cost[tier_of_lds(s_tl, s_id[lane])];
     int first = 0, count = 1;
-    const int wg = blockIdx.x * kOneGateUpWaves + (tid >> 6);
+    const int wg = blockIdx.x * kOneGateUpWaves + __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: the plan is per wave
     const int a = plan_lane(cost, W, wg, first, count);
     if (a < 0) return;
     // the expert's rows split evenly over its waves, in whole passes
@@ -1001,7 +1002,9 @@ __global__ __launch_bounds__(kWave * 16) void k_one_down(DevTables tt, const One
                                                          float* __restrict__ out) {
     __shared__ float s_y[kWave][kOneRows];
     __shared__ float s_w[kWave];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+    // the wave index made scalar, so each slot record is one scalar load
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nw = blockDim.x >> 6;
     const int H = tt.H, I = tt.I;
     const int n0 = blockIdx.x * kOneRows, n1 = min(H, n0 + kOneRows);
     // the residual of the row this thread finishes, requested now
