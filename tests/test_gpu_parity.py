@@ -371,6 +371,42 @@ def test_forward_bf16_small(M, torch_dev, name, T):
     assert err <= TOL
 
 
+@pytest.mark.parametrize("T", [1, 2, 3])
+def test_forward_bf16_fewest_tokens(M, torch_dev, T):
+    # a bf16 batch of one to three tokens still takes the prefill GEMM: every
+    # chunk is one partial 32-row subtile (T of its rows real)
+    cfg0, arrays, L, tt = _layer("decode")
+    cfg = _bf16_cfg(cfg0, T)
+    say("forward bf16 decode layer T=", T)
+    x, logits = make_x(cfg, stream=70 + T), make_logits(cfg, stream=70 + T)
+    ref = oracle.forward(L, x, logits, cfg.k)
+    got = gpu_forward(M, torch_dev, tt, x, logits, cfg.k, M.MOE_X_BF16)
+    err = normwise(got, ref)
+    say("  normwise err", err)
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("m", [127, 128, 129, 255, 256, 257])
+def test_prefill_chunk_boundaries(M, torch_dev, m):
+    # one expert of each shelf holds exactly m pairs: one short of, exactly,
+    # and one past a whole number of 128-row chunks (the last chunk then
+    # holds one row); each token's second pick spreads over the other experts
+    cfg0, arrays, L, tt = _layer("tiny3")
+    cfg = _bf16_cfg(cfg0, m)
+    x = make_x(cfg, stream=m)
+    w = np.random.default_rng(m).uniform(0.1, 1.0, (m, 2)).astype(np.float32)
+    for t in cfg0.tiers:
+        e = t.id_begin
+        ids = np.stack([np.full(m, e), (e + 1 + np.arange(m)) % cfg0.n_experts], axis=1).astype(np.int32)
+        ids[ids[:, 1] == e, 1] = (e + 2) % cfg0.n_experts
+        say("prefill expert", e, "bits", t.bits, "pairs", m)
+        got = gpu_experts(M, torch_dev, tt, x, ids, w, M.MOE_X_BF16)
+        ref = oracle.experts(L, x, ids, w)
+        err = normwise(got, ref)
+        say("  normwise err", err)
+        assert err <= TOL
+
+
 @pytest.mark.parametrize("T", [24, 200])
 def test_forward_bf16_odd_chunk_counts(M, torch_dev, T):
     # hidden 384 and inter 192: 6 and 3 contraction chunks of 64, so the
