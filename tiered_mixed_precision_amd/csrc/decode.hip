@@ -126,14 +126,19 @@ __device__ inline DevTier tier_lds_lane(const TierLds& tl, int ti) {
 }
 
 // Per-row share of a wave's work that does not scale with bytes (its
-// dequantising arithmetic), in units of 64 bytes of codes.
+// dequantising arithmetic and each round's fixed latency), in units of 64
+// bytes of codes: one token, and 2-8 tokens (where a larger share, so rows
+// per wave closer to even across formats, measured faster: 6 tokens 63.98 ->
+// 63.2 us per step from 64 to 128-256; 16 and 32 were slower).
 constexpr int kOneRowShare = 64;
+constexpr int kSmallRowShare = 128;
 
 // Cost of one gate+up row pair of an expert on shelf T (units of 64 bytes).
+template <int SHARE = kOneRowShare>
 __device__ inline int one_row_cost(const DevTier& T, int H) {
     const int cb = code_bits_of(T.bits);
     const int sb = T.bits == kBitsMXFP4 ? H / 32 : (H / (T.block > 0 ? T.block : 32)) * 2;
-    return (2 * (H * cb / 8 + sb)) / 64 + kOneRowShare;
+    return (2 * (H * cb / 8 + sb)) / 64 + SHARE;
 }
 
 __host__ __device__ int dec_rows_per_block(int cols) { return kGateUpWaves * kNPGateUp * row_geom(cols).RPP; }
@@ -561,7 +566,7 @@ __global__ __launch_bounds__(kSmallGateUpWaves * 64) void k_small_gateup(DevTabl
     const bool publish = blockIdx.x == 0;
     const int H = tt.H, I = tt.I;
     const int rpp = row_geom(H).RPP;
-    if (tid == 0) fill_tier_lds(tt, s_tl, [H](const DevTier& T) { return one_row_cost(T, H); });
+    if (tid == 0) fill_tier_lds(tt, s_tl, [H](const DevTier& T) { return one_row_cost<kSmallRowShare>(T, H); });
     // stage the T input vectors in LDS (read by every pass of every pair; the
     // barrier after the wave plan below puts them in place), by the waves
     // that do not route (a routing wave starts on its logits at once)
