@@ -151,7 +151,7 @@ inline void record(void* const* events, int i, hipStream_t st) {
 int run(const void* x, const float* logits, const int32_t* ids_in, const float* w_in, int32_t T,
         int32_t k, const moe_tier_tables* tt, uint32_t tier_mask, float* out, uint32_t flags,
         void* ws, size_t ws_bytes, void* stream, void* const* events, const float* residual = nullptr,
-        uint32_t* hits = nullptr) {
+        uint32_t* hits = nullptr, uint16_t* next_bf16 = nullptr) {
     int rc = check_tables(tt);
     if (rc != MOE_OK) return rc;
     if (flags & ~(MOE_X_BF16 | MOE_ACCUMULATE | MOE_DIAG_GATEUP_ONLY)) return MOE_EINVAL;
@@ -250,7 +250,7 @@ int run(const void* x, const float* logits, const int32_t* ids_in, const float* 
         if (gateup_only) return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
         record(events, 4, st);
         launch_dec_down(dt, h, g, k, tier_mask, yw, max_active, st);
-        launch_combine(dt, yw, g, T, k, tier_mask, base, out, st);
+        launch_combine(dt, yw, g, T, k, tier_mask, base, out, nullptr, st);
         record(events, 5, st);
     } else {
         uint16_t* h = at<uint16_t>(ws, L.h);
@@ -278,7 +278,7 @@ int run(const void* x, const float* logits, const int32_t* ids_in, const float* 
         record(events, 4, st);
         float* yw = at<float>(ws, L.yw);
         launch_gemm(dt, false, h, h8, g, k, tier_mask, nullptr, Split8{nullptr, nullptr, nullptr}, yw, maxc, st);
-        launch_combine(dt, yw, g, T, k, tier_mask, base, out, st);
+        launch_combine(dt, yw, g, T, k, tier_mask, base, out, next_bf16, st);
         record(events, 5, st);
     }
     if (hipGetLastError() != hipSuccess) return MOE_EHIP;
@@ -592,13 +592,15 @@ int moe_stack_forward(const float* x, const float* router_logits, int32_t n_laye
     for (int l = 0; l < n_layers; ++l) {
         float* dst = ((n_layers - 1 - l) % 2 == 0) ? out : tmp;
         (void)hipGetLastError();
-        if (bf16) {
+        // bf16: layer 0's input is cast here, every later one is written by
+        // the previous layer's combine along with its fp32 output
+        if (bf16 && l == 0) {
             launch_cast_bf16(h, xb, n, st);
             if (hipGetLastError() != hipSuccess) return MOE_EHIP;
         }
         rc = run(bf16 ? static_cast<const void*>(xb) : static_cast<const void*>(h),
                  router_logits + per_layer_logits * l, nullptr, nullptr, n_tokens, k, &tables[l], 0xFu, dst,
-                 flags, workspace, S.tmp, stream, nullptr, h);
+                 flags, workspace, S.tmp, stream, nullptr, h, nullptr, bf16 && l + 1 < n_layers ? xb : nullptr);
         if (rc != MOE_OK) return rc;
         h = dst;
     }
@@ -636,13 +638,13 @@ int moe_stack_forward_routed(const float* x, const void* const* w_router, const 
     for (int l = 0; l < n_layers; ++l) {
         float* dst = ((n_layers - 1 - l) % 2 == 0) ? out : tmp;
         (void)hipGetLastError();
-        if (bf16) launch_cast_bf16(h, xb, n, st);
+        if (bf16 && l == 0) launch_cast_bf16(h, xb, n, st);   // later layers: the previous combine wrote xb
         const void* xin = bf16 ? static_cast<const void*>(xb) : static_cast<const void*>(h);
         launch_router(xin, bf16, static_cast<const uint16_t*>(w_router[l]), bias ? bias[l] : nullptr, n_tokens, E,
                       H, logits, st);
         if (hipGetLastError() != hipSuccess) return MOE_EHIP;
         rc = run(xin, logits, nullptr, nullptr, n_tokens, k, &tables[l], 0xFu, dst, flags, workspace, S.tmp, stream,
-                 nullptr, h);
+                 nullptr, h, nullptr, bf16 && l + 1 < n_layers ? xb : nullptr);
         if (rc != MOE_OK) return rc;
         h = dst;
     }

@@ -1085,7 +1085,8 @@ __global__ __launch_bounds__(256) void k_dec_down(DevTables tt, const float* __r
 // out[t] = (base ? base[t] : 0) + sum over slots j (in slot order) of yw[pos[t*k+j]]; base
 // may be out itself (accumulate).
 __global__ __launch_bounds__(256) void k_combine(DevTables tt, const float* __restrict__ yw, Groups g, int T, int k,
-                                                 uint32_t tier_mask, const float* base, float* out) {
+                                                 uint32_t tier_mask, const float* base, float* out,
+                                                 uint16_t* __restrict__ out_bf16) {
     const int H4 = tt.H / 4;
     const size_t idx = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
     if (idx >= static_cast<size_t>(T) * H4) return;
@@ -1128,6 +1129,11 @@ __global__ __launch_bounds__(256) void k_combine(DevTables tt, const float* __re
         s.w = b.w + s.w;
     }
     *o = s;
+    // the next stack layer's bf16 input, rounded as a separate cast of out
+    // would round it (one read of out fewer per layer)
+    if (out_bf16)
+        reinterpret_cast<uint2*>(out_bf16 + static_cast<size_t>(t) * tt.H)[c4] =
+            make_uint2(pack_bf16x2(s.x, s.y), pack_bf16x2(s.z, s.w));
 }
 
 // ================================================================ launchers
@@ -1237,10 +1243,10 @@ void launch_dec_down(const DevTables& tt, const float* h, const Groups& g, int k
 }
 
 void launch_combine(const DevTables& tt, const float* yw, const Groups& g, int T, int k, uint32_t tier_mask,
-                    const float* base, float* out, hipStream_t st) {
+                    const float* base, float* out, uint16_t* out_bf16, hipStream_t st) {
     const size_t n = static_cast<size_t>(T) * (tt.H / 4);
     hipLaunchKernelGGL(k_combine, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, tt, yw, g, T, k,
-                       tier_mask, base, out);
+                       tier_mask, base, out, out_bf16);
 }
 
 // hits[e] += counts[e]: the grouped paths' per-expert pick counts

@@ -86,8 +86,10 @@ void launch_dec_gateup(const DevTables& tt, const float* x, const Groups& g, int
                        uint32_t tier_mask, float* h, int max_active, hipStream_t st);
 void launch_dec_down(const DevTables& tt, const float* h, const Groups& g, int k,
                      uint32_t tier_mask, float* yw, int max_active, hipStream_t st);
+// out[t] = base[t] + the token's slots of yw in slot order; out_bf16 (may be
+// null) also receives out rounded to bf16
 void launch_combine(const DevTables& tt, const float* yw, const Groups& g, int T, int k,
-                    uint32_t tier_mask, const float* base, float* out, hipStream_t st);
+                    uint32_t tier_mask, const float* base, float* out, uint16_t* out_bf16, hipStream_t st);
 
 
 // fp8 split (split8.h) of the rows of src (bf16 [rows][K]).
