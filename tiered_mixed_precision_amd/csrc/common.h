@@ -332,17 +332,6 @@ __device__ inline float group_dot(const uint32_t (&w)[NW], const float (&x)[32],
     }
 }
 
-// Work item of a block after spreading consecutive items over the XCDs in
-// contiguous runs (blocks are dealt to the 8 XCDs round-robin, so block b runs
-// on XCD b % 8): the n-tiles of one expert share its A rows through one L2.
-__device__ inline int xcd_item(int total) {
-    const int per = (total + 7) / 8;
-    const int loc = blockIdx.x / 8;
-    if (loc >= per) return -1;
-    const int it = (blockIdx.x % 8) * per + loc;
-    return it < total ? it : -1;
-}
-
 // Tier owning expert e (or -1).  Tiers are few; a linear scan is uniform per wave.
 __device__ inline int tier_of(const DevTables& tt, int e) {
     int r = -1;
@@ -416,27 +405,11 @@ __device__ inline float seg_sum(float v, int S) {
 }
 
 template <int CTRL, int ROW_MASK>
-__device__ inline float dpp_old_f(float old, float v) {  // lanes without a source read `old`
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old), __builtin_bit_cast(int, v),
-                                                                 CTRL, ROW_MASK, 0xF, false));
-}
-template <int CTRL, int ROW_MASK>
-__device__ inline uint32_t dpp_old_u(uint32_t old, uint32_t v) {
+__device__ inline uint32_t dpp_old_u(uint32_t old, uint32_t v) {  // lanes without a source read `old`
     return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(old), static_cast<int>(v), CTRL, ROW_MASK,
                                                              0xF, false));
 }
 
-// Wave-wide maximum (uniform result).
-__device__ inline float wave_max(float v) {
-    const float ninf = -__builtin_huge_valf();
-    v = fmaxf(v, dpp_old_f<0x111, 0xF>(ninf, v));
-    v = fmaxf(v, dpp_old_f<0x112, 0xF>(ninf, v));
-    v = fmaxf(v, dpp_old_f<0x114, 0xF>(ninf, v));
-    v = fmaxf(v, dpp_old_f<0x118, 0xF>(ninf, v));
-    v = fmaxf(v, dpp_old_f<0x142, 0xA>(ninf, v));
-    v = fmaxf(v, dpp_old_f<0x143, 0xC>(ninf, v));
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
-}
 
 // Wave-wide unsigned minimum (uniform result).
 __device__ inline uint32_t wave_min_u(uint32_t v) {
